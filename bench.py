@@ -1,0 +1,280 @@
+"""Benchmark of the attention block on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the hot path over one batch of synthetic input resident in HBM:
+  split-GQA workloads: headnorm(q), headnorm(k), headnorm(v), split-GQA attention;
+  sam_relpos: one rel-pos flash attention.
+The default workload is the long-cache split-GQA canvas step (4 canvases, T=256, ctx=8192,
+nh=32, nkv=8, hd=128).  W untimed steps, then K steps timed with HIP events on the stream the
+kernels run on (torch's current stream), bracketed by device synchronisation.  The dominant
+kernel's launches are timed with their own events inside the timed region.
+
+Prints ONE JSON line: metric/value/unit (algorithmic TFLOP/s of the step, or GB/s for the
+HBM-bound depformer workload), roofline of the dominant kernel against MI355X peaks, and the
+oracle timed on the host cores over a bounded sample of the same workload (a reported
+baseline, not the target).  Parity of this launch configuration is the GPU tests' job.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and HBM GB/s (% of MI355X roofline) per canvas step"
+PEAK_F32_MFMA = 157.3      # TFLOP/s, dense f32 matrix
+PEAK_HBM = 8000.0          # GB/s
+CSRC = os.path.join(ROOT, "gqa_flash_attention_dg_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
+    p = os.path.join(PROFILES, "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def split_counts(c):
+    """Algorithmic flops and bytes of one attention launch and of the three headnorm calls."""
+    if c.causal:
+        pairs = c.B * c.nh * (c.T * c.ctx + c.T * (c.T + 1) // 2)
+    else:
+        pairs = c.B * c.nh * c.T * (c.ctx + c.T)
+    flops = 4 * c.hd * pairs
+    f32 = 4
+    q = c.B * c.T * c.nh * c.hd
+    kv = c.B * c.T * c.nkv * c.hd
+    cache = c.B * c.nkv * c.ctx * c.hd
+    attn_bytes = f32 * (q + 2 * kv + 2 * cache + q)
+    norm_bytes = f32 * 2 * (q + 2 * kv) if c.normed else 0
+    return flops, attn_bytes, norm_bytes
+
+
+class SplitWork:
+    dominant = "attn_split_gqa"
+
+    def __init__(self, name, case):
+        import numpy as np
+        import torch
+        from gqa_flash_attention_dg_amd.canvas import CanvasBlock
+
+        self.name, self.c = name, case
+        d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        c = case
+        self.blk = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, d(c.kc), d(c.vc), d(c.wq),
+                               d(c.wk), eps=c.eps, theta=c.theta, scale=c.scale,
+                               causal=c.causal, rope_cache=c.rope_cache, normed=c.normed)
+        self.q, self.k, self.v = d(c.q), d(c.k), d(c.v)
+        self.out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
+        self.flops, self.attn_bytes, self.norm_bytes = split_counts(c)
+        self.bound = "mfma" if self.flops / self.attn_bytes > 20 else "hbm"
+
+    def config(self):
+        c = self.c
+        return {"workload": c.name, "batch": c.B, "T": c.T, "ctx": c.ctx, "nh": c.nh,
+                "nkv": c.nkv, "hd": c.hd, "scale": c.scale, "causal": bool(c.causal),
+                "step": ("headnorm q,k,v + " if c.normed else "") + "dg_attn_split_gqa"}
+
+    def step(self, ev=None):
+        if self.c.normed:
+            self.blk.norm(self.q, self.k, self.v)
+        if ev:
+            ev[0].record()
+        self.blk.attend(self.q, self.k, self.v, self.out)
+        if ev:
+            ev[1].record()
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on the host: all three headnorms plus attention for a row sample."""
+        import numpy as np
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from helpers import oracle_prepare, oracle_step
+
+        c = self.c
+        cs, kc = oracle_prepare(c)
+        nrows = c.B * c.T
+        per_row = self.flops / nrows
+        probe = np.arange(0, nrows, max(1, nrows // 8), dtype=np.int64)[:8]
+        t0 = time.perf_counter()
+        oracle_step(c, c.q, c.k, c.v, cs, kc, rows=probe)
+        dt = time.perf_counter() - t0
+        n = int(min(nrows, max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
+        rows = np.linspace(0, nrows - 1, n).astype(np.int64)
+        rows = np.unique(rows)
+        t0 = time.perf_counter()
+        oracle_step(c, c.q, c.k, c.v, cs, kc, rows=rows)
+        dt = time.perf_counter() - t0
+        if self.bound == "hbm":
+            value, unit = self.attn_bytes / nrows * rows.size / dt / 1e9, "GB/s"
+        else:
+            value, unit = per_row * rows.size / dt / 1e12, "TFLOP/s"
+        return {"value": value, "unit": unit, "cores": oracle.threads(), "kind": "oracle",
+                "sample": "%d of %d canvas rows (all %d heads) of one step, plus the q/k/v "
+                          "headnorms of the whole step; %.2f s wall" % (rows.size, nrows, c.nh, dt)}
+
+
+class RelposWork:
+    dominant = "relpos_flash"
+
+    def __init__(self, name, case):
+        import numpy as np
+        import torch
+        self.name, self.c = name, case
+        d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.qkv, self.rh, self.rw = d(case.qkv), d(case.rh), d(case.rw)
+        n, W = case.gh * case.gw, case.heads * case.hd
+        self.out = torch.empty((n, W), device="cuda")
+        self.flops = case.heads * n * n * 4 * case.hd + \
+            (case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0)
+        self.attn_bytes = 4 * (n * 3 * W + n * W + (case.gh ** 2 + case.gw ** 2) * case.hd)
+        self.norm_bytes = 0
+        self.bound = "mfma"
+
+    def config(self):
+        c = self.c
+        return {"workload": c.name, "grid": [c.gh, c.gw], "heads": c.heads, "hd": c.hd,
+                "scale": c.scale, "step": "relpos_flash_attn"}
+
+    def _call(self, out):
+        import gqa_flash_attention_dg_amd as dg
+        c = self.c
+        dg.relpos_flash_attn(self.qkv, self.rh, self.rw, out, c.gh, c.gw, c.heads, c.hd, c.scale)
+
+    def step(self, ev=None):
+        if ev:
+            ev[0].record()
+        self._call(self.out)
+        if ev:
+            ev[1].record()
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        import oracle
+        c = self.c
+        n = c.gh * c.gw
+        probe = np.arange(0, n, n // 8 or 1, dtype=np.int64)[:8]
+        t0 = time.perf_counter()
+        oracle.relpos_attn(c.qkv, c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale, rows=probe)
+        dt = time.perf_counter() - t0
+        m = int(min(n, max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
+        rows = np.unique(np.linspace(0, n - 1, m).astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.relpos_attn(c.qkv, c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        return {"value": self.flops / n * rows.size / dt / 1e12, "unit": "TFLOP/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": "%d of %d query rows (all %d heads); %.2f s wall" % (rows.size, n, c.heads, dt)}
+
+
+def make_work(name):
+    from gqa_flash_attention_dg_amd import synth
+    if name == "long_cache":
+        return SplitWork(name, synth.long_cache())
+    if name == "dg_canvas":
+        return SplitWork(name, synth.dg_canvas_steps(1))
+    if name == "tiny":
+        return SplitWork(name, synth.tiny_canvas_step())
+    if name == "depformer":
+        return SplitWork(name, synth.depformer_frames())
+    if name == "sam_relpos":
+        return RelposWork(name, synth.sam_global())
+    raise SystemExit("unknown workload %s" % name)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_cache",
+                    choices=["long_cache", "dg_canvas", "tiny", "depformer", "sam_relpos"])
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle wall time for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_flash_attention_dg_amd as dg
+    if not os.path.exists(dg.LIB_PATH):
+        from gqa_flash_attention_dg_amd import build
+        build.build()
+    dg.lib()
+    torch.cuda.set_device(0)
+
+    work = make_work(args.workload)
+
+    for _ in range(args.warmup):
+        work.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        work.step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+
+    step_bytes = work.attn_bytes + work.norm_bytes
+    if work.bound == "mfma":
+        achieved = work.flops / (kern_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_MFMA, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_F32_MFMA}
+        value, unit = work.flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        achieved = work.attn_bytes / (kern_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM}
+        value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+    roof["kernel"] = work.dominant
+    roof["avg_launch_ms"] = kern_avg
+    roof["traffic"] = measured_traffic(work.dominant, work.name)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = work.cpu_baseline(args.cpu_budget)
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": work.config(),
+        "step_flops": work.flops, "step_hbm_bytes_algorithmic": step_bytes,
+        "step_hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
+        "roofline": roof, "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

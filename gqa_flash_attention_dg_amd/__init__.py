@@ -1,0 +1,148 @@
+"""Python binding of libdgattn.so: the MI355X (gfx950) attention block.
+
+The functions carry the names and the argument order of the C ABI in include/dgattn.h.  They
+only marshal arguments: torch tensors become device pointers, the stream defaults to torch's
+current stream, and every tensor is checked (float32, on the GPU, contiguous, large enough for
+the extents passed) before the C call, so no launch can read or write past a tensor.  All
+computation runs in the library's HIP kernels; there is no CPU path.  A missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdgattn.so")
+
+DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
+DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP = 1, 2, 4
+
+EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_attn_split_gqa_workspace_size",
+           "dg_attn_split_gqa", "relpos_flash_attn", "dg_last_error")
+
+
+class DgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdgattn.so (built by ``python -m gqa_flash_attention_dg_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libdgattn.so is not built (run: python -m "
+                               "gqa_flash_attention_dg_amd.build); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, I, F, D, U, Z = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double,
+                             ctypes.c_uint, ctypes.c_size_t)
+        L.dg_rope_table.argtypes = [vp, I, I, I, D, vp]
+        L.dg_headnorm_rope.argtypes = [vp, vp, vp, I, I, I, I, U, F, vp]
+        L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.dg_attn_split_gqa_workspace_size.restype = Z
+        L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
+        L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp]
+        for name in ("dg_rope_table", "dg_headnorm_rope", "dg_attn_split_gqa",
+                     "relpos_flash_attn"):
+            getattr(L, name).restype = I
+        L.dg_last_error.argtypes = []
+        L.dg_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def dg_last_error() -> str:
+    return lib().dg_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != DG_OK:
+        raise DgError(status, dg_last_error())
+
+
+def _ptr(t, name: str, need: int):
+    """Device pointer of a float32 tensor holding at least `need` elements (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor or None" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < need:
+        raise ValueError("%s holds %d elements, the call needs %d" % (name, t.numel(), need))
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _nonneg(**kw):
+    for k, v in kw.items():
+        if int(v) < 0:
+            # the C side reports this too; refuse here before sizing any buffer check
+            raise DgError(DG_EINVAL, "%s must be >= 0, got %d" % (k, v))
+
+
+def dg_rope_table(cs, pos0: int, T: int, hd: int, theta: float, stream=None) -> None:
+    _nonneg(T=T, hd=hd)
+    _check(lib().dg_rope_table(_ptr(cs, "cs", T * 2 * hd), pos0, T, hd, float(theta),
+                               _stream(stream)))
+
+
+def dg_headnorm_rope(x, w, cs, batch: int, T: int, heads: int, hd: int, flags: int, eps: float,
+                     stream=None) -> None:
+    _nonneg(batch=batch, T=T, heads=heads, hd=hd)
+    need_w = (flags & DG_NORM_WEIGHTED) and not (flags & DG_NORM_SKIP)
+    need_cs = flags & DG_NORM_ROPE
+    _check(lib().dg_headnorm_rope(_ptr(x, "x", batch * T * heads * hd),
+                                  _ptr(w, "w", hd if need_w else 0),
+                                  _ptr(cs, "cs", T * 2 * hd if need_cs else 0),
+                                  batch, T, heads, hd, flags, float(eps), _stream(stream)))
+
+
+def dg_attn_split_gqa_workspace_size(batch: int, T: int, ctx: int, nh: int, nkv: int,
+                                     hd: int) -> int:
+    return int(lib().dg_attn_split_gqa_workspace_size(batch, T, ctx, nh, nkv, hd))
+
+
+def dg_attn_split_gqa(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int, nkv: int,
+                      hd: int, scale: float, causal: int, workspace=None,
+                      workspace_bytes: int = 0, stream=None) -> None:
+    _nonneg(batch=batch, T=T, ctx=ctx, nh=nh, nkv=nkv, hd=hd)
+    nq, nkvc, nc = batch * T * nh * hd, batch * T * nkv * hd, batch * nkv * ctx * hd
+    ws = None
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or \
+                not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        if workspace.numel() * workspace.element_size() < workspace_bytes:
+            raise ValueError("workspace is smaller than workspace_bytes")
+        ws = workspace.data_ptr()
+    _check(lib().dg_attn_split_gqa(_ptr(q, "q", nq), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
+                                   _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq),
+                                   batch, T, ctx, nh, nkv, hd, float(scale), int(causal), ws,
+                                   int(workspace_bytes) if ws else 0, _stream(stream)))
+
+
+def relpos_flash_attn(qkv, rh, rw, out, gh: int, gw: int, heads: int, hd: int, scale: float,
+                      stream=None) -> None:
+    _nonneg(gh=gh, gw=gw, heads=heads, hd=hd)
+    n, W = gh * gw, heads * hd
+    _check(lib().relpos_flash_attn(_ptr(qkv, "qkv", n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
+                                   _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", n * W),
+                                   gh, gw, heads, hd, float(scale), _stream(stream)))

@@ -1,0 +1,177 @@
+// relpos_flash.hip -- relpos_flash_attn: windowless vision attention with the decomposed
+// relative-position bias, flash style, on gfx950.
+//
+// Follows inferencelayer 0.2.8, src/deepencoder_gpu.rs: kernel SAM_SCORES fixes the score,
+//   scale*<q_i,k_j> + <q_i, Rh[qy,ky]> + <q_i, Rw[qx,kx]>  (bias on the unscaled q),
+// kernel DHDW hoists the two bias dot products out of the n^2 loop, `flash_reg_src` runs the
+// online softmax over 64-wide chunks with hd fixed at 64, and `sam_attn_buf` fixes the fused
+// qkv layout (q | k | v per token, heads contiguous) and the scale 1/sqrt(hd).
+//
+// The page writes dh/dw to global [heads, n, gh] / [heads, n, gw] buffers and then looks them
+// up per key.  Here each workgroup computes the bias rows of its own 128 queries into LDS in
+// a prologue (no global round trip, no workspace), then runs the same f32-MFMA flash loop as
+// the split-GQA kernel (flash_core.hpp) with the two table lookups added to each score.
+#include "dg_common.hpp"
+#include "flash_core.hpp"
+
+namespace {
+
+using dgk::f32x16;
+constexpr int HD = 64;
+constexpr int kWaves = 4;
+constexpr int kBlockQ = kWaves * dgk::kQuery;
+constexpr int kMaxGrid = 64;                 // gh, gw <= 64
+constexpr int kTabStride = 2 * kMaxGrid + 1; // dh | dw per query, padded against bank conflicts
+
+struct RelArgs {
+    const float* qkv;
+    const float* rh;
+    const float* rw;
+    float* out;
+    int n, gh, gw, heads, W;
+    int qblocks, nblocks;
+    float qmul;  // scale * log2(e)
+};
+
+__device__ inline int xcd_remap(int bid, int n) {
+    if ((n & 7) != 0) return bid;
+    return (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
+__global__ void __launch_bounds__(256) relpos_flash_kernel(RelArgs a) {
+    using TL = dgk::Tile<HD>;
+    __shared__ __attribute__((aligned(16))) float ks[dgk::kKeys * TL::kStride];
+    __shared__ __attribute__((aligned(16))) float vs[dgk::kKeys * HD];
+    __shared__ float tab[kWaves * dgk::kQuery * kTabStride];
+
+    const int lid = xcd_remap(blockIdx.x, a.nblocks);
+    const int qb = lid % a.qblocks;
+    const int head = lid / a.qblocks;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const size_t rs = (size_t)3 * a.W;  // qkv row stride
+
+    const int qi = qb * kBlockQ + wave * dgk::kQuery + l32;
+    const bool valid = qi < a.n;
+    const float* qrow = a.qkv + (size_t)(valid ? qi : 0) * rs + head * HD;
+    const bool wave_active = qb * kBlockQ + wave * dgk::kQuery < a.n;
+    const bool bias = a.rh != nullptr;
+    float* mytab = tab + (wave * dgk::kQuery + l32) * kTabStride;
+
+    // Prologue: this query's bias rows dh[ky] = <q, Rh[qy,ky]>, dw[kx] = <q, Rw[qx,kx]> (log2
+    // units); the two lane halves split the ky / kx range.
+    if (bias && wave_active) {
+        float qf[HD];
+#pragma unroll
+        for (int c = 0; c < HD; c += 4) {
+            const float4 t = valid ? *reinterpret_cast<const float4*>(qrow + c)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            qf[c] = t.x; qf[c + 1] = t.y; qf[c + 2] = t.z; qf[c + 3] = t.w;
+        }
+        const int qy = valid ? qi / a.gw : 0, qx = valid ? qi % a.gw : 0;
+        for (int ky = half; ky < a.gh; ky += 2) {
+            const float* tr = a.rh + ((size_t)qy * a.gh + ky) * HD;
+            float d = 0.0f;
+#pragma unroll
+            for (int c = 0; c < HD; c += 4) {
+                const float4 t = *reinterpret_cast<const float4*>(tr + c);
+                d += qf[c] * t.x + qf[c + 1] * t.y + qf[c + 2] * t.z + qf[c + 3] * t.w;
+            }
+            mytab[ky] = d * dgk::kLog2e;
+        }
+        for (int kx = half; kx < a.gw; kx += 2) {
+            const float* tr = a.rw + ((size_t)qx * a.gw + kx) * HD;
+            float d = 0.0f;
+#pragma unroll
+            for (int c = 0; c < HD; c += 4) {
+                const float4 t = *reinterpret_cast<const float4*>(tr + c);
+                d += qf[c] * t.x + qf[c + 1] * t.y + qf[c + 2] * t.z + qf[c + 3] * t.w;
+            }
+            mytab[kMaxGrid + kx] = d * dgk::kLog2e;
+        }
+    }
+
+    float qreg[HD / 2];
+    dgk::load_q<HD>(qrow, valid, half, a.qmul, qreg);
+    f32x16 o[TL::kVGroups];
+#pragma unroll
+    for (int t = 0; t < TL::kVGroups; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;
+
+    const float* kbase = a.qkv + a.W + head * HD;
+    const float* vbase = a.qkv + 2 * (size_t)a.W + head * HD;
+    constexpr int kVec = HD / 4;
+    constexpr int kPerThread = dgk::kKeys * kVec / 256;
+
+    for (int t0 = 0; t0 < a.n; t0 += dgk::kKeys) {
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kPerThread; ++it) {
+            const int f = tid + 256 * it;
+            const int key = f / kVec;
+            const int c = (f % kVec) * 4;
+            const int j = t0 + key;
+            float4 kf = make_float4(0.f, 0.f, 0.f, 0.f), vf = kf;
+            if (j < a.n) {
+                kf = *reinterpret_cast<const float4*>(kbase + (size_t)j * rs + c);
+                vf = *reinterpret_cast<const float4*>(vbase + (size_t)j * rs + c);
+            }
+            dgk::stage_k<HD>(ks, key, c, kf);
+            dgk::stage_v<HD>(vs, key, c, vf);
+        }
+        __syncthreads();
+        if (wave_active) {
+            f32x16 s = dgk::scores<HD>(ks, l32, half, qreg);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = t0 + dgk::key_of(r, half);
+                if (j >= a.n) {
+                    s[r] = -INFINITY;
+                } else if (bias) {
+                    s[r] += mytab[j / a.gw] + mytab[kMaxGrid + j % a.gw];
+                }
+            }
+            dgk::softmax_update<HD>(s, m, lsum, o);
+            dgk::accumulate_pv<HD>(vs, l32, half, s, o);
+        }
+    }
+    dgk::store_out<HD>(a.out + (size_t)(valid ? qi : 0) * a.W + head * HD, valid, half, lsum, o);
+}
+
+}  // namespace
+
+extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out,
+                                 int gh, int gw, int heads, int hd, float scale, void* stream) {
+    const char* fn = "relpos_flash_attn";
+    if (gh < 0 || gw < 0 || heads < 0)
+        return dg::fail(DG_EINVAL, "%s: negative size (gh %d, gw %d, heads %d)", fn, gh, gw, heads);
+    if (hd < 1) return dg::fail(DG_EINVAL, "%s: hd must be >= 1, got %d", fn, hd);
+    if (hd != HD) return dg::fail(DG_EUNSUPPORTED, "%s: hd %d not supported (64 only)", fn, hd);
+    if ((rh == nullptr) != (rw == nullptr))
+        return dg::fail(DG_EINVAL, "%s: rh and rw must both be given or both be NULL", fn);
+    if (gh > kMaxGrid || gw > kMaxGrid)
+        return dg::fail(DG_EUNSUPPORTED, "%s: grid %dx%d exceeds %d per side", fn, gh, gw, kMaxGrid);
+    if (!std::isfinite(scale)) return dg::fail(DG_EINVAL, "%s: scale is not finite", fn);
+    const long long n = (long long)gh * gw;
+    if (n == 0 || heads == 0) return dg::ok();
+    if (!qkv || !out) return dg::fail(DG_EINVAL, "%s: qkv and out must be non-NULL", fn);
+    const size_t W = (size_t)heads * HD;
+    const dg::Span so(out, (size_t)n * W * 4);
+    if (so.overlaps(dg::Span(qkv, (size_t)n * 3 * W * 4)) ||
+        so.overlaps(dg::Span(rh, (size_t)gh * gh * HD * 4)) ||
+        so.overlaps(dg::Span(rw, (size_t)gw * gw * HD * 4)))
+        return dg::fail(DG_EINVAL, "%s: out overlaps an input", fn);
+    const long long qblocks = (n + kBlockQ - 1) / kBlockQ;
+    if (qblocks * heads > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
+    RelArgs a;
+    a.qkv = qkv; a.rh = rh; a.rw = rw; a.out = out;
+    a.n = (int)n; a.gh = gh; a.gw = gw; a.heads = heads; a.W = (int)W;
+    a.qblocks = (int)qblocks;
+    a.nblocks = (int)(qblocks * heads);
+    a.qmul = scale * dgk::kLog2e;
+    hipLaunchKernelGGL(relpos_flash_kernel, dim3((unsigned)a.nblocks), dim3(256), 0,
+                       (hipStream_t)stream, a);
+    return dg::launch_status(fn);
+}

@@ -1,0 +1,151 @@
+/*
+ * dgattn.h -- C ABI of the MI355X (gfx950) attention-block library libdgattn.so.
+ *
+ * The operations follow three source pages of the `inferencelayer` crate on docs.rs:
+ *   - inferencelayer 0.2.3, src/diffusion_gemma_gpu.rs: kernels DG_HEADNORM_ROPE and DG_ATTN,
+ *     and the rope-table, headnorm and attention dispatches of `canvas_forward`;
+ *   - inferencelayer 0.2.8, src/deepencoder_gpu.rs: kernels SAM_SCORES, DHDW and the
+ *     register flash generator `flash_reg_src`, driven by `sam_attn_buf`;
+ *   - inferencelayer 0.2.4, src/moshi_gpu.rs: kernels COPY_KV and DEP_ATTN (causal
+ *     within-frame attention with a 0.125 scale).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to contiguous, row-major float32 data that
+ *     the caller allocated and owns.  The library allocates nothing, keeps no pointer after
+ *     it returns, and never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  Work is
+ *     enqueued on it asynchronously; nothing synchronises inside the library.  The caller
+ *     keeps every buffer alive until the stream has passed the launch.
+ *   - Every argument is validated on the host before any HIP call.  On failure the call
+ *     returns a negative status, launches nothing, writes nothing, and records a message
+ *     that dg_last_error() returns (per calling thread).  The library never aborts or prints.
+ *   - A call whose output is empty (T == 0, batch == 0, n == 0) returns DG_OK and launches
+ *     nothing.
+ *   - Calls on one stream run in order; calls that write the same buffer from different
+ *     streams race.
+ */
+#ifndef DGATTN_H
+#define DGATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DG_OK = 0,
+    DG_EINVAL = -1,        /* a malformed argument (negative size, NULL pointer, overlap) */
+    DG_EUNSUPPORTED = -2,  /* a well-formed argument outside what the kernels implement */
+    DG_ELAUNCH = -3        /* the HIP runtime rejected the launch (message holds its error) */
+};
+
+/* Flag bits of dg_headnorm_rope.  Bits 0 and 1 are the page's own flag bits of
+ * DG_HEADNORM_ROPE (bit0 weighted, bit1 rope).  Bit 2 is an addition: skip the norm and
+ * the weight, and only rotate -- used to rope a cache written at known positions. */
+#define DG_NORM_WEIGHTED 1u
+#define DG_NORM_ROPE 2u
+#define DG_NORM_SKIP 4u
+
+/*
+ * dg_rope_table -- cos|sin table for the NeoX rotate-half rope.
+ * Follows `canvas_forward` in diffusion_gemma_gpu.rs (rope tables per layer type: one row per
+ * canvas token at absolute position seq_len + t).  The page's table generator is not shown;
+ * the frequencies are the NeoX/HF ones: pair i (0 <= i < hd/2) turns theta^(-2i/hd) radians
+ * per position and both halves of a row carry the same angles.
+ *   cs     out  [T, 2*hd]: cs[t, c] = cos((pos0+t) * f(c mod hd/2)), cs[t, hd+c] = sin(...).
+ *               Evaluated in double precision and rounded once to float.
+ *   pos0        absolute position of row 0 (>= 0);  T >= 0 rows;  hd even, 2 <= hd <= 1024.
+ *   theta       rope base, > 0 (10000 for the configurations here).
+ * Errors: DG_EINVAL for a negative pos0/T, odd or out-of-range hd, theta <= 0, NULL cs
+ * with T > 0.
+ */
+int dg_rope_table(float* cs, int pos0, int T, int hd, double theta, void* stream);
+
+/*
+ * dg_headnorm_rope -- per-(token, head) RMSNorm, optional weight, optional NeoX rope, IN PLACE.
+ * Follows kernel DG_HEADNORM_ROPE in diffusion_gemma_gpu.rs and its three dispatches in
+ * `canvas_forward` (q: weighted + rope; k: weighted + rope; v: flags 0, the weightless,
+ * un-roped v-norm).
+ *   x      in/out [batch, T, heads*hd].  For every (b, t, head):
+ *                 inv = 1/sqrt(sum_c x[c]^2 / hd + eps);  y[c] = x[c]*inv  (skipped with SKIP)
+ *                 WEIGHTED: y[c] *= w[c]                                   (skipped with SKIP)
+ *                 ROPE: x[c] = y[c]*cs[t,c] + r[c]*cs[t,hd+c],
+ *                       r[c] = -y[c+hd/2] for c < hd/2, y[c-hd/2] otherwise
+ *                 otherwise x[c] = y[c].
+ *   w      [hd]; read iff WEIGHTED is set without SKIP (may be NULL otherwise).
+ *   cs     [T, 2*hd] table from dg_rope_table (shared by all batch entries); read iff ROPE.
+ *   flags  DG_NORM_* bits;  eps >= 0.
+ * Errors: DG_EINVAL for negative sizes, unknown flag bits, a needed pointer that is NULL,
+ * odd hd with ROPE, w or cs overlapping x, hd < 1, a negative or non-finite eps;
+ * DG_EUNSUPPORTED for hd > 128 (the page's one-thread-per-element workgroup of 128).
+ */
+int dg_headnorm_rope(float* x, const float* w, const float* cs, int batch, int T, int heads,
+                     int hd, unsigned flags, float eps, void* stream);
+
+/*
+ * dg_attn_split_gqa_workspace_size -- bytes of scratch that dg_attn_split_gqa can use to split
+ * the key range of one call across more workgroups (partial results and their combine).
+ * Returns 0 when the shape gains nothing from a split.  Arguments as for dg_attn_split_gqa;
+ * returns 0 for any argument dg_attn_split_gqa would reject.
+ */
+size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int nkv, int hd);
+
+/*
+ * dg_attn_split_gqa -- GQA flash attention over the split key/value set [cache | canvas].
+ * Follows kernel DG_ATTN in diffusion_gemma_gpu.rs (online softmax over ctx cache keys then T
+ * canvas keys, kv head = q head / (nh/nkv), cache layout [nkv, ctx, hd], canvas layout
+ * [T, nkv*hd], scaling 1.0 because the qk norms carry the scale) and, for `causal` and
+ * `scale`, kernel DEP_ATTN in moshi_gpu.rs (the step-s query sees slots 0..s, scale 0.125).
+ *   q    [batch, T, nh*hd]        queries (already normed/roped by the caller)
+ *   kc   [batch, nkv, ctx, hd]    cache keys;   may be NULL iff ctx == 0
+ *   vc   [batch, nkv, ctx, hd]    cache values; may be NULL iff ctx == 0
+ *   k    [batch, T, nkv*hd]       canvas keys
+ *   v    [batch, T, nkv*hd]       canvas values
+ *   out  [batch, T, nh*hd]        written; must not overlap any input
+ *   For every (b, i, h), with kv = h / (nh/nkv) and keys j in [0, ctx+T):
+ *     K_j = kc[b,kv,j] for j < ctx, k[b,j-ctx,kv] otherwise (V likewise),
+ *     s_j = scale * <q[b,i,h], K_j>, skipping canvas keys with j-ctx > i when causal != 0,
+ *     out[b,i,h] = sum_j softmax(s)_j V_j.
+ *   scale      finite float (1.0f for DiffusionGemma, 0.125f for the depformer).
+ *   causal     0 = bidirectional (the page); 1 = canvas row i sees canvas keys 0..i.
+ *   workspace  optional device scratch of at least dg_attn_split_gqa_workspace_size() bytes,
+ *              used for a split of the key range; NULL/0 runs unsplit (same results up to
+ *              rounding).  Must not overlap any input or `out`.
+ * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
+ * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, or a workspace
+ * pointer with workspace_bytes too small; DG_EUNSUPPORTED for hd not 64 or 128.
+ */
+int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
+                      const float* v, float* out, int batch, int T, int ctx, int nh, int nkv,
+                      int hd, float scale, int causal, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * relpos_flash_attn -- windowless vision attention with the decomposed relative-position bias,
+ * flash style (no [heads, n, n] buffer).  Follows deepencoder_gpu.rs: kernel SAM_SCORES
+ * (score definition), kernel DHDW (the bias dot products hoisted out of the n^2 loop), the
+ * register flash `flash_reg_src` with bias, and `sam_attn_buf` (fused qkv layout, scale).
+ *   qkv  [gh*gw, 3*heads*hd]: each row is q | k | v, each heads*hd wide, head h at h*hd.
+ *   rh   [gh, gh, hd] expanded height table, or NULL
+ *   rw   [gw, gw, hd] expanded width table, or NULL (both NULL = no bias; one NULL = error)
+ *   out  [gh*gw, heads*hd]; must not overlap any input
+ *   Token i is at grid cell (qy, qx) = (i / gw, i % gw).  For every head and query i:
+ *     s_j = scale*<q_i, k_j> + <q_i, rh[qy, ky_j]> + <q_i, rw[qx, kx_j]>  (bias on unscaled q)
+ *     out[i, h*hd:(h+1)*hd] = sum_j softmax(s)_j v_j
+ *   scale      finite float (1/sqrt(hd) in the page's SAM block).
+ * Errors: DG_EINVAL for gh, gw or heads < 0, exactly one of rh/rw NULL, a NULL qkv/out with
+ * n > 0, a non-finite scale, overlapping buffers; DG_EUNSUPPORTED for hd != 64 (the page's
+ * kernel fixes hd to its 64-wide workgroup) or gh or gw above 64.
+ */
+int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out, int gh,
+                      int gw, int heads, int hd, float scale, void* stream);
+
+/* Message for the last nonzero status returned on the calling thread ("" if none). */
+const char* dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGATTN_H */

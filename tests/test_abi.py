@@ -1,0 +1,122 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/dgattn.h declares, and reject malformed
+arguments with the documented status before any HIP call.  Only argument combinations that
+fail validation, or describe an empty output, are passed here: those return before touching
+the HIP runtime, so they are safe on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_flash_attention_dg_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgattn.h")
+FAKE = 0x10000000  # a non-NULL address that is never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dg.LIB_PATH):
+        from gqa_flash_attention_dg_amd import build
+        build.build()
+    return dg.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(dg.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _err(L):
+    return L.dg_last_error().decode()
+
+
+def test_headnorm_validation(L):
+    f = L.dg_headnorm_rope
+    assert f(FAKE, FAKE, FAKE, -1, 4, 2, 64, 3, 1e-6, None) == dg.DG_EINVAL
+    assert "negative" in _err(L)
+    assert f(FAKE, FAKE, FAKE, 1, 4, 2, 0, 3, 1e-6, None) == dg.DG_EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, 4, 2, 256, 3, 1e-6, None) == dg.DG_EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 4, 2, 64, 8, 1e-6, None) == dg.DG_EINVAL          # bad flag
+    assert f(FAKE, FAKE, FAKE, 1, 4, 2, 63, 2, 1e-6, None) == dg.DG_EINVAL          # odd + rope
+    assert f(FAKE, None, FAKE, 1, 4, 2, 64, 3, 1e-6, None) == dg.DG_EINVAL          # w NULL
+    assert f(FAKE, FAKE, None, 1, 4, 2, 64, 3, 1e-6, None) == dg.DG_EINVAL          # cs NULL
+    assert f(None, FAKE, FAKE, 1, 4, 2, 64, 3, 1e-6, None) == dg.DG_EINVAL          # x NULL
+    assert f(FAKE, FAKE, FAKE, 1, 4, 2, 64, 3, -1.0, None) == dg.DG_EINVAL          # eps < 0
+    assert f(FAKE, FAKE + 64, FAKE, 1, 4, 2, 64, 1, 1e-6, None) == dg.DG_EINVAL     # w inside x
+    assert "overlaps" in _err(L)
+    # empty outputs are a successful no-op
+    assert f(None, None, None, 0, 4, 2, 64, 3, 1e-6, None) == dg.DG_OK
+    assert f(None, None, None, 3, 0, 2, 64, 3, 1e-6, None) == dg.DG_OK
+    assert _err(L) == ""
+
+
+def test_rope_table_validation(L):
+    f = L.dg_rope_table
+    assert f(FAKE, -1, 4, 64, 1e4, None) == dg.DG_EINVAL
+    assert f(FAKE, 0, 4, 63, 1e4, None) == dg.DG_EINVAL
+    assert f(FAKE, 0, 4, 64, 0.0, None) == dg.DG_EINVAL
+    assert f(None, 0, 4, 64, 1e4, None) == dg.DG_EINVAL
+    assert f(None, 0, 0, 64, 1e4, None) == dg.DG_OK
+
+
+def test_attn_split_validation(L):
+    f = L.dg_attn_split_gqa
+    args = lambda **kw: [kw.get(k, d) for k, d in (
+        ("q", FAKE), ("kc", FAKE + (1 << 24)), ("vc", FAKE + (2 << 24)), ("k", FAKE + (3 << 24)),
+        ("v", FAKE + (4 << 24)), ("out", FAKE + (5 << 24)), ("batch", 1), ("T", 16),
+        ("ctx", 32), ("nh", 4), ("nkv", 2), ("hd", 64), ("scale", 1.0), ("causal", 0),
+        ("ws", None), ("wsb", 0), ("stream", None))]
+    assert f(*args(nh=5)) == dg.DG_EINVAL                   # nh % nkv != 0
+    assert "multiple" in _err(L)
+    assert f(*args(nkv=0)) == dg.DG_EINVAL
+    assert f(*args(T=-1)) == dg.DG_EINVAL
+    assert f(*args(hd=96)) == dg.DG_EUNSUPPORTED
+    assert f(*args(hd=0)) == dg.DG_EINVAL
+    assert f(*args(scale=float("nan"))) == dg.DG_EINVAL
+    assert f(*args(causal=2)) == dg.DG_EINVAL
+    assert f(*args(kc=None)) == dg.DG_EINVAL                # ctx > 0 needs a cache
+    assert f(*args(q=None)) == dg.DG_EINVAL
+    assert f(*args(out=FAKE + 16)) == dg.DG_EINVAL          # out overlaps q
+    assert "overlaps" in _err(L)
+    assert f(*args(out=FAKE + (3 << 24) + 4)) == dg.DG_EINVAL  # out overlaps canvas k
+    assert f(*args(T=0)) == dg.DG_OK                        # zero canvas: no-op
+    assert f(*args(batch=0)) == dg.DG_OK
+    assert L.dg_attn_split_gqa_workspace_size(1, 16, 32, 5, 2, 64) == 0
+
+
+def test_relpos_validation(L):
+    f = L.relpos_flash_attn
+    base = dict(qkv=FAKE, rh=FAKE + (1 << 26), rw=FAKE + (2 << 26), out=FAKE + (3 << 26),
+                gh=8, gw=8, heads=2, hd=64, scale=0.125, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(hd=32) == dg.DG_EUNSUPPORTED
+    assert call(gh=65) == dg.DG_EUNSUPPORTED
+    assert call(rh=None) == dg.DG_EINVAL                   # exactly one table
+    assert call(gw=-1) == dg.DG_EINVAL
+    assert call(scale=float("inf")) == dg.DG_EINVAL
+    assert call(out=FAKE + 4) == dg.DG_EINVAL              # overlaps qkv
+    assert call(qkv=None) == dg.DG_EINVAL
+    assert call(gh=0) == dg.DG_OK
+    assert call(heads=0) == dg.DG_OK
+
+
+def test_binding_refuses_bad_tensors_before_the_call():
+    import torch
+    x = torch.zeros(8)
+    with pytest.raises(ValueError):
+        dg._ptr(x, "x", 4)                                  # CPU tensor
+    with pytest.raises(TypeError):
+        dg._ptr(torch.zeros(8, dtype=torch.float64), "x", 4)

@@ -1,0 +1,190 @@
+"""GPU parity: every entry point of libdgattn.so, called through the C ABI, against the oracle.
+
+Bar: |gpu - oracle| <= 2e-4 + 1e-4*|oracle| on every compared element (float32).  Small shapes
+compare every element and span several key tiles, several workgroups and ragged tails; the full
+workload shapes compare sampled rows (all heads, all hd) that the oracle computes one by one,
+in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gqa_flash_attention_dg_amd as dg
+from gqa_flash_attention_dg_amd import synth
+from gqa_flash_attention_dg_amd.canvas import CanvasBlock
+
+from helpers import assert_parity, oracle_prepare, oracle_step, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dg.lib()  # the HIP library must be there; no fallback exists
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- rope + headnorm
+
+@pytest.mark.parametrize("pos0,T,hd", [(0, 1, 2), (32, 16, 64), (1024, 256, 128), (8192, 300, 128),
+                                       (5, 7, 6), (0, 3, 1024)])
+def test_rope_table(pos0, T, hd):
+    cs = torch.empty((T, 2 * hd), device="cuda")
+    dg.dg_rope_table(cs, pos0, T, hd, 10000.0)
+    ref = oracle.rope_table(pos0, T, hd, 10000.0)
+    got = host(cs)
+    assert np.max(np.abs(got - ref)) <= 1.2e-7   # one float32 rounding of a value <= 1
+
+
+@pytest.mark.parametrize("B,T,heads,hd", [(1, 16, 4, 64), (2, 37, 3, 128), (1, 5, 2, 6),
+                                          (3, 9, 5, 100), (1, 1, 1, 2), (2, 11, 7, 4)])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 6])
+def test_headnorm_rope(B, T, heads, hd, flags):
+    rng = np.random.default_rng(B * 1000 + T * 10 + hd + flags)
+    x = (rng.standard_normal((B, T, heads * hd)) * 2.0).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    cs = oracle.rope_table(17, T, hd, 10000.0)
+    ref = oracle.headnorm_rope(x, w, cs, heads, hd, flags, 1e-6)
+    xd = dev(x)
+    dg.dg_headnorm_rope(xd, dev(w) if flags & 1 else None, dev(cs) if flags & 2 else None,
+                        B, T, heads, hd, flags, 1e-6)
+    assert_parity(host(xd), ref, "headnorm flags=%d" % flags)
+
+
+# ----------------------------------------------------------------------------- split-GQA
+
+SPLIT_SHAPES = [
+    # B, T, ctx, nh, nkv, hd, scale, causal
+    (1, 16, 32, 4, 2, 64, 1.0, False),     # the tiny canvas shape
+    (2, 37, 70, 8, 2, 128, 1.0, False),    # ragged tiles, two canvases
+    (1, 33, 33, 4, 4, 128, 0.7, False),    # MHA, seam inside a tile
+    (1, 1, 0, 2, 1, 64, 1.0, False),       # one key
+    (1, 200, 0, 8, 1, 64, 0.3, False),     # empty cache, G = 8
+    (3, 8, 0, 16, 16, 64, 0.125, True),    # causal frames
+    (2, 45, 19, 6, 3, 128, 0.5, True),     # causal after a cache
+    (1, 130, 300, 16, 8, 128, 1.0, False), # several workgroups per kv head
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "B%d_T%d_ctx%d_h%d_kv%d_hd%d_c%d" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], s[7]))
+def test_attn_split_small(shape):
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=T + ctx, scale=scale, causal=causal)
+    ref = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, nh, nkv, hd, scale, causal)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    dg.dg_attn_split_gqa(dev(c.q), dev(c.kc), dev(c.vc), dev(c.k), dev(c.v), out, B, T, ctx,
+                         nh, nkv, hd, scale, int(causal))
+    assert_parity(host(out), ref, "split %s" % (shape,))
+
+
+def test_attn_split_zero_canvas_is_noop_and_nonfinite_free():
+    out = torch.full((1, 4, 128), 7.0, device="cuda")
+    q = torch.zeros(1, 4, 128, device="cuda")
+    dg.dg_attn_split_gqa(q, None, None, q, q, out, 1, 0, 0, 2, 1, 64, 1.0, 0)
+    assert np.all(host(out) == 7.0)
+
+
+def test_attn_split_on_a_side_stream():
+    c = synth.split_case(1, 40, 50, 4, 2, 128, seed=5)
+    ref = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, 4, 2, 128)
+    s = torch.cuda.Stream()
+    tensors = [dev(a) for a in (c.q, c.kc, c.vc, c.k, c.v)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = torch.empty((1, 40, 512), device="cuda")
+        dg.dg_attn_split_gqa(*tensors, out, 1, 40, 50, 4, 2, 128, 1.0, 0)
+    s.synchronize()
+    assert_parity(out.cpu().numpy(), ref, "side stream")
+
+
+# ----------------------------------------------------------------------------- full workloads
+
+def run_block(case, steps=None):
+    """Set up a CanvasBlock from a synthetic case and run the given (q, k, v) steps."""
+    blk = CanvasBlock(case.B, case.T, case.ctx, case.nh, case.nkv, case.hd, dev(case.kc),
+                      dev(case.vc), dev(case.wq), dev(case.wk), eps=case.eps, theta=case.theta,
+                      scale=case.scale, causal=case.causal, rope_cache=case.rope_cache,
+                      normed=case.normed)
+    outs = []
+    for st in steps or [{"q": case.q, "k": case.k, "v": case.v}]:
+        out = torch.empty((case.B, case.T, case.nh * case.hd), device="cuda")
+        blk.step(dev(st["q"]), dev(st["k"]), dev(st["v"]), out)
+        outs.append(host(out))
+    return blk, outs
+
+
+def test_tiny_canvas_step_every_element():
+    c = synth.tiny_canvas_step()
+    _, (got,) = run_block(c)
+    cs, kc = oracle_prepare(c)
+    ref, _ = oracle_step(c, c.q, c.k, c.v, cs, kc)
+    assert_parity(got, ref, "tiny canvas step")
+
+
+def test_dg_canvas_48_steps():
+    c = synth.dg_canvas_steps(48)
+    _, outs = run_block(c, c.steps)
+    cs, kc = oracle_prepare(c)
+    for s, st in enumerate(c.steps):
+        rows = None if s == 0 else sample_rows(c.B * c.T, 12, seed=s)
+        ref, _ = oracle_step(c, st["q"], st["k"], st["v"], cs, kc, rows=rows)
+        if rows is None:
+            assert_parity(outs[s], ref, "dg step 0")
+        else:
+            flat = lambda a: a.reshape(c.B * c.T, -1)[rows]
+            assert_parity(flat(outs[s]), flat(ref), "dg step %d" % s)
+
+
+def test_long_cache_sampled_rows():
+    c = synth.long_cache()
+    _, (got,) = run_block(c)
+    cs, kc = oracle_prepare(c)
+    rows = sample_rows(c.B * c.T, 40, seed=3)
+    ref, _ = oracle_step(c, c.q, c.k, c.v, cs, kc, rows=rows)
+    flat = lambda a: a.reshape(c.B * c.T, -1)[rows]
+    assert_parity(flat(got), flat(ref), "long cache")
+
+
+def test_depformer_frames_every_element():
+    c = synth.depformer_frames()
+    _, (got,) = run_block(c)
+    ref = oracle.attn_split_gqa(c.q, None, None, c.k, c.v, 16, 16, 64, 0.125, True)
+    assert_parity(got, ref, "depformer frames")
+    assert np.array_equal(got[:, 0], c.v[:, 0]) or \
+        np.max(np.abs(got[:, 0] - c.v[:, 0])) < 1e-6   # row 0 sees only key 0
+
+
+# ----------------------------------------------------------------------------- rel-pos
+
+@pytest.mark.parametrize("gh,gw,heads,bias", [(3, 5, 2, True), (8, 8, 3, True), (4, 64, 1, True),
+                                              (64, 4, 2, True), (1, 1, 1, True), (9, 7, 2, False),
+                                              (16, 16, 12, True)])
+def test_relpos_small(gh, gw, heads, bias):
+    c = synth.relpos_case(gh, gw, heads, 64, seed=gh * 100 + gw, bias=bias, table_std=0.3)
+    ref = oracle.relpos_attn(c.qkv, c.rh, c.rw, gh, gw, heads, 64, c.scale)
+    out = torch.full((gh * gw, heads * 64), float("nan"), device="cuda")
+    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, gh, gw, heads, 64, c.scale)
+    assert_parity(host(out), ref, "relpos %dx%d" % (gh, gw))
+
+
+def test_sam_global_sampled_rows():
+    c = synth.sam_global()
+    out = torch.empty((4096, 768), device="cuda")
+    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, 64, 64, 12, 64, c.scale)
+    got = host(out)
+    rows = sample_rows(4096, 48, seed=9)
+    rows = np.unique(np.concatenate([rows, [63, 64, 4032, 2047]])).astype(np.int64)
+    ref = oracle.relpos_attn(c.qkv, c.rh, c.rw, 64, 64, 12, 64, c.scale, rows=rows)
+    assert_parity(got[rows], ref[rows], "sam global")
