@@ -187,6 +187,34 @@ class RelposWork:
                 "sample": "%d of %d query rows (all %d heads); %.2f s wall" % (rows.size, n, c.heads, dt)}
 
 
+class CopyWork:
+    """Device-to-device copy of a 512 MiB buffer: calibrates the HBM byte counters and gives
+    the achievable copy bandwidth.  Not part of the attention block."""
+    dominant = "hbm_copy"
+
+    def __init__(self, name, nbytes=512 << 20):
+        import torch
+        self.name = name
+        self.src = torch.ones(nbytes // 4, device="cuda")
+        self.dst = torch.empty_like(self.src)
+        self.flops, self.attn_bytes, self.norm_bytes = 0, 2 * nbytes, 0
+        self.bound = "hbm"
+
+    def config(self):
+        return {"workload": "hbm_copy_512MiB", "bytes_read": self.attn_bytes // 2,
+                "bytes_written": self.attn_bytes // 2, "step": "torch copy_"}
+
+    def step(self, ev=None):
+        if ev:
+            ev[0].record()
+        self.dst.copy_(self.src)
+        if ev:
+            ev[1].record()
+
+    def cpu_baseline(self, budget_s):
+        return None
+
+
 def make_work(name):
     from gqa_flash_attention_dg_amd import synth
     if name == "long_cache":
@@ -199,6 +227,8 @@ def make_work(name):
         return SplitWork(name, synth.depformer_frames())
     if name == "sam_relpos":
         return RelposWork(name, synth.sam_global())
+    if name == "hbm_copy":
+        return CopyWork(name)
     raise SystemExit("unknown workload %s" % name)
 
 
@@ -208,7 +238,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_cache",
-                    choices=["long_cache", "dg_canvas", "tiny", "depformer", "sam_relpos"])
+                    choices=["long_cache", "dg_canvas", "tiny", "depformer", "sam_relpos",
+                             "hbm_copy"])
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle wall time for the CPU baseline (0 = skip)")
     args = ap.parse_args()

@@ -8,20 +8,31 @@
 // inferencelayer 0.2.4, src/moshi_gpu.rs (canvas row i sees canvas keys 0..i, scale 0.125).
 //
 // The page runs one workgroup per (canvas row, q head) and re-reads the whole key/value span
-// for each.  Here one workgroup owns 128 query vectors of ONE kv head -- the G = nh/nkv q heads
-// of a group times a block of canvas rows, flattened as (row, head-in-group) so they are
-// contiguous in q and out -- and stages each 32-key K/V tile once in LDS for all of them.
-// The seam between cache and canvas is resolved per key row while staging.  Scores and the
-// value product run on f32 MFMA (flash_core.hpp).  Workgroups of one kv head are placed on
-// the same XCD so its L2 serves the tile re-reads.
+// for each.  Here a workgroup of 8 wavefronts owns 128 query vectors of ONE kv head -- the
+// G = nh/nkv q heads of a group times a block of canvas rows, flattened as (row, head-in-group)
+// so they are contiguous in q and out.  Its 8 wavefronts form 4 pairs; both wavefronts of a
+// pair hold the same 32 queries and take alternate 32-key tiles, so the block walks the keys in
+// stages of 64.  Each stage's K and V tiles are fetched once into LDS for all 128 queries with
+// direct global->LDS loads, double-buffered so the next stage streams in while this one is
+// computed; the cache/canvas seam is resolved per key row when the load addresses are formed.
+// Scores and the value product run on f32 MFMA (flash_core.hpp).  At the end each pair merges
+// its two partial softmax states through LDS.
+//
+// Shapes with too few workgroups to fill the GPU also split the key range across workgroups
+// ("split-KV"): each writes an unnormalised partial (max, denominator, output) to the caller's
+// workspace and a second kernel merges them.  Workgroups that share K/V are placed on the same
+// XCD so its L2 serves the re-reads.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
 namespace {
 
 using dgk::f32x16;
-constexpr int kWaves = 4;
-constexpr int kBlockQ = kWaves * dgk::kQuery;  // query vectors per workgroup
+constexpr int kWaves = 8;
+constexpr int kPairs = 4;
+constexpr int kBlockQ = kPairs * dgk::kQuery;  // query vectors per workgroup
+constexpr int kStage = 2 * dgk::kKeys;         // keys per stage (one tile per pair member)
+constexpr int kTargetBlocks = 256;             // one 8-wave workgroup per CU
 
 struct SplitArgs {
     const float* q;
@@ -30,8 +41,11 @@ struct SplitArgs {
     const float* k;
     const float* v;
     float* out;
+    float* ws;         // split-KV partials: o [nsplit][nqtot][hd], m [nsplit][nqtot], l [...]
+    size_t nqtot;      // batch * T * nh query vectors
     int T, ctx, nh, nkv, G;
-    int qblocks;       // workgroups per (batch, kv head)
+    int qblocks;       // workgroups per (batch, kv head, split)
+    int nsplit;        // key-range splits
     int nblocks;       // total workgroups
     float qmul;        // scale * log2(e)
     int causal;
@@ -45,36 +59,34 @@ __device__ inline int xcd_remap(int bid, int n) {
 }
 
 template <int HD>
-__global__ void __launch_bounds__(256) attn_split_gqa_kernel(SplitArgs a) {
+__global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     using TL = dgk::Tile<HD>;
-    __shared__ __attribute__((aligned(16))) float ks[dgk::kKeys * TL::kStride];
-    __shared__ __attribute__((aligned(16))) float vs[dgk::kKeys * HD];
+    // [buffer][tile of the stage][K, V]
+    __shared__ __attribute__((aligned(16))) float smem[2 * 2 * 2 * TL::kFloats];
+    auto tile_ptr = [&](int buf, int tile, int isv) {
+        return smem + ((buf * 2 + tile) * 2 + isv) * TL::kFloats;
+    };
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks);
     const int qb = lid % a.qblocks;
-    const int bk = lid / a.qblocks;       // b * nkv + kv
+    const int rest = lid / a.qblocks;
+    const int split = rest % a.nsplit;
+    const int bk = rest / a.nsplit;           // b * nkv + kv
     const int kv = bk % a.nkv;
     const int b = bk / a.nkv;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int pair = wave & (kPairs - 1), hi = wave >> 2;
 
-    const int nq = a.T * a.G;                       // query vectors of this (b, kv)
-    const int qv = qb * kBlockQ + wave * dgk::kQuery + l32;
+    const int nq = a.T * a.G;                 // query vectors of this (b, kv)
+    const int qfirst = qb * kBlockQ + pair * dgk::kQuery;
+    const int qv = qfirst + l32;
     const bool valid = qv < nq;
     const int row = valid ? qv / a.G : 0;
     const int hq = kv * a.G + (valid ? qv % a.G : 0);
-    const size_t qoff = (((size_t)b * a.T + row) * a.nh + hq) * HD;
-    const bool wave_active = qb * kBlockQ + wave * dgk::kQuery < nq;
-
-    float qreg[HD / 2];
-    dgk::load_q<HD>(a.q + qoff, valid, half, a.qmul, qreg);
-
-    f32x16 o[TL::kVGroups];
-#pragma unroll
-    for (int t = 0; t < TL::kVGroups; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
-    float m = -INFINITY, lsum = 0.0f;
+    const size_t gq = ((size_t)b * a.T + row) * a.nh + hq;   // global query vector index
+    const bool pair_active = qfirst < nq;
+    const int row_min = pair_active ? qfirst / a.G : 0;
 
     const int S = a.ctx + a.T;
     int kend = S;
@@ -82,64 +94,146 @@ __global__ void __launch_bounds__(256) attn_split_gqa_kernel(SplitArgs a) {
         const int last = min(nq - 1, qb * kBlockQ + kBlockQ - 1) / a.G;
         kend = min(S, a.ctx + last + 1);
     }
+    const int nstage = (kend + kStage - 1) / kStage;
+    const int st_begin = (int)((long long)split * nstage / a.nsplit);
+    const int st_end = (int)((long long)(split + 1) * nstage / a.nsplit);
+
     const float* kcb = a.kc + (size_t)bk * a.ctx * HD;
     const float* vcb = a.vc + (size_t)bk * a.ctx * HD;
-    const size_t canvas_stride = (size_t)a.nkv * HD;
+    const size_t cstride = (size_t)a.nkv * HD;
     const float* kb = a.k + ((size_t)b * a.T * a.nkv + kv) * HD;
     const float* vb = a.v + ((size_t)b * a.T * a.nkv + kv) * HD;
 
-    constexpr int kVec = HD / 4;                        // float4 per key row
-    constexpr int kPerThread = dgk::kKeys * kVec / 256; // float4 per thread per tile
-
-    for (int t0 = 0; t0 < kend; t0 += dgk::kKeys) {
-        __syncthreads();  // the previous tile has been consumed
+    // Each wave issues an equal share of the stage's 4 * kLoadsPerTile wave-wide loads.
+    constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / kWaves;
+    auto issue_stage = [&](int st, int buf) {
 #pragma unroll
-        for (int it = 0; it < kPerThread; ++it) {
-            const int f = tid + 256 * it;
-            const int key = f / kVec;
-            const int c = (f % kVec) * 4;
-            const int j = t0 + key;
-            float4 kf = make_float4(0.f, 0.f, 0.f, 0.f), vf = kf;
-            if (j < a.ctx) {
-                kf = *reinterpret_cast<const float4*>(kcb + (size_t)j * HD + c);
-                vf = *reinterpret_cast<const float4*>(vcb + (size_t)j * HD + c);
-            } else if (j < kend) {
-                kf = *reinterpret_cast<const float4*>(kb + (size_t)(j - a.ctx) * canvas_stride + c);
-                vf = *reinterpret_cast<const float4*>(vb + (size_t)(j - a.ctx) * canvas_stride + c);
-            }
-            dgk::stage_k<HD>(ks, key, c, kf);
-            dgk::stage_v<HD>(vs, key, c, vf);
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+            const int L = wave * kLoadsPerWave + i;
+            const int part = L / TL::kLoadsPerTile;  // K0, V0, K1, V1
+            const int ld = L % TL::kLoadsPerTile;
+            const int tile = part >> 1, isv = part & 1;
+            const int j = min(st * kStage + tile * dgk::kKeys + dgk::dma_row<HD>(ld, lane), kend - 1);
+            const float* rp = j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * HD
+                                        : (isv ? vb : kb) + (size_t)(j - a.ctx) * cstride;
+            if (isv)
+                dgk::dma_load<HD, false>(tile_ptr(buf, tile, 1), ld, rp, lane);
+            else
+                dgk::dma_load<HD, true>(tile_ptr(buf, tile, 0), ld, rp, lane);
         }
-        __syncthreads();
-        if (wave_active) {
-            f32x16 s = dgk::scores<HD>(ks, l32, half, qreg);
+    };
+
+    float qreg[HD / 2];
+    dgk::load_q<HD>(a.q + gq * HD, valid, half, a.qmul, qreg);
+    f32x16 o[TL::kGroups];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = t0 + dgk::key_of(r, half);
-                const bool masked = j >= kend || (a.causal && j >= a.ctx && j - a.ctx > row);
-                if (masked) s[r] = -INFINITY;
+    for (int t = 0; t < TL::kGroups; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;
+
+    if (st_begin < st_end) issue_stage(st_begin, 0);
+    for (int st = st_begin; st < st_end; ++st) {
+        const int buf = (st - st_begin) & 1;
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
+        __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
+        if (st + 1 < st_end) issue_stage(st + 1, buf ^ 1);
+        const int t0 = st * kStage + hi * dgk::kKeys;
+        if (pair_active && t0 < kend) {
+            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg);
+            const bool need_mask =
+                t0 + dgk::kKeys > kend || (a.causal && t0 + dgk::kKeys - 1 - a.ctx > row_min);
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = t0 + dgk::key_of(r, half);
+                    if (j >= kend || (a.causal && j - a.ctx > row)) s[r] = -INFINITY;
+                }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            dgk::accumulate_pv<HD>(vs, l32, half, s, o);
+            dgk::accumulate_pv<HD>(tile_ptr(buf, hi, 1), l32, half, s, o);
         }
     }
-    dgk::store_out<HD>(a.out + qoff, valid, half, lsum, o);
+
+    __syncthreads();  // every wave is done with the stage buffers; reuse them for the merge
+    dgk::pair_merge<HD>(smem, pair, hi, pair_active, lane, m, lsum, o);
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (hi || !valid) return;
+    if (a.nsplit == 1) {
+        dgk::store_row<HD>(a.out + gq * HD, 1.0f / ltot, o, half);
+    } else {
+        dgk::store_row<HD>(a.ws + ((size_t)split * a.nqtot + gq) * HD, 1.0f, o, half);
+        if (half == 0) {
+            float* wm = a.ws + (size_t)a.nsplit * a.nqtot * HD;
+            wm[(size_t)split * a.nqtot + gq] = m;
+            wm[(size_t)(a.nsplit + split) * a.nqtot + gq] = ltot;
+        }
+    }
+}
+
+// Merges split-KV partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
+// One thread per 4 output elements.
+template <int HD>
+__global__ void __launch_bounds__(256) split_combine_kernel(const float* __restrict__ ws,
+                                                            float* __restrict__ out,
+                                                            size_t total, int nsplit) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total * (HD / 4)) return;
+    const size_t gq = idx / (HD / 4);
+    const int c = (int)(idx % (HD / 4)) * 4;
+    const float* wm = ws + (size_t)nsplit * total * HD;
+    const float* wl = wm + (size_t)nsplit * total;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wm[(size_t)s * total + gq]);
+    float L = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nsplit; ++s) {
+        const float w = dgk::fast_exp2(wm[(size_t)s * total + gq] - M);
+        L += wl[(size_t)s * total + gq] * w;
+        const float4 v = *reinterpret_cast<const float4*>(ws + ((size_t)s * total + gq) * HD + c);
+        acc.x += v.x * w; acc.y += v.y * w; acc.z += v.z * w; acc.w += v.w * w;
+    }
+    const float inv = 1.0f / L;
+    *reinterpret_cast<float4*>(out + gq * HD + c) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+// Launch plan shared by the workspace query and the launch.
+struct Plan {
+    int qblocks = 0, nsplit = 1;
+    size_t ws_bytes = 0;
+};
+
+Plan plan(int batch, int T, int ctx, int nh, int nkv, int hd, int causal) {
+    Plan p;
+    const int G = nh / nkv;
+    p.qblocks = (int)(((long long)T * G + kBlockQ - 1) / kBlockQ);
+    const long long blocks = (long long)batch * nkv * p.qblocks;
+    const int S = ctx + T;
+    const int nstage = (S + kStage - 1) / kStage;
+    if (blocks > 0 && blocks < kTargetBlocks && !causal) {
+        long long want = (kTargetBlocks + blocks - 1) / blocks;
+        long long cap = nstage / 2;  // at least two stages per split
+        p.nsplit = (int)std::max(1LL, std::min(want, cap));
+    }
+    if (p.nsplit > 1)
+        p.ws_bytes = (size_t)p.nsplit * batch * T * nh * (size_t)(hd + 2) * sizeof(float);
+    return p;
 }
 
 }  // namespace
 
 extern "C" size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int nkv,
                                                    int hd) {
-    (void)batch; (void)T; (void)ctx; (void)nh; (void)nkv; (void)hd;
-    return 0;
+    if (batch <= 0 || T <= 0 || ctx < 0 || nkv < 1 || nh < 1 || nh % nkv != 0) return 0;
+    if (hd != 64 && hd != 128) return 0;
+    return plan(batch, T, ctx, nh, nkv, hd, 0).ws_bytes;
 }
 
 extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
                                  const float* v, float* out, int batch, int T, int ctx, int nh,
                                  int nkv, int hd, float scale, int causal, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     const char* fn = "dg_attn_split_gqa";
     if (batch < 0 || T < 0 || ctx < 0 || nh < 0 || nkv < 0)
         return dg::fail(DG_EINVAL, "%s: negative size (batch %d, T %d, ctx %d, nh %d, nkv %d)", fn,
@@ -156,30 +250,55 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
         !dg::mul_ok(ncache, batch) || !dg::mul_ok(ncache, nkv) || !dg::mul_ok(ncache, ctx) ||
         !dg::mul_ok(ncache, hd))
         return dg::fail(DG_EINVAL, "%s: size overflow", fn);
+    if (workspace && workspace_bytes == 0)
+        return dg::fail(DG_EINVAL, "%s: workspace given with workspace_bytes 0", fn);
     if (nq == 0) return dg::ok();
     if (!q || !k || !v || !out) return dg::fail(DG_EINVAL, "%s: q, k, v and out must be non-NULL", fn);
     if (ncache > 0 && (!kc || !vc)) return dg::fail(DG_EINVAL, "%s: kc/vc NULL with ctx %d > 0", fn, ctx);
+    Plan p = plan(batch, T, ctx, nh, nkv, hd, causal);
+    if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes)) {
+        if (workspace)
+            return dg::fail(DG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed",
+                            fn, workspace_bytes, p.ws_bytes);
+        p.nsplit = 1;  // no workspace: run unsplit
+        p.ws_bytes = 0;
+    }
     const dg::Span so(out, nq * 4);
-    const dg::Span ins[5] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * 4), dg::Span(v, nkvc * 4),
+    const dg::Span ins[6] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * 4), dg::Span(v, nkvc * 4),
                              dg::Span(ncache ? kc : nullptr, ncache * 4),
-                             dg::Span(ncache ? vc : nullptr, ncache * 4)};
-    for (const auto& s : ins)
-        if (so.overlaps(s)) return dg::fail(DG_EINVAL, "%s: out overlaps an input", fn);
-    const long long qblocks = ((long long)T * (nh / nkv) + kBlockQ - 1) / kBlockQ;
-    const long long nblocks = (long long)batch * nkv * qblocks;
+                             dg::Span(ncache ? vc : nullptr, ncache * 4),
+                             dg::Span(p.nsplit > 1 ? workspace : nullptr, p.ws_bytes)};
+    for (int i = 0; i < 6; ++i)
+        if (so.overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: out overlaps an input or the workspace", fn);
+    for (int i = 0; i < 5; ++i)
+        if (ins[5].overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: workspace overlaps an input", fn);
+    const long long nblocks = (long long)batch * nkv * p.qblocks * p.nsplit;
     if (nblocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     SplitArgs a;
     a.q = q; a.kc = kc; a.vc = vc; a.k = k; a.v = v; a.out = out;
+    a.ws = static_cast<float*>(p.nsplit > 1 ? workspace : nullptr);
+    a.nqtot = (size_t)batch * T * nh;
     a.T = T; a.ctx = ctx; a.nh = nh; a.nkv = nkv; a.G = nh / nkv;
-    a.qblocks = (int)qblocks;
+    a.qblocks = p.qblocks;
+    a.nsplit = p.nsplit;
     a.nblocks = (int)nblocks;
     a.qmul = scale * dgk::kLog2e;
     a.causal = causal;
+    hipStream_t s = (hipStream_t)stream;
     if (hd == 128)
-        hipLaunchKernelGGL(attn_split_gqa_kernel<128>, dim3((unsigned)nblocks), dim3(256), 0,
-                           (hipStream_t)stream, a);
+        hipLaunchKernelGGL(attn_split_gqa_kernel<128>, dim3((unsigned)nblocks), dim3(512), 0, s, a);
     else
-        hipLaunchKernelGGL(attn_split_gqa_kernel<64>, dim3((unsigned)nblocks), dim3(256), 0,
-                           (hipStream_t)stream, a);
+        hipLaunchKernelGGL(attn_split_gqa_kernel<64>, dim3((unsigned)nblocks), dim3(512), 0, s, a);
+    if (p.nsplit > 1) {
+        const size_t total = (size_t)batch * T * nh;
+        const size_t threads = total * (hd / 4);
+        const unsigned blocks = (unsigned)((threads + 255) / 256);
+        if (hd == 128)
+            hipLaunchKernelGGL(split_combine_kernel<128>, dim3(blocks), dim3(256), 0, s,
+                               (const float*)a.ws, out, total, p.nsplit);
+        else
+            hipLaunchKernelGGL(split_combine_kernel<64>, dim3(blocks), dim3(256), 0, s,
+                               (const float*)a.ws, out, total, p.nsplit);
+    }
     return dg::launch_status(fn);
 }

@@ -1,7 +1,7 @@
-// flash_core.hpp -- the f32-MFMA flash-attention inner step shared by the split-GQA and the
+// flash_core.hpp -- the f32-MFMA flash-attention pieces shared by the split-GQA and the
 // rel-pos kernels (gfx950, 64-lane wavefronts).
 //
-// What it computes is the online softmax of inferencelayer 0.2.3 src/diffusion_gemma_gpu.rs
+// What they compute is the online softmax of inferencelayer 0.2.3 src/diffusion_gemma_gpu.rs
 // kernel DG_ATTN (and of the register flash in 0.2.8 src/deepencoder_gpu.rs): per key tile a
 // running max m, a correction exp(m_old - m_new) applied to the running denominator and to the
 // output accumulator, and p = exp(s - m_new).  Scores are kept in log2 units (the caller folds
@@ -15,9 +15,17 @@
 // at k-step r is exactly register r of the probabilities (key(r, l) for the lane's query), so P
 // never moves between lanes; the A operand is V^T, read from LDS at the matching keys.
 //
-// Contraction order over the head dimension is permuted so that each lane fetches 4
-// consecutive K (or Q) elements with one 16-byte access: MFMA step s, lane half h uses element
-// pi(s, h) = 8*(s/4) + 4*h + s%4.  Q is loaded with the same permutation.
+// Contraction orders are free, so both are chosen for 16-byte LDS reads:
+//  * scores: MFMA step s, lane half h contracts head element 8*(s/4) + 4*h + s%4, so one
+//    16-byte K read feeds 4 MFMAs (Q is loaded with the same permutation);
+//  * output: row m of accumulator group t holds head element m*G + t (G = hd/32 groups), so a
+//    lane's G values of one V row are contiguous.
+//
+// Tiles live in LDS in natural row-major order (row = one key, hd floats) and are filled by
+// 16-byte direct global->LDS loads (global_load_lds_dwordx4: lane i of an instruction lands at
+// base + 16*i).  K rows are stored with their 16-byte chunks permuted, chunk c of key row k at
+// position c ^ (k mod chunks-per-row), which makes the 32 lanes reading 32 different K rows hit
+// distinct banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,6 +33,7 @@
 namespace dgk {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kKeys = 32;    // keys per tile
 constexpr int kQuery = 32;   // query vectors per wavefront
@@ -32,8 +41,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int HD>
 struct Tile {
-    static constexpr int kStride = HD + 4;  // K row stride in LDS: conflict-free 16-byte reads
-    static constexpr int kVGroups = HD / 32;  // 32-wide output tiles per query
+    static constexpr int kChunks = HD / 4;            // 16-byte chunks per key row
+    static constexpr int kFloats = kKeys * HD;        // one K or V tile
+    static constexpr int kGroups = HD / 32;           // output accumulators per lane
+    static constexpr int kRowsPerLoad = 64 / kChunks; // key rows per wave-wide 1 KiB load
+    static constexpr int kLoadsPerTile = kKeys / kRowsPerLoad;
 };
 
 __device__ inline int key_of(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
@@ -53,15 +65,34 @@ __device__ inline void load_q(const float* __restrict__ qrow, bool valid, int ha
     }
 }
 
-// S^T tile (32 keys x 32 queries) from K in LDS (row stride Tile<HD>::kStride).
+// Tile row that lane `lane` fills in wave-wide load `ld` of a tile.
+template <int HD>
+__device__ inline int dma_row(int ld, int lane) {
+    return ld * Tile<HD>::kRowsPerLoad + lane / Tile<HD>::kChunks;
+}
+
+// Issues wave-wide 1 KiB direct load `ld` into a K tile (kSwizzle) or a V tile (plain).
+// `rowptr` is the global address of this lane's key row dma_row(ld, lane).
+template <int HD, bool kSwizzle>
+__device__ inline void dma_load(float* tile, int ld, const float* rowptr, int lane) {
+    using TL = Tile<HD>;
+    const int pos = lane % TL::kChunks;
+    const int chunk = kSwizzle ? (pos ^ (dma_row<HD>(ld, lane) % TL::kChunks)) : pos;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(rowptr + 4 * chunk),
+                                     (lds_void*)(tile + ld * 256), 16, 0, 0);
+}
+
+// S^T tile (32 keys x 32 queries) from a swizzled K tile in LDS.
 template <int HD>
 __device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
                                 const float (&qreg)[HD / 2]) {
+    using TL = Tile<HD>;
     f32x16 s = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float* kr = ks + l32 * Tile<HD>::kStride + 4 * half;
+    const float* kr = ks + l32 * HD;
+    const int sw = l32 % TL::kChunks;
 #pragma unroll
     for (int g = 0; g < HD / 8; ++g) {
-        const float4 kf = *reinterpret_cast<const float4*>(kr + 8 * g);
+        const float4 kf = *reinterpret_cast<const float4*>(kr + 4 * ((2 * g + half) ^ sw));
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qreg[4 * g + 0], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qreg[4 * g + 1], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qreg[4 * g + 2], s, 0, 0, 0);
@@ -70,40 +101,42 @@ __device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
     return s;
 }
 
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Online-softmax update on a masked S^T tile (masked entries hold -inf).  Turns s into
 // probabilities, rescales o and the lane's partial denominator.
 template <int HD>
 __device__ inline void softmax_update(f32x16& s, float& m, float& lsum,
-                                      f32x16 (&o)[Tile<HD>::kVGroups]) {
-    float tmax = s[0];
+                                      f32x16 (&o)[Tile<HD>::kGroups]) {
+    float tmax = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+    for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m, tmax);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float corr = exp2f(m - m_use);
+    const float corr = fast_exp2(m - m_use);
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        s[r] = exp2f(s[r] - m_use);
+        s[r] = fast_exp2(s[r] - m_use);
         psum += s[r];
     }
     lsum = lsum * corr + psum;
     m = m_new;
 #pragma unroll
-    for (int t = 0; t < Tile<HD>::kVGroups; ++t)
+    for (int t = 0; t < Tile<HD>::kGroups; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= corr;
 }
 
-// O^T += V^T P^T with V in LDS stored column-permuted: element c of a key row sits at
-// (c % 32) * (HD/32) + c / 32, so one access returns the lane's column in every 32-wide group.
+// O^T += V^T P^T from a plain V tile in LDS; the lane reads its G contiguous head elements
+// of the key row that its half supplies at k-step r.
 template <int HD>
 __device__ inline void accumulate_pv(const float* __restrict__ vs, int l32, int half,
-                                     const f32x16& p, f32x16 (&o)[Tile<HD>::kVGroups]) {
+                                     const f32x16& p, f32x16 (&o)[Tile<HD>::kGroups]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float* vr = vs + key_of(r, half) * HD + l32 * Tile<HD>::kVGroups;
+        const float* vr = vs + key_of(r, half) * HD + l32 * Tile<HD>::kGroups;
         if constexpr (HD == 128) {
             const float4 vf = *reinterpret_cast<const float4*>(vr);
             o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf.x, p[r], o[0], 0, 0, 0);
@@ -118,36 +151,58 @@ __device__ inline void accumulate_pv(const float* __restrict__ vs, int l32, int 
     }
 }
 
-// Writes o / l for the lane's query (row pointer `orow`, contiguous HD floats).
+// Head element held by accumulator register r of group t in lane half `half`.
 template <int HD>
-__device__ inline void store_out(float* __restrict__ orow, bool valid, int half, float lsum,
-                                 const f32x16 (&o)[Tile<HD>::kVGroups]) {
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (!valid) return;
-    const float inv = 1.0f / ltot;
-#pragma unroll
-    for (int t = 0; t < Tile<HD>::kVGroups; ++t)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            float4 w = make_float4(o[t][4 * b + 0] * inv, o[t][4 * b + 1] * inv,
-                                   o[t][4 * b + 2] * inv, o[t][4 * b + 3] * inv);
-            *reinterpret_cast<float4*>(orow + 32 * t + 8 * b + 4 * half) = w;
-        }
+__device__ inline int out_elem(int t, int r, int half) {
+    return (8 * (r >> 2) + 4 * half + (r & 3)) * Tile<HD>::kGroups + t;
 }
 
-// Stores one float4 of a key row into the K tile (plain) and the V tile (column-permuted).
+// Writes o * scale for the lane's query (row pointer `orow`, contiguous HD floats).
 template <int HD>
-__device__ inline void stage_k(float* ks, int key, int c, float4 v) {
-    *reinterpret_cast<float4*>(ks + key * Tile<HD>::kStride + c) = v;
+__device__ inline void store_row(float* __restrict__ orow, float scale,
+                                 const f32x16 (&o)[Tile<HD>::kGroups], int half) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float* dst = orow + out_elem<HD>(0, r, half);
+        if constexpr (HD == 128) {
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(o[0][r] * scale, o[1][r] * scale, o[2][r] * scale, o[3][r] * scale);
+        } else {
+            *reinterpret_cast<float2*>(dst) = make_float2(o[0][r] * scale, o[1][r] * scale);
+        }
+    }
 }
+
+// Merges the softmax states of the two wavefronts of a pair (same 32 queries, disjoint keys):
+// the odd-tile wavefront (hi) hands (o, m, lsum) to the even-tile one through LDS scratch
+// `smem` (at least 4 * 64 * (hd/2 + 2) floats, not in use by anyone).  Every thread of the
+// workgroup must call this; afterwards the even-tile wavefront holds the merged state.
 template <int HD>
-__device__ inline void stage_v(float* vs, int key, int c, float4 v) {
-    constexpr int G = Tile<HD>::kVGroups;
-    float* vr = vs + key * HD;
-    vr[((c + 0) & 31) * G + ((c + 0) >> 5)] = v.x;
-    vr[((c + 1) & 31) * G + ((c + 1) >> 5)] = v.y;
-    vr[((c + 2) & 31) * G + ((c + 2) >> 5)] = v.z;
-    vr[((c + 3) & 31) * G + ((c + 3) >> 5)] = v.w;
+__device__ inline void pair_merge(float* smem, int pair, bool hi, bool active, int lane,
+                                  float& m, float& lsum, f32x16 (&o)[Tile<HD>::kGroups]) {
+    constexpr int kVals = Tile<HD>::kGroups * 16 + 2;
+    float* mg = smem + pair * kVals * 64;
+    if (hi && active) {
+#pragma unroll
+        for (int t = 0; t < Tile<HD>::kGroups; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mg[(t * 16 + r) * 64 + lane] = o[t][r];
+        mg[(kVals - 2) * 64 + lane] = m;
+        mg[(kVals - 1) * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (hi || !active) return;
+    const float m2 = mg[(kVals - 2) * 64 + lane];
+    const float l2 = mg[(kVals - 1) * 64 + lane];
+    const float mn = fmaxf(m, m2);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    const float ca = fast_exp2(m - mu), cb = fast_exp2(m2 - mu);
+#pragma unroll
+    for (int t = 0; t < Tile<HD>::kGroups; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * ca + mg[(t * 16 + r) * 64 + lane] * cb;
+    lsum = lsum * ca + l2 * cb;
+    m = mn;
 }
 
 }  // namespace dgk

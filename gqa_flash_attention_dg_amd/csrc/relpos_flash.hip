@@ -10,7 +10,8 @@
 // The page writes dh/dw to global [heads, n, gh] / [heads, n, gw] buffers and then looks them
 // up per key.  Here each workgroup computes the bias rows of its own 128 queries into LDS in
 // a prologue (no global round trip, no workspace), then runs the same f32-MFMA flash loop as
-// the split-GQA kernel (flash_core.hpp) with the two table lookups added to each score.
+// the split-GQA kernel (flash_core.hpp: 4 pairs of wavefronts on alternate 32-key tiles,
+// double-buffered direct global->LDS tiles) with the two table lookups added to each score.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
@@ -18,8 +19,10 @@ namespace {
 
 using dgk::f32x16;
 constexpr int HD = 64;
-constexpr int kWaves = 4;
-constexpr int kBlockQ = kWaves * dgk::kQuery;
+constexpr int kWaves = 8;
+constexpr int kPairs = 4;
+constexpr int kBlockQ = kPairs * dgk::kQuery;
+constexpr int kStage = 2 * dgk::kKeys;
 constexpr int kMaxGrid = 64;                 // gh, gw <= 64
 constexpr int kTabStride = 2 * kMaxGrid + 1; // dh | dw per query, padded against bank conflicts
 
@@ -38,29 +41,33 @@ __device__ inline int xcd_remap(int bid, int n) {
     return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
-__global__ void __launch_bounds__(256) relpos_flash_kernel(RelArgs a) {
+__global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     using TL = dgk::Tile<HD>;
-    __shared__ __attribute__((aligned(16))) float ks[dgk::kKeys * TL::kStride];
-    __shared__ __attribute__((aligned(16))) float vs[dgk::kKeys * HD];
-    __shared__ float tab[kWaves * dgk::kQuery * kTabStride];
+    __shared__ __attribute__((aligned(16))) float smem[2 * 2 * 2 * TL::kFloats];
+    __shared__ float tab[kPairs * dgk::kQuery * kTabStride];
+    auto tile_ptr = [&](int buf, int tile, int isv) {
+        return smem + ((buf * 2 + tile) * 2 + isv) * TL::kFloats;
+    };
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks);
     const int qb = lid % a.qblocks;
     const int head = lid / a.qblocks;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int pair = wave & (kPairs - 1), hi = wave >> 2;
     const size_t rs = (size_t)3 * a.W;  // qkv row stride
 
-    const int qi = qb * kBlockQ + wave * dgk::kQuery + l32;
+    const int qfirst = qb * kBlockQ + pair * dgk::kQuery;
+    const int qi = qfirst + l32;
     const bool valid = qi < a.n;
     const float* qrow = a.qkv + (size_t)(valid ? qi : 0) * rs + head * HD;
-    const bool wave_active = qb * kBlockQ + wave * dgk::kQuery < a.n;
+    const bool pair_active = qfirst < a.n;
     const bool bias = a.rh != nullptr;
-    float* mytab = tab + (wave * dgk::kQuery + l32) * kTabStride;
+    float* mytab = tab + (pair * dgk::kQuery + l32) * kTabStride;
 
-    // Prologue: this query's bias rows dh[ky] = <q, Rh[qy,ky]>, dw[kx] = <q, Rw[qx,kx]> (log2
-    // units); the two lane halves split the ky / kx range.
-    if (bias && wave_active) {
+    // Prologue: this query's bias rows in log2 units, dh[ky] = <q, Rh[qy,ky]> (even-tile wave)
+    // and dw[kx] = <q, Rw[qx,kx]> (odd-tile wave); lane halves split the ky / kx range.
+    if (bias && pair_active) {
         float qf[HD];
 #pragma unroll
         for (int c = 0; c < HD; c += 4) {
@@ -68,62 +75,59 @@ __global__ void __launch_bounds__(256) relpos_flash_kernel(RelArgs a) {
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
             qf[c] = t.x; qf[c + 1] = t.y; qf[c + 2] = t.z; qf[c + 3] = t.w;
         }
-        const int qy = valid ? qi / a.gw : 0, qx = valid ? qi % a.gw : 0;
-        for (int ky = half; ky < a.gh; ky += 2) {
-            const float* tr = a.rh + ((size_t)qy * a.gh + ky) * HD;
+        const int g = hi ? a.gw : a.gh;
+        const int coord = valid ? (hi ? qi % a.gw : qi / a.gw) : 0;
+        const float* table = hi ? a.rw : a.rh;
+        for (int kk = half; kk < g; kk += 2) {
+            const float* tr = table + ((size_t)coord * g + kk) * HD;
             float d = 0.0f;
 #pragma unroll
             for (int c = 0; c < HD; c += 4) {
                 const float4 t = *reinterpret_cast<const float4*>(tr + c);
                 d += qf[c] * t.x + qf[c + 1] * t.y + qf[c + 2] * t.z + qf[c + 3] * t.w;
             }
-            mytab[ky] = d * dgk::kLog2e;
-        }
-        for (int kx = half; kx < a.gw; kx += 2) {
-            const float* tr = a.rw + ((size_t)qx * a.gw + kx) * HD;
-            float d = 0.0f;
-#pragma unroll
-            for (int c = 0; c < HD; c += 4) {
-                const float4 t = *reinterpret_cast<const float4*>(tr + c);
-                d += qf[c] * t.x + qf[c + 1] * t.y + qf[c + 2] * t.z + qf[c + 3] * t.w;
-            }
-            mytab[kMaxGrid + kx] = d * dgk::kLog2e;
+            mytab[hi * kMaxGrid + kk] = d * dgk::kLog2e;
         }
     }
 
+    const float* kbase = a.qkv + a.W + head * HD;
+    const float* vbase = a.qkv + 2 * (size_t)a.W + head * HD;
+    constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / kWaves;
+    auto issue_stage = [&](int st, int buf) {
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+            const int L = wave * kLoadsPerWave + i;
+            const int part = L / TL::kLoadsPerTile;  // K0, V0, K1, V1
+            const int ld = L % TL::kLoadsPerTile;
+            const int tile = part >> 1, isv = part & 1;
+            const int j = min(st * kStage + tile * dgk::kKeys + dgk::dma_row<HD>(ld, lane), a.n - 1);
+            if (isv)
+                dgk::dma_load<HD, false>(tile_ptr(buf, tile, 1), ld, vbase + (size_t)j * rs, lane);
+            else
+                dgk::dma_load<HD, true>(tile_ptr(buf, tile, 0), ld, kbase + (size_t)j * rs, lane);
+        }
+    };
+
     float qreg[HD / 2];
     dgk::load_q<HD>(qrow, valid, half, a.qmul, qreg);
-    f32x16 o[TL::kVGroups];
+    f32x16 o[TL::kGroups];
 #pragma unroll
-    for (int t = 0; t < TL::kVGroups; ++t)
+    for (int t = 0; t < TL::kGroups; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    const float* kbase = a.qkv + a.W + head * HD;
-    const float* vbase = a.qkv + 2 * (size_t)a.W + head * HD;
-    constexpr int kVec = HD / 4;
-    constexpr int kPerThread = dgk::kKeys * kVec / 256;
-
-    for (int t0 = 0; t0 < a.n; t0 += dgk::kKeys) {
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < kPerThread; ++it) {
-            const int f = tid + 256 * it;
-            const int key = f / kVec;
-            const int c = (f % kVec) * 4;
-            const int j = t0 + key;
-            float4 kf = make_float4(0.f, 0.f, 0.f, 0.f), vf = kf;
-            if (j < a.n) {
-                kf = *reinterpret_cast<const float4*>(kbase + (size_t)j * rs + c);
-                vf = *reinterpret_cast<const float4*>(vbase + (size_t)j * rs + c);
-            }
-            dgk::stage_k<HD>(ks, key, c, kf);
-            dgk::stage_v<HD>(vs, key, c, vf);
-        }
-        __syncthreads();
-        if (wave_active) {
-            f32x16 s = dgk::scores<HD>(ks, l32, half, qreg);
+    const int nstage = (a.n + kStage - 1) / kStage;
+    issue_stage(0, 0);
+    for (int st = 0; st < nstage; ++st) {
+        const int buf = st & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // stage st has landed everywhere, stage st-1 is consumed (and the
+                          // bias table is complete before the first use)
+        if (st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
+        const int t0 = st * kStage + hi * dgk::kKeys;
+        if (pair_active && t0 < a.n) {
+            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = t0 + dgk::key_of(r, half);
@@ -134,10 +138,15 @@ __global__ void __launch_bounds__(256) relpos_flash_kernel(RelArgs a) {
                 }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            dgk::accumulate_pv<HD>(vs, l32, half, s, o);
+            dgk::accumulate_pv<HD>(tile_ptr(buf, hi, 1), l32, half, s, o);
         }
     }
-    dgk::store_out<HD>(a.out + (size_t)(valid ? qi : 0) * a.W + head * HD, valid, half, lsum, o);
+
+    __syncthreads();
+    dgk::pair_merge<HD>(smem, pair, hi, pair_active, lane, m, lsum, o);
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (hi || !valid) return;
+    dgk::store_row<HD>(a.out + (size_t)qi * a.W + head * HD, 1.0f / ltot, o, half);
 }
 
 }  // namespace
@@ -171,7 +180,7 @@ extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float*
     a.qblocks = (int)qblocks;
     a.nblocks = (int)(qblocks * heads);
     a.qmul = scale * dgk::kLog2e;
-    hipLaunchKernelGGL(relpos_flash_kernel, dim3((unsigned)a.nblocks), dim3(256), 0,
+    hipLaunchKernelGGL(relpos_flash_kernel, dim3((unsigned)a.nblocks), dim3(512), 0,
                        (hipStream_t)stream, a);
     return dg::launch_status(fn);
 }

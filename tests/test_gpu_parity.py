@@ -77,16 +77,43 @@ SPLIT_SHAPES = [
 ]
 
 
+def workspace_for(B, T, ctx, nh, nkv, hd):
+    nbytes = dg.dg_attn_split_gqa_workspace_size(B, T, ctx, nh, nkv, hd)
+    if nbytes == 0:
+        return None, 0
+    return torch.full((nbytes // 4,), float("nan"), device="cuda"), nbytes
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["unsplit", "ws"])
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "B%d_T%d_ctx%d_h%d_kv%d_hd%d_c%d" % (
     s[0], s[1], s[2], s[3], s[4], s[5], s[7]))
-def test_attn_split_small(shape):
+def test_attn_split_small(shape, use_ws):
     B, T, ctx, nh, nkv, hd, scale, causal = shape
     c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=T + ctx, scale=scale, causal=causal)
     ref = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, nh, nkv, hd, scale, causal)
     out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd) if use_ws else (None, 0)
     dg.dg_attn_split_gqa(dev(c.q), dev(c.kc), dev(c.vc), dev(c.k), dev(c.v), out, B, T, ctx,
-                         nh, nkv, hd, scale, int(causal))
-    assert_parity(host(out), ref, "split %s" % (shape,))
+                         nh, nkv, hd, scale, int(causal), ws, nbytes)
+    assert_parity(host(out), ref, "split %s ws=%d" % (shape, nbytes))
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 2000, 4, 2, 128), (2, 40, 700, 8, 8, 64),
+                                   (1, 256, 1024, 16, 8, 128), (1, 3, 5000, 2, 1, 64)])
+def test_attn_split_kv_partials_and_combine(shape):
+    """Shapes with few workgroups split the key range across workgroups and merge partials."""
+    B, T, ctx, nh, nkv, hd = shape
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
+    assert nbytes > 0, "this shape is expected to take the split-KV path"
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=ctx)
+    ref = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, nh, nkv, hd)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    args = [dev(c.q), dev(c.kc), dev(c.vc), dev(c.k), dev(c.v), out, B, T, ctx, nh, nkv, hd,
+            1.0, 0]
+    dg.dg_attn_split_gqa(*args, ws, nbytes)
+    assert_parity(host(out), ref, "split-kv %s" % (shape,))
+    with pytest.raises(dg.DgError):          # a workspace that is too small is refused
+        dg.dg_attn_split_gqa(*args, ws, nbytes - 4)
 
 
 def test_attn_split_zero_canvas_is_noop_and_nonfinite_free():
