@@ -171,6 +171,101 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     }
 }
 
+// Short key sets (ctx + T <= 8, e.g. the depformer's causal frames of 8 steps): there is too
+// little work per query for matrix tiles, and the call is HBM-bound.  One wavefront per
+// (batch entry, q head): lane (r, c) = (lane / 8, lane % 8) owns query row r and the c-th
+// hd/8-wide segment of it, and loads the same segment of key/value row r into wave-private LDS.
+// Each lane forms partial dots of its query segment with every key's segment; a 3-step lane
+// exchange within each group of 8 completes them, the 8-entry softmax runs in registers, and
+// each lane writes its segment of the output row.  All global accesses are contiguous per row.
+constexpr int kSmallKeys = 8;
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long units) {
+    constexpr int SEG = HD / 8;
+    __shared__ __attribute__((aligned(16))) float kvs[4 * 2 * kSmallKeys * HD];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane >> 3, cseg = (lane & 7) * SEG;
+    const long long u = (long long)blockIdx.x * 4 + wave;   // b * nh + h
+    const bool active = u < units;
+    const int h = active ? (int)(u % a.nh) : 0;
+    const int b = active ? (int)(u / a.nh) : 0;
+    const int kv = h / a.G;
+    const int S = a.ctx + a.T;
+    float* ks = kvs + wave * 2 * kSmallKeys * HD;
+    float* vs = ks + kSmallKeys * HD;
+
+    float qr[SEG], kr[SEG], vr[SEG];
+    const bool has_key = active && r < S, has_q = active && r < a.T;
+    const float* kp = nullptr;
+    const float* vp = nullptr;
+    if (has_key) {
+        const size_t off = r < a.ctx ? (((size_t)b * a.nkv + kv) * a.ctx + r) * HD
+                                     : (((size_t)b * a.T + (r - a.ctx)) * a.nkv + kv) * HD;
+        kp = (r < a.ctx ? a.kc : a.k) + off + cseg;
+        vp = (r < a.ctx ? a.vc : a.v) + off + cseg;
+    }
+    const float* qp = a.q + (((size_t)b * a.T + r) * a.nh + h) * HD + cseg;
+#pragma unroll
+    for (int e = 0; e < SEG; e += 4) {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 k4 = has_key ? *reinterpret_cast<const float4*>(kp + e) : z;
+        const float4 v4 = has_key ? *reinterpret_cast<const float4*>(vp + e) : z;
+        const float4 q4 = has_q ? *reinterpret_cast<const float4*>(qp + e) : z;
+        kr[e] = k4.x; kr[e + 1] = k4.y; kr[e + 2] = k4.z; kr[e + 3] = k4.w;
+        vr[e] = v4.x; vr[e + 1] = v4.y; vr[e + 2] = v4.z; vr[e + 3] = v4.w;
+        qr[e] = q4.x * a.qmul; qr[e + 1] = q4.y * a.qmul; qr[e + 2] = q4.z * a.qmul; qr[e + 3] = q4.w * a.qmul;
+    }
+#pragma unroll
+    for (int e = 0; e < SEG; e += 4) {
+        *reinterpret_cast<float4*>(ks + r * HD + cseg + e) = make_float4(kr[e], kr[e + 1], kr[e + 2], kr[e + 3]);
+        *reinterpret_cast<float4*>(vs + r * HD + cseg + e) = make_float4(vr[e], vr[e + 1], vr[e + 2], vr[e + 3]);
+    }
+    __syncthreads();
+    float sc[kSmallKeys];
+#pragma unroll
+    for (int j = 0; j < kSmallKeys; ++j) {
+        float d = 0.0f;
+#pragma unroll
+        for (int e = 0; e < SEG; e += 4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(ks + j * HD + cseg + e);
+            d += qr[e] * k4.x + qr[e + 1] * k4.y + qr[e + 2] * k4.z + qr[e + 3] * k4.w;
+        }
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 4);
+        const bool visible = j < S && !(a.causal && j >= a.ctx && j - a.ctx > r);
+        sc[j] = visible ? d : -INFINITY;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int j = 1; j < kSmallKeys; ++j) mx = fmaxf(mx, sc[j]);
+    const float mu = (mx == -INFINITY) ? 0.0f : mx;
+    float l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSmallKeys; ++j) {
+        sc[j] = dgk::fast_exp2(sc[j] - mu);
+        l += sc[j];
+    }
+    float o[SEG];
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) o[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSmallKeys; ++j) {
+#pragma unroll
+        for (int e = 0; e < SEG; e += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(vs + j * HD + cseg + e);
+            o[e] += sc[j] * v4.x; o[e + 1] += sc[j] * v4.y; o[e + 2] += sc[j] * v4.z; o[e + 3] += sc[j] * v4.w;
+        }
+    }
+    if (!has_q) return;
+    const float inv = 1.0f / l;
+    float* op = a.out + (((size_t)b * a.T + r) * a.nh + h) * HD + cseg;
+#pragma unroll
+    for (int e = 0; e < SEG; e += 4)
+        *reinterpret_cast<float4*>(op + e) = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+}
+
 // Merges split-KV partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
 // One thread per 4 output elements.
 template <int HD>
@@ -211,7 +306,7 @@ Plan plan(int batch, int T, int ctx, int nh, int nkv, int hd, int causal) {
     const long long blocks = (long long)batch * nkv * p.qblocks;
     const int S = ctx + T;
     const int nstage = (S + kStage - 1) / kStage;
-    if (blocks > 0 && blocks < kTargetBlocks && !causal) {
+    if (blocks > 0 && blocks < kTargetBlocks && !causal && S > kSmallKeys) {
         long long want = (kTargetBlocks + blocks - 1) / blocks;
         long long cap = nstage / 2;  // at least two stages per split
         p.nsplit = (int)std::max(1LL, std::min(want, cap));
@@ -285,6 +380,16 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
     a.qmul = scale * dgk::kLog2e;
     a.causal = causal;
     hipStream_t s = (hipStream_t)stream;
+    if (ctx + T <= kSmallKeys) {
+        const long long units = (long long)batch * nh;
+        const long long blocks = (units + 3) / 4;
+        if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
+        if (hd == 128)
+            hipLaunchKernelGGL(attn_small_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a, units);
+        else
+            hipLaunchKernelGGL(attn_small_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, units);
+        return dg::launch_status(fn);
+    }
     if (hd == 128)
         hipLaunchKernelGGL(attn_split_gqa_kernel<128>, dim3((unsigned)nblocks), dim3(512), 0, s, a);
     else

@@ -74,6 +74,10 @@ SPLIT_SHAPES = [
     (3, 8, 0, 16, 16, 64, 0.125, True),    # causal frames
     (2, 45, 19, 6, 3, 128, 0.5, True),     # causal after a cache
     (1, 130, 300, 16, 8, 128, 1.0, False), # several workgroups per kv head
+    (2, 5, 3, 4, 2, 128, 1.0, False),      # 8 keys: short-key-set kernel, cache + canvas
+    (1, 4, 4, 6, 3, 64, 0.5, True),        # short set, causal after a cache
+    (1, 7, 0, 4, 1, 128, 0.3, True),       # short set, G = 4
+    (2, 8, 1, 4, 2, 64, 1.0, False),       # 9 keys: just past the short-set limit
 ]
 
 
