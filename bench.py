@@ -79,6 +79,8 @@ class SplitWork:
         from gqa_flash_attention_dg_amd.canvas import CanvasBlock
 
         self.name, self.c = name, case
+        # ctx + T <= 8 runs the short-key-set kernel, longer key sets the tiled MFMA kernel
+        self.dominant = "attn_small" if case.ctx + case.T <= 8 else "attn_split_gqa"
         d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
         c = case
         self.blk = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, d(c.kc), d(c.vc), d(c.wq),
