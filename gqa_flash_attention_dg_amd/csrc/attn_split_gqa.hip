@@ -75,7 +75,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const int kv = bk % a.nkv;
     const int b = bk / a.nkv;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+    const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
     const int pair = wave & (kPairs - 1), hi = wave >> 2;
 
     const int nq = a.T * a.G;                 // query vectors of this (b, kv)
@@ -104,8 +105,22 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const float* kb = a.k + ((size_t)b * a.T * a.nkv + kv) * HD;
     const float* vb = a.v + ((size_t)b * a.T * a.nkv + kv) * HD;
 
-    // Each wave issues an equal share of the stage's 4 * kLoadsPerTile wave-wide loads.
+    // Each wave issues an equal share of the stage's 4 * kLoadsPerTile wave-wide loads (K and V
+    // of both tiles).  A tile lying wholly in the cache or wholly in the canvas is addressed
+    // from a scalar base plus a loop-invariant per-lane offset; only a tile that straddles the
+    // seam or the end of the key range forms per-lane addresses.
     constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / kWaves;
+    const int pos = lane % TL::kChunks;
+    int trow[kLoadsPerWave], coff[kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int L = wave * kLoadsPerWave + i;
+        const int ld = L % TL::kLoadsPerTile;
+        const bool isv = (L / TL::kLoadsPerTile) & 1;
+        trow[i] = dgk::dma_row<HD>(ld, lane);
+        coff[i] = 16 * (isv ? pos : (pos ^ (trow[i] % TL::kChunks)));
+    }
+    const unsigned rstride_c = HD * 4, rstride_v = (unsigned)cstride * 4;
     auto issue_stage = [&](int st, int buf) {
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -113,13 +128,22 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             const int part = L / TL::kLoadsPerTile;  // K0, V0, K1, V1
             const int ld = L % TL::kLoadsPerTile;
             const int tile = part >> 1, isv = part & 1;
-            const int j = min(st * kStage + tile * dgk::kKeys + dgk::dma_row<HD>(ld, lane), kend - 1);
-            const float* rp = j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * HD
-                                        : (isv ? vb : kb) + (size_t)(j - a.ctx) * cstride;
-            if (isv)
-                dgk::dma_load<HD, false>(tile_ptr(buf, tile, 1), ld, rp, lane);
-            else
-                dgk::dma_load<HD, true>(tile_ptr(buf, tile, 0), ld, rp, lane);
+            const int j0 = st * kStage + tile * dgk::kKeys;
+            float* dst = tile_ptr(buf, tile, isv) + ld * 256;
+            const char* p;
+            if (j0 + dgk::kKeys <= a.ctx && j0 + dgk::kKeys <= kend) {
+                p = reinterpret_cast<const char*>((isv ? vcb : kcb) + (size_t)j0 * HD) +
+                    ((unsigned)trow[i] * rstride_c + (unsigned)coff[i]);
+            } else if (j0 >= a.ctx && j0 + dgk::kKeys <= kend) {
+                p = reinterpret_cast<const char*>((isv ? vb : kb) + (size_t)(j0 - a.ctx) * cstride) +
+                    ((unsigned)trow[i] * rstride_v + (unsigned)coff[i]);
+            } else {
+                const int j = min(j0 + trow[i], kend - 1);
+                p = reinterpret_cast<const char*>(j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * HD
+                                                            : (isv ? vb : kb) + (size_t)(j - a.ctx) * cstride) +
+                    coff[i];
+            }
+            __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)dst, 16, 0, 0);
         }
     };
 
@@ -140,7 +164,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         if (st + 1 < st_end) issue_stage(st + 1, buf ^ 1);
         const int t0 = st * kStage + hi * dgk::kKeys;
         if (pair_active && t0 < kend) {
-            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg);
+            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg, -dgk::ref_of(m));
             const bool need_mask =
                 t0 + dgk::kKeys > kend || (a.causal && t0 + dgk::kKeys - 1 - a.ctx > row_min);
             if (need_mask) {

@@ -82,12 +82,14 @@ __device__ inline void dma_load(float* tile, int ld, const float* rowptr, int la
                                      (lds_void*)(tile + ld * 256), 16, 0, 0);
 }
 
-// S^T tile (32 keys x 32 queries) from a swizzled K tile in LDS.
+// S^T tile (32 keys x 32 queries) from a swizzled K tile in LDS, accumulated onto `init`
+// (the caller passes minus its softmax reference, so the subtraction rides in the MFMA).
 template <int HD>
 __device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
-                                const float (&qreg)[HD / 2]) {
+                                const float (&qreg)[HD / 2], float init) {
     using TL = Tile<HD>;
-    f32x16 s = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16 s = {init, init, init, init, init, init, init, init,
+                init, init, init, init, init, init, init, init};
     const float* kr = ks + l32 * HD;
     const int sw = l32 % TL::kChunks;
 #pragma unroll
@@ -103,30 +105,47 @@ __device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Online-softmax update on a masked S^T tile (masked entries hold -inf).  Turns s into
-// probabilities, rescales o and the lane's partial denominator.
+// Online-softmax update on a masked S^T tile.  On entry s holds score - ref, where ref is the
+// lane's softmax reference m (0 while m is still -inf); masked entries hold -inf.  The
+// reference only moves when some score exceeds it by more than kHeadroom (log2 units): then
+// the tile max becomes the new reference and o and lsum are rescaled.  Otherwise the
+// probabilities exp2(score - m) are taken as they are (each below 2^kHeadroom, far from f32
+// overflow; smaller ones lose nothing relative to the terms at or above the reference).  The
+// result is the same sum as with a per-tile max; only rounding differs.  On exit s holds the
+// probabilities.
+constexpr float kHeadroom = 60.0f;
+
+__device__ inline float ref_of(float m) { return m == -INFINITY ? 0.0f : m; }
+
 template <int HD>
 __device__ inline void softmax_update(f32x16& s, float& m, float& lsum,
                                       f32x16 (&o)[Tile<HD>::kGroups]) {
-    float tmax = fmaxf(s[0], s[1]);
+    float lmax = s[0];
 #pragma unroll
-    for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float corr = fast_exp2(m - m_use);
+    for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, s[r]);
+    if (__any(lmax > kHeadroom || m == -INFINITY)) {
+        const float ref = ref_of(m);
+        const float tmax = fmaxf(lmax, __shfl_xor(lmax, 32));
+        const float m_new = fmaxf(m, ref + tmax);
+        const float nref = ref_of(m_new);
+        const float corr = fast_exp2(m - nref);
+        const float shift = ref - nref;
+        lsum *= corr;
+#pragma unroll
+        for (int t = 0; t < Tile<HD>::kGroups; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] += shift;
+        m = m_new;
+    }
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        s[r] = fast_exp2(s[r] - m_use);
+        s[r] = fast_exp2(s[r]);
         psum += s[r];
     }
-    lsum = lsum * corr + psum;
-    m = m_new;
-#pragma unroll
-    for (int t = 0; t < Tile<HD>::kGroups; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+    lsum += psum;
 }
 
 // O^T += V^T P^T from a plain V tile in LDS; the lane reads its G contiguous head elements

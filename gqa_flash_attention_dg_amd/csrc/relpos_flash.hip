@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
         if (st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
         const int t0 = st * kStage + hi * dgk::kKeys;
         if (pair_active && t0 < a.n) {
-            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg);
+            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg, -dgk::ref_of(m));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = t0 + dgk::key_of(r, half);
