@@ -105,43 +105,39 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const float* kb = a.k + ((size_t)b * a.T * a.nkv + kv) * HD;
     const float* vb = a.v + ((size_t)b * a.T * a.nkv + kv) * HD;
 
-    // Each wave issues an equal share of the stage's 4 * kLoadsPerTile wave-wide loads (K and V
-    // of both tiles).  A tile lying wholly in the cache or wholly in the canvas is addressed
-    // from a scalar base plus a loop-invariant per-lane offset; only a tile that straddles the
-    // seam or the end of the key range forms per-lane addresses.
-    constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / kWaves;
-    const int pos = lane % TL::kChunks;
-    int trow[kLoadsPerWave], coff[kLoadsPerWave];
-#pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int L = wave * kLoadsPerWave + i;
-        const int ld = L % TL::kLoadsPerTile;
-        const bool isv = (L / TL::kLoadsPerTile) & 1;
-        trow[i] = dgk::dma_row<HD>(ld, lane);
-        coff[i] = 16 * (isv ? pos : (pos ^ (trow[i] % TL::kChunks)));
-    }
+    // The four even-tile wavefronts issue the stage's 4 * kLoadsPerTile wave-wide loads (K and
+    // V of both tiles); their odd-tile partners start on the MFMAs meanwhile (on this hardware
+    // vector and scalar instructions do not overlap the f32 matrix pipe, so one member of each
+    // SIMD pair keeps it fed).  A tile lying wholly in the cache or wholly in the canvas is
+    // addressed from a scalar base plus a loop-invariant per-lane offset; only a tile that
+    // straddles the seam or the end of the key range forms per-lane addresses.
+    constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / (kWaves / 2);
+    constexpr int R = TL::kRowsPerLoad;
+    const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
     const unsigned rstride_c = HD * 4, rstride_v = (unsigned)cstride * 4;
     auto issue_stage = [&](int st, int buf) {
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
-            const int L = wave * kLoadsPerWave + i;
+            const int L = pair * kLoadsPerWave + i;
             const int part = L / TL::kLoadsPerTile;  // K0, V0, K1, V1
             const int ld = L % TL::kLoadsPerTile;
             const int tile = part >> 1, isv = part & 1;
+            const int trow = ld * R + rsub;           // tile row of this lane's chunk
+            const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
             const int j0 = st * kStage + tile * dgk::kKeys;
             float* dst = tile_ptr(buf, tile, isv) + ld * 256;
             const char* p;
             if (j0 + dgk::kKeys <= a.ctx && j0 + dgk::kKeys <= kend) {
                 p = reinterpret_cast<const char*>((isv ? vcb : kcb) + (size_t)j0 * HD) +
-                    ((unsigned)trow[i] * rstride_c + (unsigned)coff[i]);
+                    ((unsigned)trow * rstride_c + coff);
             } else if (j0 >= a.ctx && j0 + dgk::kKeys <= kend) {
                 p = reinterpret_cast<const char*>((isv ? vb : kb) + (size_t)(j0 - a.ctx) * cstride) +
-                    ((unsigned)trow[i] * rstride_v + (unsigned)coff[i]);
+                    ((unsigned)trow * rstride_v + coff);
             } else {
-                const int j = min(j0 + trow[i], kend - 1);
+                const int j = min(j0 + trow, kend - 1);
                 p = reinterpret_cast<const char*>(j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * HD
                                                             : (isv ? vb : kb) + (size_t)(j - a.ctx) * cstride) +
-                    coff[i];
+                    coff;
             }
             __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)dst, 16, 0, 0);
         }
@@ -156,12 +152,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    if (st_begin < st_end) issue_stage(st_begin, 0);
+    if (!hi && st_begin < st_end) issue_stage(st_begin, 0);
     for (int st = st_begin; st < st_end; ++st) {
         const int buf = (st - st_begin) & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
         __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
-        if (st + 1 < st_end) issue_stage(st + 1, buf ^ 1);
+        if (!hi && st + 1 < st_end) issue_stage(st + 1, buf ^ 1);
         const int t0 = st * kStage + hi * dgk::kKeys;
         if (pair_active && t0 < kend) {
             f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg, -dgk::ref_of(m));
