@@ -85,11 +85,9 @@ __device__ inline void dma_load(float* tile, int ld, const float* rowptr, int la
 // S^T tile (32 keys x 32 queries) from a swizzled K tile in LDS, accumulated onto `init`
 // (the caller passes minus its softmax reference, so the subtraction rides in the MFMA).
 template <int HD>
-__device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
-                                const float (&qreg)[HD / 2], float init) {
+__device__ inline f32x16 scores_from(const float* __restrict__ ks, int l32, int half,
+                                     const float (&qreg)[HD / 2], f32x16 s) {
     using TL = Tile<HD>;
-    f32x16 s = {init, init, init, init, init, init, init, init,
-                init, init, init, init, init, init, init, init};
     const float* kr = ks + l32 * HD;
     const int sw = l32 % TL::kChunks;
 #pragma unroll
@@ -101,6 +99,14 @@ __device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qreg[4 * g + 3], s, 0, 0, 0);
     }
     return s;
+}
+
+template <int HD>
+__device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
+                                const float (&qreg)[HD / 2], float init) {
+    const f32x16 s = {init, init, init, init, init, init, init, init,
+                      init, init, init, init, init, init, init, init};
+    return scores_from<HD>(ks, l32, half, qreg, s);
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -222,6 +228,43 @@ __device__ inline void pair_merge(float* smem, int pair, bool hi, bool active, i
         for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * ca + mg[(t * 16 + r) * 64 + lane] * cb;
     lsum = lsum * ca + l2 * cb;
     m = mn;
+}
+
+// Merges the softmax states of `nparts` wavefronts that hold the same 32 queries over disjoint
+// keys: parts 1..nparts-1 hand (o, m, lsum) to part 0 through LDS scratch `smem` (at least
+// ngroups * (nparts-1) * 64 * (hd/2 + 2) floats, not in use by anyone).  Every thread of the
+// workgroup must call this; afterwards part 0 holds the merged state.
+template <int HD>
+__device__ inline void group_merge(float* smem, int grp, int part, int nparts, bool active,
+                                   int lane, float& m, float& lsum,
+                                   f32x16 (&o)[Tile<HD>::kGroups]) {
+    constexpr int kVals = Tile<HD>::kGroups * 16 + 2;
+    float* base = smem + grp * (nparts - 1) * kVals * 64;
+    if (part > 0 && active) {
+        float* mg = base + (part - 1) * kVals * 64;
+#pragma unroll
+        for (int t = 0; t < Tile<HD>::kGroups; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mg[(t * 16 + r) * 64 + lane] = o[t][r];
+        mg[(kVals - 2) * 64 + lane] = m;
+        mg[(kVals - 1) * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (part > 0 || !active) return;
+    for (int p = 1; p < nparts; ++p) {
+        const float* mg = base + (p - 1) * kVals * 64;
+        const float m2 = mg[(kVals - 2) * 64 + lane];
+        const float l2 = mg[(kVals - 1) * 64 + lane];
+        const float mn = fmaxf(m, m2);
+        const float mu = (mn == -INFINITY) ? 0.0f : mn;
+        const float ca = fast_exp2(m - mu), cb = fast_exp2(m2 - mu);
+#pragma unroll
+        for (int t = 0; t < Tile<HD>::kGroups; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * ca + mg[(t * 16 + r) * 64 + lane] * cb;
+        lsum = lsum * ca + l2 * cb;
+        m = mn;
+    }
 }
 
 }  // namespace dgk

@@ -8,10 +8,13 @@
 // qkv layout (q | k | v per token, heads contiguous) and the scale 1/sqrt(hd).
 //
 // The page writes dh/dw to global [heads, n, gh] / [heads, n, gw] buffers and then looks them
-// up per key.  Here each workgroup computes the bias rows of its own 128 queries into LDS in
-// a prologue (no global round trip, no workspace), then runs the same f32-MFMA flash loop as
-// the split-GQA kernel (flash_core.hpp: 4 pairs of wavefronts on alternate 32-key tiles,
-// double-buffered direct global->LDS tiles) with the two table lookups added to each score.
+// up per key.  Here each workgroup computes the bias rows of its own 64 queries in a prologue
+// (into LDS and registers: no global round trip, no workspace), then runs the f32-MFMA flash
+// loop of flash_core.hpp.  A workgroup is 2 groups of 32 queries x 4 wavefronts; the 4
+// wavefronts of a group take every 4th 32-key tile (stages of 128 keys, double-buffered
+// direct global->LDS tiles) and merge their softmax states at the end.  The bias enters each
+// score through the MFMA accumulator's starting value.  64-query workgroups give 768
+// workgroups at the 64x64-grid, 12-head shape: three full rounds on 256 CUs.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
@@ -20,11 +23,11 @@ namespace {
 using dgk::f32x16;
 constexpr int HD = 64;
 constexpr int kWaves = 8;
-constexpr int kPairs = 4;
-constexpr int kBlockQ = kPairs * dgk::kQuery;
-constexpr int kStage = 2 * dgk::kKeys;
-constexpr int kMaxGrid = 64;                 // gh, gw <= 64
-constexpr int kTabStride = 2 * kMaxGrid + 1; // dh | dw per query, padded against bank conflicts
+constexpr int kQGroups = 2;                   // query groups of 32 per workgroup
+constexpr int kParts = 4;                     // wavefronts per group, one key tile each per stage
+constexpr int kBlockQ = kQGroups * dgk::kQuery;
+constexpr int kStage = kParts * dgk::kKeys;   // 128 keys per stage
+constexpr int kMaxGrid = 64;                  // gh, gw <= 64
 
 struct RelArgs {
     const float* qkv;
@@ -41,33 +44,46 @@ __device__ inline int xcd_remap(int bid, int n) {
     return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
+// kAligned: gw is 32 or 64, so every 32-key tile lies inside one grid row (one ky) and, as a
+// stage spans 128 keys, a wavefront always sees the same 32 kx values: its 16 dw terms stay
+// in registers and the dh term is one LDS read per tile.  Otherwise both terms are looked up
+// per score from LDS tables.
+template <bool kAligned>
 __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     using TL = dgk::Tile<HD>;
-    __shared__ __attribute__((aligned(16))) float smem[2 * 2 * 2 * TL::kFloats];
-    __shared__ float tab[kPairs * dgk::kQuery * kTabStride];
+    // staging: [buffer][tile][K, V] and bias tables [group][ky or kx][query] (dh, then dw)
+    __shared__ __attribute__((aligned(16))) float smem[2 * kParts * 2 * TL::kFloats];
+    __shared__ float tab[2 * kQGroups * kMaxGrid * dgk::kQuery];
     auto tile_ptr = [&](int buf, int tile, int isv) {
-        return smem + ((buf * 2 + tile) * 2 + isv) * TL::kFloats;
+        return smem + ((buf * kParts + tile) * 2 + isv) * TL::kFloats;
     };
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks);
     const int qb = lid % a.qblocks;
     const int head = lid / a.qblocks;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    const int pair = wave & (kPairs - 1), hi = wave >> 2;
-    const size_t rs = (size_t)3 * a.W;  // qkv row stride
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int grp = wave & (kQGroups - 1), part = wave >> 1;
+    const size_t rs = (size_t)3 * a.W;  // qkv row stride (floats)
 
-    const int qfirst = qb * kBlockQ + pair * dgk::kQuery;
+    const int qfirst = qb * kBlockQ + grp * dgk::kQuery;
     const int qi = qfirst + l32;
     const bool valid = qi < a.n;
     const float* qrow = a.qkv + (size_t)(valid ? qi : 0) * rs + head * HD;
-    const bool pair_active = qfirst < a.n;
+    const bool active = qfirst < a.n;
     const bool bias = a.rh != nullptr;
-    float* mytab = tab + (pair * dgk::kQuery + l32) * kTabStride;
+    float* dh_tab = tab + grp * kMaxGrid * dgk::kQuery;                   // [ky][query]
+    float* dw_tab = tab + (kQGroups + grp) * kMaxGrid * dgk::kQuery;      // [kx][query]
+    const int kxbase = (part * dgk::kKeys) % a.gw;  // aligned case: this wave's kx offset
 
-    // Prologue: this query's bias rows in log2 units, dh[ky] = <q, Rh[qy,ky]> (even-tile wave)
-    // and dw[kx] = <q, Rw[qx,kx]> (odd-tile wave); lane halves split the ky / kx range.
-    if (bias && pair_active) {
+    // Prologue: the bias dot products of this group's queries in log2 units.  dh[ky] =
+    // <q, Rh[qy,ky]> for all ky, split over the group's 4 wavefronts and 2 lane halves; dw[kx] =
+    // <q, Rw[qx,kx]>, either for this lane's own 16 kx values (aligned) or for all kx (table).
+    float dwreg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dwreg[r] = 0.0f;
+    if (bias && active) {
         float qf[HD];
 #pragma unroll
         for (int c = 0; c < HD; c += 4) {
@@ -75,36 +91,51 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
             qf[c] = t.x; qf[c + 1] = t.y; qf[c + 2] = t.z; qf[c + 3] = t.w;
         }
-        const int g = hi ? a.gw : a.gh;
-        const int coord = valid ? (hi ? qi % a.gw : qi / a.gw) : 0;
-        const float* table = hi ? a.rw : a.rh;
-        for (int kk = half; kk < g; kk += 2) {
-            const float* tr = table + ((size_t)coord * g + kk) * HD;
+        auto dot = [&](const float* tr) {
             float d = 0.0f;
 #pragma unroll
             for (int c = 0; c < HD; c += 4) {
                 const float4 t = *reinterpret_cast<const float4*>(tr + c);
                 d += qf[c] * t.x + qf[c + 1] * t.y + qf[c + 2] * t.z + qf[c + 3] * t.w;
             }
-            mytab[hi * kMaxGrid + kk] = d * dgk::kLog2e;
+            return d * dgk::kLog2e;
+        };
+        const int qy = valid ? qi / a.gw : 0, qx = valid ? qi % a.gw : 0;
+        for (int ky = part * 2 + half; ky < a.gh; ky += 2 * kParts)
+            dh_tab[ky * dgk::kQuery + l32] = dot(a.rh + ((size_t)qy * a.gh + ky) * HD);
+        if (kAligned) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dwreg[r] = dot(a.rw + ((size_t)qx * a.gw + kxbase + dgk::key_of(r, half)) * HD);
+        } else {
+            for (int kx = part * 2 + half; kx < a.gw; kx += 2 * kParts)
+                dw_tab[kx * dgk::kQuery + l32] = dot(a.rw + ((size_t)qx * a.gw + kx) * HD);
         }
     }
 
-    const float* kbase = a.qkv + a.W + head * HD;
-    const float* vbase = a.qkv + 2 * (size_t)a.W + head * HD;
-    constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / kWaves;
+    // Loads: the four wavefronts with part < 2 (one per SIMD) issue each stage's 64 wave-wide
+    // loads -- K and V of 4 tiles -- while their SIMD partners keep the matrix pipe busy.
+    constexpr int kLoadsPerWave = 2 * kParts * TL::kLoadsPerTile / 4;
+    constexpr int R = TL::kRowsPerLoad;
+    const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
+    const char* kbase = reinterpret_cast<const char*>(a.qkv + a.W + head * HD);
+    const char* vbase = reinterpret_cast<const char*>(a.qkv + 2 * (size_t)a.W + head * HD);
+    const unsigned rsb = (unsigned)(rs * 4);
     auto issue_stage = [&](int st, int buf) {
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int L = wave * kLoadsPerWave + i;
-            const int part = L / TL::kLoadsPerTile;  // K0, V0, K1, V1
+            const int tpart = L / TL::kLoadsPerTile;
             const int ld = L % TL::kLoadsPerTile;
-            const int tile = part >> 1, isv = part & 1;
-            const int j = min(st * kStage + tile * dgk::kKeys + dgk::dma_row<HD>(ld, lane), a.n - 1);
-            if (isv)
-                dgk::dma_load<HD, false>(tile_ptr(buf, tile, 1), ld, vbase + (size_t)j * rs, lane);
-            else
-                dgk::dma_load<HD, true>(tile_ptr(buf, tile, 0), ld, kbase + (size_t)j * rs, lane);
+            const int tile = tpart >> 1, isv = tpart & 1;
+            const int trow = ld * R + rsub;
+            const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
+            const int j0 = st * kStage + tile * dgk::kKeys;
+            const char* b = isv ? vbase : kbase;
+            const char* p = j0 + dgk::kKeys <= a.n
+                                ? b + (size_t)j0 * rsb + ((unsigned)trow * rsb + coff)
+                                : b + (size_t)min(j0 + trow, a.n - 1) * rsb + coff;
+            __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)(tile_ptr(buf, tile, isv) + ld * 256), 16, 0, 0);
         }
     };
 
@@ -118,34 +149,48 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     float m = -INFINITY, lsum = 0.0f;
 
     const int nstage = (a.n + kStage - 1) / kStage;
-    issue_stage(0, 0);
+    if (wave < 4) issue_stage(0, 0);
     for (int st = 0; st < nstage; ++st) {
         const int buf = st & 1;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // stage st has landed everywhere, stage st-1 is consumed (and the
-                          // bias table is complete before the first use)
-        if (st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
-        const int t0 = st * kStage + hi * dgk::kKeys;
-        if (pair_active && t0 < a.n) {
-            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg, -dgk::ref_of(m));
+                          // bias tables are complete before the first use)
+        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
+        const int t0 = st * kStage + part * dgk::kKeys;
+        if (active && t0 < a.n) {
+            const float ref = dgk::ref_of(m);
+            f32x16 s;
+            if (kAligned) {
+                const float dhv = bias ? dh_tab[(t0 / a.gw) * dgk::kQuery + l32] : 0.0f;
+                const float c0 = dhv - ref;
+                f32x16 init;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = t0 + dgk::key_of(r, half);
-                if (j >= a.n) {
-                    s[r] = -INFINITY;
-                } else if (bias) {
-                    s[r] += mytab[j / a.gw] + mytab[kMaxGrid + j % a.gw];
+                for (int r = 0; r < 16; ++r) init[r] = dwreg[r] + c0;
+                s = dgk::scores_from<HD>(tile_ptr(buf, part, 0), l32, half, qreg, init);
+            } else {
+                s = dgk::scores<HD>(tile_ptr(buf, part, 0), l32, half, qreg, -ref);
+                if (bias) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = min(t0 + dgk::key_of(r, half), a.n - 1);
+                        s[r] += dh_tab[(j / a.gw) * dgk::kQuery + l32] + dw_tab[(j % a.gw) * dgk::kQuery + l32];
+                    }
                 }
             }
+            if (t0 + dgk::kKeys > a.n) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (t0 + dgk::key_of(r, half) >= a.n) s[r] = -INFINITY;
+            }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            dgk::accumulate_pv<HD>(tile_ptr(buf, hi, 1), l32, half, s, o);
+            dgk::accumulate_pv<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
         }
     }
 
     __syncthreads();
-    dgk::pair_merge<HD>(smem, pair, hi, pair_active, lane, m, lsum, o);
+    dgk::group_merge<HD>(smem, grp, part, kParts, active, lane, m, lsum, o);
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (hi || !valid) return;
+    if (part != 0 || !valid) return;
     dgk::store_row<HD>(a.out + (size_t)qi * a.W + head * HD, 1.0f / ltot, o, half);
 }
 
@@ -180,7 +225,11 @@ extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float*
     a.qblocks = (int)qblocks;
     a.nblocks = (int)(qblocks * heads);
     a.qmul = scale * dgk::kLog2e;
-    hipLaunchKernelGGL(relpos_flash_kernel, dim3((unsigned)a.nblocks), dim3(512), 0,
-                       (hipStream_t)stream, a);
+    if (gw == 32 || gw == 64)
+        hipLaunchKernelGGL(relpos_flash_kernel<true>, dim3((unsigned)a.nblocks), dim3(512), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(relpos_flash_kernel<false>, dim3((unsigned)a.nblocks), dim3(512), 0,
+                           (hipStream_t)stream, a);
     return dg::launch_status(fn);
 }

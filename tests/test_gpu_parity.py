@@ -201,7 +201,8 @@ def test_depformer_frames_every_element():
 
 @pytest.mark.parametrize("gh,gw,heads,bias", [(3, 5, 2, True), (8, 8, 3, True), (4, 64, 1, True),
                                               (64, 4, 2, True), (1, 1, 1, True), (9, 7, 2, False),
-                                              (16, 16, 12, True)])
+                                              (16, 16, 12, True), (3, 32, 2, True), (41, 32, 1, True),
+                                              (5, 64, 3, False), (64, 64, 1, True)])
 def test_relpos_small(gh, gw, heads, bias):
     c = synth.relpos_case(gh, gw, heads, 64, seed=gh * 100 + gw, bias=bias, table_std=0.3)
     ref = oracle.relpos_attn(c.qkv, c.rh, c.rw, gh, gw, heads, 64, c.scale)
