@@ -147,8 +147,13 @@ class RelposWork:
         self.qkv, self.rh, self.rw = d(case.qkv), d(case.rh), d(case.rw)
         n, W = case.gh * case.gw, case.heads * case.hd
         self.out = torch.empty((n, W), device="cuda")
+        import gqa_flash_attention_dg_amd as dg
+        self.ws_bytes = dg.relpos_flash_attn_workspace_size(case.gh, case.gw, case.heads, case.hd)
+        self.ws = torch.empty((max(self.ws_bytes, 4) // 4,), device="cuda")
         self.flops = case.heads * n * n * 4 * case.hd + \
             (case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0)
+        # every input read once, the output written once (the bias rows it keeps in its
+        # workspace are the method's own intermediate, not counted)
         self.attn_bytes = 4 * (n * 3 * W + n * W + (case.gh ** 2 + case.gw ** 2) * case.hd)
         self.norm_bytes = 0
         self.bound = "mfma"
@@ -161,7 +166,8 @@ class RelposWork:
     def _call(self, out):
         import gqa_flash_attention_dg_amd as dg
         c = self.c
-        dg.relpos_flash_attn(self.qkv, self.rh, self.rw, out, c.gh, c.gw, c.heads, c.hd, c.scale)
+        dg.relpos_flash_attn(self.qkv, self.rh, self.rw, out, c.gh, c.gw, c.heads, c.hd, c.scale,
+                             self.ws, self.ws_bytes)
 
     def step(self, ev=None):
         if ev:

@@ -20,7 +20,8 @@ DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
 DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP = 1, 2, 4
 
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_attn_split_gqa_workspace_size",
-           "dg_attn_split_gqa", "relpos_flash_attn", "dg_last_error")
+           "dg_attn_split_gqa", "relpos_flash_attn_workspace_size", "relpos_flash_attn",
+           "dg_last_error")
 
 
 class DgError(RuntimeError):
@@ -47,7 +48,9 @@ def lib() -> ctypes.CDLL:
         L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
         L.dg_attn_split_gqa_workspace_size.restype = Z
         L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
-        L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp]
+        L.relpos_flash_attn_workspace_size.argtypes = [I, I, I, I]
+        L.relpos_flash_attn_workspace_size.restype = Z
+        L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp, Z, vp]
         for name in ("dg_rope_table", "dg_headnorm_rope", "dg_attn_split_gqa",
                      "relpos_flash_attn"):
             getattr(L, name).restype = I
@@ -120,29 +123,38 @@ def dg_attn_split_gqa_workspace_size(batch: int, T: int, ctx: int, nh: int, nkv:
     return int(lib().dg_attn_split_gqa_workspace_size(batch, T, ctx, nh, nkv, hd))
 
 
+def _workspace(workspace, workspace_bytes):
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if workspace.numel() * workspace.element_size() < workspace_bytes:
+        raise ValueError("workspace is smaller than workspace_bytes")
+    return workspace.data_ptr(), int(workspace_bytes)
+
+
 def dg_attn_split_gqa(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int, nkv: int,
                       hd: int, scale: float, causal: int, workspace=None,
                       workspace_bytes: int = 0, stream=None) -> None:
     _nonneg(batch=batch, T=T, ctx=ctx, nh=nh, nkv=nkv, hd=hd)
     nq, nkvc, nc = batch * T * nh * hd, batch * T * nkv * hd, batch * nkv * ctx * hd
-    ws = None
-    if workspace is not None:
-        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or \
-                not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        if workspace.numel() * workspace.element_size() < workspace_bytes:
-            raise ValueError("workspace is smaller than workspace_bytes")
-        ws = workspace.data_ptr()
+    ws, wsb = _workspace(workspace, workspace_bytes)
     _check(lib().dg_attn_split_gqa(_ptr(q, "q", nq), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
                                    _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq),
                                    batch, T, ctx, nh, nkv, hd, float(scale), int(causal), ws,
-                                   int(workspace_bytes) if ws else 0, _stream(stream)))
+                                   wsb, _stream(stream)))
+
+
+def relpos_flash_attn_workspace_size(gh: int, gw: int, heads: int, hd: int) -> int:
+    return int(lib().relpos_flash_attn_workspace_size(gh, gw, heads, hd))
 
 
 def relpos_flash_attn(qkv, rh, rw, out, gh: int, gw: int, heads: int, hd: int, scale: float,
-                      stream=None) -> None:
+                      workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     _nonneg(gh=gh, gw=gw, heads=heads, hd=hd)
     n, W = gh * gw, heads * hd
+    ws, wsb = _workspace(workspace, workspace_bytes)
     _check(lib().relpos_flash_attn(_ptr(qkv, "qkv", n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
                                    _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", n * W),
-                                   gh, gw, heads, hd, float(scale), _stream(stream)))
+                                   gh, gw, heads, hd, float(scale), ws, wsb, _stream(stream)))

@@ -367,6 +367,8 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
         return dg::fail(DG_EINVAL, "%s: size overflow", fn);
     if (workspace && workspace_bytes == 0)
         return dg::fail(DG_EINVAL, "%s: workspace given with workspace_bytes 0", fn);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15))
+        return dg::fail(DG_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     if (nq == 0) return dg::ok();
     if (!q || !k || !v || !out) return dg::fail(DG_EINVAL, "%s: q, k, v and out must be non-NULL", fn);
     if (ncache > 0 && (!kc || !vc)) return dg::fail(DG_EINVAL, "%s: kc/vc NULL with ctx %d > 0", fn, ctx);

@@ -82,8 +82,7 @@ __device__ inline void dma_load(float* tile, int ld, const float* rowptr, int la
                                      (lds_void*)(tile + ld * 256), 16, 0, 0);
 }
 
-// S^T tile (32 keys x 32 queries) from a swizzled K tile in LDS, accumulated onto `init`
-// (the caller passes minus its softmax reference, so the subtraction rides in the MFMA).
+// S^T tile (32 keys x 32 queries) from a swizzled K tile in LDS, accumulated onto `s`.
 template <int HD>
 __device__ inline f32x16 scores_from(const float* __restrict__ ks, int l32, int half,
                                      const float (&qreg)[HD / 2], f32x16 s) {
@@ -101,12 +100,21 @@ __device__ inline f32x16 scores_from(const float* __restrict__ ks, int l32, int 
     return s;
 }
 
+// As scores_from, plus a per-query shift added to every key of the lane's query column.  The
+// shift rides in one extra MFMA step (A = 1 and B = shift in the lower lane half, zeros in the
+// upper half) instead of a VALU pass over the 16 accumulator registers.
+template <int HD>
+__device__ inline f32x16 scores_shift(const float* __restrict__ ks, int l32, int half,
+                                      const float (&qreg)[HD / 2], float shift, f32x16 c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift, c, 0, 0, 0);
+    return scores_from<HD>(ks, l32, half, qreg, c);
+}
+
 template <int HD>
 __device__ inline f32x16 scores(const float* __restrict__ ks, int l32, int half,
-                                const float (&qreg)[HD / 2], float init) {
-    const f32x16 s = {init, init, init, init, init, init, init, init,
-                      init, init, init, init, init, init, init, init};
-    return scores_from<HD>(ks, l32, half, qreg, s);
+                                const float (&qreg)[HD / 2], float shift) {
+    const f32x16 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    return scores_shift<HD>(ks, l32, half, qreg, shift, z);
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -110,16 +110,24 @@ size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int n
  *   scale      finite float (1.0f for DiffusionGemma, 0.125f for the depformer).
  *   causal     0 = bidirectional (the page); 1 = canvas row i sees canvas keys 0..i.
  *   workspace  optional device scratch of at least dg_attn_split_gqa_workspace_size() bytes,
- *              used for a split of the key range; NULL/0 runs unsplit (same results up to
- *              rounding).  Must not overlap any input or `out`.
+ *              16-byte aligned, used for a split of the key range; NULL/0 runs unsplit (same
+ *              results up to rounding).  Must not overlap any input or `out`.
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
  * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, or a workspace
- * pointer with workspace_bytes too small; DG_EUNSUPPORTED for hd not 64 or 128.
+ * pointer that is misaligned or has workspace_bytes too small; DG_EUNSUPPORTED for hd not 64 or
+ * 128, or a cache block or canvas above 4 GiB.
  */
 int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
                       const float* v, float* out, int batch, int T, int ctx, int nh, int nkv,
                       int hd, float scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn can use to hold the
+ * hoisted bias rows (dh and dw, 64 floats per (head, query) each): 2 * heads * gh * gw * 64 * 4.
+ * Returns 0 for arguments relpos_flash_attn would reject.
+ */
+size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
 
 /*
  * relpos_flash_attn -- windowless vision attention with the decomposed relative-position bias,
@@ -134,12 +142,19 @@ int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const fl
  *     s_j = scale*<q_i, k_j> + <q_i, rh[qy, ky_j]> + <q_i, rw[qx, kx_j]>  (bias on unscaled q)
  *     out[i, h*hd:(h+1)*hd] = sum_j softmax(s)_j v_j
  *   scale      finite float (1/sqrt(hd) in the page's SAM block).
+ *   workspace  optional device scratch of at least relpos_flash_attn_workspace_size() bytes,
+ *              16-byte aligned: the bias rows are then computed once per (head, query) by a
+ *              first kernel, as the page's DHDW step does; NULL/0 computes them inside each
+ *              attention workgroup instead (same results up to rounding, slower).  Must not
+ *              overlap any input or `out`.
  * Errors: DG_EINVAL for gh, gw or heads < 0, exactly one of rh/rw NULL, a NULL qkv/out with
- * n > 0, a non-finite scale, overlapping buffers; DG_EUNSUPPORTED for hd != 64 (the page's
- * kernel fixes hd to its 64-wide workgroup) or gh or gw above 64.
+ * n > 0, a non-finite scale, overlapping buffers, a misaligned or too small workspace;
+ * DG_EUNSUPPORTED for hd != 64 (the page's kernel fixes hd to its 64-wide workgroup) or gh or
+ * gw above 64.
  */
 int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out, int gh,
-                      int gw, int heads, int hd, float scale, void* stream);
+                      int gw, int heads, int hd, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Message for the last nonzero status returned on the calling thread ("" if none). */
 const char* dg_last_error(void);

@@ -92,6 +92,7 @@ def test_attn_split_validation(L):
     assert f(*args(out=FAKE + 16)) == dg.DG_EINVAL          # out overlaps q
     assert "overlaps" in _err(L)
     assert f(*args(out=FAKE + (3 << 24) + 4)) == dg.DG_EINVAL  # out overlaps canvas k
+    assert f(*args(ws=FAKE + (6 << 24) + 8, wsb=1 << 20)) == dg.DG_EINVAL  # misaligned
     assert f(*args(T=0)) == dg.DG_OK                        # zero canvas: no-op
     assert f(*args(batch=0)) == dg.DG_OK
     assert L.dg_attn_split_gqa_workspace_size(1, 16, 32, 5, 2, 64) == 0
@@ -100,7 +101,7 @@ def test_attn_split_validation(L):
 def test_relpos_validation(L):
     f = L.relpos_flash_attn
     base = dict(qkv=FAKE, rh=FAKE + (1 << 26), rw=FAKE + (2 << 26), out=FAKE + (3 << 26),
-                gh=8, gw=8, heads=2, hd=64, scale=0.125, stream=None)
+                gh=8, gw=8, heads=2, hd=64, scale=0.125, ws=None, wsb=0, stream=None)
     call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
     assert call(hd=32) == dg.DG_EUNSUPPORTED
     assert call(gh=65) == dg.DG_EUNSUPPORTED
@@ -109,8 +110,13 @@ def test_relpos_validation(L):
     assert call(scale=float("inf")) == dg.DG_EINVAL
     assert call(out=FAKE + 4) == dg.DG_EINVAL              # overlaps qkv
     assert call(qkv=None) == dg.DG_EINVAL
+    assert call(ws=FAKE + (4 << 26) + 4, wsb=1 << 20) == dg.DG_EINVAL   # misaligned workspace
+    assert call(ws=FAKE + (4 << 26), wsb=16) == dg.DG_EINVAL           # too small
+    assert call(ws=FAKE + 64, wsb=1 << 20) == dg.DG_EINVAL              # overlaps qkv
     assert call(gh=0) == dg.DG_OK
     assert call(heads=0) == dg.DG_OK
+    assert L.relpos_flash_attn_workspace_size(64, 64, 12, 64) == 2 * 12 * 4096 * 64 * 4
+    assert L.relpos_flash_attn_workspace_size(64, 64, 12, 32) == 0
 
 
 def test_binding_refuses_bad_tensors_before_the_call():

@@ -203,18 +203,24 @@ def test_depformer_frames_every_element():
                                               (64, 4, 2, True), (1, 1, 1, True), (9, 7, 2, False),
                                               (16, 16, 12, True), (3, 32, 2, True), (41, 32, 1, True),
                                               (5, 64, 3, False), (64, 64, 1, True)])
-def test_relpos_small(gh, gw, heads, bias):
+@pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
+def test_relpos_small(gh, gw, heads, bias, use_ws):
     c = synth.relpos_case(gh, gw, heads, 64, seed=gh * 100 + gw, bias=bias, table_std=0.3)
     ref = oracle.relpos_attn(c.qkv, c.rh, c.rw, gh, gw, heads, 64, c.scale)
     out = torch.full((gh * gw, heads * 64), float("nan"), device="cuda")
-    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, gh, gw, heads, 64, c.scale)
-    assert_parity(host(out), ref, "relpos %dx%d" % (gh, gw))
+    nbytes = dg.relpos_flash_attn_workspace_size(gh, gw, heads, 64) if use_ws else 0
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), device="cuda") if use_ws else None
+    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, gh, gw, heads, 64, c.scale,
+                         ws, nbytes)
+    assert_parity(host(out), ref, "relpos %dx%d ws=%d" % (gh, gw, nbytes))
 
 
 def test_sam_global_sampled_rows():
     c = synth.sam_global()
     out = torch.empty((4096, 768), device="cuda")
-    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, 64, 64, 12, 64, c.scale)
+    nbytes = dg.relpos_flash_attn_workspace_size(64, 64, 12, 64)
+    ws = torch.empty((nbytes // 4,), device="cuda")
+    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, 64, 64, 12, 64, c.scale, ws, nbytes)
     got = host(out)
     rows = sample_rows(4096, 48, seed=9)
     rows = np.unique(np.concatenate([rows, [63, 64, 4032, 2047]])).astype(np.int64)
