@@ -3,8 +3,10 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
 A step is one pass of the hot path over one batch of synthetic input resident in HBM:
-  split-GQA workloads: headnorm(q), headnorm(k), headnorm(v), split-GQA attention;
-  sam_relpos: one rel-pos flash attention.
+  split-GQA workloads: the q, k and v headnorms in one launch, then split-GQA attention
+    (--norm in_attention: k and v in one launch, the q norm + rope applied by the attention
+    kernel in registers; --norm separate: the page's three headnorm dispatches);
+  sam_relpos: one rel-pos flash attention (bias-row pass + flash kernel).
 The default workload is the long-cache split-GQA canvas step (4 canvases, T=256, ctx=8192,
 nh=32, nkv=8, hd=128).  W untimed steps, then K steps timed with HIP events on the stream the
 kernels run on (torch's current stream), bracketed by device synchronisation.  The dominant
@@ -54,8 +56,10 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def split_counts(c):
-    """Algorithmic flops and bytes of one attention launch and of the three headnorm calls."""
+def split_counts(c, norm_mode="one_launch"):
+    """Algorithmic flops and bytes of one attention launch and of the headnorm work: q, k and v
+    each read and written once, or with the q norm inside attention only k and v (q is read by
+    the attention launch either way)."""
     if c.causal:
         pairs = c.B * c.nh * (c.T * c.ctx + c.T * (c.T + 1) // 2)
     else:
@@ -66,43 +70,61 @@ def split_counts(c):
     kv = c.B * c.T * c.nkv * c.hd
     cache = c.B * c.nkv * c.ctx * c.hd
     attn_bytes = f32 * (q + 2 * kv + 2 * cache + q)
-    norm_bytes = f32 * 2 * (q + 2 * kv) if c.normed else 0
+    qn = 0 if norm_mode == "in_attention" else q
+    norm_bytes = (f32 * 2 * (qn + 2 * kv)) if c.normed else 0
     return flops, attn_bytes, norm_bytes
 
 
 class SplitWork:
     dominant = "attn_split_gqa"
 
-    def __init__(self, name, case):
+    def __init__(self, name, case, norm_mode="one_launch"):
         import numpy as np
         import torch
         from gqa_flash_attention_dg_amd.canvas import CanvasBlock
 
-        self.name, self.c = name, case
+        self.name, self.c, self.norm_mode = name, case, norm_mode
         # ctx + T <= 8 runs the short-key-set kernel, longer key sets the tiled MFMA kernel
         self.dominant = "attn_small" if case.ctx + case.T <= 8 else "attn_split_gqa"
         d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
         c = case
         self.blk = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, d(c.kc), d(c.vc), d(c.wq),
                                d(c.wk), eps=c.eps, theta=c.theta, scale=c.scale,
-                               causal=c.causal, rope_cache=c.rope_cache, normed=c.normed)
+                               causal=c.causal, rope_cache=c.rope_cache, normed=c.normed,
+                               norm_mode=norm_mode)
         self.q, self.k, self.v = d(c.q), d(c.k), d(c.v)
         self.out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
-        self.flops, self.attn_bytes, self.norm_bytes = split_counts(c)
+        self.flops, self.attn_bytes, self.norm_bytes = split_counts(c, norm_mode)
         self.bound = "mfma" if self.flops / self.attn_bytes > 20 else "hbm"
 
     def config(self):
         c = self.c
         return {"workload": c.name, "batch": c.B, "T": c.T, "ctx": c.ctx, "nh": c.nh,
                 "nkv": c.nkv, "hd": c.hd, "scale": c.scale, "causal": bool(c.causal),
-                "step": ("headnorm q,k,v + " if c.normed else "") + "dg_attn_split_gqa"}
+                "step": self.step_name()}
+
+    def step_name(self):
+        if not self.c.normed:
+            return "dg_attn_split_gqa"
+        return {"one_launch": "dg_qkv_headnorm_rope(q, k, v) + dg_attn_split_gqa",
+                "in_attention": "dg_qkv_headnorm_rope(k, v) + dg_attn_split_gqa_qnorm",
+                "separate": "dg_headnorm_rope x3 (q, k, v) + dg_attn_split_gqa"}[self.norm_mode]
 
     def step(self, ev=None):
+        normed_q = self.c.normed and self.norm_mode == "in_attention"
         if self.c.normed:
-            self.blk.norm(self.q, self.k, self.v)
+            if self.norm_mode == "in_attention":
+                self.blk.norm_qkv(None, self.k, self.v)
+            elif self.norm_mode == "one_launch":
+                self.blk.norm_qkv(self.q, self.k, self.v)
+            else:
+                self.blk.norm(self.q, self.k, self.v)
         if ev:
             ev[0].record()
-        self.blk.attend(self.q, self.k, self.v, self.out)
+        if normed_q:
+            self.blk.attend_qnorm(self.q, self.k, self.v, self.out)
+        else:
+            self.blk.attend(self.q, self.k, self.v, self.out)
         if ev:
             ev[1].record()
 
@@ -223,16 +245,16 @@ class CopyWork:
         return None
 
 
-def make_work(name):
+def make_work(name, norm_mode="one_launch"):
     from gqa_flash_attention_dg_amd import synth
     if name == "long_cache":
-        return SplitWork(name, synth.long_cache())
+        return SplitWork(name, synth.long_cache(), norm_mode)
     if name == "dg_canvas":
-        return SplitWork(name, synth.dg_canvas_steps(1))
+        return SplitWork(name, synth.dg_canvas_steps(1), norm_mode)
     if name == "tiny":
-        return SplitWork(name, synth.tiny_canvas_step())
+        return SplitWork(name, synth.tiny_canvas_step(), norm_mode)
     if name == "depformer":
-        return SplitWork(name, synth.depformer_frames())
+        return SplitWork(name, synth.depformer_frames(), norm_mode)
     if name == "sam_relpos":
         return RelposWork(name, synth.sam_global())
     if name == "hbm_copy":
@@ -248,6 +270,11 @@ def main():
     ap.add_argument("--workload", default="long_cache",
                     choices=["long_cache", "dg_canvas", "tiny", "depformer", "sam_relpos",
                              "hbm_copy"])
+    ap.add_argument("--norm", default="one_launch",
+                    choices=["one_launch", "in_attention", "separate"],
+                    help="one_launch: q, k, v norms in one launch; in_attention: k/v norms in "
+                         "one launch + q norm inside attention; separate: the page's three "
+                         "headnorm dispatches")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle wall time for the CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -264,7 +291,7 @@ def main():
     dg.lib()
     torch.cuda.set_device(0)
 
-    work = make_work(args.workload)
+    work = make_work(args.workload, norm_mode=args.norm)
 
     for _ in range(args.warmup):
         work.step()

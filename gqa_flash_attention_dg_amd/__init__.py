@@ -19,9 +19,9 @@ LIB_PATH = os.path.join(HERE, "libdgattn.so")
 DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
 DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP = 1, 2, 4
 
-EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_attn_split_gqa_workspace_size",
-           "dg_attn_split_gqa", "relpos_flash_attn_workspace_size", "relpos_flash_attn",
-           "dg_last_error")
+EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
+           "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
+           "relpos_flash_attn_workspace_size", "relpos_flash_attn", "dg_last_error")
 
 
 class DgError(RuntimeError):
@@ -45,14 +45,17 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_uint, ctypes.c_size_t)
         L.dg_rope_table.argtypes = [vp, I, I, I, D, vp]
         L.dg_headnorm_rope.argtypes = [vp, vp, vp, I, I, I, I, U, F, vp]
+        L.dg_qkv_headnorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, U, F, vp]
         L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
         L.dg_attn_split_gqa_workspace_size.restype = Z
         L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
+        L.dg_attn_split_gqa_qnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, U,
+                                              F, F, I, vp, Z, vp]
         L.relpos_flash_attn_workspace_size.argtypes = [I, I, I, I]
         L.relpos_flash_attn_workspace_size.restype = Z
         L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp, Z, vp]
-        for name in ("dg_rope_table", "dg_headnorm_rope", "dg_attn_split_gqa",
-                     "relpos_flash_attn"):
+        for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
+                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "relpos_flash_attn"):
             getattr(L, name).restype = I
         L.dg_last_error.argtypes = []
         L.dg_last_error.restype = ctypes.c_char_p
@@ -118,6 +121,19 @@ def dg_headnorm_rope(x, w, cs, batch: int, T: int, heads: int, hd: int, flags: i
                                   batch, T, heads, hd, flags, float(eps), _stream(stream)))
 
 
+def dg_qkv_headnorm_rope(q, wq, k, wk, v, cs, batch: int, T: int, nh: int, nkv: int, hd: int,
+                         flags: int, eps: float, stream=None) -> None:
+    _nonneg(batch=batch, T=T, nh=nh, nkv=nkv, hd=hd)
+    need_w = (flags & DG_NORM_WEIGHTED) and not (flags & DG_NORM_SKIP)
+    need_cs = (flags & DG_NORM_ROPE) and (q is not None or k is not None)
+    nq, nk = batch * T * nh * hd, batch * T * nkv * hd
+    _check(lib().dg_qkv_headnorm_rope(
+        _ptr(q, "q", nq), _ptr(wq, "wq", hd if need_w and q is not None else 0),
+        _ptr(k, "k", nk), _ptr(wk, "wk", hd if need_w and k is not None else 0),
+        _ptr(v, "v", nk), _ptr(cs, "cs", T * 2 * hd if need_cs else 0),
+        batch, T, nh, nkv, hd, flags, float(eps), _stream(stream)))
+
+
 def dg_attn_split_gqa_workspace_size(batch: int, T: int, ctx: int, nh: int, nkv: int,
                                      hd: int) -> int:
     return int(lib().dg_attn_split_gqa_workspace_size(batch, T, ctx, nh, nkv, hd))
@@ -144,6 +160,22 @@ def dg_attn_split_gqa(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: in
                                    _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq),
                                    batch, T, ctx, nh, nkv, hd, float(scale), int(causal), ws,
                                    wsb, _stream(stream)))
+
+
+def dg_attn_split_gqa_qnorm(q, wq, cs, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int,
+                            nkv: int, hd: int, qflags: int, eps: float, scale: float,
+                            causal: int, workspace=None, workspace_bytes: int = 0,
+                            stream=None) -> None:
+    _nonneg(batch=batch, T=T, ctx=ctx, nh=nh, nkv=nkv, hd=hd)
+    nq, nkvc, nc = batch * T * nh * hd, batch * T * nkv * hd, batch * nkv * ctx * hd
+    need_w = (qflags & DG_NORM_WEIGHTED) and not (qflags & DG_NORM_SKIP)
+    need_cs = qflags & DG_NORM_ROPE
+    ws, wsb = _workspace(workspace, workspace_bytes)
+    _check(lib().dg_attn_split_gqa_qnorm(
+        _ptr(q, "q", nq), _ptr(wq, "wq", hd if need_w else 0),
+        _ptr(cs, "cs", T * 2 * hd if need_cs else 0), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
+        _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq), batch, T, ctx, nh, nkv, hd,
+        qflags, float(eps), float(scale), int(causal), ws, wsb, _stream(stream)))
 
 
 def relpos_flash_attn_workspace_size(gh: int, gw: int, heads: int, hd: int) -> int:

@@ -18,6 +18,10 @@
 // Scores and the value product run on f32 MFMA (flash_core.hpp).  At the end each pair merges
 // its two partial softmax states through LDS.
 //
+// dg_attn_split_gqa_qnorm takes the raw q projection instead and applies the q dispatch of
+// DG_HEADNORM_ROPE (RMSNorm, weight, NeoX rope) to each query vector in registers while loading
+// it, so q never makes the extra round trip through HBM; q itself is left unchanged.
+//
 // Shapes with too few workgroups to fill the GPU also split the key range across workgroups
 // ("split-KV"): each writes an unnormalised partial (max, denominator, output) to the caller's
 // workspace and a second kernel merges them.  Workgroups that share K/V are placed on the same
@@ -49,7 +53,65 @@ struct SplitArgs {
     int nblocks;       // total workgroups
     float qmul;        // scale * log2(e)
     int causal;
+    const float* wq;   // q norm weight [hd] (qnorm entry with WEIGHTED)
+    const float* cs;   // rope table [T, 2*hd] (qnorm entry with ROPE)
+    unsigned qflags;   // DG_NORM_* bits of the q norm
+    float eps;
 };
+
+// Loads the lane's share of a raw query vector (the layout of dgk::load_q: slot 4*g + e holds
+// element 8*g + 4*half + e) and applies the headnorm of the q dispatch in registers.  The two
+// lane halves hold complementary elements, so the sum of squares needs one exchange with lane
+// l^32; the rope partner of element e (e +- hd/2) is slot 4*(g +- hd/16) + e of the same lane.
+// The weight and the rope are linear and the norm is one scalar per vector, so they are applied
+// to the raw values first and the norm factor last, folded with scale*log2(e): every load is
+// then independent of the sum of squares and can be in flight at once.  Invalid lanes (row 0
+// of the table, a valid address) end with zeros.
+template <int HD>
+__device__ inline void load_q_normed(const SplitArgs& a, const float* __restrict__ qrow,
+                                     bool valid, int half, int row, float (&qreg)[HD / 2]) {
+    dgk::load_q<HD>(qrow, valid, half, 1.0f, qreg);
+    const bool norm = !(a.qflags & DG_NORM_SKIP);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < HD / 2; ++i) ss += qreg[i] * qreg[i];
+    if (norm && (a.qflags & DG_NORM_WEIGHTED)) {
+#pragma unroll
+        for (int g = 0; g < HD / 8; ++g) {
+            const float4 w4 = *reinterpret_cast<const float4*>(a.wq + 8 * g + 4 * half);
+            qreg[4 * g + 0] *= w4.x;
+            qreg[4 * g + 1] *= w4.y;
+            qreg[4 * g + 2] *= w4.z;
+            qreg[4 * g + 3] *= w4.w;
+        }
+    }
+    if (a.qflags & DG_NORM_ROPE) {
+        constexpr int H = HD / 16;  // float4 groups per half of the head
+        const float* cr = a.cs + (size_t)row * 2 * HD;
+#pragma unroll
+        for (int g = 0; g < H; ++g) {
+            const float* lo = cr + 8 * g + 4 * half;
+            const float* hi = lo + HD / 2;
+            const float4 cl = *reinterpret_cast<const float4*>(lo);
+            const float4 sl = *reinterpret_cast<const float4*>(lo + HD);
+            const float4 ch = *reinterpret_cast<const float4*>(hi);
+            const float4 sh = *reinterpret_cast<const float4*>(hi + HD);
+            const float cla[4] = {cl.x, cl.y, cl.z, cl.w}, sla[4] = {sl.x, sl.y, sl.z, sl.w};
+            const float cha[4] = {ch.x, ch.y, ch.z, ch.w}, sha[4] = {sh.x, sh.y, sh.z, sh.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = qreg[4 * g + e], y = qreg[4 * (g + H) + e];
+                qreg[4 * g + e] = x * cla[e] + (-y) * sla[e];
+                qreg[4 * (g + H) + e] = y * cha[e] + x * sha[e];
+            }
+        }
+    }
+    ss += __shfl_xor(ss, 32);
+    float mul = a.qmul;
+    if (norm) mul = valid ? mul / sqrtf(ss / (float)HD + a.eps) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < HD / 2; ++i) qreg[i] *= mul;
+}
 
 // Workgroup id -> logical id such that consecutive logical ids share an XCD (the hardware
 // deals workgroups to the 8 XCDs round robin).
@@ -58,7 +120,7 @@ __device__ inline int xcd_remap(int bid, int n) {
     return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
-template <int HD>
+template <int HD, bool kNormQ>
 __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     using TL = dgk::Tile<HD>;
     // [buffer][tile of the stage][K, V]
@@ -143,8 +205,13 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         }
     };
 
+    // The first stage's loads go out before the queries are fetched, so the two overlap.
+    if (!hi && st_begin < st_end) issue_stage(st_begin, 0);
     float qreg[HD / 2];
-    dgk::load_q<HD>(a.q + gq * HD, valid, half, a.qmul, qreg);
+    if constexpr (kNormQ)
+        load_q_normed<HD>(a, a.q + gq * HD, valid, half, row, qreg);
+    else
+        dgk::load_q<HD>(a.q + gq * HD, valid, half, a.qmul, qreg);
     f32x16 o[TL::kGroups];
 #pragma unroll
     for (int t = 0; t < TL::kGroups; ++t)
@@ -152,7 +219,6 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    if (!hi && st_begin < st_end) issue_stage(st_begin, 0);
     for (int st = st_begin; st < st_end; ++st) {
         const int buf = (st - st_begin) & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
@@ -200,7 +266,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 // each lane writes its segment of the output row.  All global accesses are contiguous per row.
 constexpr int kSmallKeys = 8;
 
-template <int HD>
+template <int HD, bool kNormQ>
 __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long units) {
     constexpr int SEG = HD / 8;
     __shared__ __attribute__((aligned(16))) float kvs[4 * 2 * kSmallKeys * HD];
@@ -234,8 +300,39 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
         const float4 q4 = has_q ? *reinterpret_cast<const float4*>(qp + e) : z;
         kr[e] = k4.x; kr[e + 1] = k4.y; kr[e + 2] = k4.z; kr[e + 3] = k4.w;
         vr[e] = v4.x; vr[e + 1] = v4.y; vr[e + 2] = v4.z; vr[e + 3] = v4.w;
-        qr[e] = q4.x * a.qmul; qr[e + 1] = q4.y * a.qmul; qr[e + 2] = q4.z * a.qmul; qr[e + 3] = q4.w * a.qmul;
+        qr[e] = q4.x; qr[e + 1] = q4.y; qr[e + 2] = q4.z; qr[e + 3] = q4.w;
     }
+    if constexpr (kNormQ) {
+        // q headnorm in registers: the 8 lanes of row r hold its 8 segments, so the sum of
+        // squares takes 3 exchanges, and the rope partner (segment c +- 4) is lane ^ 4.
+        if (!(a.qflags & DG_NORM_SKIP)) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) ss += qr[e] * qr[e];
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            ss += __shfl_xor(ss, 4);
+            const float inv = has_q ? 1.0f / sqrtf(ss / (float)HD + a.eps) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) qr[e] *= inv;
+            if (a.qflags & DG_NORM_WEIGHTED) {
+#pragma unroll
+                for (int e = 0; e < SEG; ++e) qr[e] *= a.wq[cseg + e];
+            }
+        }
+        if (a.qflags & DG_NORM_ROPE) {
+            const bool lower = cseg < HD / 2;
+            const float* cr = a.cs + (size_t)(has_q ? r : 0) * 2 * HD + cseg;
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) {
+                const float partner = __shfl_xor(qr[e], 4);
+                const float rot = lower ? -partner : partner;
+                qr[e] = has_q ? qr[e] * cr[e] + rot * cr[HD + e] : 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) qr[e] *= a.qmul;
 #pragma unroll
     for (int e = 0; e < SEG; e += 4) {
         *reinterpret_cast<float4*>(ks + r * HD + cseg + e) = make_float4(kr[e], kr[e + 1], kr[e + 2], kr[e + 3]);
@@ -345,11 +442,14 @@ extern "C" size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, in
     return plan(batch, T, ctx, nh, nkv, hd, 0).ws_bytes;
 }
 
-extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
-                                 const float* v, float* out, int batch, int T, int ctx, int nh,
-                                 int nkv, int hd, float scale, int causal, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    const char* fn = "dg_attn_split_gqa";
+namespace {
+
+// Shared body of both attention entry points.  `normq` selects the q-norm variant, whose extra
+// arguments (wq, cs, qflags, eps) were validated by the caller.
+int attn_call(const char* fn, const float* q, const float* kc, const float* vc, const float* k,
+              const float* v, float* out, int batch, int T, int ctx, int nh, int nkv, int hd,
+              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream,
+              bool normq, const float* wq, const float* cs, unsigned qflags, float eps) {
     if (batch < 0 || T < 0 || ctx < 0 || nh < 0 || nkv < 0)
         return dg::fail(DG_EINVAL, "%s: negative size (batch %d, T %d, ctx %d, nh %d, nkv %d)", fn,
                         batch, T, ctx, nh, nkv);
@@ -381,14 +481,22 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
         p.ws_bytes = 0;
     }
     const dg::Span so(out, nq * 4);
-    const dg::Span ins[6] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * 4), dg::Span(v, nkvc * 4),
+    const dg::Span ins[8] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * 4), dg::Span(v, nkvc * 4),
                              dg::Span(ncache ? kc : nullptr, ncache * 4),
                              dg::Span(ncache ? vc : nullptr, ncache * 4),
+                             dg::Span(normq ? wq : nullptr, (size_t)hd * 4),
+                             dg::Span(normq ? cs : nullptr, (size_t)T * 2 * hd * 4),
                              dg::Span(p.nsplit > 1 ? workspace : nullptr, p.ws_bytes)};
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 8; ++i)
         if (so.overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: out overlaps an input or the workspace", fn);
-    for (int i = 0; i < 5; ++i)
-        if (ins[5].overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: workspace overlaps an input", fn);
+    for (int i = 0; i < 7; ++i)
+        if (ins[7].overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: workspace overlaps an input", fn);
+    // The kernels read and write these with 16-byte vector accesses.
+    const void* vec[8] = {q, k, v, out, ncache ? kc : nullptr, ncache ? vc : nullptr,
+                          normq ? wq : nullptr, normq ? cs : nullptr};
+    for (int i = 0; i < 8; ++i)
+        if (reinterpret_cast<uintptr_t>(vec[i]) & 15)
+            return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
     const long long nblocks = (long long)batch * nkv * p.qblocks * p.nsplit;
     if (nblocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     SplitArgs a;
@@ -401,21 +509,23 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
     a.nblocks = (int)nblocks;
     a.qmul = scale * dgk::kLog2e;
     a.causal = causal;
+    a.wq = normq ? wq : nullptr;
+    a.cs = normq ? cs : nullptr;
+    a.qflags = normq ? qflags : 0u;
+    a.eps = eps;
     hipStream_t s = (hipStream_t)stream;
     if (ctx + T <= kSmallKeys) {
         const long long units = (long long)batch * nh;
         const long long blocks = (units + 3) / 4;
         if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
-        if (hd == 128)
-            hipLaunchKernelGGL(attn_small_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a, units);
-        else
-            hipLaunchKernelGGL(attn_small_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, units);
+        auto* kern = hd == 128 ? (normq ? attn_small_kernel<128, true> : attn_small_kernel<128, false>)
+                               : (normq ? attn_small_kernel<64, true> : attn_small_kernel<64, false>);
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, a, units);
         return dg::launch_status(fn);
     }
-    if (hd == 128)
-        hipLaunchKernelGGL(attn_split_gqa_kernel<128>, dim3((unsigned)nblocks), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL(attn_split_gqa_kernel<64>, dim3((unsigned)nblocks), dim3(512), 0, s, a);
+    auto* kern = hd == 128 ? (normq ? attn_split_gqa_kernel<128, true> : attn_split_gqa_kernel<128, false>)
+                           : (normq ? attn_split_gqa_kernel<64, true> : attn_split_gqa_kernel<64, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(512), 0, s, a);
     if (p.nsplit > 1) {
         const size_t total = (size_t)batch * T * nh;
         const size_t threads = total * (hd / 4);
@@ -428,4 +538,35 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
                                (const float*)a.ws, out, total, p.nsplit);
     }
     return dg::launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
+                                 const float* v, float* out, int batch, int T, int ctx, int nh,
+                                 int nkv, int hd, float scale, int causal, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return attn_call("dg_attn_split_gqa", q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale,
+                     causal, workspace, workspace_bytes, stream, false, nullptr, nullptr, 0u, 0.0f);
+}
+
+extern "C" int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs,
+                                       const float* kc, const float* vc, const float* k,
+                                       const float* v, float* out, int batch, int T, int ctx,
+                                       int nh, int nkv, int hd, unsigned qflags, float eps,
+                                       float scale, int causal, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    const char* fn = "dg_attn_split_gqa_qnorm";
+    if (qflags & ~(DG_NORM_WEIGHTED | DG_NORM_ROPE | DG_NORM_SKIP))
+        return dg::fail(DG_EINVAL, "%s: unknown flag bits 0x%x", fn, qflags);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return dg::fail(DG_EINVAL, "%s: eps must be finite and >= 0", fn);
+    const bool need_w = (qflags & DG_NORM_WEIGHTED) && !(qflags & DG_NORM_SKIP);
+    const bool need_cs = (qflags & DG_NORM_ROPE) != 0;
+    const bool empty = batch == 0 || T == 0;
+    if (!empty && need_w && !wq) return dg::fail(DG_EINVAL, "%s: WEIGHTED set but wq is NULL", fn);
+    if (!empty && need_cs && !cs) return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
+    return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal,
+                     workspace, workspace_bytes, stream, true, need_w ? wq : nullptr,
+                     need_cs ? cs : nullptr, qflags, eps);
 }

@@ -299,6 +299,10 @@ extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float*
         return dg::fail(DG_EINVAL, "%s: out overlaps an input or the workspace", fn);
     if (sws.overlaps(sq) || sws.overlaps(sh) || sws.overlaps(sw))
         return dg::fail(DG_EINVAL, "%s: workspace overlaps an input", fn);
+    // The kernels use 16-byte vector accesses on every tensor.
+    if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(out) |
+         reinterpret_cast<uintptr_t>(rh) | reinterpret_cast<uintptr_t>(rw)) & 15)
+        return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
     const long long qblocks = (n + kBlockQ - 1) / kBlockQ;
     if (qblocks * heads > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     RelArgs a;

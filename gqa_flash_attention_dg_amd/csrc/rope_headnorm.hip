@@ -6,10 +6,12 @@
 // builds for positions seq_len + t.
 //
 // Both are HBM-bound.  The page runs one 128-thread workgroup per (token, head) with shared
-// memory trees; here one 64-lane wavefront owns one (token, head) row: lane l holds elements
-// l and l+64, so every global access is one coalesced 256-byte wave load/store, the sum of
-// squares is a wave butterfly (no LDS, no barrier), and the rotate-half partner is either in
-// the same lane (hd = 128) or one lane shuffle away.
+// memory trees, and dispatches q, k and v separately; here one 64-lane wavefront owns one
+// (token, head) row: lane l holds elements l and l+64, so every global access is one coalesced
+// 256-byte wave load/store, the sum of squares is a wave butterfly (no LDS, no barrier), and
+// the rotate-half partner is either in the same lane (hd = 128) or one lane shuffle away.  One
+// launch can cover the rows of q, k and v together (dg_qkv_headnorm_rope): at canvas sizes
+// the three calls are launch-bound.
 #include "dg_common.hpp"
 
 namespace {
@@ -37,16 +39,27 @@ __global__ void __launch_bounds__(256) rope_table_kernel(float* __restrict__ cs,
     cs[(size_t)t * 2 * hd + hd + c] = (float)s;
 }
 
-__global__ void __launch_bounds__(256) headnorm_rope_kernel(float* __restrict__ x,
-                                                            const float* __restrict__ w,
-                                                            const float* __restrict__ cs,
-                                                            long long units, int T, int heads,
-                                                            int hd, unsigned flags, float eps) {
-    const int lane = threadIdx.x & 63;
-    const long long u = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (u >= units) return;  // wave-uniform
-    const int t = (int)((u / heads) % T);
-    float* xr = x + (size_t)u * hd;
+// One tensor of a headnorm launch: rows of hd floats, `heads` rows per token, normed in place
+// with its own weight and flags.  A launch covers up to three of them (q, k, v of a step).
+struct NormSeg {
+    float* x;
+    const float* w;
+    long long rows;   // batch * T * heads
+    int heads;
+    unsigned flags;
+};
+
+struct NormArgs {
+    NormSeg seg[3];
+    int nseg;
+    const float* cs;  // [T, 2*hd], shared by every segment that ropes
+    int T, hd;
+    float eps;
+};
+
+__device__ inline void headnorm_row(float* __restrict__ xr, const float* __restrict__ w,
+                                    const float* __restrict__ cr, int hd, unsigned flags,
+                                    float eps, int lane) {
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = e0 < hd, v1 = e1 < hd;
     float y0 = v0 ? xr[e0] : 0.0f;
@@ -77,7 +90,6 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(float* __restrict__ 
             q0 = p0 >= 64 ? b0 : a0;
             q1 = p1 >= 64 ? b1 : a1;
         }
-        const float* cr = cs + (size_t)t * 2 * hd;
         if (v0) {
             const float rot = e0 < half ? -q0 : q0;
             xr[e0] = y0 * cr[e0] + rot * cr[hd + e0];
@@ -90,6 +102,19 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(float* __restrict__ 
         if (v0) xr[e0] = y0;
         if (v1) xr[e1] = y1;
     }
+}
+
+// Rows of all segments are numbered consecutively (segment 0 first); each wavefront takes one.
+__global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
+    const int lane = threadIdx.x & 63;
+    long long u = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    int s = 0;
+    while (s < a.nseg && u >= a.seg[s].rows) u -= a.seg[s++].rows;  // wave-uniform
+    if (s >= a.nseg) return;
+    const NormSeg& g = a.seg[s];
+    const int t = (int)((u / g.heads) % a.T);
+    const float* cr = (g.flags & DG_NORM_ROPE) ? a.cs + (size_t)t * 2 * a.hd : nullptr;
+    headnorm_row(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane);
 }
 
 }  // namespace
@@ -109,36 +134,100 @@ extern "C" int dg_rope_table(float* cs, int pos0, int T, int hd, double theta, v
     return dg::launch_status("dg_rope_table");
 }
 
+namespace {
+
+// Checks shared by both headnorm entry points (sizes, flags, eps).
+int check_norm_common(const char* fn, int batch, int T, int hd, unsigned flags, float eps) {
+    if (batch < 0 || T < 0) return dg::fail(DG_EINVAL, "%s: negative size (batch %d, T %d)", fn, batch, T);
+    if (hd < 1) return dg::fail(DG_EINVAL, "%s: hd must be >= 1, got %d", fn, hd);
+    if (hd > 128) return dg::fail(DG_EUNSUPPORTED, "%s: hd %d > 128 is not supported", fn, hd);
+    if (flags & ~(DG_NORM_WEIGHTED | DG_NORM_ROPE | DG_NORM_SKIP))
+        return dg::fail(DG_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
+    if ((flags & DG_NORM_ROPE) && (hd & 1))
+        return dg::fail(DG_EINVAL, "%s: rope needs an even hd, got %d", fn, hd);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return dg::fail(DG_EINVAL, "%s: eps must be finite and >= 0", fn);
+    return DG_OK;
+}
+
+int launch_norm(const char* fn, NormArgs& a, void* stream) {
+    long long rows = 0;
+    for (int i = 0; i < a.nseg; ++i) rows += a.seg[i].rows;
+    if (rows == 0) return dg::ok();
+    const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many rows", fn);
+    hipLaunchKernelGGL(headnorm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, a);
+    return dg::launch_status(fn);
+}
+
+}  // namespace
+
 extern "C" int dg_headnorm_rope(float* x, const float* w, const float* cs, int batch, int T,
                                 int heads, int hd, unsigned flags, float eps, void* stream) {
-    if (batch < 0 || T < 0 || heads < 0)
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: negative size (batch %d, T %d, heads %d)", batch, T, heads);
-    if (hd < 1) return dg::fail(DG_EINVAL, "dg_headnorm_rope: hd must be >= 1, got %d", hd);
-    if (hd > 128) return dg::fail(DG_EUNSUPPORTED, "dg_headnorm_rope: hd %d > 128 is not supported", hd);
-    if (flags & ~(DG_NORM_WEIGHTED | DG_NORM_ROPE | DG_NORM_SKIP))
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: unknown flag bits 0x%x", flags);
-    if ((flags & DG_NORM_ROPE) && (hd & 1))
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: rope needs an even hd, got %d", hd);
-    if (!(eps >= 0.0f) || !std::isfinite(eps))
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: eps must be finite and >= 0");
+    const char* fn = "dg_headnorm_rope";
+    if (heads < 0) return dg::fail(DG_EINVAL, "%s: negative size (heads %d)", fn, heads);
+    if (int st = check_norm_common(fn, batch, T, hd, flags, eps)) return st;
     size_t n = 1;
     if (!dg::mul_ok(n, batch) || !dg::mul_ok(n, T) || !dg::mul_ok(n, heads) || !dg::mul_ok(n, hd))
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: size overflow");
+        return dg::fail(DG_EINVAL, "%s: size overflow", fn);
     if (n == 0) return dg::ok();
     const bool need_w = (flags & DG_NORM_WEIGHTED) && !(flags & DG_NORM_SKIP);
     const bool need_cs = (flags & DG_NORM_ROPE) != 0;
-    if (!x) return dg::fail(DG_EINVAL, "dg_headnorm_rope: x is NULL");
-    if (need_w && !w) return dg::fail(DG_EINVAL, "dg_headnorm_rope: WEIGHTED set but w is NULL");
-    if (need_cs && !cs) return dg::fail(DG_EINVAL, "dg_headnorm_rope: ROPE set but cs is NULL");
+    if (!x) return dg::fail(DG_EINVAL, "%s: x is NULL", fn);
+    if (need_w && !w) return dg::fail(DG_EINVAL, "%s: WEIGHTED set but w is NULL", fn);
+    if (need_cs && !cs) return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
     const dg::Span xs(x, n * sizeof(float));
     if (need_w && xs.overlaps(dg::Span(w, (size_t)hd * sizeof(float))))
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: w overlaps x");
+        return dg::fail(DG_EINVAL, "%s: w overlaps x", fn);
     if (need_cs && xs.overlaps(dg::Span(cs, (size_t)T * 2 * hd * sizeof(float))))
-        return dg::fail(DG_EINVAL, "dg_headnorm_rope: cs overlaps x");
-    const long long units = (long long)batch * T * heads;
-    const long long blocks = (units + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "dg_headnorm_rope: too many rows");
-    hipLaunchKernelGGL(headnorm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                       x, need_w ? w : nullptr, need_cs ? cs : nullptr, units, T, heads, hd, flags, eps);
-    return dg::launch_status("dg_headnorm_rope");
+        return dg::fail(DG_EINVAL, "%s: cs overlaps x", fn);
+    NormArgs a{};
+    a.seg[0] = NormSeg{x, need_w ? w : nullptr, (long long)batch * T * heads, heads, flags};
+    a.nseg = 1;
+    a.cs = need_cs ? cs : nullptr;
+    a.T = T;
+    a.hd = hd;
+    a.eps = eps;
+    return launch_norm(fn, a, stream);
+}
+
+extern "C" int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, float* v,
+                                    const float* cs, int batch, int T, int nh, int nkv, int hd,
+                                    unsigned flags, float eps, void* stream) {
+    const char* fn = "dg_qkv_headnorm_rope";
+    if (nh < 0 || nkv < 0) return dg::fail(DG_EINVAL, "%s: negative size (nh %d, nkv %d)", fn, nh, nkv);
+    if (int st = check_norm_common(fn, batch, T, hd, flags, eps)) return st;
+    size_t nq = 1, nk = 1;
+    if (!dg::mul_ok(nq, batch) || !dg::mul_ok(nq, T) || !dg::mul_ok(nq, nh) || !dg::mul_ok(nq, hd) ||
+        !dg::mul_ok(nk, batch) || !dg::mul_ok(nk, T) || !dg::mul_ok(nk, nkv) || !dg::mul_ok(nk, hd))
+        return dg::fail(DG_EINVAL, "%s: size overflow", fn);
+    const bool need_w = (flags & DG_NORM_WEIGHTED) && !(flags & DG_NORM_SKIP);
+    const bool need_cs = (flags & DG_NORM_ROPE) != 0;
+    const bool do_q = q && nq > 0, do_k = k && nk > 0, do_v = v && nk > 0;
+    if (!do_q && !do_k && !do_v) return dg::ok();
+    if (need_w && ((do_q && !wq) || (do_k && !wk)))
+        return dg::fail(DG_EINVAL, "%s: WEIGHTED set but wq or wk is NULL", fn);
+    if (need_cs && (do_q || do_k) && !cs)
+        return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
+    const dg::Span xs[3] = {dg::Span(do_q ? q : nullptr, nq * 4), dg::Span(do_k ? k : nullptr, nk * 4),
+                            dg::Span(do_v ? v : nullptr, nk * 4)};
+    const dg::Span ro[3] = {dg::Span(need_w && do_q ? wq : nullptr, (size_t)hd * 4),
+                            dg::Span(need_w && do_k ? wk : nullptr, (size_t)hd * 4),
+                            dg::Span(need_cs && (do_q || do_k) ? cs : nullptr, (size_t)T * 2 * hd * 4)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (xs[i].overlaps(xs[j])) return dg::fail(DG_EINVAL, "%s: q, k and v overlap", fn);
+        for (int j = 0; j < 3; ++j)
+            if (xs[i].overlaps(ro[j])) return dg::fail(DG_EINVAL, "%s: wq, wk or cs overlaps q, k or v", fn);
+    }
+    NormArgs a{};
+    if (do_q) a.seg[a.nseg++] = NormSeg{q, need_w ? wq : nullptr, (long long)batch * T * nh, nh, flags};
+    if (do_k) a.seg[a.nseg++] = NormSeg{k, need_w ? wk : nullptr, (long long)batch * T * nkv, nkv, flags};
+    if (do_v) a.seg[a.nseg++] = NormSeg{v, nullptr, (long long)batch * T * nkv, nkv, 0u};
+    a.cs = need_cs ? cs : nullptr;
+    a.T = T;
+    a.hd = hd;
+    a.eps = eps;
+    return launch_norm(fn, a, stream);
 }

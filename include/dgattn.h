@@ -84,6 +84,26 @@ int dg_headnorm_rope(float* x, const float* w, const float* cs, int batch, int T
                      int hd, unsigned flags, float eps, void* stream);
 
 /*
+ * dg_qkv_headnorm_rope -- the three headnorm dispatches of one canvas step in ONE launch.
+ * Follows the q, k and v dispatches of DG_HEADNORM_ROPE in `canvas_forward`
+ * (diffusion_gemma_gpu.rs): q and k get `flags` with their own weights, v gets the
+ * weightless, un-roped norm (the page's flags 0).  Each row is computed exactly as
+ * dg_headnorm_rope computes it.
+ *   q   in/out [batch, T, nh*hd], or NULL to leave q alone (e.g. when the attention call
+ *       normalises q itself, see dg_attn_split_gqa_qnorm)
+ *   wq  [hd]; read iff q != NULL and WEIGHTED is set without SKIP
+ *   k   in/out [batch, T, nkv*hd], or NULL;  wk [hd] as wq
+ *   v   in/out [batch, T, nkv*hd], or NULL
+ *   cs  [T, 2*hd] rope table; read iff ROPE is set and q or k is given
+ *   flags, eps as dg_headnorm_rope (flags apply to q and k only).
+ * Errors: as dg_headnorm_rope, plus DG_EINVAL for negative nh/nkv, overlapping q/k/v, or a
+ * weight or table overlapping any of them.  All of q, k, v NULL (or empty) is a no-op.
+ */
+int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, float* v,
+                         const float* cs, int batch, int T, int nh, int nkv, int hd,
+                         unsigned flags, float eps, void* stream);
+
+/*
  * dg_attn_split_gqa_workspace_size -- bytes of scratch that dg_attn_split_gqa can use to split
  * the key range of one call across more workgroups (partial results and their combine).
  * Returns 0 when the shape gains nothing from a split.  Arguments as for dg_attn_split_gqa;
@@ -112,15 +132,38 @@ size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int n
  *   workspace  optional device scratch of at least dg_attn_split_gqa_workspace_size() bytes,
  *              16-byte aligned, used for a split of the key range; NULL/0 runs unsplit (same
  *              results up to rounding).  Must not overlap any input or `out`.
+ *   Every tensor pointer must be 16-byte aligned (the kernels use 16-byte vector accesses;
+ *   torch allocations are).
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
- * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, or a workspace
- * pointer that is misaligned or has workspace_bytes too small; DG_EUNSUPPORTED for hd not 64 or
- * 128, or a cache block or canvas above 4 GiB.
+ * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, a tensor pointer
+ * that is not 16-byte aligned, or a workspace pointer that is misaligned or has
+ * workspace_bytes too small; DG_EUNSUPPORTED for hd not 64 or 128.
  */
 int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
                       const float* v, float* out, int batch, int T, int ctx, int nh, int nkv,
                       int hd, float scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * dg_attn_split_gqa_qnorm -- dg_attn_split_gqa on the RAW q projection: each query vector gets
+ * the q dispatch of DG_HEADNORM_ROPE (`canvas_forward`, diffusion_gemma_gpu.rs) in registers as
+ * the attention kernel loads it, so the separate in-place pass over q is not needed.  The
+ * result equals dg_headnorm_rope(q, wq, cs, ..., qflags, eps) followed by dg_attn_split_gqa,
+ * up to rounding; q itself is NOT modified.  k and v must already be normalised (e.g. by
+ * dg_qkv_headnorm_rope with q = NULL).
+ *   q       [batch, T, nh*hd] raw queries
+ *   wq      [hd]; read iff WEIGHTED is set without SKIP
+ *   cs      [T, 2*hd] rope table (row t = canvas row t); read iff ROPE is set
+ *   qflags  DG_NORM_* bits for q;  eps >= 0
+ *   every other argument as dg_attn_split_gqa (same workspace size function).
+ * Errors: as dg_attn_split_gqa, plus DG_EINVAL for unknown flag bits, a negative or
+ * non-finite eps, a needed wq/cs that is NULL, or out overlapping wq or cs.
+ */
+int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs, const float* kc,
+                            const float* vc, const float* k, const float* v, float* out,
+                            int batch, int T, int ctx, int nh, int nkv, int hd, unsigned qflags,
+                            float eps, float scale, int causal, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn can use to hold the
@@ -147,8 +190,10 @@ size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
  *              first kernel, as the page's DHDW step does; NULL/0 computes them inside each
  *              attention workgroup instead (same results up to rounding, slower).  Must not
  *              overlap any input or `out`.
+ *   Every tensor pointer must be 16-byte aligned.
  * Errors: DG_EINVAL for gh, gw or heads < 0, exactly one of rh/rw NULL, a NULL qkv/out with
- * n > 0, a non-finite scale, overlapping buffers, a misaligned or too small workspace;
+ * n > 0, a non-finite scale, overlapping buffers, a tensor pointer that is not 16-byte
+ * aligned, a misaligned or too small workspace;
  * DG_EUNSUPPORTED for hd != 64 (the page's kernel fixes hd to its 64-wide workgroup) or gh or
  * gw above 64.
  */

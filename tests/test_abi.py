@@ -98,6 +98,53 @@ def test_attn_split_validation(L):
     assert L.dg_attn_split_gqa_workspace_size(1, 16, 32, 5, 2, 64) == 0
 
 
+def test_qkv_headnorm_validation(L):
+    f = L.dg_qkv_headnorm_rope
+    base = dict(q=FAKE, wq=FAKE + (1 << 24), k=FAKE + (2 << 24), wk=FAKE + (3 << 24),
+                v=FAKE + (4 << 24), cs=FAKE + (5 << 24), batch=1, T=4, nh=4, nkv=2, hd=64,
+                flags=3, eps=1e-6, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(nh=-1) == dg.DG_EINVAL
+    assert call(hd=256) == dg.DG_EUNSUPPORTED
+    assert call(flags=8) == dg.DG_EINVAL
+    assert call(wq=None) == dg.DG_EINVAL                   # WEIGHTED needs wq for q
+    assert call(cs=None) == dg.DG_EINVAL
+    assert call(k=FAKE + 64) == dg.DG_EINVAL               # k inside q
+    assert "overlap" in _err(L)
+    assert call(cs=FAKE + (2 << 24) + 256) == dg.DG_EINVAL  # table inside k
+    assert call(eps=float("nan")) == dg.DG_EINVAL
+    assert call(q=None, k=None, v=None) == dg.DG_OK        # nothing to do
+    assert call(T=0) == dg.DG_OK
+    assert _err(L) == ""
+
+
+def test_attn_qnorm_validation(L):
+    f = L.dg_attn_split_gqa_qnorm
+    base = dict(q=FAKE, wq=FAKE + (1 << 24), cs=FAKE + (2 << 24), kc=FAKE + (3 << 24),
+                vc=FAKE + (4 << 24), k=FAKE + (5 << 24), v=FAKE + (6 << 24),
+                out=FAKE + (7 << 24), batch=1, T=16, ctx=32, nh=4, nkv=2, hd=64, qflags=3,
+                eps=1e-6, scale=1.0, causal=0, ws=None, wsb=0, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(qflags=16) == dg.DG_EINVAL
+    assert call(eps=-1.0) == dg.DG_EINVAL
+    assert call(wq=None) == dg.DG_EINVAL
+    assert call(cs=None) == dg.DG_EINVAL
+    assert call(out=FAKE + (1 << 24)) == dg.DG_EINVAL       # out overlaps wq
+    assert call(out=FAKE + (2 << 24) + 512) == dg.DG_EINVAL # out overlaps the rope table
+    assert call(hd=96) == dg.DG_EUNSUPPORTED
+    assert call(nh=3) == dg.DG_EINVAL
+    assert call(q=FAKE + 4, out=FAKE + (8 << 24)) == dg.DG_EINVAL   # misaligned q
+    assert "aligned" in _err(L)
+    assert call(T=0) == dg.DG_OK
+
+
+def test_attn_alignment_validation(L):
+    f = L.dg_attn_split_gqa
+    assert f(FAKE, FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24) + 8, FAKE + (4 << 24),
+             FAKE + (5 << 24), 1, 16, 32, 4, 2, 64, 1.0, 0, None, 0, None) == dg.DG_EINVAL
+    assert "aligned" in _err(L)
+
+
 def test_relpos_validation(L):
     f = L.relpos_flash_attn
     base = dict(qkv=FAKE, rh=FAKE + (1 << 26), rw=FAKE + (2 << 26), out=FAKE + (3 << 26),
@@ -113,6 +160,8 @@ def test_relpos_validation(L):
     assert call(ws=FAKE + (4 << 26) + 4, wsb=1 << 20) == dg.DG_EINVAL   # misaligned workspace
     assert call(ws=FAKE + (4 << 26), wsb=16) == dg.DG_EINVAL           # too small
     assert call(ws=FAKE + 64, wsb=1 << 20) == dg.DG_EINVAL              # overlaps qkv
+    assert call(rw=FAKE + (2 << 26) + 4) == dg.DG_EINVAL                # misaligned table
+    assert "aligned" in _err(L)
     assert call(gh=0) == dg.DG_OK
     assert call(heads=0) == dg.DG_OK
     assert L.relpos_flash_attn_workspace_size(64, 64, 12, 64) == 2 * 12 * 4096 * 64 * 4

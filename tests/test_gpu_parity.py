@@ -62,6 +62,34 @@ def test_headnorm_rope(B, T, heads, hd, flags):
     assert_parity(host(xd), ref, "headnorm flags=%d" % flags)
 
 
+@pytest.mark.parametrize("B,T,nh,nkv,hd", [(1, 16, 4, 2, 64), (2, 37, 6, 3, 128), (1, 5, 2, 1, 6),
+                                            (3, 9, 4, 4, 100)])
+@pytest.mark.parametrize("flags", [0, 3, 6])
+@pytest.mark.parametrize("which", ["qkv", "kv", "q", "v"])
+def test_qkv_headnorm_rope(B, T, nh, nkv, hd, flags, which):
+    """One launch over q, k and v equals the three separate dispatches of the page."""
+    rng = np.random.default_rng(B * 100 + T + hd + flags)
+    q = (rng.standard_normal((B, T, nh * hd)) * 2.0).astype(np.float32)
+    k = (rng.standard_normal((B, T, nkv * hd)) * 0.5).astype(np.float32)
+    v = rng.standard_normal((B, T, nkv * hd)).astype(np.float32)
+    wq = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    wk = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    cs = oracle.rope_table(40, T, hd, 10000.0)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    dg.dg_qkv_headnorm_rope(qd if "q" in which else None, dev(wq) if flags & 1 else None,
+                            kd if "k" in which else None, dev(wk) if flags & 1 else None,
+                            vd if "v" in which else None, dev(cs) if flags & 2 else None,
+                            B, T, nh, nkv, hd, flags, 1e-6)
+    refs = {"q": oracle.headnorm_rope(q, wq, cs, nh, hd, flags, 1e-6),
+            "k": oracle.headnorm_rope(k, wk, cs, nkv, hd, flags, 1e-6),
+            "v": oracle.headnorm_rope(v, None, None, nkv, hd, 0, 1e-6)}
+    for name, x, t in (("q", q, qd), ("k", k, kd), ("v", v, vd)):
+        if name in which:
+            assert_parity(host(t), refs[name], "qkv headnorm %s flags=%d" % (name, flags))
+        else:
+            assert np.array_equal(host(t), x), "%s was not passed and must be unchanged" % name
+
+
 # ----------------------------------------------------------------------------- split-GQA
 
 SPLIT_SHAPES = [
@@ -120,6 +148,52 @@ def test_attn_split_kv_partials_and_combine(shape):
         dg.dg_attn_split_gqa(*args, ws, nbytes - 4)
 
 
+def qnorm_case(shape, qflags, seed):
+    """A split case whose q is raw (un-normed), with q weight and rope table for the q norm."""
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=seed, scale=scale, causal=causal)
+    rng = np.random.default_rng(seed + 7)
+    q = (rng.standard_normal(c.q.shape) * 3.0).astype(np.float32)   # raw projection scale
+    wq = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    cs = oracle.rope_table(ctx, T, hd, 10000.0)
+    qn = oracle.headnorm_rope(q, wq, cs, nh, hd, qflags, 1e-6)
+    ref = oracle.attn_split_gqa(qn, c.kc, c.vc, c.k, c.v, nh, nkv, hd, scale, causal)
+    return c, q, wq, cs, ref
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["unsplit", "ws"])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "B%d_T%d_ctx%d_h%d_kv%d_hd%d_c%d" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], s[7]))
+def test_attn_split_qnorm_small(shape, use_ws):
+    """q normed and roped inside the attention kernel == headnorm(q) then attention."""
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    flags = dg.DG_NORM_WEIGHTED | dg.DG_NORM_ROPE
+    c, q, wq, cs, ref = qnorm_case(shape, flags, seed=3 * T + ctx)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd) if use_ws else (None, 0)
+    qd = dev(q)
+    dg.dg_attn_split_gqa_qnorm(qd, dev(wq), dev(cs), dev(c.kc), dev(c.vc), dev(c.k), dev(c.v),
+                               out, B, T, ctx, nh, nkv, hd, flags, 1e-6, scale, int(causal), ws,
+                               nbytes)
+    assert_parity(host(out), ref, "qnorm %s ws=%d" % (shape, nbytes))
+    assert np.array_equal(host(qd), q), "q must be left unchanged"
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 6])
+@pytest.mark.parametrize("shape", [(1, 40, 90, 4, 2, 128, 1.0, False), (2, 6, 2, 4, 2, 64, 0.5, True),
+                                   (1, 70, 0, 8, 2, 64, 0.3, True)],
+                         ids=["hd128", "short-set", "causal-hd64"])
+def test_attn_split_qnorm_flags(shape, flags):
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c, q, wq, cs, ref = qnorm_case(shape, flags, seed=11 + flags)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    dg.dg_attn_split_gqa_qnorm(dev(q), dev(wq) if flags & 1 else None,
+                               dev(cs) if flags & 2 else None, dev(c.kc), dev(c.vc), dev(c.k),
+                               dev(c.v), out, B, T, ctx, nh, nkv, hd, flags, 1e-6, scale,
+                               int(causal))
+    assert_parity(host(out), ref, "qnorm flags=%d %s" % (flags, shape))
+
+
 def test_attn_split_zero_canvas_is_noop_and_nonfinite_free():
     out = torch.full((1, 4, 128), 7.0, device="cuda")
     q = torch.zeros(1, 4, 128, device="cuda")
@@ -142,12 +216,12 @@ def test_attn_split_on_a_side_stream():
 
 # ----------------------------------------------------------------------------- full workloads
 
-def run_block(case, steps=None):
+def run_block(case, steps=None, norm_mode="one_launch"):
     """Set up a CanvasBlock from a synthetic case and run the given (q, k, v) steps."""
     blk = CanvasBlock(case.B, case.T, case.ctx, case.nh, case.nkv, case.hd, dev(case.kc),
                       dev(case.vc), dev(case.wq), dev(case.wk), eps=case.eps, theta=case.theta,
                       scale=case.scale, causal=case.causal, rope_cache=case.rope_cache,
-                      normed=case.normed)
+                      normed=case.normed, norm_mode=norm_mode)
     outs = []
     for st in steps or [{"q": case.q, "k": case.k, "v": case.v}]:
         out = torch.empty((case.B, case.T, case.nh * case.hd), device="cuda")
@@ -156,17 +230,22 @@ def run_block(case, steps=None):
     return blk, outs
 
 
-def test_tiny_canvas_step_every_element():
+NORM_MODES = ["one_launch", "in_attention", "separate"]
+
+
+@pytest.mark.parametrize("norm_mode", NORM_MODES)
+def test_tiny_canvas_step_every_element(norm_mode):
     c = synth.tiny_canvas_step()
-    _, (got,) = run_block(c)
+    _, (got,) = run_block(c, norm_mode=norm_mode)
     cs, kc = oracle_prepare(c)
     ref, _ = oracle_step(c, c.q, c.k, c.v, cs, kc)
     assert_parity(got, ref, "tiny canvas step")
 
 
-def test_dg_canvas_48_steps():
+@pytest.mark.parametrize("norm_mode", NORM_MODES)
+def test_dg_canvas_48_steps(norm_mode):
     c = synth.dg_canvas_steps(48)
-    _, outs = run_block(c, c.steps)
+    _, outs = run_block(c, c.steps, norm_mode=norm_mode)
     cs, kc = oracle_prepare(c)
     for s, st in enumerate(c.steps):
         rows = None if s == 0 else sample_rows(c.B * c.T, 12, seed=s)
@@ -178,9 +257,10 @@ def test_dg_canvas_48_steps():
             assert_parity(flat(outs[s]), flat(ref), "dg step %d" % s)
 
 
-def test_long_cache_sampled_rows():
+@pytest.mark.parametrize("norm_mode", ["one_launch", "in_attention"])
+def test_long_cache_sampled_rows(norm_mode):
     c = synth.long_cache()
-    _, (got,) = run_block(c)
+    _, (got,) = run_block(c, norm_mode=norm_mode)
     cs, kc = oracle_prepare(c)
     rows = sample_rows(c.B * c.T, 40, seed=3)
     ref, _ = oracle_step(c, c.q, c.k, c.v, cs, kc, rows=rows)
