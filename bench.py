@@ -3,9 +3,10 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
 A step is one pass of the hot path over one batch of synthetic input resident in HBM:
-  split-GQA workloads: the q, k and v headnorms in one launch, then split-GQA attention
-    (--norm in_attention: k and v in one launch, the q norm + rope applied by the attention
-    kernel in registers; --norm separate: the page's three headnorm dispatches);
+  split-GQA workloads: the k and v headnorms in one launch, then split-GQA attention that
+    applies the q headnorm + rope as it stages q (--norm one_launch: q, k and v in one launch,
+    then plain attention; --norm separate: the page's three headnorm dispatches);
+  dg_layers: the same for each layer of a sliding/global layer stack (one step = all layers);
   sam_relpos: one rel-pos flash attention (bias-row pass + flash kernel).
 The default workload is the long-cache split-GQA canvas step (4 canvases, T=256, ctx=8192,
 nh=32, nkv=8, hd=128).  W untimed steps, then K steps timed with HIP events on the stream the
@@ -56,7 +57,7 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def split_counts(c, norm_mode="one_launch"):
+def split_counts(c, norm_mode="in_attention"):
     """Algorithmic flops and bytes of one attention launch and of the headnorm work: q, k and v
     each read and written once, or with the q norm inside attention only k and v (q is read by
     the attention launch either way)."""
@@ -78,7 +79,7 @@ def split_counts(c, norm_mode="one_launch"):
 class SplitWork:
     dominant = "attn_split_gqa"
 
-    def __init__(self, name, case, norm_mode="one_launch"):
+    def __init__(self, name, case, norm_mode="in_attention"):
         import numpy as np
         import torch
         from gqa_flash_attention_dg_amd.canvas import CanvasBlock
@@ -104,7 +105,7 @@ class SplitWork:
                 "step": self.step_name()}
 
     def step_name(self):
-        if not self.c.normed:
+        if not getattr(self.c, "normed", True):
             return "dg_attn_split_gqa"
         return {"one_launch": "dg_qkv_headnorm_rope(q, k, v) + dg_attn_split_gqa",
                 "in_attention": "dg_qkv_headnorm_rope(k, v) + dg_attn_split_gqa_qnorm",
@@ -156,6 +157,70 @@ class SplitWork:
         return {"value": value, "unit": unit, "cores": oracle.threads(), "kind": "oracle",
                 "sample": "%d of %d canvas rows (all %d heads) of one step, plus the q/k/v "
                           "headnorms of the whole step; %.2f s wall" % (rows.size, nrows, c.nh, dt)}
+
+
+class LayerStackWork:
+    """One canvas step through a sliding/global layer stack: per layer the k/v norm launch and
+    the attention (with the q norm inside, by default).  The attention launches of all layers
+    are timed together as the dominant kernel."""
+    dominant = "attn_split_gqa"
+
+    def __init__(self, name, case, norm_mode="in_attention"):
+        import numpy as np
+        import torch
+        from gqa_flash_attention_dg_amd.canvas import CanvasStack
+
+        self.name, self.c, self.norm_mode = name, case, norm_mode
+        d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        c = case
+        self.stack = CanvasStack(c.B, c.T, c.nh, c.pos0, c.layers,
+                                 [(d(p["kc"]), d(p["vc"])) for p in c.per_layer],
+                                 [(d(p["wq"]), d(p["wk"])) for p in c.per_layer],
+                                 theta_sliding=c.theta_sliding, theta_full=c.theta_full,
+                                 eps=c.eps, scale=c.scale, norm_mode=norm_mode)
+        self.io = []
+        self.flops = self.attn_bytes = self.norm_bytes = 0
+        for l, p in zip(c.layers, c.per_layer):
+            v = torch.empty((c.B, c.T, l.nkv * l.hd), device="cuda") if l.k_eq_v else d(p["v"])
+            out = torch.empty((c.B, c.T, c.nh * l.hd), device="cuda")
+            self.io.append((d(p["q"]), d(p["k"]), v, out))
+            q, kv = c.B * c.T * c.nh * l.hd, c.B * c.T * l.nkv * l.hd
+            cache = c.B * l.nkv * l.ctx * l.hd
+            self.flops += 4 * l.hd * c.B * c.nh * c.T * (l.ctx + c.T)
+            self.attn_bytes += 4 * (2 * q + 2 * kv + 2 * cache)
+            qn = 0 if norm_mode == "in_attention" else q
+            self.norm_bytes += 4 * 2 * (qn + kv) + 4 * (kv if l.k_eq_v else 2 * kv)
+        self.bound = "mfma"
+
+    def config(self):
+        c = self.c
+        return {"workload": c.name, "batch": c.B, "T": c.T, "nh": c.nh, "pos0": c.pos0,
+                "layers": [{"type": "sliding" if l.sliding else "global", "hd": l.hd,
+                            "nkv": l.nkv, "ctx": l.ctx, "k_eq_v": l.k_eq_v} for l in c.layers],
+                "rope_base": {"sliding": c.theta_sliding, "global": c.theta_full},
+                "step": "per layer: " + SplitWork.step_name(self)}
+
+    def step(self, ev=None):
+        blocks = self.stack.blocks
+        for li, (q, k, v, out) in enumerate(self.io):
+            blk = blocks[li]
+            if self.norm_mode == "in_attention":
+                blk.norm_qkv(None, k, v)
+            elif self.norm_mode == "one_launch":
+                blk.norm_qkv(q, k, v)
+            else:
+                blk.norm(q, k, v)
+            if ev:
+                ev[li][0].record()
+            if self.norm_mode == "in_attention":
+                blk.attend_qnorm(q, k, v, out)
+            else:
+                blk.attend(q, k, v, out)
+            if ev:
+                ev[li][1].record()
+
+    def cpu_baseline(self, budget_s):
+        return None
 
 
 class RelposWork:
@@ -245,7 +310,7 @@ class CopyWork:
         return None
 
 
-def make_work(name, norm_mode="one_launch"):
+def make_work(name, norm_mode="in_attention"):
     from gqa_flash_attention_dg_amd import synth
     if name == "long_cache":
         return SplitWork(name, synth.long_cache(), norm_mode)
@@ -255,6 +320,8 @@ def make_work(name, norm_mode="one_launch"):
         return SplitWork(name, synth.tiny_canvas_step(), norm_mode)
     if name == "depformer":
         return SplitWork(name, synth.depformer_frames(), norm_mode)
+    if name == "dg_layers":
+        return LayerStackWork(name, synth.dg_layer_stack(), norm_mode)
     if name == "sam_relpos":
         return RelposWork(name, synth.sam_global())
     if name == "hbm_copy":
@@ -268,12 +335,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_cache",
-                    choices=["long_cache", "dg_canvas", "tiny", "depformer", "sam_relpos",
-                             "hbm_copy"])
-    ap.add_argument("--norm", default="one_launch",
-                    choices=["one_launch", "in_attention", "separate"],
-                    help="one_launch: q, k, v norms in one launch; in_attention: k/v norms in "
-                         "one launch + q norm inside attention; separate: the page's three "
+                    choices=["long_cache", "dg_canvas", "dg_layers", "tiny", "depformer",
+                             "sam_relpos", "hbm_copy"])
+    ap.add_argument("--norm", default="in_attention",
+                    choices=["in_attention", "one_launch", "separate"],
+                    help="in_attention: k/v norms in one launch + q norm inside attention; "
+                         "one_launch: q, k, v norms in one launch; separate: the page's three "
                          "headnorm dispatches")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle wall time for the CPU baseline (0 = skip)")
@@ -296,8 +363,9 @@ def main():
     for _ in range(args.warmup):
         work.step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    nev = len(work.io) if isinstance(work, LayerStackWork) else 0
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [[mk() for _ in range(nev)] if nev else mk() for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -307,7 +375,10 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    if nev:
+        kern_ms = [sum(a.elapsed_time(b) for a, b in step) for step in evs]
+    else:
+        kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)
 
     step_bytes = work.attn_bytes + work.norm_bytes

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdgattn.so")
 
 DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
-DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP = 1, 2, 4
+DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
 
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",

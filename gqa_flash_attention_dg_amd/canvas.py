@@ -1,51 +1,76 @@
-"""One canvas step of the attention block, as a sequence of C-ABI calls on the GPU.
+"""Canvas steps of the attention block, as sequences of C-ABI calls on the GPU.
 
 Follows the per-layer dispatch order of `canvas_forward` in inferencelayer 0.2.3,
-src/diffusion_gemma_gpu.rs: the per-token rope table for positions seq_len + t is built once
-per forward, then each step runs the headnorm on q (weighted + rope), on k (weighted + rope),
-the weightless, un-roped norm on v, and the split-GQA attention over [cache | canvas].
+src/diffusion_gemma_gpu.rs: the per-token rope tables for positions seq_len + t are built once
+per forward, one per layer type (sliding layers: head_dim and the sliding rope base; global
+layers: head_dim_global and the full rope base); then each layer's step normalises q (weighted
++ rope) and k (weighted + rope), runs the weightless, un-roped norm on v, and the split-GQA
+attention over that layer's [cache | canvas].  A k_eq_v layer has no v projection: its v is
+the raw k projection, normalised without weight or rope.
 
 Set-up work (rope tables, roping a cache that is stored un-roped) happens once per canvas
 block in the constructor; `step` is the per-denoising-step hot path.  Three ways to run the
 norms of a step (`norm_mode`):
+  "in_attention"  k and v normalised by one launch, the q norm and rope applied by the
+                  attention kernel as it stages q (q is left un-normalised in memory);
   "one_launch"    q, k and v normalised in place by one launch, then plain attention;
-  "in_attention"  k and v normalised by one launch, the q norm and rope applied in registers
-                  by the attention kernel as it loads q (q is left un-normalised in memory);
-  "separate"      the page's three in-place headnorm dispatches, then plain attention.  This module only orders
-calls into libdgattn.so; it does no arithmetic of its own.
+  "separate"      the page's three in-place headnorm dispatches, then plain attention.
+This module only orders calls into libdgattn.so; it does no arithmetic of its own.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_WEIGHTED, dg_attn_split_gqa,
-               dg_attn_split_gqa_qnorm, dg_attn_split_gqa_workspace_size, dg_headnorm_rope,
-               dg_qkv_headnorm_rope, dg_rope_table)
+from . import (DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K, DG_NORM_WEIGHTED,
+               dg_attn_split_gqa, dg_attn_split_gqa_qnorm, dg_attn_split_gqa_workspace_size,
+               dg_headnorm_rope, dg_qkv_headnorm_rope, dg_rope_table)
+
+NORM_MODES = ("in_attention", "one_launch", "separate")
+
+
+def rope_table(pos0, T, hd, theta, device="cuda"):
+    """[T, 2*hd] cos|sin table for positions pos0..pos0+T-1 (one launch)."""
+    cs = torch.empty((T, 2 * hd), dtype=torch.float32, device=device)
+    dg_rope_table(cs, pos0, T, hd, theta)
+    return cs
 
 
 class CanvasBlock:
-    """Device-resident state of one canvas block: cache, norm weights, rope table, workspace.
+    """Device-resident state of one layer's canvas attention: cache, norm weights, rope table,
+    workspace.
 
     kc, vc: [B, nkv, ctx, hd] float32 GPU tensors (None when ctx == 0); wq, wk: [hd] or None.
-    rope_cache: the cache keys are stored un-roped and get roped at positions 0..ctx-1 here
-    (in place on kc).  normed: normalise q, k and v in each step, as `norm_mode` says.
+    pos0: absolute position of canvas row 0 (default ctx: the cache holds positions before it).
+    cs: a [T, 2*hd] rope table to share (e.g. one per layer type); built here when None.
+    rope_cache: the cache keys are stored un-roped and get roped here, in place on kc, at the
+    ctx positions just before pos0.  normed: normalise q, k and v in each step, as `norm_mode`
+    says.  k_eq_v: the layer has no v projection; each step's v buffer is written with the
+    weightless norm of the raw k (its input contents are ignored).
     """
 
     def __init__(self, B, T, ctx, nh, nkv, hd, kc=None, vc=None, wq=None, wk=None, *,
                  eps=1e-6, theta=10000.0, scale=1.0, causal=False, rope_cache=False,
-                 normed=True, norm_mode="one_launch", use_workspace=True, device="cuda"):
-        if norm_mode not in ("one_launch", "in_attention", "separate"):
+                 normed=True, norm_mode="in_attention", use_workspace=True, pos0=None, cs=None,
+                 k_eq_v=False, device="cuda"):
+        if norm_mode not in NORM_MODES:
             raise ValueError("unknown norm_mode %r" % (norm_mode,))
+        if k_eq_v and not normed:
+            raise ValueError("k_eq_v needs the norms (v is derived from the raw k)")
         self.B, self.T, self.ctx, self.nh, self.nkv, self.hd = B, T, ctx, nh, nkv, hd
         self.kc, self.vc, self.wq, self.wk = kc, vc, wq, wk
         self.eps, self.scale, self.causal, self.normed = eps, scale, int(causal), normed
-        self.norm_mode = norm_mode
-        self.cs = torch.empty((T, 2 * hd), dtype=torch.float32, device=device)
-        if normed:
-            dg_rope_table(self.cs, ctx, T, hd, theta)
+        self.norm_mode, self.k_eq_v = norm_mode, k_eq_v
+        pos0 = ctx if pos0 is None else pos0
+        if cs is not None:
+            if tuple(cs.shape) != (T, 2 * hd):
+                raise ValueError("cs must be [T, 2*hd] = [%d, %d]" % (T, 2 * hd))
+            self.cs = cs
+        else:
+            self.cs = rope_table(pos0, T, hd, theta, device) if normed else None
         if rope_cache and ctx > 0:
-            cs_cache = torch.empty((ctx, 2 * hd), dtype=torch.float32, device=device)
-            dg_rope_table(cs_cache, 0, ctx, hd, theta)
+            if pos0 < ctx:
+                raise ValueError("rope_cache needs pos0 >= ctx")
+            cs_cache = rope_table(pos0 - ctx, ctx, hd, theta, device)
             dg_headnorm_rope(kc, None, cs_cache, B * nkv, ctx, 1, hd,
                              DG_NORM_ROPE | DG_NORM_SKIP, 0.0)
         self.ws_bytes = dg_attn_split_gqa_workspace_size(B, T, ctx, nh, nkv, hd) \
@@ -54,18 +79,23 @@ class CanvasBlock:
             if self.ws_bytes > 0 else None
 
     def norm(self, q, k, v):
-        """The three per-step headnorm calls, in place on q, k and v."""
+        """The page's per-step headnorm calls, in place on q, k and v (for a k_eq_v layer the
+        k and v norms share one launch, since v is derived from the raw k)."""
         B, T, nh, nkv, hd = self.B, self.T, self.nh, self.nkv, self.hd
         flags = DG_NORM_WEIGHTED | DG_NORM_ROPE
         dg_headnorm_rope(q, self.wq, self.cs, B, T, nh, hd, flags, self.eps)
+        if self.k_eq_v:
+            self.norm_qkv(None, k, v)
+            return
         dg_headnorm_rope(k, self.wk, self.cs, B, T, nkv, hd, flags, self.eps)
         dg_headnorm_rope(v, None, None, B, T, nkv, hd, 0, self.eps)
 
     def norm_qkv(self, q, k, v):
         """q, k (weighted + rope) and v (weightless) norms in one launch, in place; q may be
         None to leave it for the attention kernel."""
+        flags = DG_NORM_WEIGHTED | DG_NORM_ROPE | (DG_NORM_V_FROM_K if self.k_eq_v else 0)
         dg_qkv_headnorm_rope(q, self.wq, k, self.wk, v, self.cs, self.B, self.T, self.nh,
-                             self.nkv, self.hd, DG_NORM_WEIGHTED | DG_NORM_ROPE, self.eps)
+                             self.nkv, self.hd, flags, self.eps)
 
     def attend_qnorm(self, q, k, v, out):
         """Attention on the raw q, normalised and roped inside the kernel (q is not written)."""
@@ -89,3 +119,40 @@ class CanvasBlock:
         elif self.normed:
             self.norm(q, k, v)
         self.attend(q, k, v, out)
+
+
+class CanvasStack:
+    """The attention blocks of a stack of decoder layers over one canvas.
+
+    Each layer has its own type (sliding or global), head dim, kv heads, cache and k_eq_v
+    flag (`layers`: objects with fields sliding, hd, nkv, ctx, k_eq_v).  Layers of one type
+    share one rope table, built once for canvas positions pos0..pos0+T-1 with that type's
+    head dim and rope base, as `canvas_forward` builds `cs_sliding` and `cs_full`.
+    caches[i] = (kc, vc) and weights[i] = (wq, wk) are layer i's GPU tensors.
+    """
+
+    def __init__(self, B, T, nh, pos0, layers, caches, weights, *, theta_sliding, theta_full,
+                 eps=1e-6, scale=1.0, norm_mode="in_attention", use_workspace=True,
+                 device="cuda"):
+        self.layers = list(layers)
+        tables = {}
+        for l in self.layers:
+            key = (l.sliding, l.hd)
+            if key not in tables:
+                theta = theta_sliding if l.sliding else theta_full
+                tables[key] = rope_table(pos0, T, l.hd, theta, device)
+        for sliding in (True, False):
+            if len({l.hd for l in self.layers if l.sliding == sliding}) > 1:
+                raise ValueError("all layers of one type share one head dim (one rope table)")
+        self.tables = tables
+        self.blocks = []
+        for l, (kc, vc), (wq, wk) in zip(self.layers, caches, weights):
+            self.blocks.append(CanvasBlock(
+                B, T, l.ctx, nh, l.nkv, l.hd, kc, vc, wq, wk, eps=eps, scale=scale,
+                norm_mode=norm_mode, use_workspace=use_workspace, pos0=pos0,
+                cs=tables[(l.sliding, l.hd)], k_eq_v=l.k_eq_v, device=device))
+
+    def step(self, li, q, k, v, out):
+        """Layer li's attention for this canvas step (q, k, v are its projections; for a
+        k_eq_v layer v is an output buffer)."""
+        self.blocks[li].step(q, k, v, out)

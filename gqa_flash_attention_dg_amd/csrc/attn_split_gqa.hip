@@ -47,6 +47,7 @@ struct SplitArgs {
     float* out;
     float* ws;         // split-KV partials: o [nsplit][nqtot][hd], m [nsplit][nqtot], l [...]
     size_t nqtot;      // batch * T * nh query vectors
+    int hd;            // head dim (a multiple of 4; the tile width HD is 64 or 128)
     int T, ctx, nh, nkv, G;
     int qblocks;       // workgroups per (batch, kv head, split)
     int nsplit;        // key-range splits
@@ -59,58 +60,101 @@ struct SplitArgs {
     float eps;
 };
 
-// Loads the lane's share of a raw query vector (the layout of dgk::load_q: slot 4*g + e holds
-// element 8*g + 4*half + e) and applies the headnorm of the q dispatch in registers.  The two
-// lane halves hold complementary elements, so the sum of squares needs one exchange with lane
-// l^32; the rope partner of element e (e +- hd/2) is slot 4*(g +- hd/16) + e of the same lane.
-// The weight and the rope are linear and the norm is one scalar per vector, so they are applied
-// to the raw values first and the norm factor last, folded with scale*log2(e): every load is
-// then independent of the sum of squares and can be in flight at once.  Invalid lanes (row 0
-// of the table, a valid address) end with zeros.
+// Row stride (floats) of the normalised queries staged in LDS: HD + 4 keeps the 16-byte
+// operand reads (32 lanes on 32 different rows) free of bank conflicts.
 template <int HD>
-__device__ inline void load_q_normed(const SplitArgs& a, const float* __restrict__ qrow,
-                                     bool valid, int half, int row, float (&qreg)[HD / 2]) {
-    dgk::load_q<HD>(qrow, valid, half, 1.0f, qreg);
+constexpr int kQStride = HD + 4;
+
+// The q dispatch of DG_HEADNORM_ROPE for the workgroup's kBlockQ query vectors, written to LDS
+// rows qs[v][kQStride] (pre-multiplied by scale*log2(e), zero past hd and for vectors past the
+// end) for the dgk::load_q layout to read back.  Row-oriented, so every global access is
+// coalesced: 8 lanes share one query vector, lane c holding its float4 chunks c, c+8, c+16 and
+// c+24; a wave covers 8 vectors per pass, and the sum of squares takes 3 lane exchanges.  The
+// rope partner of element e (e +- hd/2, any even hd) is read back from the staged row, which
+// the same wavefront wrote (LDS accesses of one wavefront complete in order).
+template <int HD>
+__device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs, int b, int kv,
+                                      int qb, int wave, int lane, int hd) {
+    constexpr int kPerLane = HD / 32;  // float4 chunks per lane
+    const int sub = lane >> 3, c = lane & 7;
+    const int nq = a.T * a.G;
     const bool norm = !(a.qflags & DG_NORM_SKIP);
-    float ss = 0.0f;
+    const bool weighted = norm && (a.qflags & DG_NORM_WEIGHTED);
+    const bool rope = (a.qflags & DG_NORM_ROPE) != 0;
+    const int half_hd = hd >> 1;
+    float4 w[kPerLane];
 #pragma unroll
-    for (int i = 0; i < HD / 2; ++i) ss += qreg[i] * qreg[i];
-    if (norm && (a.qflags & DG_NORM_WEIGHTED)) {
-#pragma unroll
-        for (int g = 0; g < HD / 8; ++g) {
-            const float4 w4 = *reinterpret_cast<const float4*>(a.wq + 8 * g + 4 * half);
-            qreg[4 * g + 0] *= w4.x;
-            qreg[4 * g + 1] *= w4.y;
-            qreg[4 * g + 2] *= w4.z;
-            qreg[4 * g + 3] *= w4.w;
-        }
+    for (int k = 0; k < kPerLane; ++k) {
+        const int e0 = 4 * (c + 8 * k);
+        w[k] = weighted && e0 < hd ? *reinterpret_cast<const float4*>(a.wq + e0)
+                                   : make_float4(1.f, 1.f, 1.f, 1.f);
     }
-    if (a.qflags & DG_NORM_ROPE) {
-        constexpr int H = HD / 16;  // float4 groups per half of the head
-        const float* cr = a.cs + (size_t)row * 2 * HD;
+#pragma unroll 1
+    for (int pass = 0; pass < kBlockQ / (8 * kWaves); ++pass) {
+        const int vloc = (pass * kWaves + wave) * 8 + sub;
+        const int qv = qb * kBlockQ + vloc;
+        const bool valid = qv < nq;
+        const int row = valid ? qv / a.G : 0;
+        const int hq = kv * a.G + (valid ? qv % a.G : 0);
+        const float* qrow = a.q + (((size_t)b * a.T + row) * a.nh + hq) * hd;
+        float* srow = qs + vloc * kQStride<HD>;
+        float4 x[kPerLane];
+        float ss = 0.0f;
 #pragma unroll
-        for (int g = 0; g < H; ++g) {
-            const float* lo = cr + 8 * g + 4 * half;
-            const float* hi = lo + HD / 2;
-            const float4 cl = *reinterpret_cast<const float4*>(lo);
-            const float4 sl = *reinterpret_cast<const float4*>(lo + HD);
-            const float4 ch = *reinterpret_cast<const float4*>(hi);
-            const float4 sh = *reinterpret_cast<const float4*>(hi + HD);
-            const float cla[4] = {cl.x, cl.y, cl.z, cl.w}, sla[4] = {sl.x, sl.y, sl.z, sl.w};
-            const float cha[4] = {ch.x, ch.y, ch.z, ch.w}, sha[4] = {sh.x, sh.y, sh.z, sh.w};
+        for (int k = 0; k < kPerLane; ++k) {
+            const int e0 = 4 * (c + 8 * k);
+            x[k] = valid && e0 < hd ? *reinterpret_cast<const float4*>(qrow + e0)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+            ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
+        }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        const float inv = norm ? (valid ? 1.0f / sqrtf(ss / (float)hd + a.eps) : 0.0f) : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x = qreg[4 * g + e], y = qreg[4 * (g + H) + e];
-                qreg[4 * g + e] = x * cla[e] + (-y) * sla[e];
-                qreg[4 * (g + H) + e] = y * cha[e] + x * sha[e];
+        for (int k = 0; k < kPerLane; ++k) {
+            x[k].x = x[k].x * inv * w[k].x;
+            x[k].y = x[k].y * inv * w[k].y;
+            x[k].z = x[k].z * inv * w[k].z;
+            x[k].w = x[k].w * inv * w[k].w;
+        }
+        if (rope) {
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k)
+                *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) = x[k];
+            const float* cr = a.cs + (size_t)row * 2 * hd;
+            float part[kPerLane][4];
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * (c + 8 * k) + i;
+                    const int pe = e < half_hd ? e + half_hd : e - half_hd;
+                    part[k][i] = e < hd ? srow[pe] : 0.0f;
+                }
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                const int e0 = 4 * (c + 8 * k);
+                if (e0 < hd) {
+                    const float4 co = *reinterpret_cast<const float4*>(cr + e0);
+                    const float4 si = *reinterpret_cast<const float4*>(cr + hd + e0);
+                    const float y[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+                    const float cc[4] = {co.x, co.y, co.z, co.w}, sn[4] = {si.x, si.y, si.z, si.w};
+                    float r[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float rot = e0 + i < half_hd ? -part[k][i] : part[k][i];
+                        r[i] = y[i] * cc[i] + rot * sn[i];
+                    }
+                    x[k] = make_float4(r[0], r[1], r[2], r[3]);
+                }
             }
         }
-    }
-    ss += __shfl_xor(ss, 32);
-    float mul = a.qmul;
-    if (norm) mul = valid ? mul / sqrtf(ss / (float)HD + a.eps) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < HD / 2; ++i) qreg[i] *= mul;
+        for (int k = 0; k < kPerLane; ++k)
+            *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) =
+                make_float4(x[k].x * a.qmul, x[k].y * a.qmul, x[k].z * a.qmul, x[k].w * a.qmul);
+    }
 }
 
 // Workgroup id -> logical id such that consecutive logical ids share an XCD (the hardware
@@ -120,11 +164,20 @@ __device__ inline int xcd_remap(int bid, int n) {
     return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
-template <int HD, bool kNormQ>
+// kPad: the head dim hd is narrower than the HD-wide tile (hd < HD, a multiple of 4).  Queries
+// are zero past hd; key/value rows are loaded with their chunks past hd taken from a valid
+// chunk of the same row (finite values that meet zero query elements, and output elements
+// past hd that are never stored).
+template <int HD, bool kNormQ, bool kPad>
 __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     using TL = dgk::Tile<HD>;
-    // [buffer][tile of the stage][K, V]
-    __shared__ __attribute__((aligned(16))) float smem[2 * 2 * 2 * TL::kFloats];
+    // [buffer][tile of the stage][K, V]; with kNormQ the normalised queries are staged over
+    // buffer 1 (free until the second stage is issued) and a little past it.
+    constexpr int kStageFloats = 2 * 2 * 2 * TL::kFloats;
+    constexpr int kQStageEnd = 2 * 2 * TL::kFloats + kBlockQ * kQStride<HD>;
+    constexpr int kSmemFloats = kNormQ && kQStageEnd > kStageFloats ? kQStageEnd : kStageFloats;
+    __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
+    const int hd = kPad ? a.hd : HD;
     auto tile_ptr = [&](int buf, int tile, int isv) {
         return smem + ((buf * 2 + tile) * 2 + isv) * TL::kFloats;
     };
@@ -161,11 +214,11 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const int st_begin = (int)((long long)split * nstage / a.nsplit);
     const int st_end = (int)((long long)(split + 1) * nstage / a.nsplit);
 
-    const float* kcb = a.kc + (size_t)bk * a.ctx * HD;
-    const float* vcb = a.vc + (size_t)bk * a.ctx * HD;
-    const size_t cstride = (size_t)a.nkv * HD;
-    const float* kb = a.k + ((size_t)b * a.T * a.nkv + kv) * HD;
-    const float* vb = a.v + ((size_t)b * a.T * a.nkv + kv) * HD;
+    const float* kcb = a.kc + (size_t)bk * a.ctx * hd;
+    const float* vcb = a.vc + (size_t)bk * a.ctx * hd;
+    const size_t cstride = (size_t)a.nkv * hd;
+    const float* kb = a.k + ((size_t)b * a.T * a.nkv + kv) * hd;
+    const float* vb = a.v + ((size_t)b * a.T * a.nkv + kv) * hd;
 
     // The four even-tile wavefronts issue the stage's 4 * kLoadsPerTile wave-wide loads (K and
     // V of both tiles); their odd-tile partners start on the MFMAs meanwhile (on this hardware
@@ -176,7 +229,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / (kWaves / 2);
     constexpr int R = TL::kRowsPerLoad;
     const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
-    const unsigned rstride_c = HD * 4, rstride_v = (unsigned)cstride * 4;
+    const unsigned rstride_c = (unsigned)hd * 4, rstride_v = (unsigned)cstride * 4;
     auto issue_stage = [&](int st, int buf) {
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -185,19 +238,21 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             const int ld = L % TL::kLoadsPerTile;
             const int tile = part >> 1, isv = part & 1;
             const int trow = ld * R + rsub;           // tile row of this lane's chunk
-            const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
+            int chunk = isv ? pos : (pos ^ (trow % TL::kChunks));
+            if (kPad) chunk = min(chunk, hd / 4 - 1);
+            const unsigned coff = 16u * chunk;
             const int j0 = st * kStage + tile * dgk::kKeys;
             float* dst = tile_ptr(buf, tile, isv) + ld * 256;
             const char* p;
             if (j0 + dgk::kKeys <= a.ctx && j0 + dgk::kKeys <= kend) {
-                p = reinterpret_cast<const char*>((isv ? vcb : kcb) + (size_t)j0 * HD) +
+                p = reinterpret_cast<const char*>((isv ? vcb : kcb) + (size_t)j0 * hd) +
                     ((unsigned)trow * rstride_c + coff);
             } else if (j0 >= a.ctx && j0 + dgk::kKeys <= kend) {
                 p = reinterpret_cast<const char*>((isv ? vb : kb) + (size_t)(j0 - a.ctx) * cstride) +
                     ((unsigned)trow * rstride_v + coff);
             } else {
                 const int j = min(j0 + trow, kend - 1);
-                p = reinterpret_cast<const char*>(j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * HD
+                p = reinterpret_cast<const char*>(j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * hd
                                                             : (isv ? vb : kb) + (size_t)(j - a.ctx) * cstride) +
                     coff;
             }
@@ -208,10 +263,14 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     // The first stage's loads go out before the queries are fetched, so the two overlap.
     if (!hi && st_begin < st_end) issue_stage(st_begin, 0);
     float qreg[HD / 2];
-    if constexpr (kNormQ)
-        load_q_normed<HD>(a, a.q + gq * HD, valid, half, row, qreg);
-    else
-        dgk::load_q<HD>(a.q + gq * HD, valid, half, a.qmul, qreg);
+    if constexpr (kNormQ) {
+        float* qs = smem + 2 * 2 * TL::kFloats;
+        stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
+        __syncthreads();
+        dgk::load_q<HD>(qs + (pair * dgk::kQuery + l32) * kQStride<HD>, true, half, 1.0f, qreg);
+    } else {
+        dgk::load_q<HD>(a.q + gq * hd, valid, half, a.qmul, qreg, hd);
+    }
     f32x16 o[TL::kGroups];
 #pragma unroll
     for (int t = 0; t < TL::kGroups; ++t)
@@ -246,11 +305,11 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
     if (hi || !valid) return;
     if (a.nsplit == 1) {
-        dgk::store_row<HD>(a.out + gq * HD, 1.0f / ltot, o, half);
+        dgk::store_row<HD>(a.out + gq * hd, 1.0f / ltot, o, half, hd);
     } else {
-        dgk::store_row<HD>(a.ws + ((size_t)split * a.nqtot + gq) * HD, 1.0f, o, half);
+        dgk::store_row<HD>(a.ws + ((size_t)split * a.nqtot + gq) * hd, 1.0f, o, half, hd);
         if (half == 0) {
-            float* wm = a.ws + (size_t)a.nsplit * a.nqtot * HD;
+            float* wm = a.ws + (size_t)a.nsplit * a.nqtot * hd;
             wm[(size_t)split * a.nqtot + gq] = m;
             wm[(size_t)(a.nsplit + split) * a.nqtot + gq] = ltot;
         }
@@ -260,16 +319,20 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 // Short key sets (ctx + T <= 8, e.g. the depformer's causal frames of 8 steps): there is too
 // little work per query for matrix tiles, and the call is HBM-bound.  One wavefront per
 // (batch entry, q head): lane (r, c) = (lane / 8, lane % 8) owns query row r and the c-th
-// hd/8-wide segment of it, and loads the same segment of key/value row r into wave-private LDS.
+// HD/8-wide segment of it, and loads the same segment of key/value row r into wave-private LDS.
 // Each lane forms partial dots of its query segment with every key's segment; a 3-step lane
 // exchange within each group of 8 completes them, the 8-entry softmax runs in registers, and
 // each lane writes its segment of the output row.  All global accesses are contiguous per row.
+// Elements at or past hd (kPad) are zero.  With kNormQ the q norm runs on the lane's segment
+// (3 exchanges for the sum of squares) and the rope partner is read back from a staged row.
 constexpr int kSmallKeys = 8;
 
-template <int HD, bool kNormQ>
+template <int HD, bool kNormQ, bool kPad>
 __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long units) {
     constexpr int SEG = HD / 8;
-    __shared__ __attribute__((aligned(16))) float kvs[4 * 2 * kSmallKeys * HD];
+    constexpr int kRows = kNormQ ? 3 : 2;   // K, V (and the staged q) per wave
+    __shared__ __attribute__((aligned(16))) float kvs[4 * kRows * kSmallKeys * HD];
+    const int hd = kPad ? a.hd : HD;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane >> 3, cseg = (lane & 7) * SEG;
     const long long u = (long long)blockIdx.x * 4 + wave;   // b * nh + h
@@ -278,7 +341,7 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
     const int b = active ? (int)(u / a.nh) : 0;
     const int kv = h / a.G;
     const int S = a.ctx + a.T;
-    float* ks = kvs + wave * 2 * kSmallKeys * HD;
+    float* ks = kvs + wave * kRows * kSmallKeys * HD;
     float* vs = ks + kSmallKeys * HD;
 
     float qr[SEG], kr[SEG], vr[SEG];
@@ -286,25 +349,24 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
     const float* kp = nullptr;
     const float* vp = nullptr;
     if (has_key) {
-        const size_t off = r < a.ctx ? (((size_t)b * a.nkv + kv) * a.ctx + r) * HD
-                                     : (((size_t)b * a.T + (r - a.ctx)) * a.nkv + kv) * HD;
+        const size_t off = r < a.ctx ? (((size_t)b * a.nkv + kv) * a.ctx + r) * hd
+                                     : (((size_t)b * a.T + (r - a.ctx)) * a.nkv + kv) * hd;
         kp = (r < a.ctx ? a.kc : a.k) + off + cseg;
         vp = (r < a.ctx ? a.vc : a.v) + off + cseg;
     }
-    const float* qp = a.q + (((size_t)b * a.T + r) * a.nh + h) * HD + cseg;
+    const float* qp = a.q + (((size_t)b * a.T + r) * a.nh + h) * hd + cseg;
 #pragma unroll
     for (int e = 0; e < SEG; e += 4) {
+        const bool in = cseg + e < hd;
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 k4 = has_key ? *reinterpret_cast<const float4*>(kp + e) : z;
-        const float4 v4 = has_key ? *reinterpret_cast<const float4*>(vp + e) : z;
-        const float4 q4 = has_q ? *reinterpret_cast<const float4*>(qp + e) : z;
+        const float4 k4 = has_key && in ? *reinterpret_cast<const float4*>(kp + e) : z;
+        const float4 v4 = has_key && in ? *reinterpret_cast<const float4*>(vp + e) : z;
+        const float4 q4 = has_q && in ? *reinterpret_cast<const float4*>(qp + e) : z;
         kr[e] = k4.x; kr[e + 1] = k4.y; kr[e + 2] = k4.z; kr[e + 3] = k4.w;
         vr[e] = v4.x; vr[e + 1] = v4.y; vr[e + 2] = v4.z; vr[e + 3] = v4.w;
         qr[e] = q4.x; qr[e + 1] = q4.y; qr[e + 2] = q4.z; qr[e + 3] = q4.w;
     }
     if constexpr (kNormQ) {
-        // q headnorm in registers: the 8 lanes of row r hold its 8 segments, so the sum of
-        // squares takes 3 exchanges, and the rope partner (segment c +- 4) is lane ^ 4.
         if (!(a.qflags & DG_NORM_SKIP)) {
             float ss = 0.0f;
 #pragma unroll
@@ -312,22 +374,34 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
             ss += __shfl_xor(ss, 1);
             ss += __shfl_xor(ss, 2);
             ss += __shfl_xor(ss, 4);
-            const float inv = has_q ? 1.0f / sqrtf(ss / (float)HD + a.eps) : 0.0f;
+            const float inv = has_q ? 1.0f / sqrtf(ss / (float)hd + a.eps) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < SEG; ++e) qr[e] *= inv;
-            if (a.qflags & DG_NORM_WEIGHTED) {
-#pragma unroll
-                for (int e = 0; e < SEG; ++e) qr[e] *= a.wq[cseg + e];
+            for (int e = 0; e < SEG; ++e) {
+                qr[e] *= inv;
+                if ((a.qflags & DG_NORM_WEIGHTED) && cseg + e < hd) qr[e] *= a.wq[cseg + e];
             }
         }
         if (a.qflags & DG_NORM_ROPE) {
-            const bool lower = cseg < HD / 2;
-            const float* cr = a.cs + (size_t)(has_q ? r : 0) * 2 * HD + cseg;
+            float* qs = vs + kSmallKeys * HD + r * HD;   // this row's staging, wave-private
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) qs[cseg + e] = qr[e];
+            const int half_hd = hd >> 1;
+            const float* cr = a.cs + (size_t)(has_q ? r : 0) * 2 * hd;
+            float part[SEG];
 #pragma unroll
             for (int e = 0; e < SEG; ++e) {
-                const float partner = __shfl_xor(qr[e], 4);
-                const float rot = lower ? -partner : partner;
-                qr[e] = has_q ? qr[e] * cr[e] + rot * cr[HD + e] : 0.0f;
+                const int el = cseg + e;
+                part[e] = el < hd ? qs[el < half_hd ? el + half_hd : el - half_hd] : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) {
+                const int el = cseg + e;
+                if (el < hd && has_q) {
+                    const float rot = el < half_hd ? -part[e] : part[e];
+                    qr[e] = qr[e] * cr[el] + rot * cr[hd + el];
+                } else {
+                    qr[e] = 0.0f;
+                }
             }
         }
     }
@@ -377,23 +451,24 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
     }
     if (!has_q) return;
     const float inv = 1.0f / l;
-    float* op = a.out + (((size_t)b * a.T + r) * a.nh + h) * HD + cseg;
+    float* op = a.out + (((size_t)b * a.T + r) * a.nh + h) * hd + cseg;
 #pragma unroll
     for (int e = 0; e < SEG; e += 4)
-        *reinterpret_cast<float4*>(op + e) = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+        if (cseg + e < hd)
+            *reinterpret_cast<float4*>(op + e) = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
 }
 
 // Merges split-KV partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
-// One thread per 4 output elements.
-template <int HD>
+// One thread per 4 output elements (hd is a multiple of 4).
 __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restrict__ ws,
                                                             float* __restrict__ out,
-                                                            size_t total, int nsplit) {
+                                                            size_t total, int nsplit, int hd) {
+    const int c4 = hd / 4;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total * (HD / 4)) return;
-    const size_t gq = idx / (HD / 4);
-    const int c = (int)(idx % (HD / 4)) * 4;
-    const float* wm = ws + (size_t)nsplit * total * HD;
+    if (idx >= total * c4) return;
+    const size_t gq = idx / c4;
+    const int c = (int)(idx % c4) * 4;
+    const float* wm = ws + (size_t)nsplit * total * hd;
     const float* wl = wm + (size_t)nsplit * total;
     float M = -INFINITY;
     for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wm[(size_t)s * total + gq]);
@@ -402,11 +477,11 @@ __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restr
     for (int s = 0; s < nsplit; ++s) {
         const float w = dgk::fast_exp2(wm[(size_t)s * total + gq] - M);
         L += wl[(size_t)s * total + gq] * w;
-        const float4 v = *reinterpret_cast<const float4*>(ws + ((size_t)s * total + gq) * HD + c);
+        const float4 v = *reinterpret_cast<const float4*>(ws + ((size_t)s * total + gq) * hd + c);
         acc.x += v.x * w; acc.y += v.y * w; acc.z += v.z * w; acc.w += v.w * w;
     }
     const float inv = 1.0f / L;
-    *reinterpret_cast<float4*>(out + gq * HD + c) =
+    *reinterpret_cast<float4*>(out + gq * hd + c) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
@@ -438,11 +513,36 @@ Plan plan(int batch, int T, int ctx, int nh, int nkv, int hd, int causal) {
 extern "C" size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int nkv,
                                                    int hd) {
     if (batch <= 0 || T <= 0 || ctx < 0 || nkv < 1 || nh < 1 || nh % nkv != 0) return 0;
-    if (hd != 64 && hd != 128) return 0;
+    if (hd < 4 || hd > 128 || hd % 4 != 0) return 0;
     return plan(batch, T, ctx, nh, nkv, hd, 0).ws_bytes;
 }
 
 namespace {
+
+// Kernel variant for a head dim: the tile is 64 wide for hd <= 64 and 128 wide above; a
+// narrower hd runs padded.
+using SplitKernel = void (*)(SplitArgs);
+using SmallKernel = void (*)(SplitArgs, long long);
+
+template <int HD, bool kNormQ>
+SplitKernel split_variant(int hd) {
+    return hd == HD ? attn_split_gqa_kernel<HD, kNormQ, false> : attn_split_gqa_kernel<HD, kNormQ, true>;
+}
+
+SplitKernel pick_split(int hd, bool normq) {
+    if (hd > 64) return normq ? split_variant<128, true>(hd) : split_variant<128, false>(hd);
+    return normq ? split_variant<64, true>(hd) : split_variant<64, false>(hd);
+}
+
+template <int HD, bool kNormQ>
+SmallKernel small_variant(int hd) {
+    return hd == HD ? attn_small_kernel<HD, kNormQ, false> : attn_small_kernel<HD, kNormQ, true>;
+}
+
+SmallKernel pick_small(int hd, bool normq) {
+    if (hd > 64) return normq ? small_variant<128, true>(hd) : small_variant<128, false>(hd);
+    return normq ? small_variant<64, true>(hd) : small_variant<64, false>(hd);
+}
 
 // Shared body of both attention entry points.  `normq` selects the q-norm variant, whose extra
 // arguments (wq, cs, qflags, eps) were validated by the caller.
@@ -456,7 +556,8 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
     if (nkv < 1 || nh < 1 || nh % nkv != 0)
         return dg::fail(DG_EINVAL, "%s: nh (%d) must be a positive multiple of nkv (%d)", fn, nh, nkv);
     if (hd < 1) return dg::fail(DG_EINVAL, "%s: hd must be >= 1, got %d", fn, hd);
-    if (hd != 64 && hd != 128) return dg::fail(DG_EUNSUPPORTED, "%s: hd %d not supported (64 or 128)", fn, hd);
+    if (hd > 128 || hd % 4 != 0)
+        return dg::fail(DG_EUNSUPPORTED, "%s: hd %d not supported (a multiple of 4, at most 128)", fn, hd);
     if (!std::isfinite(scale)) return dg::fail(DG_EINVAL, "%s: scale is not finite", fn);
     if (causal != 0 && causal != 1) return dg::fail(DG_EINVAL, "%s: causal must be 0 or 1", fn);
     size_t nq = 1, nkvc = 1, ncache = 1;
@@ -503,6 +604,7 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
     a.q = q; a.kc = kc; a.vc = vc; a.k = k; a.v = v; a.out = out;
     a.ws = static_cast<float*>(p.nsplit > 1 ? workspace : nullptr);
     a.nqtot = (size_t)batch * T * nh;
+    a.hd = hd;
     a.T = T; a.ctx = ctx; a.nh = nh; a.nkv = nkv; a.G = nh / nkv;
     a.qblocks = p.qblocks;
     a.nsplit = p.nsplit;
@@ -518,24 +620,16 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
         const long long units = (long long)batch * nh;
         const long long blocks = (units + 3) / 4;
         if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
-        auto* kern = hd == 128 ? (normq ? attn_small_kernel<128, true> : attn_small_kernel<128, false>)
-                               : (normq ? attn_small_kernel<64, true> : attn_small_kernel<64, false>);
-        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, a, units);
+        hipLaunchKernelGGL(pick_small(hd, normq), dim3((unsigned)blocks), dim3(256), 0, s, a, units);
         return dg::launch_status(fn);
     }
-    auto* kern = hd == 128 ? (normq ? attn_split_gqa_kernel<128, true> : attn_split_gqa_kernel<128, false>)
-                           : (normq ? attn_split_gqa_kernel<64, true> : attn_split_gqa_kernel<64, false>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(pick_split(hd, normq), dim3((unsigned)nblocks), dim3(512), 0, s, a);
     if (p.nsplit > 1) {
         const size_t total = (size_t)batch * T * nh;
         const size_t threads = total * (hd / 4);
         const unsigned blocks = (unsigned)((threads + 255) / 256);
-        if (hd == 128)
-            hipLaunchKernelGGL(split_combine_kernel<128>, dim3(blocks), dim3(256), 0, s,
-                               (const float*)a.ws, out, total, p.nsplit);
-        else
-            hipLaunchKernelGGL(split_combine_kernel<64>, dim3(blocks), dim3(256), 0, s,
-                               (const float*)a.ws, out, total, p.nsplit);
+        hipLaunchKernelGGL(split_combine_kernel, dim3(blocks), dim3(256), 0, s, (const float*)a.ws,
+                           out, total, p.nsplit, hd);
     }
     return dg::launch_status(fn);
 }

@@ -51,13 +51,16 @@ struct Tile {
 __device__ inline int key_of(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
 // Loads this lane's share of a query vector: qreg[4*g + e] = q[8*g + 4*half + e] * mul.
+// Elements at or past `lim` (the true head dim when a narrower head is padded to the HD-wide
+// tile; a multiple of 4) read as zero.
 template <int HD>
 __device__ inline void load_q(const float* __restrict__ qrow, bool valid, int half, float mul,
-                              float (&qreg)[HD / 2]) {
+                              float (&qreg)[HD / 2], int lim = HD) {
 #pragma unroll
     for (int g = 0; g < HD / 8; ++g) {
-        float4 v = valid ? *reinterpret_cast<const float4*>(qrow + 8 * g + 4 * half)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool in = valid && 8 * g + 4 * half < lim;
+        float4 v = in ? *reinterpret_cast<const float4*>(qrow + 8 * g + 4 * half)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
         qreg[4 * g + 0] = v.x * mul;
         qreg[4 * g + 1] = v.y * mul;
         qreg[4 * g + 2] = v.z * mul;
@@ -190,12 +193,14 @@ __device__ inline int out_elem(int t, int r, int half) {
     return (8 * (r >> 2) + 4 * half + (r & 3)) * Tile<HD>::kGroups + t;
 }
 
-// Writes o * scale for the lane's query (row pointer `orow`, contiguous HD floats).
+// Writes o * scale for the lane's query (row pointer `orow`, contiguous floats); only head
+// elements below `lim` (a multiple of 4) are written.
 template <int HD>
 __device__ inline void store_row(float* __restrict__ orow, float scale,
-                                 const f32x16 (&o)[Tile<HD>::kGroups], int half) {
+                                 const f32x16 (&o)[Tile<HD>::kGroups], int half, int lim = HD) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+        if (out_elem<HD>(0, r, half) >= lim) continue;
         float* dst = orow + out_elem<HD>(0, r, half);
         if constexpr (HD == 128) {
             *reinterpret_cast<float4*>(dst) =

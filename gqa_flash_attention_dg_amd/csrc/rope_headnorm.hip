@@ -47,6 +47,7 @@ struct NormSeg {
     long long rows;   // batch * T * heads
     int heads;
     unsigned flags;
+    float* vout;      // k_eq_v: also write the weightless norm of the raw rows here, or NULL
 };
 
 struct NormArgs {
@@ -59,7 +60,7 @@ struct NormArgs {
 
 __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restrict__ w,
                                     const float* __restrict__ cr, int hd, unsigned flags,
-                                    float eps, int lane) {
+                                    float eps, int lane, float* __restrict__ vr) {
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = e0 < hd, v1 = e1 < hd;
     float y0 = v0 ? xr[e0] : 0.0f;
@@ -69,6 +70,10 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
         const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
         y0 *= inv;
         y1 *= inv;
+        if (vr) {  // the v-norm of the same raw rows: weightless, un-roped
+            if (v0) vr[e0] = y0;
+            if (v1) vr[e1] = y1;
+        }
         if (flags & DG_NORM_WEIGHTED) {
             if (v0) y0 *= w[e0];
             if (v1) y1 *= w[e1];
@@ -114,7 +119,8 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     const NormSeg& g = a.seg[s];
     const int t = (int)((u / g.heads) % a.T);
     const float* cr = (g.flags & DG_NORM_ROPE) ? a.cs + (size_t)t * 2 * a.hd : nullptr;
-    headnorm_row(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane);
+    headnorm_row(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane,
+                 g.vout ? g.vout + (size_t)u * a.hd : nullptr);
 }
 
 }  // namespace
@@ -183,7 +189,7 @@ extern "C" int dg_headnorm_rope(float* x, const float* w, const float* cs, int b
     if (need_cs && xs.overlaps(dg::Span(cs, (size_t)T * 2 * hd * sizeof(float))))
         return dg::fail(DG_EINVAL, "%s: cs overlaps x", fn);
     NormArgs a{};
-    a.seg[0] = NormSeg{x, need_w ? w : nullptr, (long long)batch * T * heads, heads, flags};
+    a.seg[0] = NormSeg{x, need_w ? w : nullptr, (long long)batch * T * heads, heads, flags, nullptr};
     a.nseg = 1;
     a.cs = need_cs ? cs : nullptr;
     a.T = T;
@@ -197,11 +203,17 @@ extern "C" int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const f
                                     unsigned flags, float eps, void* stream) {
     const char* fn = "dg_qkv_headnorm_rope";
     if (nh < 0 || nkv < 0) return dg::fail(DG_EINVAL, "%s: negative size (nh %d, nkv %d)", fn, nh, nkv);
+    const bool v_from_k = (flags & DG_NORM_V_FROM_K) != 0;
+    flags &= ~DG_NORM_V_FROM_K;
     if (int st = check_norm_common(fn, batch, T, hd, flags, eps)) return st;
+    if (v_from_k && (flags & DG_NORM_SKIP))
+        return dg::fail(DG_EINVAL, "%s: V_FROM_K needs the norm (SKIP is set)", fn);
     size_t nq = 1, nk = 1;
     if (!dg::mul_ok(nq, batch) || !dg::mul_ok(nq, T) || !dg::mul_ok(nq, nh) || !dg::mul_ok(nq, hd) ||
         !dg::mul_ok(nk, batch) || !dg::mul_ok(nk, T) || !dg::mul_ok(nk, nkv) || !dg::mul_ok(nk, hd))
         return dg::fail(DG_EINVAL, "%s: size overflow", fn);
+    if (v_from_k && nk > 0 && (!k || !v))
+        return dg::fail(DG_EINVAL, "%s: V_FROM_K needs both k and v", fn);
     const bool need_w = (flags & DG_NORM_WEIGHTED) && !(flags & DG_NORM_SKIP);
     const bool need_cs = (flags & DG_NORM_ROPE) != 0;
     const bool do_q = q && nq > 0, do_k = k && nk > 0, do_v = v && nk > 0;
@@ -222,9 +234,13 @@ extern "C" int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const f
             if (xs[i].overlaps(ro[j])) return dg::fail(DG_EINVAL, "%s: wq, wk or cs overlaps q, k or v", fn);
     }
     NormArgs a{};
-    if (do_q) a.seg[a.nseg++] = NormSeg{q, need_w ? wq : nullptr, (long long)batch * T * nh, nh, flags};
-    if (do_k) a.seg[a.nseg++] = NormSeg{k, need_w ? wk : nullptr, (long long)batch * T * nkv, nkv, flags};
-    if (do_v) a.seg[a.nseg++] = NormSeg{v, nullptr, (long long)batch * T * nkv, nkv, 0u};
+    if (do_q)
+        a.seg[a.nseg++] = NormSeg{q, need_w ? wq : nullptr, (long long)batch * T * nh, nh, flags, nullptr};
+    if (do_k)
+        a.seg[a.nseg++] = NormSeg{k, need_w ? wk : nullptr, (long long)batch * T * nkv, nkv, flags,
+                                  v_from_k ? v : nullptr};
+    if (do_v && !v_from_k)
+        a.seg[a.nseg++] = NormSeg{v, nullptr, (long long)batch * T * nkv, nkv, 0u, nullptr};
     a.cs = need_cs ? cs : nullptr;
     a.T = T;
     a.hd = hd;

@@ -160,6 +160,63 @@ def depformer_frames(seed=0, frames=4096) -> SplitCase:
                      q, k, v, None, None, None, None, scale=0.125, causal=True, normed=False)
 
 
+@dataclass
+class LayerSpec:
+    """Attention geometry of one decoder layer over a shared canvas: its type (sliding layers
+    use the sliding rope table, global layers the full one), head dim, kv heads, cache length,
+    and whether it lacks a v projection (k_eq_v: v is the raw k projection)."""
+    sliding: bool
+    hd: int
+    nkv: int
+    ctx: int
+    k_eq_v: bool = False
+
+
+@dataclass
+class LayerStackCase:
+    """One canvas step through a stack of layers.  ``per_layer[i]`` holds layer i's host
+    tensors: q [B,T,nh*hd], k [B,T,nkv*hd], v (None for k_eq_v), kc/vc [B,nkv,ctx,hd], wq, wk.
+    Canvas row t sits at position pos0 + t in every layer."""
+    name: str
+    B: int
+    T: int
+    nh: int
+    pos0: int
+    theta_sliding: float
+    theta_full: float
+    layers: List[LayerSpec]
+    per_layer: List[Dict[str, Optional[np.ndarray]]]
+    eps: float = 1e-6
+    scale: float = 1.0
+
+
+def layer_stack(B, T, nh, pos0, layers, seed=0, theta_sliding=1e4, theta_full=1e6,
+                name="layer_stack") -> LayerStackCase:
+    """Per layer in order: kc, vc [B,nkv,ctx,hd], q, k, then v unless k_eq_v, then wq, wk."""
+    g = torch.Generator().manual_seed(seed)
+    per = []
+    for l in layers:
+        d = {"kc": _randn(g, B, l.nkv, l.ctx, l.hd) if l.ctx > 0 else None}
+        d["vc"] = _randn(g, B, l.nkv, l.ctx, l.hd) if l.ctx > 0 else None
+        d["q"] = _randn(g, B, T, nh * l.hd)
+        d["k"] = _randn(g, B, T, l.nkv * l.hd)
+        d["v"] = None if l.k_eq_v else _randn(g, B, T, l.nkv * l.hd)
+        d["wq"] = _weight(g, l.hd)
+        d["wk"] = _weight(g, l.hd)
+        per.append(d)
+    return LayerStackCase(name, B, T, nh, pos0, theta_sliding, theta_full, list(layers), per)
+
+
+def dg_layer_stack(seed=0) -> LayerStackCase:
+    """DiffusionGemma-like layer types over one canvas (T=256, nh=16, positions 1024..1279):
+    sliding layers hd 128, nkv 8, rope base 1e4, a 512-entry cache; one global layer hd 96
+    (run padded in the 128-wide kernel), nkv 4, rope base 1e6, a 1024-entry cache, k_eq_v."""
+    layers = [LayerSpec(True, 128, 8, 512), LayerSpec(False, 96, 4, 1024, k_eq_v=True),
+              LayerSpec(True, 128, 8, 512)]
+    return layer_stack(1, 256, 16, 1024, layers, seed=seed,
+                       name="dg_layers_T256_h16_sliding128kv8ctx512_global96kv4ctx1024")
+
+
 def relpos_case(gh, gw, heads, hd, seed=0, scale=None, bias=True, table_std=0.02,
                 name="relpos") -> RelposCase:
     """Fused qkv [gh*gw, 3*heads*hd] ~ N(0,1), then Rh [gh,gh,hd], Rw [gw,gw,hd]."""

@@ -46,6 +46,10 @@ enum {
 #define DG_NORM_WEIGHTED 1u
 #define DG_NORM_ROPE 2u
 #define DG_NORM_SKIP 4u
+/* Accepted by dg_qkv_headnorm_rope only: the page's k_eq_v layers, whose v is the RAW k
+ * projection.  v is then an output: each v row is the weightless, un-roped norm of the raw k
+ * row (computed before k is normed and roped in place), and v's prior contents are ignored. */
+#define DG_NORM_V_FROM_K 8u
 
 /*
  * dg_rope_table -- cos|sin table for the NeoX rotate-half rope.
@@ -93,11 +97,12 @@ int dg_headnorm_rope(float* x, const float* w, const float* cs, int batch, int T
  *       normalises q itself, see dg_attn_split_gqa_qnorm)
  *   wq  [hd]; read iff q != NULL and WEIGHTED is set without SKIP
  *   k   in/out [batch, T, nkv*hd], or NULL;  wk [hd] as wq
- *   v   in/out [batch, T, nkv*hd], or NULL
+ *   v   in/out [batch, T, nkv*hd], or NULL; with DG_NORM_V_FROM_K an output only
  *   cs  [T, 2*hd] rope table; read iff ROPE is set and q or k is given
- *   flags, eps as dg_headnorm_rope (flags apply to q and k only).
- * Errors: as dg_headnorm_rope, plus DG_EINVAL for negative nh/nkv, overlapping q/k/v, or a
- * weight or table overlapping any of them.  All of q, k, v NULL (or empty) is a no-op.
+ *   flags, eps as dg_headnorm_rope (flags apply to q and k only), plus DG_NORM_V_FROM_K.
+ * Errors: as dg_headnorm_rope, plus DG_EINVAL for negative nh/nkv, overlapping q/k/v, a
+ * weight or table overlapping any of them, V_FROM_K without k or v, or V_FROM_K with SKIP.
+ * All of q, k, v NULL (or empty) is a no-op.
  */
 int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, float* v,
                          const float* cs, int batch, int T, int nh, int nkv, int hd,
@@ -134,10 +139,12 @@ size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int n
  *              results up to rounding).  Must not overlap any input or `out`.
  *   Every tensor pointer must be 16-byte aligned (the kernels use 16-byte vector accesses;
  *   torch allocations are).
+ *   hd         any multiple of 4 up to 128 (the page allows hd <= 128); heads narrower than
+ *              64 or 128 run in the 64- or 128-wide kernel with zero padding.
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
  * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, a tensor pointer
  * that is not 16-byte aligned, or a workspace pointer that is misaligned or has
- * workspace_bytes too small; DG_EUNSUPPORTED for hd not 64 or 128.
+ * workspace_bytes too small; DG_EUNSUPPORTED for hd above 128 or not a multiple of 4.
  */
 int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
                       const float* v, float* out, int batch, int T, int ctx, int nh, int nkv,

@@ -83,7 +83,8 @@ def test_attn_split_validation(L):
     assert "multiple" in _err(L)
     assert f(*args(nkv=0)) == dg.DG_EINVAL
     assert f(*args(T=-1)) == dg.DG_EINVAL
-    assert f(*args(hd=96)) == dg.DG_EUNSUPPORTED
+    assert f(*args(hd=98)) == dg.DG_EUNSUPPORTED            # not a multiple of 4
+    assert f(*args(hd=132)) == dg.DG_EUNSUPPORTED
     assert f(*args(hd=0)) == dg.DG_EINVAL
     assert f(*args(scale=float("nan"))) == dg.DG_EINVAL
     assert f(*args(causal=2)) == dg.DG_EINVAL
@@ -106,7 +107,7 @@ def test_qkv_headnorm_validation(L):
     call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
     assert call(nh=-1) == dg.DG_EINVAL
     assert call(hd=256) == dg.DG_EUNSUPPORTED
-    assert call(flags=8) == dg.DG_EINVAL
+    assert call(flags=16) == dg.DG_EINVAL                  # unknown bit
     assert call(wq=None) == dg.DG_EINVAL                   # WEIGHTED needs wq for q
     assert call(cs=None) == dg.DG_EINVAL
     assert call(k=FAKE + 64) == dg.DG_EINVAL               # k inside q
@@ -114,6 +115,11 @@ def test_qkv_headnorm_validation(L):
     assert call(cs=FAKE + (2 << 24) + 256) == dg.DG_EINVAL  # table inside k
     assert call(eps=float("nan")) == dg.DG_EINVAL
     assert call(q=None, k=None, v=None) == dg.DG_OK        # nothing to do
+    vfk = dg.DG_NORM_V_FROM_K
+    assert call(flags=3 | vfk, v=None) == dg.DG_EINVAL      # V_FROM_K needs an output v
+    assert call(flags=4 | vfk) == dg.DG_EINVAL              # ... and the norm
+    assert L.dg_headnorm_rope(FAKE, FAKE + (1 << 24), FAKE + (2 << 24), 1, 4, 2, 64, 3 | vfk,
+                              1e-6, None) == dg.DG_EINVAL   # single-tensor entry: unknown bit
     assert call(T=0) == dg.DG_OK
     assert _err(L) == ""
 
@@ -131,7 +137,7 @@ def test_attn_qnorm_validation(L):
     assert call(cs=None) == dg.DG_EINVAL
     assert call(out=FAKE + (1 << 24)) == dg.DG_EINVAL       # out overlaps wq
     assert call(out=FAKE + (2 << 24) + 512) == dg.DG_EINVAL # out overlaps the rope table
-    assert call(hd=96) == dg.DG_EUNSUPPORTED
+    assert call(hd=66) == dg.DG_EUNSUPPORTED
     assert call(nh=3) == dg.DG_EINVAL
     assert call(q=FAKE + 4, out=FAKE + (8 << 24)) == dg.DG_EINVAL   # misaligned q
     assert "aligned" in _err(L)

@@ -90,6 +90,25 @@ def test_qkv_headnorm_rope(B, T, nh, nkv, hd, flags, which):
             assert np.array_equal(host(t), x), "%s was not passed and must be unchanged" % name
 
 
+@pytest.mark.parametrize("B,T,nh,nkv,hd", [(1, 16, 4, 2, 64), (2, 37, 6, 3, 96), (1, 5, 2, 1, 20)])
+def test_qkv_headnorm_v_from_k(B, T, nh, nkv, hd):
+    """k_eq_v layers: v is written as the weightless norm of the RAW k, then k is normed + roped."""
+    rng = np.random.default_rng(T + hd)
+    q = (rng.standard_normal((B, T, nh * hd)) * 2.0).astype(np.float32)
+    k = (rng.standard_normal((B, T, nkv * hd)) * 0.5).astype(np.float32)
+    wq = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    wk = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    cs = oracle.rope_table(9, T, hd, 1e6)
+    qd, kd = dev(q), dev(k)
+    vd = torch.full((B, T, nkv * hd), float("nan"), device="cuda")
+    flags = dg.DG_NORM_WEIGHTED | dg.DG_NORM_ROPE
+    dg.dg_qkv_headnorm_rope(qd, dev(wq), kd, dev(wk), vd, dev(cs), B, T, nh, nkv, hd,
+                            flags | dg.DG_NORM_V_FROM_K, 1e-6)
+    assert_parity(host(qd), oracle.headnorm_rope(q, wq, cs, nh, hd, flags, 1e-6), "q")
+    assert_parity(host(kd), oracle.headnorm_rope(k, wk, cs, nkv, hd, flags, 1e-6), "k")
+    assert_parity(host(vd), oracle.headnorm_rope(k, None, None, nkv, hd, 0, 1e-6), "v from raw k")
+
+
 # ----------------------------------------------------------------------------- split-GQA
 
 SPLIT_SHAPES = [
@@ -106,6 +125,14 @@ SPLIT_SHAPES = [
     (1, 4, 4, 6, 3, 64, 0.5, True),        # short set, causal after a cache
     (1, 7, 0, 4, 1, 128, 0.3, True),       # short set, G = 4
     (2, 8, 1, 4, 2, 64, 1.0, False),       # 9 keys: just past the short-set limit
+    # head dims other than 64 and 128 run padded in the 64- or 128-wide kernels
+    (1, 40, 70, 4, 2, 96, 1.0, False),     # hd 96 in the 128-wide tile
+    (2, 19, 33, 6, 3, 80, 0.5, True),      # hd 80, causal after a cache
+    (1, 24, 50, 8, 2, 32, 1.0, False),     # hd 32 in the 64-wide tile
+    (1, 9, 100, 4, 1, 4, 1.0, False),      # hd 4: one 16-byte chunk per row
+    (1, 130, 300, 8, 4, 112, 1.0, False),  # hd 112, several workgroups per kv head
+    (2, 3, 4, 4, 2, 96, 0.7, False),       # short set, hd 96
+    (1, 5, 0, 2, 1, 20, 1.0, True),        # short set, hd 20
 ]
 
 
@@ -131,7 +158,8 @@ def test_attn_split_small(shape, use_ws):
 
 
 @pytest.mark.parametrize("shape", [(1, 64, 2000, 4, 2, 128), (2, 40, 700, 8, 8, 64),
-                                   (1, 256, 1024, 16, 8, 128), (1, 3, 5000, 2, 1, 64)])
+                                   (1, 256, 1024, 16, 8, 128), (1, 3, 5000, 2, 1, 64),
+                                   (1, 64, 2000, 4, 2, 96)])
 def test_attn_split_kv_partials_and_combine(shape):
     """Shapes with few workgroups split the key range across workgroups and merge partials."""
     B, T, ctx, nh, nkv, hd = shape
@@ -181,8 +209,9 @@ def test_attn_split_qnorm_small(shape, use_ws):
 
 @pytest.mark.parametrize("flags", [0, 1, 2, 6])
 @pytest.mark.parametrize("shape", [(1, 40, 90, 4, 2, 128, 1.0, False), (2, 6, 2, 4, 2, 64, 0.5, True),
-                                   (1, 70, 0, 8, 2, 64, 0.3, True)],
-                         ids=["hd128", "short-set", "causal-hd64"])
+                                   (1, 70, 0, 8, 2, 64, 0.3, True), (1, 33, 20, 4, 2, 80, 1.0, False),
+                                   (1, 4, 3, 2, 1, 20, 1.0, False)],
+                         ids=["hd128", "short-set", "causal-hd64", "hd80", "short-set-hd20"])
 def test_attn_split_qnorm_flags(shape, flags):
     B, T, ctx, nh, nkv, hd, scale, causal = shape
     c, q, wq, cs, ref = qnorm_case(shape, flags, seed=11 + flags)
@@ -216,7 +245,7 @@ def test_attn_split_on_a_side_stream():
 
 # ----------------------------------------------------------------------------- full workloads
 
-def run_block(case, steps=None, norm_mode="one_launch"):
+def run_block(case, steps=None, norm_mode="in_attention"):
     """Set up a CanvasBlock from a synthetic case and run the given (q, k, v) steps."""
     blk = CanvasBlock(case.B, case.T, case.ctx, case.nh, case.nkv, case.hd, dev(case.kc),
                       dev(case.vc), dev(case.wq), dev(case.wk), eps=case.eps, theta=case.theta,
@@ -230,7 +259,7 @@ def run_block(case, steps=None, norm_mode="one_launch"):
     return blk, outs
 
 
-NORM_MODES = ["one_launch", "in_attention", "separate"]
+NORM_MODES = ["in_attention", "one_launch", "separate"]
 
 
 @pytest.mark.parametrize("norm_mode", NORM_MODES)
@@ -257,7 +286,7 @@ def test_dg_canvas_48_steps(norm_mode):
             assert_parity(flat(outs[s]), flat(ref), "dg step %d" % s)
 
 
-@pytest.mark.parametrize("norm_mode", ["one_launch", "in_attention"])
+@pytest.mark.parametrize("norm_mode", ["in_attention", "one_launch"])
 def test_long_cache_sampled_rows(norm_mode):
     c = synth.long_cache()
     _, (got,) = run_block(c, norm_mode=norm_mode)
@@ -275,6 +304,38 @@ def test_depformer_frames_every_element():
     assert_parity(got, ref, "depformer frames")
     assert np.array_equal(got[:, 0], c.v[:, 0]) or \
         np.max(np.abs(got[:, 0] - c.v[:, 0])) < 1e-6   # row 0 sees only key 0
+
+
+def oracle_layer(case, li):
+    """Layer li of a layer stack on the oracle: its type's rope table, the norms (v from the
+    raw k for a k_eq_v layer), then attention over its own cache."""
+    l, d = case.layers[li], case.per_layer[li]
+    theta = case.theta_sliding if l.sliding else case.theta_full
+    cs = oracle.rope_table(case.pos0, case.T, l.hd, theta)
+    q = oracle.headnorm_rope(d["q"], d["wq"], cs, case.nh, l.hd, 3, case.eps)
+    k = oracle.headnorm_rope(d["k"], d["wk"], cs, l.nkv, l.hd, 3, case.eps)
+    v = oracle.headnorm_rope(d["k"] if l.k_eq_v else d["v"], None, None, l.nkv, l.hd, 0, case.eps)
+    return oracle.attn_split_gqa(q, d["kc"], d["vc"], k, v, case.nh, l.nkv, l.hd, case.scale,
+                                 False)
+
+
+@pytest.mark.parametrize("norm_mode", NORM_MODES)
+def test_dg_layer_stack_every_element(norm_mode):
+    """Sliding and global layers (own hd, nkv, rope base, cache length; a k_eq_v layer) over
+    one canvas, every output element of every layer."""
+    from gqa_flash_attention_dg_amd.canvas import CanvasStack
+    c = synth.dg_layer_stack()
+    caches = [(dev(d["kc"]), dev(d["vc"])) for d in c.per_layer]
+    weights = [(dev(d["wq"]), dev(d["wk"])) for d in c.per_layer]
+    stack = CanvasStack(c.B, c.T, c.nh, c.pos0, c.layers, caches, weights,
+                        theta_sliding=c.theta_sliding, theta_full=c.theta_full, eps=c.eps,
+                        scale=c.scale, norm_mode=norm_mode)
+    for li, (l, d) in enumerate(zip(c.layers, c.per_layer)):
+        v = torch.full((c.B, c.T, l.nkv * l.hd), float("nan"), device="cuda") if l.k_eq_v \
+            else dev(d["v"])
+        out = torch.full((c.B, c.T, c.nh * l.hd), float("nan"), device="cuda")
+        stack.step(li, dev(d["q"]), dev(d["k"]), v, out)
+        assert_parity(host(out), oracle_layer(c, li), "layer %d (%s)" % (li, l))
 
 
 # ----------------------------------------------------------------------------- rel-pos

@@ -88,7 +88,7 @@ def _rope_complex(y, cs, hd):
 
 
 @pytest.mark.parametrize("hd,heads,weighted", [(64, 4, True), (128, 3, True), (128, 2, False),
-                                               (6, 5, True)])
+                                               (6, 5, True), (96, 2, True), (20, 3, False)])
 def test_headnorm_rope_matches_rms_norm_and_complex_rotation(hd, heads, weighted):
     rng = np.random.default_rng(1)
     T = 7
@@ -206,6 +206,11 @@ SMALL_SPLIT = [
     (3, 8, 0, 4, 4, 64, True, 0.125),
     (1, 7, 9, 6, 3, 64, True, 0.5),
     (1, 16, 1, 4, 4, 128, False, 0.2),
+    # head dims other than 64 and 128 (the pages allow any hd <= 128)
+    (1, 5, 7, 4, 2, 96, False, 1.0),
+    (2, 4, 3, 6, 3, 80, True, 0.5),
+    (1, 6, 2, 2, 1, 20, False, 1.0),
+    (1, 3, 4, 4, 4, 4, True, 1.0),
 ]
 
 
