@@ -7,7 +7,8 @@ A step is one pass of the hot path over one batch of synthetic input resident in
     applies the q headnorm + rope as it stages q (--norm one_launch: q, k and v in one launch,
     then plain attention; --norm separate: the page's three headnorm dispatches);
   dg_layers: the same for each layer of a sliding/global layer stack (one step = all layers);
-  sam_relpos: one rel-pos flash attention (bias-row pass + flash kernel).
+  sam_relpos: one rel-pos flash attention (bias-row pass + flash kernel);
+  sam_windowed: the same over the SAM windowed block's 25 windows of 14x14 tokens.
 The default workload is the long-cache split-GQA canvas step (4 canvases, T=256, ctx=8192,
 nh=32, nkv=8, hd=128).  W untimed steps, then K steps timed with HIP events on the stream the
 kernels run on (torch's current stream), bracketed by device synchronisation.  The dominant
@@ -224,37 +225,48 @@ class LayerStackWork:
 
 
 class RelposWork:
+    """Rel-pos flash attention over one grid (sam_relpos) or a batch of windows
+    (sam_windowed): the bias-row pass into the workspace, then the flash kernel."""
     dominant = "relpos_flash"
 
     def __init__(self, name, case):
         import numpy as np
         import torch
+        import gqa_flash_attention_dg_amd as dg
         self.name, self.c = name, case
+        self.nwin = getattr(case, "nwin", 1)
         d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.qkv, self.rh, self.rw = d(case.qkv), d(case.rh), d(case.rw)
         n, W = case.gh * case.gw, case.heads * case.hd
-        self.out = torch.empty((n, W), device="cuda")
-        import gqa_flash_attention_dg_amd as dg
-        self.ws_bytes = dg.relpos_flash_attn_workspace_size(case.gh, case.gw, case.heads, case.hd)
+        self.out = torch.empty((self.nwin, n, W), device="cuda")
+        self.ws_bytes = dg.relpos_flash_attn_windows_workspace_size(
+            self.nwin, case.gh, case.gw, case.heads, case.hd)
         self.ws = torch.empty((max(self.ws_bytes, 4) // 4,), device="cuda")
-        self.flops = case.heads * n * n * 4 * case.hd + \
-            (case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0)
+        self.flops = self.nwin * (case.heads * n * n * 4 * case.hd + (
+            case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0))
         # every input read once, the output written once (the bias rows it keeps in its
         # workspace are the method's own intermediate, not counted)
-        self.attn_bytes = 4 * (n * 3 * W + n * W + (case.gh ** 2 + case.gw ** 2) * case.hd)
+        self.attn_bytes = 4 * (self.nwin * (n * 3 * W + n * W) +
+                               (case.gh ** 2 + case.gw ** 2) * case.hd)
         self.norm_bytes = 0
         self.bound = "mfma"
 
     def config(self):
         c = self.c
-        return {"workload": c.name, "grid": [c.gh, c.gw], "heads": c.heads, "hd": c.hd,
-                "scale": c.scale, "step": "relpos_flash_attn"}
+        cfg = {"workload": c.name, "grid": [c.gh, c.gw], "heads": c.heads, "hd": c.hd,
+               "scale": c.scale}
+        if self.nwin > 1:
+            cfg["windows"] = self.nwin
+            cfg["step"] = "relpos_flash_attn_windows"
+        else:
+            cfg["step"] = "relpos_flash_attn"
+        return cfg
 
     def _call(self, out):
         import gqa_flash_attention_dg_amd as dg
         c = self.c
-        dg.relpos_flash_attn(self.qkv, self.rh, self.rw, out, c.gh, c.gw, c.heads, c.hd, c.scale,
-                             self.ws, self.ws_bytes)
+        dg.relpos_flash_attn_windows(self.qkv, self.rh, self.rw, out, self.nwin, c.gh, c.gw,
+                                     c.heads, c.hd, c.scale, self.ws, self.ws_bytes)
 
     def step(self, ev=None):
         if ev:
@@ -268,18 +280,22 @@ class RelposWork:
         import oracle
         c = self.c
         n = c.gh * c.gw
+        qkv0 = c.qkv if self.nwin == 1 else c.qkv[0]
         probe = np.arange(0, n, n // 8 or 1, dtype=np.int64)[:8]
         t0 = time.perf_counter()
-        oracle.relpos_attn(c.qkv, c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale, rows=probe)
+        oracle.relpos_attn(qkv0, c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale, rows=probe)
         dt = time.perf_counter() - t0
         m = int(min(n, max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
         rows = np.unique(np.linspace(0, n - 1, m).astype(np.int64))
         t0 = time.perf_counter()
-        oracle.relpos_attn(c.qkv, c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale, rows=rows)
+        oracle.relpos_attn(qkv0, c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale, rows=rows)
         dt = time.perf_counter() - t0
-        return {"value": self.flops / n * rows.size / dt / 1e12, "unit": "TFLOP/s",
+        per_row = self.flops / (self.nwin * n)
+        where = "" if self.nwin == 1 else " of window 0 (of %d)" % self.nwin
+        return {"value": per_row * rows.size / dt / 1e12, "unit": "TFLOP/s",
                 "cores": oracle.threads(), "kind": "oracle",
-                "sample": "%d of %d query rows (all %d heads); %.2f s wall" % (rows.size, n, c.heads, dt)}
+                "sample": "%d of %d query rows%s (all %d heads); %.2f s wall"
+                          % (rows.size, n, where, c.heads, dt)}
 
 
 class CopyWork:
@@ -324,6 +340,8 @@ def make_work(name, norm_mode="in_attention"):
         return LayerStackWork(name, synth.dg_layer_stack(), norm_mode)
     if name == "sam_relpos":
         return RelposWork(name, synth.sam_global())
+    if name == "sam_windowed":
+        return RelposWork(name, synth.sam_windowed())
     if name == "hbm_copy":
         return CopyWork(name)
     raise SystemExit("unknown workload %s" % name)
@@ -336,7 +354,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_cache",
                     choices=["long_cache", "dg_canvas", "dg_layers", "tiny", "depformer",
-                             "sam_relpos", "hbm_copy"])
+                             "sam_relpos", "sam_windowed", "hbm_copy"])
     ap.add_argument("--norm", default="in_attention",
                     choices=["in_attention", "one_launch", "separate"],
                     help="in_attention: k/v norms in one launch + q norm inside attention; "

@@ -21,7 +21,9 @@ DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
 
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
-           "relpos_flash_attn_workspace_size", "relpos_flash_attn", "dg_last_error")
+           "relpos_flash_attn_workspace_size", "relpos_flash_attn",
+           "relpos_flash_attn_windows_workspace_size", "relpos_flash_attn_windows",
+           "dg_last_error")
 
 
 class DgError(RuntimeError):
@@ -54,8 +56,12 @@ def lib() -> ctypes.CDLL:
         L.relpos_flash_attn_workspace_size.argtypes = [I, I, I, I]
         L.relpos_flash_attn_workspace_size.restype = Z
         L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp, Z, vp]
+        L.relpos_flash_attn_windows_workspace_size.argtypes = [I, I, I, I, I]
+        L.relpos_flash_attn_windows_workspace_size.restype = Z
+        L.relpos_flash_attn_windows.argtypes = [vp, vp, vp, vp, I, I, I, I, I, F, vp, Z, vp]
         for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
-                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "relpos_flash_attn"):
+                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "relpos_flash_attn",
+                     "relpos_flash_attn_windows"):
             getattr(L, name).restype = I
         L.dg_last_error.argtypes = []
         L.dg_last_error.restype = ctypes.c_char_p
@@ -190,3 +196,20 @@ def relpos_flash_attn(qkv, rh, rw, out, gh: int, gw: int, heads: int, hd: int, s
     _check(lib().relpos_flash_attn(_ptr(qkv, "qkv", n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
                                    _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", n * W),
                                    gh, gw, heads, hd, float(scale), ws, wsb, _stream(stream)))
+
+
+def relpos_flash_attn_windows_workspace_size(nwin: int, gh: int, gw: int, heads: int,
+                                             hd: int) -> int:
+    return int(lib().relpos_flash_attn_windows_workspace_size(nwin, gh, gw, heads, hd))
+
+
+def relpos_flash_attn_windows(qkv, rh, rw, out, nwin: int, gh: int, gw: int, heads: int, hd: int,
+                              scale: float, workspace=None, workspace_bytes: int = 0,
+                              stream=None) -> None:
+    _nonneg(nwin=nwin, gh=gh, gw=gw, heads=heads, hd=hd)
+    n, W = gh * gw, heads * hd
+    ws, wsb = _workspace(workspace, workspace_bytes)
+    _check(lib().relpos_flash_attn_windows(
+        _ptr(qkv, "qkv", nwin * n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
+        _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", nwin * n * W), nwin, gh, gw, heads, hd,
+        float(scale), ws, wsb, _stream(stream)))

@@ -1,20 +1,23 @@
-// relpos_flash.hip -- relpos_flash_attn: windowless vision attention with the decomposed
+// relpos_flash.hip -- relpos_flash_attn(_windows): vision attention with the decomposed
 // relative-position bias, flash style, on gfx950.
 //
 // Follows inferencelayer 0.2.8, src/deepencoder_gpu.rs: kernel SAM_SCORES fixes the score,
 //   scale*<q_i,k_j> + <q_i, Rh[qy,ky]> + <q_i, Rw[qx,kx]>  (bias on the unscaled q),
 // kernel DHDW hoists the two bias dot products out of the n^2 loop, `flash_reg_src` runs the
 // online softmax over 64-wide chunks with hd fixed at 64, and `sam_attn_buf` fixes the fused
-// qkv layout (q | k | v per token, heads contiguous) and the scale 1/sqrt(hd).
+// qkv layout (q | k | v per token, heads contiguous) and the scale 1/sqrt(hd).  The windowed
+// SAM blocks that the page's encoder cost model counts (25 windows of 14 x 14 tokens) are the
+// same attention run independently per window with shared tables: a batch of grids.
 //
-// The page writes dh/dw to global [heads, n, gh] / [heads, n, gw] buffers and then looks them
-// up per key.  Here each workgroup computes the bias rows of its own 64 queries in a prologue
-// (into LDS and registers: no global round trip, no workspace), then runs the f32-MFMA flash
-// loop of flash_core.hpp.  A workgroup is 2 groups of 32 queries x 4 wavefronts; the 4
-// wavefronts of a group take every 4th 32-key tile (stages of 128 keys, double-buffered
-// direct global->LDS tiles) and merge their softmax states at the end.  The bias enters each
-// score through the MFMA accumulator's starting value.  64-query workgroups give 768
-// workgroups at the 64x64-grid, 12-head shape: three full rounds on 256 CUs.
+// With a workspace, relpos_bias_kernel first writes the hoisted bias rows (dh, dw: 64 floats
+// per (window, head, query) each, in log2 units), as the page's DHDW step does; without one,
+// each attention workgroup forms the dot products of its own queries in a prologue.  The
+// attention is the f32-MFMA flash loop of flash_core.hpp.  A workgroup is 2 groups of 32
+// queries x 4 wavefronts; the 4 wavefronts of a group take every 4th 32-key tile (stages of
+// 128 keys, double-buffered direct global->LDS tiles) and merge their softmax states at the
+// end.  The bias enters each score through the MFMA accumulator's starting value where the
+// grid width allows (see relpos_flash_kernel).  64-query workgroups give 768 workgroups at the
+// 64x64-grid, 12-head shape: three full rounds on 256 CUs.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
@@ -30,14 +33,17 @@ constexpr int kStage = kParts * dgk::kKeys;   // 128 keys per stage
 constexpr int kMaxGrid = 64;                  // gh, gw <= 64
 
 struct RelArgs {
-    const float* qkv;
+    const float* qkv;  // [nwin][n][3W]
     const float* rh;
     const float* rw;
-    const float* dhw;  // precomputed bias rows (dh [heads][n][64], then dw), or null
-    float* out;
-    int n, gh, gw, heads, W;
+    const float* dhw;  // precomputed bias rows (dh [nwin][heads][n][gh], then dw [..][gw]), or null
+    float* out;        // [nwin][n][W]
+    int n, gh, gw, heads, W, nwin;
     int qblocks, nblocks;
     float qmul;  // scale * log2(e)
+    // key tiling (see make_tiling): tile t starts at key (t >> tsh) * ta + (t & tmsk) * tb and
+    // holds min(tl0 + (t & tmsk) * td, n - start) keys
+    int tsh, ta, tmsk, tb, tl0, td, ntiles;
 };
 
 __device__ inline int xcd_remap(int bid, int n) {
@@ -45,103 +51,145 @@ __device__ inline int xcd_remap(int bid, int n) {
     return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
-// Bias rows in log2 units, the page's DHDW step as small matrix products: workgroup (head,
-// line) takes one grid row qy (line < gh; dh[i][ky] = <q_i, Rh[qy,ky]> for the gw queries of
-// that row) or one grid column qx (dw[i][kx] = <q_i, Rw[qx,kx]> for the gh queries of that
-// column).  Both operands (at most 64 x 64 each) are staged in LDS with coalesced loads; each
-// thread forms 16 dot products.  Output rows are 64 wide: dh [heads][n][64], dw after it.
-__global__ void __launch_bounds__(256) relpos_bias_kernel(RelArgs a, float* __restrict__ dhw) {
-    __shared__ float qs[kMaxGrid * (HD + 1)];
-    __shared__ float ts[kMaxGrid * (HD + 1)];
-    const int head = blockIdx.x / (a.gh + a.gw);
-    const int line = blockIdx.x % (a.gh + a.gw);
+// Bias rows in log2 units, the page's DHDW step, as small matrix products on MFMA.  A "line"
+// is one grid row qy (its gw queries against the gh table rows Rh[qy, :]) or one grid column qx
+// (its gh queries against Rw[qx, :]); its output is [queries x table rows] = Q_line T^T with a
+// 64-long contraction.  One wavefront computes one 32x32 tile of one line: lane l supplies
+// query row l%32 (A) and table row l%32 (B), both read straight from memory in the
+// contraction order of the attention (half h holds chunks 8g+4h..8g+4h+3), and the 16
+// accumulators hold 16 queries of table row l%32.  Output rows follow the page's buffers:
+// dh [nwin][heads][n][gh], then dw [nwin][heads][n][gw].
+constexpr int kBiasWaves = 4;
+
+__global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias_kernel(RelArgs a, float* __restrict__ dhw,
+                                                                     long long ntasks) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
+    const long long task = (long long)blockIdx.x * kBiasWaves + (threadIdx.x >> 6);
+    if (task >= ntasks) return;  // wave-uniform
+    // task = ((unit * (gh + gw) + line) * 2 + qt) * 2 + rt, unit = win * heads + head
+    const int rt = (int)(task & 1), qt = (int)((task >> 1) & 1);
+    const long long lt = task >> 2;
+    const int line = (int)(lt % (a.gh + a.gw));
+    const int unit = (int)(lt / (a.gh + a.gw));
+    const int head = unit % a.heads, win = unit / a.heads;
     const bool is_h = line < a.gh;
     const int nq = is_h ? a.gw : a.gh;      // queries on this line
     const int nr = is_h ? a.gh : a.gw;      // table rows (ky or kx)
+    if (qt * 32 >= nq || rt * 32 >= nr) return;
+    const int u = qt * 32 + l32, rrow = rt * 32 + l32;
+    auto qidx = [&](int v) { return is_h ? line * a.gw + v : v * a.gw + (line - a.gh); };
     const size_t rs = (size_t)3 * a.W;
-    auto qidx = [&](int u) { return is_h ? line * a.gw + u : u * a.gw + (line - a.gh); };
-    const float* tab = is_h ? a.rh + (size_t)line * a.gh * HD : a.rw + (size_t)(line - a.gh) * a.gw * HD;
-    for (int e = threadIdx.x; e < kMaxGrid * HD; e += 256) {
-        const int row = e / HD, c = e % HD;
-        qs[row * (HD + 1) + c] = row < nq ? a.qkv[(size_t)qidx(row) * rs + head * HD + c] : 0.0f;
-        ts[row * (HD + 1) + c] = row < nr ? tab[(size_t)row * HD + c] : 0.0f;
+    const float* qr = a.qkv + ((size_t)win * a.n + qidx(min(u, nq - 1))) * rs + head * HD;
+    const float* tr = (is_h ? a.rh + (size_t)line * a.gh * HD : a.rw + (size_t)(line - a.gh) * a.gw * HD) +
+                      (size_t)min(rrow, nr - 1) * HD;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < HD / 8; ++g) {
+        const float4 qv = *reinterpret_cast<const float4*>(qr + 8 * g + 4 * half);
+        const float4 tv = *reinterpret_cast<const float4*>(tr + 8 * g + 4 * half);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.x, tv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.y, tv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.z, tv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.w, tv.w, acc, 0, 0, 0);
     }
-    __syncthreads();
-    const int u = threadIdx.x & 63;          // query on the line
-    const int r0 = (threadIdx.x >> 6) * 16;  // first of this thread's 16 table rows
-    float acc[16];
+    if (rrow >= nr) return;
+    float* base = dhw + (is_h ? (size_t)unit * a.n * a.gh
+                              : (size_t)a.nwin * a.heads * a.n * a.gh + (size_t)unit * a.n * a.gw);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-    for (int c = 0; c < HD; ++c) {
-        const float qv = qs[u * (HD + 1) + c];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) acc[k] += qv * ts[(r0 + k) * (HD + 1) + c];
+    for (int r = 0; r < 16; ++r) {
+        const int v = qt * 32 + dgk::key_of(r, half);   // accumulator row r: query on the line
+        if (v < nq) base[(size_t)qidx(v) * nr + rrow] = acc[r] * dgk::kLog2e;
     }
-    if (u >= nq) return;
-    float* dst = dhw + ((is_h ? 0 : (size_t)a.heads * a.n) + (size_t)head * a.n + qidx(u)) * kMaxGrid;
-#pragma unroll
-    for (int k = 0; k < 16; k += 4)
-        if (r0 + k < nr)
-            *reinterpret_cast<float4*>(dst + r0 + k) =
-                make_float4(acc[k] * dgk::kLog2e, acc[k + 1] * dgk::kLog2e, acc[k + 2] * dgk::kLog2e,
-                            acc[k + 3] * dgk::kLog2e);
 }
 
-// kAligned: gw is 32 or 64, so every 32-key tile lies inside one grid row (one ky) and, as a
-// stage spans 128 keys, a wavefront always sees the same 32 kx values: its 16 dw terms stay
-// in registers and the dh term is one LDS read per tile.  Otherwise both terms are looked up
-// per score from LDS tables.
-template <bool kAligned>
+// Key tiles are cut along grid rows, so that every lane sees the same kx at the same register
+// slot in every tile:
+//  * gw <= 32 ("row tiles"): a tile holds rpt = min(8, 32 / gw) whole grid rows (rpt * gw keys,
+//    the rest of the 32 slots is padding);
+//  * 32 < gw <= 64 ("half-row tiles"): a tile holds one half of a grid row, kh = ceil(gw / 2)
+//    or gw - kh keys; as a wavefront takes every 4th tile it always sees the same half.
+// The lane's 16 width-bias terms dw[q][kx] then stay in registers as the starting value of the
+// score accumulator, with -inf at padding slots (which masks them for free), and the height
+// bias dh[q][ky] - ref rides in ceil(rpt / 2) extra MFMA steps: step m contracts over the two
+// rows 2m and 2m+1 of the tile, with A one-hot on the key's row within the tile.
+struct Tiling {
+    int half_rows;   // 1: half-row tiles; 0: row tiles
+    int rpt;         // grid rows per tile (row tiles)
+    int kh;          // keys in the first half of a row (half-row tiles)
+    int kpt;         // keys in a full tile
+    int ntiles;
+    int nshift;      // extra MFMA steps for the height bias
+};
+
+__host__ __device__ inline Tiling make_tiling(int gh, int gw) {
+    Tiling t;
+    if (gw > 32) {
+        t.half_rows = 1; t.rpt = 1; t.kh = (gw + 1) / 2; t.kpt = t.kh;
+        t.ntiles = 2 * gh; t.nshift = 1;
+    } else {
+        t.half_rows = 0; t.rpt = min(8, 32 / gw); t.kh = 0; t.kpt = t.rpt * gw;
+        t.ntiles = (gh + t.rpt - 1) / t.rpt; t.nshift = (t.rpt + 1) / 2;
+    }
+    return t;
+}
+
+// kFull: every tile holds 32 keys (no padding slots, no short last tile); kOneShift: the height
+// bias takes one MFMA step (at most two grid rows per tile).
+template <bool kFull, bool kOneShift>
 __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     using TL = dgk::Tile<HD>;
-    // staging: [buffer][tile][K, V] and bias tables [group][ky or kx][query] (dh, then dw)
+    // staging: [buffer][tile][K, V] and bias tables [group][ky][query] (dh)
     __shared__ __attribute__((aligned(16))) float smem[2 * kParts * 2 * TL::kFloats];
-    __shared__ float tab[2 * kQGroups * kMaxGrid * dgk::kQuery];
+    __shared__ float tab[kQGroups * kMaxGrid * dgk::kQuery];
     auto tile_ptr = [&](int buf, int tile, int isv) {
         return smem + ((buf * kParts + tile) * 2 + isv) * TL::kFloats;
     };
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks);
     const int qb = lid % a.qblocks;
-    const int head = lid / a.qblocks;
+    const int unit = lid / a.qblocks;          // win * heads + head
+    const int head = unit % a.heads, win = unit / a.heads;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
     const int grp = wave & (kQGroups - 1), part = wave >> 1;
     const size_t rs = (size_t)3 * a.W;  // qkv row stride (floats)
+    const Tiling tl = make_tiling(a.gh, a.gw);
 
     const int qfirst = qb * kBlockQ + grp * dgk::kQuery;
     const int qi = qfirst + l32;
     const bool valid = qi < a.n;
-    const float* qrow = a.qkv + (size_t)(valid ? qi : 0) * rs + head * HD;
+    const float* qkvw = a.qkv + (size_t)win * a.n * rs;   // this window's rows
+    const float* qrow = qkvw + (size_t)(valid ? qi : 0) * rs + head * HD;
     const bool active = qfirst < a.n;
     const bool bias = a.rh != nullptr;
-    float* dh_tab = tab + grp * kMaxGrid * dgk::kQuery;                   // [ky][query]
-    float* dw_tab = tab + (kQGroups + grp) * kMaxGrid * dgk::kQuery;      // [kx][query]
-    const int kxbase = (part * dgk::kKeys) % a.gw;  // aligned case: this wave's kx offset
+    float* dh_tab = tab + grp * kMaxGrid * dgk::kQuery;   // [ky][query]
 
-    // Prologue: the bias dot products of this group's queries in log2 units.  dh[ky] =
-    // <q, Rh[qy,ky]> for all ky, split over the group's 4 wavefronts and 2 lane halves; dw[kx] =
-    // <q, Rw[qx,kx]>, either for this lane's own 16 kx values (aligned) or for all kx (table).
+    // Where the lane's 16 score slots sit in its tiles (the same in every tile of this wave).
+    const int parity = part & 1;                           // half-row tiles: which half
+    const int tlen_w = tl.half_rows ? (parity ? a.gw - tl.kh : tl.kh) : tl.kpt;
+    const int kx0 = tl.half_rows ? parity * tl.kh : 0;
+    // A operand of the height-bias steps: this lane supplies key row l32 at contraction index
+    // `half`; it is 1 in step m iff that key lies in tile row 2m + half.
+    const int arow = l32 < tlen_w ? (tl.half_rows ? 0 : l32 / a.gw) : -1;
+    const float aone = arow == half ? 1.0f : 0.0f;   // the single step's A (kOneShift)
+
+    // Prologue: the dh rows of this group's queries (all ky) into LDS, and the lane's dw terms.
     f32x16 dwreg;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dwreg[r] = 0.0f;
+    const int qx = valid ? qi % a.gw : 0, qy = valid ? qi / a.gw : 0;
     if (bias && active && a.dhw) {
-        // Gather this group's slice of the precomputed bias rows.
-        const float* dhq = a.dhw + ((size_t)head * a.n + (valid ? qi : 0)) * kMaxGrid;
-        const float* dwq = dhq + (size_t)a.heads * a.n * kMaxGrid;
+        const float* dhq = a.dhw + ((size_t)unit * a.n + (valid ? qi : 0)) * a.gh;
+        const float* dwq = a.dhw + (size_t)a.nwin * a.heads * a.n * a.gh +
+                           ((size_t)unit * a.n + (valid ? qi : 0)) * a.gw;
         for (int ky = part * 2 + half; ky < a.gh; ky += 2 * kParts)
             dh_tab[ky * dgk::kQuery + l32] = valid ? dhq[ky] : 0.0f;
-        if (kAligned) {
 #pragma unroll
-            for (int r4 = 0; r4 < 16; r4 += 4) {
-                const float4 t = valid ? *reinterpret_cast<const float4*>(dwq + kxbase + dgk::key_of(r4, half))
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-                dwreg[r4] = t.x; dwreg[r4 + 1] = t.y; dwreg[r4 + 2] = t.z; dwreg[r4 + 3] = t.w;
-            }
-        } else {
-            for (int kx = part * 2 + half; kx < a.gw; kx += 2 * kParts)
-                dw_tab[kx * dgk::kQuery + l32] = valid ? dwq[kx] : 0.0f;
+        for (int r = 0; r < 16; ++r) {
+            const int i = dgk::key_of(r, half);
+            const int kx = min(tl.half_rows ? kx0 + i : i % a.gw, a.gw - 1);   // in range even
+            dwreg[r] = i < tlen_w ? (valid ? dwq[kx] : 0.0f) : -INFINITY;      // at padding slots
         }
     } else if (bias && active) {
         float qf[HD];
@@ -160,53 +208,49 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
             }
             return d * dgk::kLog2e;
         };
-        const int qy = valid ? qi / a.gw : 0, qx = valid ? qi % a.gw : 0;
         for (int ky = part * 2 + half; ky < a.gh; ky += 2 * kParts)
             dh_tab[ky * dgk::kQuery + l32] = dot(a.rh + ((size_t)qy * a.gh + ky) * HD);
-        if (kAligned) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dwreg[r] = dot(a.rw + ((size_t)qx * a.gw + kxbase + dgk::key_of(r, half)) * HD);
-        } else {
-            for (int kx = part * 2 + half; kx < a.gw; kx += 2 * kParts)
-                dw_tab[kx * dgk::kQuery + l32] = dot(a.rw + ((size_t)qx * a.gw + kx) * HD);
+        for (int r = 0; r < 16; ++r) {
+            const int i = dgk::key_of(r, half);
+            const int kx = min(tl.half_rows ? kx0 + i : i % a.gw, a.gw - 1);
+            dwreg[r] = i < tlen_w ? dot(a.rw + ((size_t)qx * a.gw + kx) * HD) : -INFINITY;
         }
+    } else {
+        for (int ky = part * 2 + half; ky < a.gh; ky += 2 * kParts) dh_tab[ky * dgk::kQuery + l32] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dwreg[r] = dgk::key_of(r, half) < tlen_w ? 0.0f : -INFINITY;
     }
 
+    // Tile t's first key and length (wave-uniform, branch-free).
+    auto tile_start = [&](int t) { return (t >> a.tsh) * a.ta + (t & a.tmsk) * a.tb; };
+    auto tile_len = [&](int t) { return min(a.tl0 + (t & a.tmsk) * a.td, a.n - tile_start(t)); };
+
     // Loads: the four wavefronts with part < 2 (one per SIMD) issue each stage's 64 wave-wide
-    // loads -- K and V of 4 tiles -- while their SIMD partners keep the matrix pipe busy.
+    // loads -- K and V of 4 tiles -- while their SIMD partners keep the matrix pipe busy.  A
+    // full 32-key tile is a scalar row base plus loop-invariant lane offsets; a shorter one
+    // repeats its last key in the padding rows.
     constexpr int kLoadsPerWave = 2 * kParts * TL::kLoadsPerTile / 4;
     constexpr int R = TL::kRowsPerLoad;
     const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
-    const char* kbase = reinterpret_cast<const char*>(a.qkv + a.W + head * HD);
-    const char* vbase = reinterpret_cast<const char*>(a.qkv + 2 * (size_t)a.W + head * HD);
+    const char* kbase = reinterpret_cast<const char*>(qkvw + a.W + head * HD);
+    const char* vbase = reinterpret_cast<const char*>(qkvw + 2 * (size_t)a.W + head * HD);
     const unsigned rsb = (unsigned)(rs * 4);
-    const int nfull = a.n / kStage;  // stages whose 128 key rows all exist
     auto issue_stage = [&](int st, int buf) {
-        if (st < nfull) {  // wave-uniform: scalar row base + loop-invariant lane offsets
 #pragma unroll
-            for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int L = wave * kLoadsPerWave + i;
-                const int tpart = L / TL::kLoadsPerTile, ld = L % TL::kLoadsPerTile;
-                const int tile = tpart >> 1, isv = tpart & 1;
-                const int trow = ld * R + rsub;
-                const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
-                const int j0 = st * kStage + tile * dgk::kKeys;
-                const char* p = (isv ? vbase : kbase) + (size_t)j0 * rsb + ((unsigned)trow * rsb + coff);
-                __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)(tile_ptr(buf, tile, isv) + ld * 256), 16, 0, 0);
-            }
-        } else {           // the partial last stage: rows past the end repeat the last key
-#pragma unroll
-            for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int L = wave * kLoadsPerWave + i;
-                const int tpart = L / TL::kLoadsPerTile, ld = L % TL::kLoadsPerTile;
-                const int tile = tpart >> 1, isv = tpart & 1;
-                const int trow = ld * R + rsub;
-                const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
-                const int j = min(st * kStage + tile * dgk::kKeys + trow, a.n - 1);
-                const char* p = (isv ? vbase : kbase) + (size_t)j * rsb + coff;
-                __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)(tile_ptr(buf, tile, isv) + ld * 256), 16, 0, 0);
-            }
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+            const int L = wave * kLoadsPerWave + i;
+            const int tpart = L / TL::kLoadsPerTile, ld = L % TL::kLoadsPerTile;
+            const int tile = tpart >> 1, isv = tpart & 1;
+            const int trow = ld * R + rsub;
+            const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
+            // a tile past the last one reloads keys that exist (its results are never used)
+            const int t = min(st * kParts + tile, a.ntiles - 1);
+            const int j0 = tile_start(t);
+            const char* b = (isv ? vbase : kbase) + (size_t)j0 * rsb;
+            const unsigned off = kFull ? (unsigned)trow * rsb + coff
+                                       : (unsigned)min(trow, tile_len(t) - 1) * rsb + coff;
+            __builtin_amdgcn_global_load_lds(b + off, (dgk::lds_void*)(tile_ptr(buf, tile, isv) + ld * 256), 16, 0, 0);
         }
     };
 
@@ -219,7 +263,7 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    const int nstage = (a.n + kStage - 1) / kStage;
+    const int nstage = (a.ntiles + kParts - 1) / kParts;
     if (wave < 4) issue_stage(0, 0);
     for (int st = 0; st < nstage; ++st) {
         const int buf = st & 1;
@@ -227,27 +271,32 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
         __syncthreads();  // stage st has landed everywhere, stage st-1 is consumed (and the
                           // bias tables are complete before the first use)
         if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
-        const int t0 = st * kStage + part * dgk::kKeys;
-        if (active && t0 < a.n) {
+        const int t = st * kParts + part;
+        if (active && t < a.ntiles) {
             const float ref = dgk::ref_of(m);
+            const int row0 = tl.half_rows ? (t >> 1) : t * tl.rpt;
             f32x16 s;
-            if (kAligned) {
-                const float dhv = bias ? dh_tab[(t0 / a.gw) * dgk::kQuery + l32] : 0.0f;
-                s = dgk::scores_shift<HD>(tile_ptr(buf, part, 0), l32, half, qreg, dhv - ref, dwreg);
+            if (kOneShift) {
+                const int ky = min(row0 + (tl.half_rows ? 0 : half), a.gh - 1);
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(aone, dh_tab[ky * dgk::kQuery + l32] - ref,
+                                                         dwreg, 0, 0, 0);
             } else {
-                s = dgk::scores<HD>(tile_ptr(buf, part, 0), l32, half, qreg, -ref);
-                if (bias) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = min(t0 + dgk::key_of(r, half), a.n - 1);
-                        s[r] += dh_tab[(j / a.gw) * dgk::kQuery + l32] + dw_tab[(j % a.gw) * dgk::kQuery + l32];
-                    }
+                s = dwreg;
+                for (int ms = 0; ms < tl.nshift; ++ms) {
+                    const int ky = row0 + 2 * ms + half;
+                    const float bv = (ky < a.gh ? dh_tab[ky * dgk::kQuery + l32] : 0.0f) - ref;
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(arow == 2 * ms + half ? 1.0f : 0.0f, bv, s,
+                                                             0, 0, 0);
                 }
             }
-            if (t0 + dgk::kKeys > a.n) {
+            s = dgk::scores_from<HD>(tile_ptr(buf, part, 0), l32, half, qreg, s);
+            if (!kFull) {
+                const int len = tile_len(t);
+                if (len < tlen_w) {  // the last row tile is short
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (t0 + dgk::key_of(r, half) >= a.n) s[r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r)
+                        if (dgk::key_of(r, half) >= len) s[r] = -INFINITY;
+                }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
             dgk::accumulate_pv<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
@@ -258,22 +307,30 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     dgk::group_merge<HD>(smem, grp, part, kParts, active, lane, m, lsum, o);
     const float ltot = lsum + __shfl_xor(lsum, 32);
     if (part != 0 || !valid) return;
-    dgk::store_row<HD>(a.out + (size_t)qi * a.W + head * HD, 1.0f / ltot, o, half);
+    dgk::store_row<HD>(a.out + ((size_t)win * a.n + qi) * a.W + head * HD, 1.0f / ltot, o, half);
 }
 
 }  // namespace
 
-extern "C" size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd) {
-    if (gh < 1 || gw < 1 || heads < 1 || hd != HD || gh > kMaxGrid || gw > kMaxGrid) return 0;
-    return (size_t)2 * heads * gh * gw * kMaxGrid * sizeof(float);
+extern "C" size_t relpos_flash_attn_windows_workspace_size(int nwin, int gh, int gw, int heads,
+                                                          int hd) {
+    if (nwin < 1 || gh < 1 || gw < 1 || heads < 1 || hd != HD || gh > kMaxGrid || gw > kMaxGrid)
+        return 0;
+    return (size_t)nwin * heads * gh * gw * (gh + gw) * sizeof(float);
 }
 
-extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out,
-                                 int gh, int gw, int heads, int hd, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    const char* fn = "relpos_flash_attn";
-    if (gh < 0 || gw < 0 || heads < 0)
-        return dg::fail(DG_EINVAL, "%s: negative size (gh %d, gw %d, heads %d)", fn, gh, gw, heads);
+extern "C" size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd) {
+    return relpos_flash_attn_windows_workspace_size(1, gh, gw, heads, hd);
+}
+
+namespace {
+
+int relpos_call(const char* fn, const float* qkv, const float* rh, const float* rw, float* out,
+                int nwin, int gh, int gw, int heads, int hd, float scale, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (nwin < 0 || gh < 0 || gw < 0 || heads < 0)
+        return dg::fail(DG_EINVAL, "%s: negative size (nwin %d, gh %d, gw %d, heads %d)", fn, nwin,
+                        gh, gw, heads);
     if (hd < 1) return dg::fail(DG_EINVAL, "%s: hd must be >= 1, got %d", fn, hd);
     if (hd != HD) return dg::fail(DG_EUNSUPPORTED, "%s: hd %d not supported (64 only)", fn, hd);
     if ((rh == nullptr) != (rw == nullptr))
@@ -284,16 +341,20 @@ extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float*
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15))
         return dg::fail(DG_EINVAL, "%s: workspace must be 16-byte aligned", fn);
     const long long n = (long long)gh * gw;
-    if (n == 0 || heads == 0) return dg::ok();
+    if (n == 0 || heads == 0 || nwin == 0) return dg::ok();
     if (!qkv || !out) return dg::fail(DG_EINVAL, "%s: qkv and out must be non-NULL", fn);
+    size_t rows = 1;
+    if (!dg::mul_ok(rows, nwin) || !dg::mul_ok(rows, n) || !dg::mul_ok(rows, 3LL * heads * HD))
+        return dg::fail(DG_EINVAL, "%s: size overflow", fn);
     const size_t W = (size_t)heads * HD;
-    const size_t need = relpos_flash_attn_workspace_size(gh, gw, heads, hd);
+    const size_t ntok = (size_t)nwin * n;
+    const size_t need = relpos_flash_attn_windows_workspace_size(nwin, gh, gw, heads, hd);
     if (workspace && workspace_bytes < need)
         return dg::fail(DG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
                         workspace_bytes, need);
     const bool use_ws = workspace && rh;
-    const dg::Span so(out, (size_t)n * W * 4);
-    const dg::Span sq(qkv, (size_t)n * 3 * W * 4), sh(rh, (size_t)gh * gh * HD * 4),
+    const dg::Span so(out, ntok * W * 4);
+    const dg::Span sq(qkv, ntok * 3 * W * 4), sh(rh, (size_t)gh * gh * HD * 4),
         sw(rw, (size_t)gw * gw * HD * 4), sws(use_ws ? workspace : nullptr, need);
     if (so.overlaps(sq) || so.overlaps(sh) || so.overlaps(sw) || so.overlaps(sws))
         return dg::fail(DG_EINVAL, "%s: out overlaps an input or the workspace", fn);
@@ -304,21 +365,50 @@ extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float*
          reinterpret_cast<uintptr_t>(rh) | reinterpret_cast<uintptr_t>(rw)) & 15)
         return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
     const long long qblocks = (n + kBlockQ - 1) / kBlockQ;
-    if (qblocks * heads > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
+    const long long nblocks = qblocks * heads * nwin;
+    if (nblocks > 0x7fffffffLL || (long long)nwin * heads * (gh + gw) > 0x1fffffffLL)
+        return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     RelArgs a;
     a.qkv = qkv; a.rh = rh; a.rw = rw; a.out = out;
     a.dhw = use_ws ? static_cast<const float*>(workspace) : nullptr;
-    a.n = (int)n; a.gh = gh; a.gw = gw; a.heads = heads; a.W = (int)W;
+    a.n = (int)n; a.gh = gh; a.gw = gw; a.heads = heads; a.W = (int)W; a.nwin = nwin;
     a.qblocks = (int)qblocks;
-    a.nblocks = (int)(qblocks * heads);
+    a.nblocks = (int)nblocks;
     a.qmul = scale * dgk::kLog2e;
+    const Tiling tl = make_tiling(gh, gw);
+    a.ntiles = tl.ntiles;
+    if (tl.half_rows) {
+        a.tsh = 1; a.ta = gw; a.tmsk = 1; a.tb = tl.kh; a.tl0 = tl.kh; a.td = gw - 2 * tl.kh;
+    } else {
+        a.tsh = 0; a.ta = tl.kpt; a.tmsk = 0; a.tb = 0; a.tl0 = tl.kpt; a.td = 0;
+    }
     hipStream_t s = (hipStream_t)stream;
-    if (use_ws)
-        hipLaunchKernelGGL(relpos_bias_kernel, dim3((unsigned)(heads * (gh + gw))), dim3(256), 0, s, a,
-                           static_cast<float*>(workspace));
-    if (gw == 32 || gw == 64)
-        hipLaunchKernelGGL(relpos_flash_kernel<true>, dim3((unsigned)a.nblocks), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL(relpos_flash_kernel<false>, dim3((unsigned)a.nblocks), dim3(512), 0, s, a);
+    if (use_ws) {
+        const long long ntasks = (long long)nwin * heads * (gh + gw) * 4;
+        hipLaunchKernelGGL(relpos_bias_kernel, dim3((unsigned)((ntasks + kBiasWaves - 1) / kBiasWaves)),
+                           dim3(64 * kBiasWaves), 0, s, a, static_cast<float*>(workspace), ntasks);
+    }
+    const bool full = tl.half_rows ? gw == 64 : (tl.kpt == dgk::kKeys && gh % tl.rpt == 0);
+    const bool one = tl.nshift == 1;
+    auto* kern = full ? (one ? relpos_flash_kernel<true, true> : relpos_flash_kernel<true, false>)
+                      : (one ? relpos_flash_kernel<false, true> : relpos_flash_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.nblocks), dim3(512), 0, s, a);
     return dg::launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" int relpos_flash_attn_windows(const float* qkv, const float* rh, const float* rw,
+                                         float* out, int nwin, int gh, int gw, int heads, int hd,
+                                         float scale, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    return relpos_call("relpos_flash_attn_windows", qkv, rh, rw, out, nwin, gh, gw, heads, hd,
+                       scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out,
+                                 int gh, int gw, int heads, int hd, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return relpos_call("relpos_flash_attn", qkv, rh, rw, out, 1, gh, gw, heads, hd, scale,
+                       workspace, workspace_bytes, stream);
 }

@@ -230,6 +230,40 @@ def relpos_case(gh, gw, heads, hd, seed=0, scale=None, bias=True, table_std=0.02
     return RelposCase(name, gh, gw, heads, hd, qkv, rh, rw, float(scale))
 
 
+@dataclass
+class WindowsCase:
+    """A batch of windows for windowed rel-pos attention: qkv [nwin, gh*gw, 3*heads*hd]."""
+    name: str
+    nwin: int
+    gh: int
+    gw: int
+    heads: int
+    hd: int
+    qkv: np.ndarray
+    rh: Optional[np.ndarray]
+    rw: Optional[np.ndarray]
+    scale: float
+
+
+def windows_case(nwin, gh, gw, heads, hd, seed=0, scale=None, bias=True, table_std=0.02,
+                 name="relpos_windows") -> WindowsCase:
+    """qkv [nwin, gh*gw, 3*heads*hd] ~ N(0,1), then Rh [gh,gh,hd], Rw [gw,gw,hd] (0.02*N)."""
+    g = torch.Generator().manual_seed(seed)
+    qkv = _randn(g, nwin, gh * gw, 3 * heads * hd)
+    rh = (table_std * torch.randn(gh, gh, hd, generator=g)).numpy() if bias else None
+    rw = (table_std * torch.randn(gw, gw, hd, generator=g)).numpy() if bias else None
+    if scale is None:
+        scale = float(hd) ** -0.5
+    return WindowsCase(name, nwin, gh, gw, heads, hd, qkv, rh, rw, float(scale))
+
+
+def sam_windowed(seed=0) -> WindowsCase:
+    """SAM windowed attention: 25 windows of 14x14 tokens (a 64x64 map padded to 70x70),
+    12 heads, hd 64, scale 1/8."""
+    return windows_case(25, 14, 14, 12, 64, seed=seed, scale=0.125,
+                        name="sam_windowed_25x14x14_h12_hd64")
+
+
 def sam_global(seed=0) -> RelposCase:
     """SAM-style windowless attention: 64x64 grid, 12 heads, hd 64, scale 1/8."""
     return relpos_case(64, 64, 12, 64, seed=seed, scale=0.125,

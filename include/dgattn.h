@@ -174,8 +174,9 @@ int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs, co
 
 /*
  * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn can use to hold the
- * hoisted bias rows (dh and dw, 64 floats per (head, query) each): 2 * heads * gh * gw * 64 * 4.
- * Returns 0 for arguments relpos_flash_attn would reject.
+ * hoisted bias rows, the page's DHDW buffers: dh [heads][n][gh] then dw [heads][n][gw], i.e.
+ * heads * n * (gh + gw) * 4 bytes with n = gh * gw.  Returns 0 for arguments relpos_flash_attn
+ * would reject.
  */
 size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
 
@@ -207,6 +208,27 @@ size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
 int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out, int gh,
                       int gw, int heads, int hd, float scale, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * relpos_flash_attn_windows_workspace_size -- as relpos_flash_attn_workspace_size for a batch of
+ * nwin windows: nwin * heads * n * (gh + gw) * 4 bytes; 0 for arguments the call would reject.
+ */
+size_t relpos_flash_attn_windows_workspace_size(int nwin, int gh, int gw, int heads, int hd);
+
+/*
+ * relpos_flash_attn_windows -- relpos_flash_attn over a batch of independent windows sharing
+ * the tables: the windowed SAM blocks of deepencoder_gpu.rs's encoder (its cost model: 25
+ * windows of 14 x 14 tokens; a 64 x 64 map padded to 70 x 70).  Window partitioning and its
+ * padding belong to the caller, whose qkv already holds the padded tokens.
+ *   qkv  [nwin, gh*gw, 3*heads*hd]   window w's tokens, each row q | k | v as in relpos_flash_attn
+ *   out  [nwin, gh*gw, heads*hd]
+ *   rh, rw, gh, gw, heads, hd, scale, workspace as relpos_flash_attn (workspace size from
+ *   relpos_flash_attn_windows_workspace_size).  Each window is exactly one relpos_flash_attn.
+ * Errors: as relpos_flash_attn, plus DG_EINVAL for nwin < 0.  nwin == 0 is a no-op.
+ */
+int relpos_flash_attn_windows(const float* qkv, const float* rh, const float* rw, float* out,
+                              int nwin, int gh, int gw, int heads, int hd, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last nonzero status returned on the calling thread ("" if none). */
 const char* dg_last_error(void);

@@ -170,8 +170,26 @@ def test_relpos_validation(L):
     assert "aligned" in _err(L)
     assert call(gh=0) == dg.DG_OK
     assert call(heads=0) == dg.DG_OK
-    assert L.relpos_flash_attn_workspace_size(64, 64, 12, 64) == 2 * 12 * 4096 * 64 * 4
+    assert L.relpos_flash_attn_workspace_size(64, 64, 12, 64) == 12 * 4096 * (64 + 64) * 4
+    assert L.relpos_flash_attn_workspace_size(14, 20, 2, 64) == 2 * 280 * (14 + 20) * 4
     assert L.relpos_flash_attn_workspace_size(64, 64, 12, 32) == 0
+
+
+def test_relpos_windows_validation(L):
+    f = L.relpos_flash_attn_windows
+    base = dict(qkv=FAKE, rh=FAKE + (1 << 26), rw=FAKE + (2 << 26), out=FAKE + (3 << 26),
+                nwin=4, gh=8, gw=8, heads=2, hd=64, scale=0.125, ws=None, wsb=0, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(nwin=-1) == dg.DG_EINVAL
+    assert "negative" in _err(L)
+    assert call(hd=32) == dg.DG_EUNSUPPORTED
+    assert call(gw=65) == dg.DG_EUNSUPPORTED
+    assert call(rw=None) == dg.DG_EINVAL
+    assert call(out=FAKE + 4 * 8 * 8 * 3 * 128 * 4 - 16) == dg.DG_EINVAL   # inside the last window
+    assert call(ws=FAKE + (4 << 26), wsb=1024) == dg.DG_EINVAL             # too small for 4 windows
+    assert call(nwin=0) == dg.DG_OK
+    assert L.relpos_flash_attn_windows_workspace_size(25, 14, 14, 12, 64) == 25 * 12 * 196 * 28 * 4
+    assert L.relpos_flash_attn_windows_workspace_size(0, 14, 14, 12, 64) == 0
 
 
 def test_binding_refuses_bad_tensors_before_the_call():

@@ -343,7 +343,12 @@ def test_dg_layer_stack_every_element(norm_mode):
 @pytest.mark.parametrize("gh,gw,heads,bias", [(3, 5, 2, True), (8, 8, 3, True), (4, 64, 1, True),
                                               (64, 4, 2, True), (1, 1, 1, True), (9, 7, 2, False),
                                               (16, 16, 12, True), (3, 32, 2, True), (41, 32, 1, True),
-                                              (5, 64, 3, False), (64, 64, 1, True)])
+                                              (5, 64, 3, False), (64, 64, 1, True),
+                                              # half-row tiles of odd width, row tiles of
+                                              # several rows, one-column grids
+                                              (6, 33, 2, True), (5, 47, 1, True), (3, 63, 2, True),
+                                              (7, 17, 1, True), (9, 10, 2, True), (11, 3, 1, True),
+                                              (20, 2, 1, True), (33, 1, 1, True), (13, 14, 2, False)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
 def test_relpos_small(gh, gw, heads, bias, use_ws):
     c = synth.relpos_case(gh, gw, heads, 64, seed=gh * 100 + gw, bias=bias, table_std=0.3)
@@ -367,3 +372,38 @@ def test_sam_global_sampled_rows():
     rows = np.unique(np.concatenate([rows, [63, 64, 4032, 2047]])).astype(np.int64)
     ref = oracle.relpos_attn(c.qkv, c.rh, c.rw, 64, 64, 12, 64, c.scale, rows=rows)
     assert_parity(got[rows], ref[rows], "sam global")
+
+
+def oracle_windows(c):
+    """Windowed rel-pos attention on the oracle: each window is one independent grid."""
+    return np.stack([oracle.relpos_attn(c.qkv[w], c.rh, c.rw, c.gh, c.gw, c.heads, c.hd, c.scale)
+                     for w in range(c.nwin)])
+
+
+@pytest.mark.parametrize("nwin,gh,gw,heads,bias", [(3, 5, 7, 2, True), (25, 14, 14, 2, True),
+                                                   (4, 8, 8, 3, True), (2, 3, 32, 1, True),
+                                                   (5, 1, 1, 1, True), (3, 14, 14, 2, False),
+                                                   (2, 12, 64, 1, True), (3, 9, 47, 1, True)])
+@pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
+def test_relpos_windows_small(nwin, gh, gw, heads, bias, use_ws):
+    c = synth.windows_case(nwin, gh, gw, heads, 64, seed=nwin * 1000 + gh * 10 + gw, bias=bias,
+                           table_std=0.3)
+    ref = oracle_windows(c)
+    out = torch.full((nwin, gh * gw, heads * 64), float("nan"), device="cuda")
+    nbytes = dg.relpos_flash_attn_windows_workspace_size(nwin, gh, gw, heads, 64) if use_ws else 0
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), device="cuda") if use_ws else None
+    dg.relpos_flash_attn_windows(dev(c.qkv), dev(c.rh), dev(c.rw), out, nwin, gh, gw, heads, 64,
+                                 c.scale, ws, nbytes)
+    assert_parity(host(out), ref, "windows %dx%dx%d ws=%d" % (nwin, gh, gw, nbytes))
+
+
+def test_sam_windowed_every_element():
+    """The SAM windowed block's attention: 25 windows of 14x14 tokens, 12 heads, with the
+    bias-row workspace, as the benchmark runs it."""
+    c = synth.sam_windowed()
+    out = torch.full((c.nwin, c.gh * c.gw, c.heads * c.hd), float("nan"), device="cuda")
+    nbytes = dg.relpos_flash_attn_windows_workspace_size(c.nwin, c.gh, c.gw, c.heads, c.hd)
+    ws = torch.empty((nbytes // 4,), device="cuda")
+    dg.relpos_flash_attn_windows(dev(c.qkv), dev(c.rh), dev(c.rw), out, c.nwin, c.gh, c.gw,
+                                 c.heads, c.hd, c.scale, ws, nbytes)
+    assert_parity(host(out), oracle_windows(c), "sam windowed")
