@@ -23,6 +23,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 NORM_WEIGHTED = 1
 NORM_ROPE = 2
 NORM_SKIP = 4
+KV_F16 = 1      # IEEE binary16 storage
+KV_BF16 = 2     # bfloat16 storage
 
 _lib = None
 
@@ -56,6 +58,11 @@ def _load():
         lib.oracle_attn_split_gqa.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p,
                                               I, I, I, I, I, I, F, I, lp, ctypes.c_long]
         lib.oracle_attn_split_gqa.restype = None
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        lib.oracle_pack16.argtypes = [f32p, u16p, ctypes.c_long, I]
+        lib.oracle_pack16.restype = None
+        lib.oracle_widen16.argtypes = [u16p, f32p, ctypes.c_long, I]
+        lib.oracle_widen16.restype = None
         lib.oracle_relpos_attn.argtypes = [f32p, f32p, f32p, f32p, I, I, I, I, F, lp,
                                            ctypes.c_long]
         lib.oracle_relpos_attn.restype = None
@@ -134,4 +141,22 @@ def relpos_attn(qkv, rh, rw, gh: int, gw: int, heads: int, hd: int, scale: float
     rr, rp, nr = _rows(rows)
     _load().oracle_relpos_attn(_ptr(qkv), _ptr(rh), _ptr(rw), _ptr(out), gh, gw, heads, hd,
                                float(scale), rp, nr)
+    return out
+
+
+def pack16(x, fmt: int) -> np.ndarray:
+    """f32 -> 16-bit storage (uint16 bit patterns), round to nearest, ties to even."""
+    x = _f32(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_pack16(_ptr(x), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), x.size,
+                          int(fmt))
+    return out
+
+
+def widen16(h, fmt: int) -> np.ndarray:
+    """16-bit storage (uint16 bit patterns) -> the f32 values they hold (exact)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    _load().oracle_widen16(h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), _ptr(out), h.size,
+                           int(fmt))
     return out

@@ -28,6 +28,7 @@
  */
 #include <math.h>
 #include <stddef.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -263,4 +264,67 @@ void oracle_relpos_attn(const float *qkv, const float *rh, const float *rw, floa
         free(dh);
         free(dw);
     }
+}
+
+/*
+ * 16-bit storage of K and V ([DE] `flash_reg_kv16_src`: the flash reads an f16-packed twin of
+ * its inputs and widens each value to f32 before the unchanged f32 math).  The page does not
+ * print its pack pass; the reading taken is IEEE 754 round-to-nearest, ties-to-even, for both
+ * formats.  format 1 = IEEE binary16 (f16), format 2 = bfloat16 (the upper half of an f32).
+ */
+static uint16_t pack_f16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const uint32_t exp = (u >> 23) & 0xffu;
+    const uint32_t man = u & 0x7fffffu;
+    if (exp == 0xffu) return (uint16_t)(sign | (man ? 0x7e00u : 0x7c00u));  /* NaN, inf */
+    if (exp == 0) return sign;              /* |f| < 2^-126: far below half the f16 minimum */
+    const int e = (int)exp - 127;           /* f = sig * 2^(e-23), sig = 1.man in 24 bits */
+    if (e > 15) return (uint16_t)(sign | 0x7c00u);
+    const uint32_t sig = man | 0x800000u;
+    /* f16 normals are (1024 + m) * 2^(E-25), E = e + 15 >= 1: keep 11 bits of sig.
+     * f16 subnormals are m * 2^-24: keep sig * 2^(e+1), i.e. drop 13 + (-14 - e) bits. */
+    const int shift = e >= -14 ? 13 : 13 + (-14 - e);
+    if (shift > 24) return sign;            /* below 2^-25: rounds to zero */
+    uint32_t q = sig >> shift;
+    const uint32_t rem = sig & ((1u << shift) - 1u);
+    const uint32_t halfway = 1u << (shift - 1);
+    if (rem > halfway || (rem == halfway && (q & 1u))) ++q;
+    if (e >= -14) /* a carry out of the 11 bits moves into the exponent field, up to inf */
+        return (uint16_t)(sign | (((uint32_t)(e + 15) << 10) + (q - 1024u)));
+    return (uint16_t)(sign | q);            /* q == 1024 is the smallest normal, as wanted */
+}
+
+static float widen_f16(uint16_t h) {
+    const uint32_t exp = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    float v;
+    if (exp == 0) v = ldexpf((float)m, -24);
+    else if (exp == 0x1fu) v = m ? NAN : INFINITY;
+    else v = ldexpf((float)(1024u + m), (int)exp - 25);
+    return (h & 0x8000u) ? -v : v;
+}
+
+static uint16_t pack_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
+        return (uint16_t)((u >> 16) | 0x0040u);                    /* quiet NaN, sign kept */
+    const uint32_t lsb = (u >> 16) & 1u;                             /* ties to even */
+    return (uint16_t)((u + 0x7fffu + lsb) >> 16);
+}
+
+static float widen_bf16(uint16_t h) {
+    const uint32_t u = (uint32_t)h << 16;
+    float v;
+    memcpy(&v, &u, 4);
+    return v;
+}
+
+void oracle_pack16(const float *src, uint16_t *dst, long n, int format) {
+    for (long i = 0; i < n; ++i) dst[i] = format == 1 ? pack_f16(src[i]) : pack_bf16(src[i]);
+}
+
+void oracle_widen16(const uint16_t *src, float *dst, long n, int format) {
+    for (long i = 0; i < n; ++i) dst[i] = format == 1 ? widen_f16(src[i]) : widen_bf16(src[i]);
 }

@@ -399,3 +399,61 @@ def test_relpos_rows_subset_bitwise():
     rows = np.array([1, 13, 23], dtype=np.int64)
     part = oracle.relpos_attn(case.qkv, case.rh, case.rw, 4, 6, 2, 64, case.scale, rows=rows)
     assert np.array_equal(part[rows], full[rows])
+
+
+# ----------------------------------------------------------------------------- 16-bit K/V storage
+
+def _pack_inputs(seed):
+    """Values across the whole f16 range and beyond: log-uniform magnitudes, random signs,
+    plus zeros, infinities, NaN and the extremes of each format."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.uniform(-30.0, 18.0, 200000))
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 65504.0, 65519.99, 65520.0, 2.0 ** -24,
+                        2.0 ** -25, 2.0 ** -25 * 1.0001, 2.0 ** -14, 3.4e38, 1e-40, -1e-45],
+                       dtype=np.float32)
+    return np.concatenate([x, special])
+
+
+def _f16_ties():
+    """f32 values exactly halfway between neighbouring f16 values (normal and subnormal)."""
+    h = np.arange(0, 0x7bff, 7, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    return ((lo + hi) / 2).astype(np.float32)
+
+
+def test_pack16_f16_matches_numpy_ieee_rounding():
+    x = np.concatenate([_pack_inputs(1), _f16_ties(), -_f16_ties()])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = oracle.pack16(x, oracle.KV_F16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(oracle.widen16(got[nan], oracle.KV_F16)))
+
+
+def test_pack16_bf16_matches_torch_rounding():
+    ties = (np.arange(1, 60000, dtype=np.uint32) * 65536 + 32768).view(np.float32)  # exact halves
+    x = np.concatenate([_pack_inputs(2), ties[np.isfinite(ties)]])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.pack16(x, oracle.KV_BF16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(oracle.widen16(got[nan], oracle.KV_BF16)))
+
+
+def test_widen16_is_exact():
+    h = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    f16 = oracle.widen16(h, oracle.KV_F16)
+    ref = h.view(np.float16).astype(np.float32)
+    fin = np.isfinite(ref)
+    assert np.array_equal(f16[fin], ref[fin]) and np.array_equal(np.isnan(f16), np.isnan(ref))
+    bf = oracle.widen16(h, oracle.KV_BF16)
+    refb = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).float().numpy()
+    finb = np.isfinite(refb)
+    assert np.array_equal(bf[finb], refb[finb])
+    # packing what a 16-bit value holds gives that value back
+    for fmt, w in ((oracle.KV_F16, f16), (oracle.KV_BF16, bf)):
+        ok = np.isfinite(w)
+        assert np.array_equal(oracle.pack16(w[ok], fmt), h[ok])
