@@ -80,12 +80,14 @@ def split_counts(c, norm_mode="in_attention"):
 class SplitWork:
     dominant = "attn_split_gqa"
 
-    def __init__(self, name, case, norm_mode="in_attention"):
+    def __init__(self, name, case, norm_mode="in_attention", kv16=None):
         import numpy as np
         import torch
         from gqa_flash_attention_dg_amd.canvas import CanvasBlock
 
-        self.name, self.c, self.norm_mode = name, case, norm_mode
+        if kv16 and norm_mode == "in_attention":
+            norm_mode = "one_launch"   # the 16-bit attention takes a normed q
+        self.name, self.c, self.norm_mode, self.kv16 = name, case, norm_mode, kv16
         # ctx + T <= 8 runs the short-key-set kernel, longer key sets the tiled MFMA kernel
         self.dominant = "attn_small" if case.ctx + case.T <= 8 else "attn_split_gqa"
         d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -93,10 +95,14 @@ class SplitWork:
         self.blk = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, d(c.kc), d(c.vc), d(c.wq),
                                d(c.wk), eps=c.eps, theta=c.theta, scale=c.scale,
                                causal=c.causal, rope_cache=c.rope_cache, normed=c.normed,
-                               norm_mode=norm_mode)
+                               norm_mode=norm_mode, kv16=kv16)
         self.q, self.k, self.v = d(c.q), d(c.k), d(c.v)
         self.out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
         self.flops, self.attn_bytes, self.norm_bytes = split_counts(c, norm_mode)
+        if kv16:  # K/V read as 16-bit values; the per-step pack reads and writes canvas k, v
+            kvn = c.B * c.T * c.nkv * c.hd
+            self.attn_bytes -= 2 * (2 * kvn + 2 * c.B * c.nkv * c.ctx * c.hd)
+            self.norm_bytes += 2 * kvn * (4 + 2)
         self.bound = "mfma" if self.flops / self.attn_bytes > 20 else "hbm"
 
     def config(self):
@@ -106,6 +112,9 @@ class SplitWork:
                 "step": self.step_name()}
 
     def step_name(self):
+        if getattr(self, "kv16", None):
+            return ("dg_qkv_headnorm_rope(q, k, v) + dg_pack_kv16(k), dg_pack_kv16(v) + "
+                    "dg_attn_split_gqa_kv16 (%s K/V)" % self.kv16)
         if not getattr(self.c, "normed", True):
             return "dg_attn_split_gqa"
         return {"one_launch": "dg_qkv_headnorm_rope(q, k, v) + dg_attn_split_gqa",
@@ -121,9 +130,13 @@ class SplitWork:
                 self.blk.norm_qkv(self.q, self.k, self.v)
             else:
                 self.blk.norm(self.q, self.k, self.v)
+        if self.kv16:
+            self.blk.pack_canvas(self.k, self.v)
         if ev:
             ev[0].record()
-        if normed_q:
+        if self.kv16:
+            self.blk.attend_kv16(self.q, self.out)
+        elif normed_q:
             self.blk.attend_qnorm(self.q, self.k, self.v, self.out)
         else:
             self.blk.attend(self.q, self.k, self.v, self.out)
@@ -326,12 +339,12 @@ class CopyWork:
         return None
 
 
-def make_work(name, norm_mode="in_attention"):
+def make_work(name, norm_mode="in_attention", kv16=None):
     from gqa_flash_attention_dg_amd import synth
     if name == "long_cache":
-        return SplitWork(name, synth.long_cache(), norm_mode)
+        return SplitWork(name, synth.long_cache(), norm_mode, kv16)
     if name == "dg_canvas":
-        return SplitWork(name, synth.dg_canvas_steps(1), norm_mode)
+        return SplitWork(name, synth.dg_canvas_steps(1), norm_mode, kv16)
     if name == "tiny":
         return SplitWork(name, synth.tiny_canvas_step(), norm_mode)
     if name == "depformer":
@@ -360,6 +373,9 @@ def main():
                     help="in_attention: k/v norms in one launch + q norm inside attention; "
                          "one_launch: q, k, v norms in one launch; separate: the page's three "
                          "headnorm dispatches")
+    ap.add_argument("--kv16", default=None, choices=["f16", "bf16"],
+                    help="long_cache / dg_canvas: keys and values stored in 16 bits, widened to "
+                         "f32 inside attention")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle wall time for the CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -376,7 +392,7 @@ def main():
     dg.lib()
     torch.cuda.set_device(0)
 
-    work = make_work(args.workload, norm_mode=args.norm)
+    work = make_work(args.workload, norm_mode=args.norm, kv16=args.kv16)
 
     for _ in range(args.warmup):
         work.step()
@@ -412,7 +428,8 @@ def main():
         value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
     roof["kernel"] = work.dominant
     roof["avg_launch_ms"] = kern_avg
-    roof["traffic"] = measured_traffic(work.dominant, work.name)
+    roof["traffic"] = measured_traffic(work.dominant, work.name + (
+        "_kv16" + args.kv16 if getattr(args, "kv16", None) else ""))
 
     cpu = None
     if args.cpu_budget > 0:

@@ -18,9 +18,11 @@ LIB_PATH = os.path.join(HERE, "libdgattn.so")
 
 DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
 DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
+DG_KV_F16, DG_KV_BF16 = 1, 2
 
-EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
+EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
+           "dg_attn_split_gqa_kv16",
            "relpos_flash_attn_workspace_size", "relpos_flash_attn",
            "relpos_flash_attn_windows_workspace_size", "relpos_flash_attn_windows",
            "dg_last_error")
@@ -48,6 +50,9 @@ def lib() -> ctypes.CDLL:
         L.dg_rope_table.argtypes = [vp, I, I, I, D, vp]
         L.dg_headnorm_rope.argtypes = [vp, vp, vp, I, I, I, I, U, F, vp]
         L.dg_qkv_headnorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, U, F, vp]
+        L.dg_pack_kv16.argtypes = [vp, vp, Z, I, vp]
+        L.dg_attn_split_gqa_kv16.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, I, vp,
+                                             Z, vp]
         L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
         L.dg_attn_split_gqa_workspace_size.restype = Z
         L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
@@ -59,8 +64,9 @@ def lib() -> ctypes.CDLL:
         L.relpos_flash_attn_windows_workspace_size.argtypes = [I, I, I, I, I]
         L.relpos_flash_attn_windows_workspace_size.restype = Z
         L.relpos_flash_attn_windows.argtypes = [vp, vp, vp, vp, I, I, I, I, I, F, vp, Z, vp]
-        for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope",
-                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "relpos_flash_attn",
+        for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
+                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "dg_attn_split_gqa_kv16",
+                     "relpos_flash_attn",
                      "relpos_flash_attn_windows"):
             getattr(L, name).restype = I
         L.dg_last_error.argtypes = []
@@ -86,6 +92,24 @@ def _ptr(t, name: str, need: int):
         raise TypeError("%s must be a torch.Tensor or None" % name)
     if t.dtype != torch.float32:
         raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < need:
+        raise ValueError("%s holds %d elements, the call needs %d" % (name, t.numel(), need))
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _ptr16(t, name: str, need: int):
+    """Device pointer of a tensor of 16-bit elements (uint16/int16/float16/bfloat16 storage of
+    f16 or bf16 bit patterns) holding at least `need` elements (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor or None" % name)
+    if t.element_size() != 2:
+        raise TypeError("%s must have 2-byte elements, got %s" % (name, t.dtype))
     if t.device.type != "cuda":
         raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
     if not t.is_contiguous():
@@ -140,6 +164,12 @@ def dg_qkv_headnorm_rope(q, wq, k, wk, v, cs, batch: int, T: int, nh: int, nkv: 
         batch, T, nh, nkv, hd, flags, float(eps), _stream(stream)))
 
 
+def dg_pack_kv16(src, dst, n: int, format: int, stream=None) -> None:
+    _nonneg(n=n)
+    _check(lib().dg_pack_kv16(_ptr(src, "src", n), _ptr16(dst, "dst", n), n, int(format),
+                              _stream(stream)))
+
+
 def dg_attn_split_gqa_workspace_size(batch: int, T: int, ctx: int, nh: int, nkv: int,
                                      hd: int) -> int:
     return int(lib().dg_attn_split_gqa_workspace_size(batch, T, ctx, nh, nkv, hd))
@@ -182,6 +212,18 @@ def dg_attn_split_gqa_qnorm(q, wq, cs, kc, vc, k, v, out, batch: int, T: int, ct
         _ptr(cs, "cs", T * 2 * hd if need_cs else 0), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
         _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq), batch, T, ctx, nh, nkv, hd,
         qflags, float(eps), float(scale), int(causal), ws, wsb, _stream(stream)))
+
+
+def dg_attn_split_gqa_kv16(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int, nkv: int,
+                           hd: int, scale: float, causal: int, kv_format: int, workspace=None,
+                           workspace_bytes: int = 0, stream=None) -> None:
+    _nonneg(batch=batch, T=T, ctx=ctx, nh=nh, nkv=nkv, hd=hd)
+    nq, nkvc, nc = batch * T * nh * hd, batch * T * nkv * hd, batch * nkv * ctx * hd
+    ws, wsb = _workspace(workspace, workspace_bytes)
+    _check(lib().dg_attn_split_gqa_kv16(
+        _ptr(q, "q", nq), _ptr16(kc, "kc", nc), _ptr16(vc, "vc", nc), _ptr16(k, "k", nkvc),
+        _ptr16(v, "v", nkvc), _ptr(out, "out", nq), batch, T, ctx, nh, nkv, hd, float(scale),
+        int(causal), int(kv_format), ws, wsb, _stream(stream)))
 
 
 def relpos_flash_attn_workspace_size(gh: int, gw: int, heads: int, hd: int) -> int:

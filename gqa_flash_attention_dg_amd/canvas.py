@@ -21,9 +21,12 @@ from __future__ import annotations
 
 import torch
 
-from . import (DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K, DG_NORM_WEIGHTED,
-               dg_attn_split_gqa, dg_attn_split_gqa_qnorm, dg_attn_split_gqa_workspace_size,
-               dg_headnorm_rope, dg_qkv_headnorm_rope, dg_rope_table)
+from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K,
+               DG_NORM_WEIGHTED, dg_attn_split_gqa, dg_attn_split_gqa_kv16,
+               dg_attn_split_gqa_qnorm, dg_attn_split_gqa_workspace_size, dg_headnorm_rope,
+               dg_pack_kv16, dg_qkv_headnorm_rope, dg_rope_table)
+
+KV_FORMATS = {"f16": DG_KV_F16, "bf16": DG_KV_BF16}
 
 NORM_MODES = ("in_attention", "one_launch", "separate")
 
@@ -46,12 +49,19 @@ class CanvasBlock:
     ctx positions just before pos0.  normed: normalise q, k and v in each step, as `norm_mode`
     says.  k_eq_v: the layer has no v projection; each step's v buffer is written with the
     weightless norm of the raw k (its input contents are ignored).
+    kv16: None (f32 K/V) or "f16" / "bf16": the cache is packed once into 16-bit twins here, each
+    step packs its normalised canvas k and v, and the attention widens them to f32 as it reads
+    them (the q norm then runs in the one-launch norm, not inside attention).
     """
 
     def __init__(self, B, T, ctx, nh, nkv, hd, kc=None, vc=None, wq=None, wk=None, *,
                  eps=1e-6, theta=10000.0, scale=1.0, causal=False, rope_cache=False,
                  normed=True, norm_mode="in_attention", use_workspace=True, pos0=None, cs=None,
-                 k_eq_v=False, device="cuda"):
+                 k_eq_v=False, kv16=None, device="cuda"):
+        if kv16 is not None and kv16 not in KV_FORMATS:
+            raise ValueError("kv16 must be None, 'f16' or 'bf16'")
+        if kv16 is not None and norm_mode == "in_attention":
+            norm_mode = "one_launch"
         if norm_mode not in NORM_MODES:
             raise ValueError("unknown norm_mode %r" % (norm_mode,))
         if k_eq_v and not normed:
@@ -73,6 +83,15 @@ class CanvasBlock:
             cs_cache = rope_table(pos0 - ctx, ctx, hd, theta, device)
             dg_headnorm_rope(kc, None, cs_cache, B * nkv, ctx, 1, hd,
                              DG_NORM_ROPE | DG_NORM_SKIP, 0.0)
+        self.kv16 = KV_FORMATS[kv16] if kv16 else 0
+        if self.kv16:
+            half = lambda n: torch.empty(n, dtype=torch.int16, device=device)
+            nc, nk = B * nkv * ctx * hd, B * T * nkv * hd
+            self.kc16, self.vc16 = (half(nc), half(nc)) if ctx > 0 else (None, None)
+            if ctx > 0:
+                dg_pack_kv16(kc, self.kc16, nc, self.kv16)
+                dg_pack_kv16(vc, self.vc16, nc, self.kv16)
+            self.k16, self.v16 = half(nk), half(nk)
         self.ws_bytes = dg_attn_split_gqa_workspace_size(B, T, ctx, nh, nkv, hd) \
             if use_workspace else 0
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
@@ -104,7 +123,22 @@ class CanvasBlock:
                                 DG_NORM_WEIGHTED | DG_NORM_ROPE, self.eps, self.scale,
                                 self.causal, self.ws, self.ws_bytes)
 
+    def pack_canvas(self, k, v):
+        """16-bit twins of this step's normed canvas k and v (kv16 blocks)."""
+        nk = self.B * self.T * self.nkv * self.hd
+        dg_pack_kv16(k, self.k16, nk, self.kv16)
+        dg_pack_kv16(v, self.v16, nk, self.kv16)
+
+    def attend_kv16(self, q, out):
+        dg_attn_split_gqa_kv16(q, self.kc16, self.vc16, self.k16, self.v16, out, self.B, self.T,
+                               self.ctx, self.nh, self.nkv, self.hd, self.scale, self.causal,
+                               self.kv16, self.ws, self.ws_bytes)
+
     def attend(self, q, k, v, out):
+        if self.kv16:
+            self.pack_canvas(k, v)
+            self.attend_kv16(q, out)
+            return
         dg_attn_split_gqa(q, self.kc, self.vc, k, v, out, self.B, self.T, self.ctx, self.nh,
                           self.nkv, self.hd, self.scale, self.causal, self.ws, self.ws_bytes)
 

@@ -60,6 +60,71 @@ struct SplitArgs {
     float eps;
 };
 
+// K/V element storage: 0 = f32, DG_KV_F16, DG_KV_BF16.  16-bit tiles are loaded into LDS as
+// they are stored (half the bytes of a stage) and widened to f32 in registers as the MFMA
+// operands are read, so the arithmetic is the f32 arithmetic of the f32 path.
+template <int HD, int kKV>
+struct KVTile {
+    static constexpr int kEsz = kKV ? 2 : 4;                  // bytes per element
+    static constexpr int kChunks = HD * kEsz / 16;            // 16-byte chunks per key row
+    static constexpr int kBytes = dgk::kKeys * HD * kEsz;     // one K or V tile
+    static constexpr int kRowsPerLoad = 64 / kChunks;         // key rows per wave-wide 1 KiB load
+    static constexpr int kLoadsPerTile = dgk::kKeys / kRowsPerLoad;
+};
+
+template <int kKV>
+__device__ inline float lo16(uint32_t w) {
+    if constexpr (kKV == DG_KV_BF16) return __uint_as_float(w << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+
+template <int kKV>
+__device__ inline float hi16(uint32_t w) {
+    if constexpr (kKV == DG_KV_BF16) return __uint_as_float(w & 0xffff0000u);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// dgk::scores_from on a 16-bit K tile: chunk g of a row holds elements 8g..8g+7, so the lane's
+// elements 8g+4*half..+3 are the 8 bytes at offset 8*half of chunk g (swizzled like f32 rows).
+template <int HD, int kKV>
+__device__ inline f32x16 scores_from16(const char* __restrict__ ks, int l32, int half,
+                                       const float (&qreg)[HD / 2], f32x16 s) {
+    using KT = KVTile<HD, kKV>;
+    const char* kr = ks + l32 * HD * 2;
+    const int sw = l32 % KT::kChunks;
+#pragma unroll
+    for (int g = 0; g < HD / 8; ++g) {
+        const uint2 w = *reinterpret_cast<const uint2*>(kr + 16 * (g ^ sw) + 8 * half);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(lo16<kKV>(w.x), qreg[4 * g + 0], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(hi16<kKV>(w.x), qreg[4 * g + 1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(lo16<kKV>(w.y), qreg[4 * g + 2], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(hi16<kKV>(w.y), qreg[4 * g + 3], s, 0, 0, 0);
+    }
+    return s;
+}
+
+// dgk::accumulate_pv on a 16-bit V tile: the lane's G = HD/32 contiguous elements of a row are
+// 2G bytes.
+template <int HD, int kKV>
+__device__ inline void accumulate_pv16(const char* __restrict__ vs, int l32, int half,
+                                       const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const char* vr = vs + (dgk::key_of(r, half) * HD + l32 * dgk::Tile<HD>::kGroups) * 2;
+        if constexpr (HD == 128) {
+            const uint2 w = *reinterpret_cast<const uint2*>(vr);
+            o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo16<kKV>(w.x), p[r], o[0], 0, 0, 0);
+            o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(hi16<kKV>(w.x), p[r], o[1], 0, 0, 0);
+            o[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo16<kKV>(w.y), p[r], o[2], 0, 0, 0);
+            o[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(hi16<kKV>(w.y), p[r], o[3], 0, 0, 0);
+        } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(vr);
+            o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo16<kKV>(w), p[r], o[0], 0, 0, 0);
+            o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(hi16<kKV>(w), p[r], o[1], 0, 0, 0);
+        }
+    }
+}
+
 // Row stride (floats) of the normalised queries staged in LDS: HD + 4 keeps the 16-byte
 // operand reads (32 lanes on 32 different rows) free of bank conflicts.
 template <int HD>
@@ -168,18 +233,22 @@ __device__ inline int xcd_remap(int bid, int n) {
 // are zero past hd; key/value rows are loaded with their chunks past hd taken from a valid
 // chunk of the same row (finite values that meet zero query elements, and output elements
 // past hd that are never stored).
-template <int HD, bool kNormQ, bool kPad>
+template <int HD, bool kNormQ, bool kPad, int kKV>
 __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     using TL = dgk::Tile<HD>;
+    using KT = KVTile<HD, kKV>;
     // [buffer][tile of the stage][K, V]; with kNormQ the normalised queries are staged over
-    // buffer 1 (free until the second stage is issued) and a little past it.
-    constexpr int kStageFloats = 2 * 2 * 2 * TL::kFloats;
-    constexpr int kQStageEnd = 2 * 2 * TL::kFloats + kBlockQ * kQStride<HD>;
-    constexpr int kSmemFloats = kNormQ && kQStageEnd > kStageFloats ? kQStageEnd : kStageFloats;
+    // buffer 1 (free until the second stage is issued) and a little past it; the pair merge
+    // reuses the space at the end.
+    constexpr int kStageFloats = 2 * 2 * 2 * KT::kBytes / 4;
+    constexpr int kQStageEnd = 2 * 2 * KT::kBytes / 4 + kBlockQ * kQStride<HD>;
+    constexpr int kMergeFloats = kPairs * 64 * (TL::kGroups * 16 + 2);
+    constexpr int kA = kNormQ && kQStageEnd > kStageFloats ? kQStageEnd : kStageFloats;
+    constexpr int kSmemFloats = kA > kMergeFloats ? kA : kMergeFloats;
     __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
     const int hd = kPad ? a.hd : HD;
     auto tile_ptr = [&](int buf, int tile, int isv) {
-        return smem + ((buf * 2 + tile) * 2 + isv) * TL::kFloats;
+        return reinterpret_cast<char*>(smem) + ((buf * 2 + tile) * 2 + isv) * KT::kBytes;
     };
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks);
@@ -214,11 +283,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const int st_begin = (int)((long long)split * nstage / a.nsplit);
     const int st_end = (int)((long long)(split + 1) * nstage / a.nsplit);
 
-    const float* kcb = a.kc + (size_t)bk * a.ctx * hd;
-    const float* vcb = a.vc + (size_t)bk * a.ctx * hd;
-    const size_t cstride = (size_t)a.nkv * hd;
-    const float* kb = a.k + ((size_t)b * a.T * a.nkv + kv) * hd;
-    const float* vb = a.v + ((size_t)b * a.T * a.nkv + kv) * hd;
+    constexpr int kEsz = KT::kEsz;
+    const char* kcb = reinterpret_cast<const char*>(a.kc) + (size_t)bk * a.ctx * hd * kEsz;
+    const char* vcb = reinterpret_cast<const char*>(a.vc) + (size_t)bk * a.ctx * hd * kEsz;
+    const size_t cstride = (size_t)a.nkv * hd;   // canvas row stride, elements
+    const char* kb = reinterpret_cast<const char*>(a.k) + ((size_t)b * a.T * a.nkv + kv) * hd * kEsz;
+    const char* vb = reinterpret_cast<const char*>(a.v) + ((size_t)b * a.T * a.nkv + kv) * hd * kEsz;
 
     // The four even-tile wavefronts issue the stage's 4 * kLoadsPerTile wave-wide loads (K and
     // V of both tiles); their odd-tile partners start on the MFMAs meanwhile (on this hardware
@@ -226,35 +296,32 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     // SIMD pair keeps it fed).  A tile lying wholly in the cache or wholly in the canvas is
     // addressed from a scalar base plus a loop-invariant per-lane offset; only a tile that
     // straddles the seam or the end of the key range forms per-lane addresses.
-    constexpr int kLoadsPerWave = 4 * TL::kLoadsPerTile / (kWaves / 2);
-    constexpr int R = TL::kRowsPerLoad;
-    const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
-    const unsigned rstride_c = (unsigned)hd * 4, rstride_v = (unsigned)cstride * 4;
+    constexpr int kLoadsPerWave = 4 * KT::kLoadsPerTile / (kWaves / 2);
+    constexpr int R = KT::kRowsPerLoad;
+    const int pos = lane % KT::kChunks, rsub = lane / KT::kChunks;
+    const unsigned rstride_c = (unsigned)hd * kEsz, rstride_v = (unsigned)cstride * kEsz;
     auto issue_stage = [&](int st, int buf) {
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int L = pair * kLoadsPerWave + i;
-            const int part = L / TL::kLoadsPerTile;  // K0, V0, K1, V1
-            const int ld = L % TL::kLoadsPerTile;
+            const int part = L / KT::kLoadsPerTile;  // K0, V0, K1, V1
+            const int ld = L % KT::kLoadsPerTile;
             const int tile = part >> 1, isv = part & 1;
             const int trow = ld * R + rsub;           // tile row of this lane's chunk
-            int chunk = isv ? pos : (pos ^ (trow % TL::kChunks));
-            if (kPad) chunk = min(chunk, hd / 4 - 1);
+            int chunk = isv ? pos : (pos ^ (trow % KT::kChunks));
+            if (kPad) chunk = min(chunk, hd * kEsz / 16 - 1);
             const unsigned coff = 16u * chunk;
             const int j0 = st * kStage + tile * dgk::kKeys;
-            float* dst = tile_ptr(buf, tile, isv) + ld * 256;
+            char* dst = tile_ptr(buf, tile, isv) + ld * 1024;
             const char* p;
             if (j0 + dgk::kKeys <= a.ctx && j0 + dgk::kKeys <= kend) {
-                p = reinterpret_cast<const char*>((isv ? vcb : kcb) + (size_t)j0 * hd) +
-                    ((unsigned)trow * rstride_c + coff);
+                p = (isv ? vcb : kcb) + (size_t)j0 * rstride_c + ((unsigned)trow * rstride_c + coff);
             } else if (j0 >= a.ctx && j0 + dgk::kKeys <= kend) {
-                p = reinterpret_cast<const char*>((isv ? vb : kb) + (size_t)(j0 - a.ctx) * cstride) +
-                    ((unsigned)trow * rstride_v + coff);
+                p = (isv ? vb : kb) + (size_t)(j0 - a.ctx) * rstride_v + ((unsigned)trow * rstride_v + coff);
             } else {
                 const int j = min(j0 + trow, kend - 1);
-                p = reinterpret_cast<const char*>(j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * hd
-                                                            : (isv ? vb : kb) + (size_t)(j - a.ctx) * cstride) +
-                    coff;
+                p = (j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * rstride_c
+                               : (isv ? vb : kb) + (size_t)(j - a.ctx) * rstride_v) + coff;
             }
             __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)dst, 16, 0, 0);
         }
@@ -264,7 +331,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     if (!hi && st_begin < st_end) issue_stage(st_begin, 0);
     float qreg[HD / 2];
     if constexpr (kNormQ) {
-        float* qs = smem + 2 * 2 * TL::kFloats;
+        float* qs = smem + 2 * 2 * KT::kBytes / 4;
         stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
         __syncthreads();
         dgk::load_q<HD>(qs + (pair * dgk::kQuery + l32) * kQStride<HD>, true, half, 1.0f, qreg);
@@ -285,7 +352,16 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         if (!hi && st + 1 < st_end) issue_stage(st + 1, buf ^ 1);
         const int t0 = st * kStage + hi * dgk::kKeys;
         if (pair_active && t0 < kend) {
-            f32x16 s = dgk::scores<HD>(tile_ptr(buf, hi, 0), l32, half, qreg, -dgk::ref_of(m));
+            f32x16 s;
+            if constexpr (kKV == 0) {
+                s = dgk::scores<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 0)), l32, half,
+                                    qreg, -dgk::ref_of(m));
+            } else {
+                const float shift = -dgk::ref_of(m);
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
+                                                         f32x16{}, 0, 0, 0);
+                s = scores_from16<HD, kKV>(tile_ptr(buf, hi, 0), l32, half, qreg, s);
+            }
             const bool need_mask =
                 t0 + dgk::kKeys > kend || (a.causal && t0 + dgk::kKeys - 1 - a.ctx > row_min);
             if (need_mask) {
@@ -296,7 +372,10 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
                 }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            dgk::accumulate_pv<HD>(tile_ptr(buf, hi, 1), l32, half, s, o);
+            if constexpr (kKV == 0)
+                dgk::accumulate_pv<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 1)), l32, half, s, o);
+            else
+                accumulate_pv16<HD, kKV>(tile_ptr(buf, hi, 1), l32, half, s, o);
         }
     }
 
@@ -327,7 +406,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 // (3 exchanges for the sum of squares) and the rope partner is read back from a staged row.
 constexpr int kSmallKeys = 8;
 
-template <int HD, bool kNormQ, bool kPad>
+template <int HD, bool kNormQ, bool kPad, int kKV>
 __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long units) {
     constexpr int SEG = HD / 8;
     constexpr int kRows = kNormQ ? 3 : 2;   // K, V (and the staged q) per wave
@@ -346,24 +425,42 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
 
     float qr[SEG], kr[SEG], vr[SEG];
     const bool has_key = active && r < S, has_q = active && r < a.T;
-    const float* kp = nullptr;
-    const float* vp = nullptr;
+    constexpr int kEsz = kKV ? 2 : 4;
+    const char* kp = nullptr;
+    const char* vp = nullptr;
     if (has_key) {
         const size_t off = r < a.ctx ? (((size_t)b * a.nkv + kv) * a.ctx + r) * hd
                                      : (((size_t)b * a.T + (r - a.ctx)) * a.nkv + kv) * hd;
-        kp = (r < a.ctx ? a.kc : a.k) + off + cseg;
-        vp = (r < a.ctx ? a.vc : a.v) + off + cseg;
+        kp = reinterpret_cast<const char*>(r < a.ctx ? a.kc : a.k) + (off + cseg) * kEsz;
+        vp = reinterpret_cast<const char*>(r < a.ctx ? a.vc : a.v) + (off + cseg) * kEsz;
     }
     const float* qp = a.q + (((size_t)b * a.T + r) * a.nh + h) * hd + cseg;
+    constexpr int kStep = kKV ? 8 : 4;   // elements per 16-byte load
+#pragma unroll
+    for (int e = 0; e < SEG; e += kStep) {
+        const bool in = cseg + e < hd;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 k4 = has_key && in ? *reinterpret_cast<const uint4*>(kp + e * kEsz) : z;
+        const uint4 v4 = has_key && in ? *reinterpret_cast<const uint4*>(vp + e * kEsz) : z;
+        const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w}, vw[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if constexpr (kKV == 0) {
+                kr[e + w] = __uint_as_float(kw[w]);
+                vr[e + w] = __uint_as_float(vw[w]);
+            } else {
+                kr[e + 2 * w] = lo16<kKV>(kw[w]);
+                kr[e + 2 * w + 1] = hi16<kKV>(kw[w]);
+                vr[e + 2 * w] = lo16<kKV>(vw[w]);
+                vr[e + 2 * w + 1] = hi16<kKV>(vw[w]);
+            }
+        }
+    }
 #pragma unroll
     for (int e = 0; e < SEG; e += 4) {
         const bool in = cseg + e < hd;
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 k4 = has_key && in ? *reinterpret_cast<const float4*>(kp + e) : z;
-        const float4 v4 = has_key && in ? *reinterpret_cast<const float4*>(vp + e) : z;
-        const float4 q4 = has_q && in ? *reinterpret_cast<const float4*>(qp + e) : z;
-        kr[e] = k4.x; kr[e + 1] = k4.y; kr[e + 2] = k4.z; kr[e + 3] = k4.w;
-        vr[e] = v4.x; vr[e + 1] = v4.y; vr[e + 2] = v4.z; vr[e + 3] = v4.w;
+        const float4 q4 = has_q && in ? *reinterpret_cast<const float4*>(qp + e)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
         qr[e] = q4.x; qr[e + 1] = q4.y; qr[e + 2] = q4.z; qr[e + 3] = q4.w;
     }
     if constexpr (kNormQ) {
@@ -524,32 +621,38 @@ namespace {
 using SplitKernel = void (*)(SplitArgs);
 using SmallKernel = void (*)(SplitArgs, long long);
 
-template <int HD, bool kNormQ>
+template <int HD, bool kNormQ, int kKV>
 SplitKernel split_variant(int hd) {
-    return hd == HD ? attn_split_gqa_kernel<HD, kNormQ, false> : attn_split_gqa_kernel<HD, kNormQ, true>;
+    return hd == HD ? attn_split_gqa_kernel<HD, kNormQ, false, kKV>
+                    : attn_split_gqa_kernel<HD, kNormQ, true, kKV>;
 }
 
-SplitKernel pick_split(int hd, bool normq) {
-    if (hd > 64) return normq ? split_variant<128, true>(hd) : split_variant<128, false>(hd);
-    return normq ? split_variant<64, true>(hd) : split_variant<64, false>(hd);
+// kv: 0 (f32), DG_KV_F16 or DG_KV_BF16; the 16-bit variants take no in-kernel q norm.
+SplitKernel pick_split(int hd, bool normq, int kv) {
+    if (kv == DG_KV_F16) return hd > 64 ? split_variant<128, false, DG_KV_F16>(hd) : split_variant<64, false, DG_KV_F16>(hd);
+    if (kv == DG_KV_BF16) return hd > 64 ? split_variant<128, false, DG_KV_BF16>(hd) : split_variant<64, false, DG_KV_BF16>(hd);
+    if (hd > 64) return normq ? split_variant<128, true, 0>(hd) : split_variant<128, false, 0>(hd);
+    return normq ? split_variant<64, true, 0>(hd) : split_variant<64, false, 0>(hd);
 }
 
-template <int HD, bool kNormQ>
+template <int HD, bool kNormQ, int kKV>
 SmallKernel small_variant(int hd) {
-    return hd == HD ? attn_small_kernel<HD, kNormQ, false> : attn_small_kernel<HD, kNormQ, true>;
+    return hd == HD ? attn_small_kernel<HD, kNormQ, false, kKV> : attn_small_kernel<HD, kNormQ, true, kKV>;
 }
 
-SmallKernel pick_small(int hd, bool normq) {
-    if (hd > 64) return normq ? small_variant<128, true>(hd) : small_variant<128, false>(hd);
-    return normq ? small_variant<64, true>(hd) : small_variant<64, false>(hd);
+SmallKernel pick_small(int hd, bool normq, int kv) {
+    if (kv == DG_KV_F16) return hd > 64 ? small_variant<128, false, DG_KV_F16>(hd) : small_variant<64, false, DG_KV_F16>(hd);
+    if (kv == DG_KV_BF16) return hd > 64 ? small_variant<128, false, DG_KV_BF16>(hd) : small_variant<64, false, DG_KV_BF16>(hd);
+    if (hd > 64) return normq ? small_variant<128, true, 0>(hd) : small_variant<128, false, 0>(hd);
+    return normq ? small_variant<64, true, 0>(hd) : small_variant<64, false, 0>(hd);
 }
 
 // Shared body of both attention entry points.  `normq` selects the q-norm variant, whose extra
 // arguments (wq, cs, qflags, eps) were validated by the caller.
-int attn_call(const char* fn, const float* q, const float* kc, const float* vc, const float* k,
-              const float* v, float* out, int batch, int T, int ctx, int nh, int nkv, int hd,
+int attn_call(const char* fn, const float* q, const void* kc, const void* vc, const void* k,
+              const void* v, float* out, int batch, int T, int ctx, int nh, int nkv, int hd,
               float scale, int causal, void* workspace, size_t workspace_bytes, void* stream,
-              bool normq, const float* wq, const float* cs, unsigned qflags, float eps) {
+              bool normq, const float* wq, const float* cs, unsigned qflags, float eps, int kv) {
     if (batch < 0 || T < 0 || ctx < 0 || nh < 0 || nkv < 0)
         return dg::fail(DG_EINVAL, "%s: negative size (batch %d, T %d, ctx %d, nh %d, nkv %d)", fn,
                         batch, T, ctx, nh, nkv);
@@ -558,6 +661,9 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
     if (hd < 1) return dg::fail(DG_EINVAL, "%s: hd must be >= 1, got %d", fn, hd);
     if (hd > 128 || hd % 4 != 0)
         return dg::fail(DG_EUNSUPPORTED, "%s: hd %d not supported (a multiple of 4, at most 128)", fn, hd);
+    if (kv && hd % 8 != 0)
+        return dg::fail(DG_EUNSUPPORTED, "%s: 16-bit K/V need hd a multiple of 8, got %d", fn, hd);
+    const size_t esz = kv ? 2 : 4;
     if (!std::isfinite(scale)) return dg::fail(DG_EINVAL, "%s: scale is not finite", fn);
     if (causal != 0 && causal != 1) return dg::fail(DG_EINVAL, "%s: causal must be 0 or 1", fn);
     size_t nq = 1, nkvc = 1, ncache = 1;
@@ -582,9 +688,9 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
         p.ws_bytes = 0;
     }
     const dg::Span so(out, nq * 4);
-    const dg::Span ins[8] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * 4), dg::Span(v, nkvc * 4),
-                             dg::Span(ncache ? kc : nullptr, ncache * 4),
-                             dg::Span(ncache ? vc : nullptr, ncache * 4),
+    const dg::Span ins[8] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * esz), dg::Span(v, nkvc * esz),
+                             dg::Span(ncache ? kc : nullptr, ncache * esz),
+                             dg::Span(ncache ? vc : nullptr, ncache * esz),
                              dg::Span(normq ? wq : nullptr, (size_t)hd * 4),
                              dg::Span(normq ? cs : nullptr, (size_t)T * 2 * hd * 4),
                              dg::Span(p.nsplit > 1 ? workspace : nullptr, p.ws_bytes)};
@@ -601,7 +707,9 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
     const long long nblocks = (long long)batch * nkv * p.qblocks * p.nsplit;
     if (nblocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     SplitArgs a;
-    a.q = q; a.kc = kc; a.vc = vc; a.k = k; a.v = v; a.out = out;
+    a.q = q; a.out = out;   // K/V are addressed bytewise in the kernels, whatever their storage
+    a.kc = static_cast<const float*>(kc); a.vc = static_cast<const float*>(vc);
+    a.k = static_cast<const float*>(k); a.v = static_cast<const float*>(v);
     a.ws = static_cast<float*>(p.nsplit > 1 ? workspace : nullptr);
     a.nqtot = (size_t)batch * T * nh;
     a.hd = hd;
@@ -620,10 +728,10 @@ int attn_call(const char* fn, const float* q, const float* kc, const float* vc, 
         const long long units = (long long)batch * nh;
         const long long blocks = (units + 3) / 4;
         if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
-        hipLaunchKernelGGL(pick_small(hd, normq), dim3((unsigned)blocks), dim3(256), 0, s, a, units);
+        hipLaunchKernelGGL(pick_small(hd, normq, kv), dim3((unsigned)blocks), dim3(256), 0, s, a, units);
         return dg::launch_status(fn);
     }
-    hipLaunchKernelGGL(pick_split(hd, normq), dim3((unsigned)nblocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(pick_split(hd, normq, kv), dim3((unsigned)nblocks), dim3(512), 0, s, a);
     if (p.nsplit > 1) {
         const size_t total = (size_t)batch * T * nh;
         const size_t threads = total * (hd / 4);
@@ -641,7 +749,7 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
                                  int nkv, int hd, float scale, int causal, void* workspace,
                                  size_t workspace_bytes, void* stream) {
     return attn_call("dg_attn_split_gqa", q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale,
-                     causal, workspace, workspace_bytes, stream, false, nullptr, nullptr, 0u, 0.0f);
+                     causal, workspace, workspace_bytes, stream, false, nullptr, nullptr, 0u, 0.0f, 0);
 }
 
 extern "C" int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs,
@@ -662,5 +770,16 @@ extern "C" int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const fl
     if (!empty && need_cs && !cs) return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
     return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal,
                      workspace, workspace_bytes, stream, true, need_w ? wq : nullptr,
-                     need_cs ? cs : nullptr, qflags, eps);
+                     need_cs ? cs : nullptr, qflags, eps, 0);
+}
+
+extern "C" int dg_attn_split_gqa_kv16(const float* q, const void* kc, const void* vc, const void* k,
+                                      const void* v, float* out, int batch, int T, int ctx, int nh,
+                                      int nkv, int hd, float scale, int causal, int kv_format,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "dg_attn_split_gqa_kv16";
+    if (kv_format != DG_KV_F16 && kv_format != DG_KV_BF16)
+        return dg::fail(DG_EINVAL, "%s: kv_format must be DG_KV_F16 or DG_KV_BF16, got %d", fn, kv_format);
+    return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal, workspace,
+                     workspace_bytes, stream, false, nullptr, nullptr, 0u, 0.0f, kv_format);
 }

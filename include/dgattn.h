@@ -28,6 +28,7 @@
 #define DGATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -108,6 +109,21 @@ int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, f
                          const float* cs, int batch, int T, int nh, int nkv, int hd,
                          unsigned flags, float eps, void* stream);
 
+/* 16-bit storage formats of K and V (dg_pack_kv16, dg_attn_split_gqa_kv16). */
+#define DG_KV_F16 1   /* IEEE binary16 */
+#define DG_KV_BF16 2  /* bfloat16: the upper 16 bits of an f32 */
+
+/*
+ * dg_pack_kv16 -- f32 -> 16-bit storage of keys or values, the pack pass of deepencoder_gpu.rs
+ * `flash_reg_kv16_src` (the flash reads an f16 twin of its inputs and widens each value to f32
+ * before the unchanged f32 math).  Round to nearest, ties to even; values beyond the format's
+ * range become infinities, NaN stays NaN.
+ *   src  [n] f32;  dst [n] 16-bit values (uint16 bit patterns);  format DG_KV_F16 or DG_KV_BF16.
+ *   src and dst must be 16-byte aligned and must not overlap.
+ * Errors: DG_EINVAL for an unknown format, NULL pointers with n > 0, misalignment or overlap.
+ */
+int dg_pack_kv16(const float* src, void* dst, size_t n, int format, void* stream);
+
 /*
  * dg_attn_split_gqa_workspace_size -- bytes of scratch that dg_attn_split_gqa can use to split
  * the key range of one call across more workgroups (partial results and their combine).
@@ -171,6 +187,23 @@ int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs, co
                             int batch, int T, int ctx, int nh, int nkv, int hd, unsigned qflags,
                             float eps, float scale, int causal, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * dg_attn_split_gqa_kv16 -- dg_attn_split_gqa with keys and values stored in 16 bits (the
+ * page's kv16 twin, §8(f)-style reduced-precision K/V storage): kc, vc, k and v hold f16 or
+ * bf16 values (`kv_format`), in the same layouts as dg_attn_split_gqa's f32 tensors.  Every
+ * value is widened exactly to f32 and the arithmetic is that of dg_attn_split_gqa, so the
+ * result equals dg_attn_split_gqa on the widened values up to rounding.  Stage tiles in LDS are
+ * half the bytes; the widening costs vector instructions per tile.
+ *   hd must be a multiple of 8 (16-byte rows of 16-bit values); q and out are f32.
+ *   Other arguments, the workspace and its size function as dg_attn_split_gqa.
+ * Errors: as dg_attn_split_gqa, plus DG_EINVAL for an unknown kv_format and DG_EUNSUPPORTED
+ * for hd not a multiple of 8.
+ */
+int dg_attn_split_gqa_kv16(const float* q, const void* kc, const void* vc, const void* k,
+                           const void* v, float* out, int batch, int T, int ctx, int nh, int nkv,
+                           int hd, float scale, int causal, int kv_format, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn can use to hold the

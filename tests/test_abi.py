@@ -192,6 +192,23 @@ def test_relpos_windows_validation(L):
     assert L.relpos_flash_attn_windows_workspace_size(0, 14, 14, 12, 64) == 0
 
 
+def test_kv16_validation(L):
+    assert L.dg_pack_kv16(FAKE, FAKE + (1 << 24), 100, 3, None) == dg.DG_EINVAL       # format
+    assert L.dg_pack_kv16(FAKE, FAKE + 8, 100, dg.DG_KV_F16, None) == dg.DG_EINVAL     # misaligned
+    assert L.dg_pack_kv16(FAKE, FAKE + 16, 100, dg.DG_KV_F16, None) == dg.DG_EINVAL    # overlap
+    assert L.dg_pack_kv16(None, None, 0, dg.DG_KV_BF16, None) == dg.DG_OK
+    f = L.dg_attn_split_gqa_kv16
+    base = dict(q=FAKE, kc=FAKE + (1 << 24), vc=FAKE + (2 << 24), k=FAKE + (3 << 24),
+                v=FAKE + (4 << 24), out=FAKE + (5 << 24), batch=1, T=16, ctx=32, nh=4, nkv=2,
+                hd=64, scale=1.0, causal=0, fmt=dg.DG_KV_BF16, ws=None, wsb=0, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(fmt=0) == dg.DG_EINVAL
+    assert call(hd=20) == dg.DG_EUNSUPPORTED                 # 16-bit rows need hd % 8 == 0
+    assert call(out=FAKE + (3 << 24) + 16 * 2 * 64 * 2 - 16) == dg.DG_EINVAL   # 2-byte extents
+    assert call(kc=FAKE + (1 << 24) + 8) == dg.DG_EINVAL     # misaligned
+    assert call(T=0) == dg.DG_OK
+
+
 def test_binding_refuses_bad_tensors_before_the_call():
     import torch
     x = torch.zeros(8)

@@ -407,3 +407,94 @@ def test_sam_windowed_every_element():
     dg.relpos_flash_attn_windows(dev(c.qkv), dev(c.rh), dev(c.rw), out, c.nwin, c.gh, c.gw,
                                  c.heads, c.hd, c.scale, ws, nbytes)
     assert_parity(host(out), oracle_windows(c), "sam windowed")
+
+
+# ----------------------------------------------------------------------------- 16-bit K/V
+
+KV_FMTS = [(dg.DG_KV_F16, "f16"), (dg.DG_KV_BF16, "bf16")]
+
+
+def dev16(h):
+    """uint16 bit patterns -> a GPU int16 tensor holding the same bits."""
+    return None if h is None else torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("fmt,name", KV_FMTS, ids=[n for _, n in KV_FMTS])
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 65539])
+def test_pack_kv16_bit_exact(fmt, name, n):
+    rng = np.random.default_rng(n + fmt)
+    x = (np.exp2(rng.uniform(-30, 18, n)) * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    x[: min(n, 6)] = np.array([0.0, -0.0, np.inf, 65520.0, 2.0 ** -25, 1e-40], np.float32)[: min(n, 6)]
+    dst = torch.full((n + 8,), -1, dtype=torch.int16, device="cuda")   # guard past the end
+    dg.dg_pack_kv16(dev(x), dst, n, fmt)
+    got = host(dst).view(np.uint16)
+    assert np.array_equal(got[:n], oracle.pack16(x, fmt)), name
+    assert np.all(got[n:] == 0xffff), "wrote past n"
+
+
+def kv16_case(shape, fmt, seed):
+    """A split case whose K/V are packed to 16 bits; the oracle sees the widened values."""
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=seed, scale=scale, causal=causal)
+    pk = {n: (oracle.pack16(getattr(c, n), fmt) if getattr(c, n) is not None else None)
+          for n in ("kc", "vc", "k", "v")}
+    wd = {n: (oracle.widen16(h, fmt) if h is not None else None) for n, h in pk.items()}
+    return c, pk, wd
+
+
+KV16_SHAPES = [s for s in SPLIT_SHAPES if s[5] % 8 == 0]
+
+
+@pytest.mark.parametrize("fmt,name", KV_FMTS, ids=[n for _, n in KV_FMTS])
+@pytest.mark.parametrize("use_ws", [False, True], ids=["unsplit", "ws"])
+@pytest.mark.parametrize("shape", KV16_SHAPES, ids=lambda s: "B%d_T%d_ctx%d_h%d_kv%d_hd%d_c%d" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], s[7]))
+def test_attn_split_kv16(shape, use_ws, fmt, name):
+    """16-bit K/V, widened in the kernel: equal to f32 attention on the widened values."""
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c, pk, wd = kv16_case(shape, fmt, seed=5 * T + ctx)
+    ref = oracle.attn_split_gqa(c.q, wd["kc"], wd["vc"], wd["k"], wd["v"], nh, nkv, hd, scale,
+                                causal)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd) if use_ws else (None, 0)
+    dg.dg_attn_split_gqa_kv16(dev(c.q), dev16(pk["kc"]), dev16(pk["vc"]), dev16(pk["k"]),
+                              dev16(pk["v"]), out, B, T, ctx, nh, nkv, hd, scale, int(causal), fmt,
+                              ws, nbytes)
+    assert_parity(host(out), ref, "kv16 %s %s ws=%d" % (name, shape, nbytes))
+
+
+# Distance of 16-bit K/V storage from the f32 path on normed canvas data (q, k rows of unit
+# RMS, scale 1): rounding k by a relative eps moves a score by about sqrt(hd)*eps/sqrt(3) and
+# an output by that times |v|, plus eps*|v| from v itself; over ~1e5 outputs the maximum sits
+# a few deviations out.  f16: eps = 2^-11; bf16: eps = 2^-8.
+KV16_VS_F32 = {dg.DG_KV_F16: 2e-2, dg.DG_KV_BF16: 1.5e-1}
+
+
+@pytest.mark.parametrize("fmt,name", KV_FMTS, ids=[n for _, n in KV_FMTS])
+def test_canvas_step_kv16(fmt, name):
+    """DiffusionGemma-like step with 16-bit K/V: every packed value bit-exact against the
+    oracle's packing of the same f32 data, the attention at the f32 bar on those values, and the
+    distance from the all-f32 step within the stated bound."""
+    c = synth.dg_canvas_steps(1)
+    blk16 = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, dev(c.kc), dev(c.vc), dev(c.wq),
+                        dev(c.wk), eps=c.eps, theta=c.theta, rope_cache=True, kv16=name)
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
+    blk16.step(q, k, v, out)
+    kc_roped = host(blk16.kc)                       # the f32 cache after the set-up rope
+    assert np.array_equal(host(blk16.kc16).view(np.uint16), oracle.pack16(kc_roped, fmt).ravel())
+    assert np.array_equal(host(blk16.vc16).view(np.uint16), oracle.pack16(c.vc, fmt).ravel())
+    kn, vn, qn = host(k), host(v), host(q)          # normed in place by the step
+    k16, v16 = host(blk16.k16).view(np.uint16), host(blk16.v16).view(np.uint16)
+    assert np.array_equal(k16, oracle.pack16(kn, fmt).ravel())
+    assert np.array_equal(v16, oracle.pack16(vn, fmt).ravel())
+    w = lambda h, shape: oracle.widen16(h, fmt).reshape(shape)
+    ref = oracle.attn_split_gqa(qn, w(host(blk16.kc16).view(np.uint16), c.kc.shape),
+                                w(host(blk16.vc16).view(np.uint16), c.vc.shape), w(k16, kn.shape),
+                                w(v16, vn.shape), c.nh, c.nkv, c.hd)
+    got = host(out)
+    assert_parity(got, ref, "kv16 canvas %s" % name)
+    ref32 = oracle.attn_split_gqa(qn, kc_roped, c.vc, kn, vn, c.nh, c.nkv, c.hd)
+    dist = float(np.max(np.abs(got - ref32)))
+    assert dist <= KV16_VS_F32[fmt], "%s storage moved the output by %.3e" % (name, dist)
+    print("kv16 %s: max |out - f32 out| = %.3e" % (name, dist))
