@@ -426,22 +426,25 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
     float qr[SEG], kr[SEG], vr[SEG];
     const bool has_key = active && r < S, has_q = active && r < a.T;
     constexpr int kEsz = kKV ? 2 : 4;
-    const char* kp = nullptr;
-    const char* vp = nullptr;
-    if (has_key) {
-        const size_t off = r < a.ctx ? (((size_t)b * a.nkv + kv) * a.ctx + r) * hd
-                                     : (((size_t)b * a.T + (r - a.ctx)) * a.nkv + kv) * hd;
-        kp = reinterpret_cast<const char*>(r < a.ctx ? a.kc : a.k) + (off + cseg) * kEsz;
-        vp = reinterpret_cast<const char*>(r < a.ctx ? a.vc : a.v) + (off + cseg) * kEsz;
-    }
-    const float* qp = a.q + (((size_t)b * a.T + r) * a.nh + h) * hd + cseg;
+    // Every lane loads from an address that exists (key row 0 and query row 0 stand in for
+    // rows past the end, a last chunk for padding) and zeroes by selection afterwards: guarded
+    // loads would become divergent branches that issue the loads one at a time.
+    const int rk = has_key ? r : 0, rq = has_q ? r : 0;
+    const size_t off = rk < a.ctx ? (((size_t)b * a.nkv + kv) * a.ctx + rk) * hd
+                                  : (((size_t)b * a.T + (rk - a.ctx)) * a.nkv + kv) * hd;
+    const char* kp = reinterpret_cast<const char*>(rk < a.ctx ? a.kc : a.k) + off * kEsz;
+    const char* vp = reinterpret_cast<const char*>(rk < a.ctx ? a.vc : a.v) + off * kEsz;
+    const float* qrow = a.q + (((size_t)b * a.T + rq) * a.nh + h) * hd;
     constexpr int kStep = kKV ? 8 : 4;   // elements per 16-byte load
 #pragma unroll
     for (int e = 0; e < SEG; e += kStep) {
         const bool in = cseg + e < hd;
+        const int el = in ? cseg + e : hd - kStep;
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        const uint4 k4 = has_key && in ? *reinterpret_cast<const uint4*>(kp + e * kEsz) : z;
-        const uint4 v4 = has_key && in ? *reinterpret_cast<const uint4*>(vp + e * kEsz) : z;
+        const uint4 kl = *reinterpret_cast<const uint4*>(kp + el * kEsz);
+        const uint4 vl = *reinterpret_cast<const uint4*>(vp + el * kEsz);
+        const uint4 k4 = has_key && in ? kl : z;
+        const uint4 v4 = has_key && in ? vl : z;
         const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w}, vw[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -459,8 +462,8 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
 #pragma unroll
     for (int e = 0; e < SEG; e += 4) {
         const bool in = cseg + e < hd;
-        const float4 q4 = has_q && in ? *reinterpret_cast<const float4*>(qp + e)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 ql = *reinterpret_cast<const float4*>(qrow + (in ? cseg + e : hd - 4));
+        const float4 q4 = has_q && in ? ql : make_float4(0.f, 0.f, 0.f, 0.f);
         qr[e] = q4.x; qr[e + 1] = q4.y; qr[e + 2] = q4.z; qr[e + 3] = q4.w;
     }
     if constexpr (kNormQ) {
