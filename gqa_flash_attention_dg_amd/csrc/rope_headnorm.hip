@@ -58,13 +58,21 @@ struct NormArgs {
     float eps;
 };
 
+// kHD: the head dim when it is 128 or 64 (no per-lane guards), 0 for any other hd <= 128.  Lanes
+// past hd read an element that exists (element 0 of the row) and discard it by selection, so
+// the loads are not turned into divergent branches.
+template <int kHD>
 __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restrict__ w,
-                                    const float* __restrict__ cr, int hd, unsigned flags,
+                                    const float* __restrict__ cr, int hd_rt, unsigned flags,
                                     float eps, int lane, float* __restrict__ vr) {
+    const int hd = kHD ? kHD : hd_rt;
     const int e0 = lane, e1 = lane + 64;
-    const bool v0 = e0 < hd, v1 = e1 < hd;
-    float y0 = v0 ? xr[e0] : 0.0f;
-    float y1 = v1 ? xr[e1] : 0.0f;
+    const bool v0 = kHD ? true : e0 < hd;
+    const bool v1 = kHD == 128 ? true : (kHD == 64 ? false : e1 < hd);
+    const float x0 = xr[v0 ? e0 : 0];
+    const float x1 = kHD == 64 ? 0.0f : xr[v1 ? e1 : 0];
+    float y0 = v0 ? x0 : 0.0f;
+    float y1 = v1 ? x1 : 0.0f;
     if (!(flags & DG_NORM_SKIP)) {
         const float ss = wave_sum(y0 * y0 + y1 * y1);
         const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
@@ -75,8 +83,10 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
             if (v1) vr[e1] = y1;
         }
         if (flags & DG_NORM_WEIGHTED) {
-            if (v0) y0 *= w[e0];
-            if (v1) y1 *= w[e1];
+            const float w0 = w[v0 ? e0 : 0];
+            const float w1 = kHD == 64 ? 0.0f : w[v1 ? e1 : 0];
+            y0 *= w0;
+            y1 *= w1;
         }
     }
     if (flags & DG_NORM_ROPE) {
@@ -85,9 +95,12 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
         const int p0 = e0 < half ? e0 + half : e0 - half;
         const int p1 = e1 < half ? e1 + half : e1 - half;
         float q0, q1;
-        if (hd == 128) {  // partners share the lane: e0 <-> e1
+        if (kHD == 128) {  // partners share the lane: e0 <-> e1
             q0 = y1;
             q1 = y0;
+        } else if (kHD == 64) {
+            q0 = __shfl_xor(y0, 32);
+            q1 = 0.0f;
         } else {
             const int s0 = v0 ? (p0 & 63) : lane, s1 = v1 ? (p1 & 63) : lane;
             const float a0 = __shfl(y0, s0), b0 = __shfl(y1, s0);
@@ -95,14 +108,13 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
             q0 = p0 >= 64 ? b0 : a0;
             q1 = p1 >= 64 ? b1 : a1;
         }
-        if (v0) {
-            const float rot = e0 < half ? -q0 : q0;
-            xr[e0] = y0 * cr[e0] + rot * cr[hd + e0];
-        }
-        if (v1) {
-            const float rot = e1 < half ? -q1 : q1;
-            xr[e1] = y1 * cr[e1] + rot * cr[hd + e1];
-        }
+        const float c0 = cr[v0 ? e0 : 0], s0v = cr[hd + (v0 ? e0 : 0)];
+        const float c1 = kHD == 64 ? 0.0f : cr[v1 ? e1 : 0];
+        const float s1v = kHD == 64 ? 0.0f : cr[hd + (v1 ? e1 : 0)];
+        const float rot0 = e0 < half ? -q0 : q0;
+        const float rot1 = e1 < half ? -q1 : q1;
+        if (v0) xr[e0] = y0 * c0 + rot0 * s0v;
+        if (v1) xr[e1] = y1 * c1 + rot1 * s1v;
     } else {
         if (v0) xr[e0] = y0;
         if (v1) xr[e1] = y1;
@@ -110,6 +122,7 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
 }
 
 // Rows of all segments are numbered consecutively (segment 0 first); each wavefront takes one.
+template <int kHD>
 __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
     long long u = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
@@ -119,8 +132,8 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     const NormSeg& g = a.seg[s];
     const int t = (int)((u / g.heads) % a.T);
     const float* cr = (g.flags & DG_NORM_ROPE) ? a.cs + (size_t)t * 2 * a.hd : nullptr;
-    headnorm_row(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane,
-                 g.vout ? g.vout + (size_t)u * a.hd : nullptr);
+    headnorm_row<kHD>(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane,
+                      g.vout ? g.vout + (size_t)u * a.hd : nullptr);
 }
 
 }  // namespace
@@ -162,8 +175,9 @@ int launch_norm(const char* fn, NormArgs& a, void* stream) {
     if (rows == 0) return dg::ok();
     const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many rows", fn);
-    hipLaunchKernelGGL(headnorm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)stream, a);
+    auto* kern = a.hd == 128 ? headnorm_rope_kernel<128>
+                             : (a.hd == 64 ? headnorm_rope_kernel<64> : headnorm_rope_kernel<0>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
     return dg::launch_status(fn);
 }
 
