@@ -559,10 +559,13 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
 }
 
 // Merges split-KV partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
-// One thread per 4 output elements (hd is a multiple of 4).
+// One thread per 4 output elements (hd is a multiple of 4).  Splits are taken 8 at a time with
+// all their loads issued together, and the running maximum is folded in as it grows (the
+// same rescaling as the online softmax), so no pass waits for a previous one.
 __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restrict__ ws,
                                                             float* __restrict__ out,
                                                             size_t total, int nsplit, int hd) {
+    constexpr int kBatch = 8;
     const int c4 = hd / 4;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total * c4) return;
@@ -570,15 +573,33 @@ __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restr
     const int c = (int)(idx % c4) * 4;
     const float* wm = ws + (size_t)nsplit * total * hd;
     const float* wl = wm + (size_t)nsplit * total;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wm[(size_t)s * total + gq]);
-    float L = 0.0f;
+    float M = -INFINITY, L = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
-        const float w = dgk::fast_exp2(wm[(size_t)s * total + gq] - M);
-        L += wl[(size_t)s * total + gq] * w;
-        const float4 v = *reinterpret_cast<const float4*>(ws + ((size_t)s * total + gq) * hd + c);
-        acc.x += v.x * w; acc.y += v.y * w; acc.z += v.z * w; acc.w += v.w * w;
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+        float mv[kBatch], lv[kBatch];
+        float4 ov[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int sp = min(s0 + i, nsplit - 1);   // a repeated split is masked below
+            mv[i] = wm[(size_t)sp * total + gq];
+            lv[i] = wl[(size_t)sp * total + gq];
+            ov[i] = *reinterpret_cast<const float4*>(ws + ((size_t)sp * total + gq) * hd + c);
+        }
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (s0 + i < nsplit) bm = fmaxf(bm, mv[i]);
+        const float ref = bm == -INFINITY ? 0.0f : bm;
+        const float corr = dgk::fast_exp2(M - ref);
+        L *= corr;
+        acc.x *= corr; acc.y *= corr; acc.z *= corr; acc.w *= corr;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const float w = s0 + i < nsplit ? dgk::fast_exp2(mv[i] - ref) : 0.0f;
+            L += lv[i] * w;
+            acc.x += ov[i].x * w; acc.y += ov[i].y * w; acc.z += ov[i].z * w; acc.w += ov[i].w * w;
+        }
+        M = bm;
     }
     const float inv = 1.0f / L;
     *reinterpret_cast<float4*>(out + gq * hd + c) =
