@@ -373,6 +373,10 @@ def main():
                     help="in_attention: k/v norms in one launch + q norm inside attention; "
                          "one_launch: q, k, v norms in one launch; separate: the page's three "
                          "headnorm dispatches")
+    ap.add_argument("--graph", type=int, default=0, metavar="STEPS",
+                    help="split-GQA workloads: capture STEPS consecutive steps as one HIP graph "
+                         "and replay it (timed per step; the dominant-kernel events then cover "
+                         "the whole replay)")
     ap.add_argument("--kv16", default=None, choices=["f16", "bf16"],
                     help="long_cache / dg_canvas: keys and values stored in 16 bits, widened to "
                          "f32 inside attention")
@@ -393,10 +397,35 @@ def main():
     torch.cuda.set_device(0)
 
     work = make_work(args.workload, norm_mode=args.norm, kv16=args.kv16)
+    if args.graph:
+        if not isinstance(work, SplitWork):
+            raise SystemExit("--graph applies to the split-GQA workloads")
+        from gqa_flash_attention_dg_amd.canvas import CanvasGraph
+        if args.steps % args.graph:
+            raise SystemExit("--steps must be a multiple of --graph")
+        cg = CanvasGraph(work.blk, work.q, work.k, work.v, work.out, steps=args.graph)
+        work.graph = args.graph
+        steps_run = [0]
+
+        def graph_step(ev=None, _cg=cg, _k=args.graph):
+            # one replay every _k steps; the events of a replay are split evenly over its steps
+            if steps_run[0] % _k == 0:
+                if ev:
+                    ev[0].record()
+                _cg.replay()
+                if ev:
+                    ev[1].record()
+            elif ev:
+                ev[0].record()
+                ev[1].record()
+            steps_run[0] += 1
+        work.step = graph_step
 
     for _ in range(args.warmup):
         work.step()
     torch.cuda.synchronize()
+    if args.graph:
+        steps_run[0] = 0   # the timed steps start on a replay boundary
     nev = len(work.io) if isinstance(work, LayerStackWork) else 0
     mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     evs = [[mk() for _ in range(nev)] if nev else mk() for _ in range(args.steps)]
@@ -439,7 +468,7 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": work.config(),
+        "config": dict(work.config(), **({"hip_graph_steps": work.graph} if getattr(work, "graph", 0) else {})),
         "step_flops": work.flops, "step_hbm_bytes_algorithmic": step_bytes,
         "step_hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "roofline": roof, "cpu_baseline": cpu,

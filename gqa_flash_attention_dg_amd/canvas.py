@@ -155,6 +155,29 @@ class CanvasBlock:
         self.attend(q, k, v, out)
 
 
+class CanvasGraph:
+    """`steps` canvas steps of a CanvasBlock captured as one HIP graph (through
+    torch.cuda.CUDAGraph): the steps' launches (norms, attention, split-KV combine; no memset or
+    host work) replay with one submission.  The graph is bound to the q, k, v and out tensors given at capture; a
+    caller refreshes their contents in place between replays."""
+
+    def __init__(self, blk, q, k, v, out, warmup=2, steps=1):
+        self.blk, self.io, self.steps = blk, (q, k, v, out), steps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):      # launch once outside capture (loads the code objects)
+            for _ in range(warmup):
+                blk.step(q, k, v, out)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for _ in range(steps):   # `steps` consecutive steps on the same buffers
+                blk.step(q, k, v, out)
+
+    def replay(self):
+        self.graph.replay()
+
+
 class CanvasStack:
     """The attention blocks of a stack of decoder layers over one canvas.
 

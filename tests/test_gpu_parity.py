@@ -498,3 +498,34 @@ def test_canvas_step_kv16(fmt, name):
     dist = float(np.max(np.abs(got - ref32)))
     assert dist <= KV16_VS_F32[fmt], "%s storage moved the output by %.3e" % (name, dist)
     print("kv16 %s: max |out - f32 out| = %.3e" % (name, dist))
+
+
+# ----------------------------------------------------------------------------- HIP graphs
+
+@pytest.mark.parametrize("norm_mode", ["in_attention", "one_launch"])
+def test_canvas_step_graph_replays(norm_mode):
+    """A canvas step captured as a HIP graph: every replay (with fresh inputs copied in place,
+    eager launches and synchronisations in between) equals the eager step on the same inputs."""
+    from gqa_flash_attention_dg_amd.canvas import CanvasGraph
+    c = synth.dg_canvas_steps(4)
+    mk = lambda: CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, dev(c.kc), dev(c.vc), dev(c.wq),
+                             dev(c.wk), eps=c.eps, theta=c.theta, rope_cache=True,
+                             norm_mode=norm_mode)
+    blk_g, blk_e = mk(), mk()
+    q, k, v = dev(c.steps[0]["q"]), dev(c.steps[0]["k"]), dev(c.steps[0]["v"])
+    out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
+    g = CanvasGraph(blk_g, q, k, v, out)
+    for rep in range(6):
+        st = c.steps[rep % len(c.steps)]
+        q.copy_(dev(st["q"])); k.copy_(dev(st["k"])); v.copy_(dev(st["v"]))
+        g.replay()
+        got = host(out)
+        qe, ke, ve = dev(st["q"]), dev(st["k"]), dev(st["v"])
+        oe = torch.empty_like(out)
+        blk_e.step(qe, ke, ve, oe)
+        assert np.array_equal(got, host(oe)), "replay %d differs from the eager step" % rep
+    cs, kc = oracle_prepare(c)
+    rows = sample_rows(c.B * c.T, 16, seed=1)
+    ref, _ = oracle_step(c, st["q"], st["k"], st["v"], cs, kc, rows=rows)
+    flat = lambda a: a.reshape(c.B * c.T, -1)[rows]
+    assert_parity(flat(got), flat(ref), "graph replay")
