@@ -26,11 +26,17 @@ namespace {
 using dgk::f32x16;
 constexpr int HD = 64;
 constexpr int kWaves = 8;
-constexpr int kQGroups = 2;                   // query groups of 32 per workgroup
-constexpr int kParts = 4;                     // wavefronts per group, one key tile each per stage
-constexpr int kBlockQ = kQGroups * dgk::kQuery;
-constexpr int kStage = kParts * dgk::kKeys;   // 128 keys per stage
+// A workgroup of 8 wavefronts is kQGroups = 8 / kParts query groups of 32 times kParts
+// wavefronts per group, each taking every kParts-th key tile: 2 x 4 for large grids (64
+// queries per workgroup, 4-way key split), 4 x 2 for small ones (128 queries, 2-way), where
+// fewer, longer-running workgroups amortise their prologue and merge.
+template <int kParts>
+struct RelShape {
+    static constexpr int kQGroups = 8 / kParts;
+    static constexpr int kBlockQ = kQGroups * dgk::kQuery;
+};
 constexpr int kMaxGrid = 64;                  // gh, gw <= 64
+constexpr int kSmallGrid = 512;               // grids of at most this many tokens use 4 x 2
 
 struct RelArgs {
     const float* qkv;  // [nwin][n][3W]
@@ -60,6 +66,49 @@ __device__ inline int xcd_remap(int bid, int n) {
 // accumulators hold 16 queries of table row l%32.  Output rows follow the page's buffers:
 // dh [nwin][heads][n][gh], then dw [nwin][heads][n][gw].
 constexpr int kBiasWaves = 4;
+
+// Lines of at most 16 queries against at most 16 table rows (windowed grids): one 16x16 tile
+// per line with v_mfma_f32_16x16x4f32, a quarter of the 32x32 tile's matrix work.  Lane l
+// supplies query row l%16 (A) and table row l%16 (B) at contraction index k = l/16, which
+// covers elements 16k..16k+15 over the 16 steps (4 contiguous float4 loads per operand); the
+// 4 accumulators hold queries 4*(l/16)+r of table row l%16.
+__global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs a, float* __restrict__ dhw,
+                                                                       long long ntasks) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    const long long task = (long long)blockIdx.x * kBiasWaves + (threadIdx.x >> 6);
+    if (task >= ntasks) return;  // wave-uniform; task = unit * (gh + gw) + line
+    const int line = (int)(task % (a.gh + a.gw));
+    const int unit = (int)(task / (a.gh + a.gw));
+    const int head = unit % a.heads, win = unit / a.heads;
+    const bool is_h = line < a.gh;
+    const int nq = is_h ? a.gw : a.gh;
+    const int nr = is_h ? a.gh : a.gw;
+    auto qidx = [&](int v) { return is_h ? line * a.gw + v : v * a.gw + (line - a.gh); };
+    const size_t rs = (size_t)3 * a.W;
+    const float* qr = a.qkv + ((size_t)win * a.n + qidx(min(l16, nq - 1))) * rs + head * HD + 16 * kq;
+    const float* tr = (is_h ? a.rh + (size_t)line * a.gh * HD : a.rw + (size_t)(line - a.gh) * a.gw * HD) +
+                      (size_t)min(l16, nr - 1) * HD + 16 * kq;
+    float qv[16], tv[16];
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(qr + c);
+        const float4 y = *reinterpret_cast<const float4*>(tr + c);
+        qv[c] = x.x; qv[c + 1] = x.y; qv[c + 2] = x.z; qv[c + 3] = x.w;
+        tv[c] = y.x; tv[c + 1] = y.y; tv[c + 2] = y.z; tv[c + 3] = y.w;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s], tv[s], acc, 0, 0, 0);
+    if (l16 >= nr) return;
+    float* base = dhw + (is_h ? (size_t)unit * a.n * a.gh
+                              : (size_t)a.nwin * a.heads * a.n * a.gh + (size_t)unit * a.n * a.gw);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int v = 4 * kq + r;   // accumulator r: query on the line
+        if (v < nq) base[(size_t)qidx(v) * nr + l16] = acc[r] * dgk::kLog2e;
+    }
+}
 
 __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias_kernel(RelArgs a, float* __restrict__ dhw,
                                                                      long long ntasks) {
@@ -137,9 +186,11 @@ __host__ __device__ inline Tiling make_tiling(int gh, int gw) {
 
 // kFull: every tile holds 32 keys (no padding slots, no short last tile); kOneShift: the height
 // bias takes one MFMA step (at most two grid rows per tile).
-template <bool kFull, bool kOneShift>
+template <bool kFull, bool kOneShift, int kParts>
 __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     using TL = dgk::Tile<HD>;
+    constexpr int kQGroups = RelShape<kParts>::kQGroups;
+    constexpr int kBlockQ = RelShape<kParts>::kBlockQ;
     // staging: [buffer][tile][K, V] and bias tables [group][ky][query] (dh)
     __shared__ __attribute__((aligned(16))) float smem[2 * kParts * 2 * TL::kFloats];
     __shared__ float tab[kQGroups * kMaxGrid * dgk::kQuery];
@@ -154,7 +205,8 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    const int grp = wave & (kQGroups - 1), part = wave >> 1;
+    // wavefronts w and w+4 share a SIMD: the same group, parts p and p + kParts/2
+    const int grp = wave & (kQGroups - 1), part = wave / kQGroups;
     const size_t rs = (size_t)3 * a.W;  // qkv row stride (floats)
     const Tiling tl = make_tiling(a.gh, a.gw);
 
@@ -364,7 +416,9 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(out) |
          reinterpret_cast<uintptr_t>(rh) | reinterpret_cast<uintptr_t>(rw)) & 15)
         return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
-    const long long qblocks = (n + kBlockQ - 1) / kBlockQ;
+    const bool small = n <= kSmallGrid;   // 4 x 2 workgroups for small grids
+    const long long kbq = small ? RelShape<2>::kBlockQ : RelShape<4>::kBlockQ;
+    const long long qblocks = (n + kbq - 1) / kbq;
     const long long nblocks = qblocks * heads * nwin;
     if (nblocks > 0x7fffffffLL || (long long)nwin * heads * (gh + gw) > 0x1fffffffLL)
         return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
@@ -384,14 +438,22 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     }
     hipStream_t s = (hipStream_t)stream;
     if (use_ws) {
-        const long long ntasks = (long long)nwin * heads * (gh + gw) * 4;
-        hipLaunchKernelGGL(relpos_bias_kernel, dim3((unsigned)((ntasks + kBiasWaves - 1) / kBiasWaves)),
-                           dim3(64 * kBiasWaves), 0, s, a, static_cast<float*>(workspace), ntasks);
+        const bool b16 = gh <= 16 && gw <= 16;   // every line fits one 16x16 tile
+        const long long ntasks = (long long)nwin * heads * (gh + gw) * (b16 ? 1 : 4);
+        const dim3 grid((unsigned)((ntasks + kBiasWaves - 1) / kBiasWaves));
+        if (b16)
+            hipLaunchKernelGGL(relpos_bias16_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
+                               static_cast<float*>(workspace), ntasks);
+        else
+            hipLaunchKernelGGL(relpos_bias_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
+                               static_cast<float*>(workspace), ntasks);
     }
     const bool full = tl.half_rows ? gw == 64 : (tl.kpt == dgk::kKeys && gh % tl.rpt == 0);
     const bool one = tl.nshift == 1;
-    auto* kern = full ? (one ? relpos_flash_kernel<true, true> : relpos_flash_kernel<true, false>)
-                      : (one ? relpos_flash_kernel<false, true> : relpos_flash_kernel<false, false>);
+    auto* kern = small ? (full ? (one ? relpos_flash_kernel<true, true, 2> : relpos_flash_kernel<true, false, 2>)
+                               : (one ? relpos_flash_kernel<false, true, 2> : relpos_flash_kernel<false, false, 2>))
+                       : (full ? (one ? relpos_flash_kernel<true, true, 4> : relpos_flash_kernel<true, false, 4>)
+                               : (one ? relpos_flash_kernel<false, true, 4> : relpos_flash_kernel<false, false, 4>));
     hipLaunchKernelGGL(kern, dim3((unsigned)a.nblocks), dim3(512), 0, s, a);
     return dg::launch_status(fn);
 }
