@@ -687,6 +687,10 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
         return dg::fail(DG_EUNSUPPORTED, "%s: hd %d not supported (a multiple of 4, at most 128)", fn, hd);
     if (kv && hd % 8 != 0)
         return dg::fail(DG_EUNSUPPORTED, "%s: 16-bit K/V need hd a multiple of 8, got %d", fn, hd);
+    // Key and query-vector indices inside the kernels are 32-bit.
+    if ((long long)ctx + T > (1LL << 30) || (long long)T * (nh / nkv) > (1LL << 30))
+        return dg::fail(DG_EUNSUPPORTED, "%s: ctx + T (%lld) or T * nh/nkv above 2^30", fn,
+                        (long long)ctx + T);
     const size_t esz = kv ? 2 : 4;
     if (!std::isfinite(scale)) return dg::fail(DG_EINVAL, "%s: scale is not finite", fn);
     if (causal != 0 && causal != 1) return dg::fail(DG_EINVAL, "%s: causal must be 0 or 1", fn);

@@ -160,7 +160,8 @@ size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int n
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
  * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, a tensor pointer
  * that is not 16-byte aligned, or a workspace pointer that is misaligned or has
- * workspace_bytes too small; DG_EUNSUPPORTED for hd above 128 or not a multiple of 4.
+ * workspace_bytes too small; DG_EUNSUPPORTED for hd above 128 or not a multiple of 4, or
+ * ctx + T or T * nh/nkv above 2^30 (the kernels index keys and query vectors in 32 bits).
  */
 int dg_attn_split_gqa(const float* q, const float* kc, const float* vc, const float* k,
                       const float* v, float* out, int batch, int T, int ctx, int nh, int nkv,

@@ -94,6 +94,8 @@ def test_attn_split_validation(L):
     assert "overlaps" in _err(L)
     assert f(*args(out=FAKE + (3 << 24) + 4)) == dg.DG_EINVAL  # out overlaps canvas k
     assert f(*args(ws=FAKE + (6 << 24) + 8, wsb=1 << 20)) == dg.DG_EINVAL  # misaligned
+    assert f(*args(ctx=(1 << 30))) == dg.DG_EUNSUPPORTED    # 32-bit key indices
+    assert f(*args(T=(1 << 29), nh=8, nkv=2)) == dg.DG_EUNSUPPORTED
     assert f(*args(T=0)) == dg.DG_OK                        # zero canvas: no-op
     assert f(*args(batch=0)) == dg.DG_OK
     assert L.dg_attn_split_gqa_workspace_size(1, 16, 32, 5, 2, 64) == 0
