@@ -520,3 +520,59 @@ def test_canvas_step_graph_replays(norm_mode):
     ref, _ = oracle_step(c, st["q"], st["k"], st["v"], cs, kc, rows=rows)
     flat = lambda a: a.reshape(c.B * c.T, -1)[rows]
     assert_parity(flat(got), flat(ref), "graph replay")
+
+
+# ----------------------------------------------------------------------------- seeded shape sweep
+
+def _sweep_shapes(n, seed):
+    """Random valid split-GQA shapes: batch, canvas and cache lengths (short sets, tile seams,
+    several workgroups), GQA ratios, head dims (exact and padded), causal and scale."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        nkv = int(rng.choice([1, 2, 3, 4]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        hd = int(rng.choice([8, 16, 32, 40, 64, 72, 96, 128]))
+        T = int(rng.choice([1, 2, 5, 8, 17, 33, 64, 100, 130]))
+        ctx = int(rng.choice([0, 1, 3, 31, 32, 63, 64, 65, 127, 300, 777]))
+        B = int(rng.choice([1, 2, 3]))
+        causal = bool(rng.random() < 0.3)
+        scale = float(rng.choice([1.0, 0.5, 0.125]))
+        out.append((B, T, ctx, nkv * G, nkv, hd, scale, causal))
+    return out
+
+
+SWEEP = _sweep_shapes(40, seed=2024)
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_split_shape_sweep(i):
+    """Each random shape through all three attention entry points: plain (with and without the
+    split-KV workspace), q norm inside attention, and 16-bit K/V."""
+    shape = SWEEP[i]
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=100 + i, scale=scale, causal=causal)
+    ref = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, nh, nkv, hd, scale, causal)
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
+    for use_ws in (False, True):
+        out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+        dg.dg_attn_split_gqa(dev(c.q), dev(c.kc), dev(c.vc), dev(c.k), dev(c.v), out, B, T, ctx,
+                             nh, nkv, hd, scale, int(causal), ws if use_ws else None,
+                             nbytes if use_ws else 0)
+        assert_parity(host(out), ref, "sweep %d %s ws=%d" % (i, shape, use_ws))
+    flags = dg.DG_NORM_WEIGHTED | dg.DG_NORM_ROPE
+    cq, q, wq, cs, refq = qnorm_case(shape, flags, seed=200 + i)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    dg.dg_attn_split_gqa_qnorm(dev(q), dev(wq), dev(cs), dev(cq.kc), dev(cq.vc), dev(cq.k),
+                               dev(cq.v), out, B, T, ctx, nh, nkv, hd, flags, 1e-6, scale,
+                               int(causal), ws, nbytes)
+    assert_parity(host(out), refq, "sweep qnorm %d %s" % (i, shape))
+    fmt = dg.DG_KV_BF16 if i % 2 else dg.DG_KV_F16
+    c16, pk, wd = kv16_case(shape, fmt, seed=300 + i)
+    ref16 = oracle.attn_split_gqa(c16.q, wd["kc"], wd["vc"], wd["k"], wd["v"], nh, nkv, hd, scale,
+                                  causal)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    dg.dg_attn_split_gqa_kv16(dev(c16.q), dev16(pk["kc"]), dev16(pk["vc"]), dev16(pk["k"]),
+                              dev16(pk["v"]), out, B, T, ctx, nh, nkv, hd, scale, int(causal), fmt,
+                              ws, nbytes)
+    assert_parity(host(out), ref16, "sweep kv16 %d %s" % (i, shape))
