@@ -1,7 +1,7 @@
 // kv16_pack.hip -- dg_pack_kv16: f32 -> 16-bit storage for K and V on gfx950.
 //
 // inferencelayer 0.2.8, src/deepencoder_gpu.rs, `flash_reg_kv16_src`: the flash reads its keys
-// and values from an f16-packed twin made by one cheap pack pass, widening each value to f32
+// and values from an f16 copy of its inputs made by a separate packing pass, widening each to f32
 // before the unchanged f32 math.  This is that pack pass, for IEEE binary16 or bfloat16, both
 // rounded to nearest with ties to even.  HBM-bound: each thread turns 8 floats (two 16-byte
 // loads) into one 16-byte store.
