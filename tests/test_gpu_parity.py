@@ -576,3 +576,77 @@ def test_split_shape_sweep(i):
                               dev16(pk["v"]), out, B, T, ctx, nh, nkv, hd, scale, int(causal), fmt,
                               ws, nbytes)
     assert_parity(host(out), ref16, "sweep kv16 %d %s" % (i, shape))
+
+
+# ----------------------------------------------------------------------------- extreme scores
+
+@pytest.mark.parametrize("scale", [8.0, 30.0])
+@pytest.mark.parametrize("shape", [(1, 40, 300, 4, 2, 128), (2, 6, 0, 4, 1, 64), (1, 70, 1000, 8, 2, 64)],
+                         ids=["tiled-hd128", "short-set", "split-kv"])
+def test_attn_split_extreme_scores(shape, scale):
+    """Scores far beyond exp's f32 range (scale 30 on N(0,1) data reaches several hundred, in
+    log2 units): the running reference must keep every exponential finite."""
+    B, T, ctx, nh, nkv, hd = shape
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=int(scale) + T, scale=scale)
+    ref = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, nh, nkv, hd, scale, False)
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
+    out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+    dg.dg_attn_split_gqa(dev(c.q), dev(c.kc), dev(c.vc), dev(c.k), dev(c.v), out, B, T, ctx, nh,
+                         nkv, hd, scale, 0, ws, nbytes)
+    got = host(out)
+    # At these score magnitudes f32 rounding of the scores alone moves an output by more than
+    # the 2e-4 bar (the oracle measures 2.4e-4 from float64 at scale 30), so both sides are
+    # held to float64: the GPU may be at most twice as far from it as the oracle is.
+    exact = _attn_f64(c, scale)
+    e_oracle = float(np.max(np.abs(ref - exact)))
+    e_gpu = float(np.max(np.abs(got - exact)))
+    assert np.all(np.isfinite(got))
+    assert e_gpu <= max(2e-4, 2.0 * e_oracle), "gpu %.2e vs oracle %.2e from float64" % (e_gpu, e_oracle)
+    assert_parity(got, ref, "extreme scale %g %s" % (scale, shape), atol=2e-4 + 2.0 * e_oracle)
+
+
+def _attn_f64(c, scale):
+    """Split-GQA attention in float64 with numpy (a full-row softmax), for the extreme tests."""
+    B, T, ctx, nh, nkv, hd = c.B, c.T, c.ctx, c.nh, c.nkv, c.hd
+    G = nh // nkv
+    out = np.zeros((B, T, nh, hd))
+    for b in range(B):
+        kparts = [c.k[b].reshape(T, nkv, hd)]
+        vparts = [c.v[b].reshape(T, nkv, hd)]
+        if ctx > 0:
+            kparts.insert(0, c.kc[b].transpose(1, 0, 2))
+            vparts.insert(0, c.vc[b].transpose(1, 0, 2))
+        K = np.concatenate(kparts, 0).astype(np.float64)
+        V = np.concatenate(vparts, 0).astype(np.float64)
+        q = c.q[b].reshape(T, nh, hd).astype(np.float64)
+        for h in range(nh):
+            s = scale * q[:, h, :] @ K[:, h // G, :].T
+            s -= s.max(1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(1, keepdims=True)
+            out[b, :, h, :] = p @ V[:, h // G, :]
+    return out.reshape(B, T, nh * hd)
+
+
+def test_attn_split_scores_rising_along_the_keys():
+    """Keys whose scores climb tile after tile (every key is the previous one scaled up), so
+    the softmax reference has to move again and again and every earlier partial sum is
+    rescaled."""
+    B, T, ctx, nh, nkv, hd = 1, 32, 2000, 2, 1, 64
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((B, T, nh * hd)).astype(np.float32)
+    base = rng.standard_normal(hd).astype(np.float32)
+    ramp = np.linspace(0.0, 12.0, ctx + T, dtype=np.float32)          # score grows ~linearly
+    keys = (ramp[:, None] * base[None, :] + 0.05 * rng.standard_normal((ctx + T, hd))).astype(np.float32)
+    q[:] = np.tile(base, nh)[None, None, :] + 0.1 * q
+    kc = keys[:ctx][None, None].copy()
+    k = keys[ctx:][None].reshape(B, T, nkv * hd).copy()
+    vc = rng.standard_normal((B, nkv, ctx, hd)).astype(np.float32)
+    v = rng.standard_normal((B, T, nkv * hd)).astype(np.float32)
+    ref = oracle.attn_split_gqa(q, kc, vc, k, v, nh, nkv, hd, 1.0, False)
+    for use_ws in (False, True):
+        ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd) if use_ws else (None, 0)
+        out = torch.full((B, T, nh * hd), float("nan"), device="cuda")
+        dg.dg_attn_split_gqa(dev(q), dev(kc), dev(vc), dev(k), dev(v), out, B, T, ctx, nh, nkv,
+                             hd, 1.0, 0, ws, nbytes)
+        assert_parity(host(out), ref, "rising scores ws=%d" % nbytes)
