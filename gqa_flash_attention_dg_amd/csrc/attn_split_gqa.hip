@@ -300,30 +300,42 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     constexpr int R = KT::kRowsPerLoad;
     const int pos = lane % KT::kChunks, rsub = lane / KT::kChunks;
     const unsigned rstride_c = (unsigned)hd * kEsz, rstride_v = (unsigned)cstride * kEsz;
+    // Each issuing wavefront fills one part of the stage -- K0, V0, K1 or V1, part = pair --
+    // with all kLoadsPerTile wave-wide loads of that tile, so which address form applies is
+    // decided once per stage, outside the loads.
+    static_assert(kLoadsPerWave == KT::kLoadsPerTile, "one tile part per issuing wavefront");
+    const int ld_tile = pair >> 1, ld_isv = pair & 1;
+    const char* cache_base = ld_isv ? vcb : kcb;
+    const char* canvas_base = ld_isv ? vb : kb;
+    const int last_chunk = hd * kEsz / 16 - 1;   // kPad: chunks past it repeat it
     auto issue_stage = [&](int st, int buf) {
+        const int j0 = st * kStage + ld_tile * dgk::kKeys;
+        char* dst = tile_ptr(buf, ld_tile, ld_isv);
+        const bool in_cache = j0 + dgk::kKeys <= a.ctx, in_canvas = j0 >= a.ctx;
+        if ((in_cache || in_canvas) && j0 + dgk::kKeys <= kend) {   // one side of the seam
+            const char* b = in_cache ? cache_base + (size_t)j0 * rstride_c
+                                     : canvas_base + (size_t)(j0 - a.ctx) * rstride_v;
+            const unsigned rs = in_cache ? rstride_c : rstride_v;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerWave; ++i) {
-            const int L = pair * kLoadsPerWave + i;
-            const int part = L / KT::kLoadsPerTile;  // K0, V0, K1, V1
-            const int ld = L % KT::kLoadsPerTile;
-            const int tile = part >> 1, isv = part & 1;
-            const int trow = ld * R + rsub;           // tile row of this lane's chunk
-            int chunk = isv ? pos : (pos ^ (trow % KT::kChunks));
-            if (kPad) chunk = min(chunk, hd * kEsz / 16 - 1);
-            const unsigned coff = 16u * chunk;
-            const int j0 = st * kStage + tile * dgk::kKeys;
-            char* dst = tile_ptr(buf, tile, isv) + ld * 1024;
-            const char* p;
-            if (j0 + dgk::kKeys <= a.ctx && j0 + dgk::kKeys <= kend) {
-                p = (isv ? vcb : kcb) + (size_t)j0 * rstride_c + ((unsigned)trow * rstride_c + coff);
-            } else if (j0 >= a.ctx && j0 + dgk::kKeys <= kend) {
-                p = (isv ? vb : kb) + (size_t)(j0 - a.ctx) * rstride_v + ((unsigned)trow * rstride_v + coff);
-            } else {
-                const int j = min(j0 + trow, kend - 1);
-                p = (j < a.ctx ? (isv ? vcb : kcb) + (size_t)j * rstride_c
-                               : (isv ? vb : kb) + (size_t)(j - a.ctx) * rstride_v) + coff;
+            for (int i = 0; i < kLoadsPerWave; ++i) {
+                const int trow = i * R + rsub;
+                int chunk = ld_isv ? pos : (pos ^ (trow % KT::kChunks));
+                if (kPad) chunk = min(chunk, last_chunk);
+                __builtin_amdgcn_global_load_lds(b + ((unsigned)trow * rs + 16u * chunk),
+                                                 (dgk::lds_void*)(dst + i * 1024), 16, 0, 0);
             }
-            __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)dst, 16, 0, 0);
+        } else {                           // straddles the seam or the end: per-row addresses
+#pragma unroll
+            for (int i = 0; i < kLoadsPerWave; ++i) {
+                const int trow = i * R + rsub;
+                const int j = min(j0 + trow, kend - 1);
+                int chunk = ld_isv ? pos : (pos ^ (trow % KT::kChunks));
+                if (kPad) chunk = min(chunk, last_chunk);
+                const char* p = (j < a.ctx ? cache_base + (size_t)j * rstride_c
+                                           : canvas_base + (size_t)(j - a.ctx) * rstride_v) +
+                                16u * chunk;
+                __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)(dst + i * 1024), 16, 0, 0);
+            }
         }
     };
 
