@@ -11,7 +11,9 @@ A step is one pass of the hot path over one batch of synthetic input resident in
   sam_windowed: the same over the SAM windowed block's 25 windows of 14x14 tokens.
 The default workload is the long-cache split-GQA canvas step (4 canvases, T=256, ctx=8192,
 nh=32, nkv=8, hd=128).  W untimed steps, then K steps timed with HIP events on the stream the
-kernels run on (torch's current stream), bracketed by device synchronisation.  The dominant
+kernels run on (torch's current stream), bracketed by device synchronisation.  By default W
+covers about half a second (the GPU raises its clock over the first tens of milliseconds of
+sustained load) and K about a quarter second; both are reported.  The dominant
 kernel's launches are timed with their own events inside the timed region.
 
 Prints ONE JSON line: metric/value/unit (algorithmic TFLOP/s of the step, or GB/s for the
@@ -363,8 +365,11 @@ def make_work(name, norm_mode="in_attention", kv16=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: about 0.25 s of steps, at least 20)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before them (default: about 0.5 s of steps, at least 3, "
+                         "so the timed steps run at the clock the GPU holds under sustained load)")
     ap.add_argument("--workload", default="long_cache",
                     choices=["long_cache", "dg_canvas", "dg_layers", "tiny", "depformer",
                              "sam_relpos", "sam_windowed", "hbm_copy"])
@@ -401,7 +406,7 @@ def main():
         if not isinstance(work, SplitWork):
             raise SystemExit("--graph applies to the split-GQA workloads")
         from gqa_flash_attention_dg_amd.canvas import CanvasGraph
-        if args.steps % args.graph:
+        if args.steps is not None and args.steps % args.graph:
             raise SystemExit("--steps must be a multiple of --graph")
         cg = CanvasGraph(work.blk, work.q, work.k, work.v, work.out, steps=args.graph)
         work.graph = args.graph
@@ -421,7 +426,28 @@ def main():
             steps_run[0] += 1
         work.step = graph_step
 
-    for _ in range(args.warmup):
+    # Default step counts from the wall time of a few probe steps (which count as warmup; the
+    # first one, which loads the code objects, is not timed).
+    nprobe, est = 0, None
+    if args.warmup is None or args.steps is None:
+        nprobe = 4 if args.warmup is None else min(4, args.warmup)
+        if nprobe >= 2:
+            work.step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(nprobe - 1):
+                work.step()
+            torch.cuda.synchronize()
+            est = max((time.perf_counter() - t0) / (nprobe - 1), 1e-6)
+        if args.warmup is None:
+            args.warmup = max(nprobe, min(5000, int(0.5 / est)))
+        elif nprobe < 2:
+            nprobe = 0
+        if args.steps is None:
+            args.steps = max(20, min(2000, int(0.25 / est))) if est else 20
+            if args.graph:
+                args.steps = -(-args.steps // args.graph) * args.graph
+    for _ in range(args.warmup - nprobe):
         work.step()
     torch.cuda.synchronize()
     if args.graph:
