@@ -279,9 +279,14 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         const int last = min(nq - 1, qb * kBlockQ + kBlockQ - 1) / a.G;
         kend = min(S, a.ctx + last + 1);
     }
-    const int nstage = (kend + kStage - 1) / kStage;
-    const int st_begin = (int)((long long)split * nstage / a.nsplit);
-    const int st_end = (int)((long long)(split + 1) * nstage / a.nsplit);
+    // Splits divide the key range in whole kKeys-key tiles, so the splits of a launch differ by
+    // at most one tile (stages take two tiles; a split's last stage may hold only one).
+    const int ntile = (kend + dgk::kKeys - 1) / dgk::kKeys;
+    const int tile_begin = (int)((long long)split * ntile / a.nsplit);
+    const int tile_end = (int)((long long)(split + 1) * ntile / a.nsplit);
+    const int kbeg = tile_begin * dgk::kKeys;   // this split's keys: [kbeg, kend)
+    kend = min(kend, tile_end * dgk::kKeys);
+    const int nst = (tile_end - tile_begin + 1) / 2;
 
     constexpr int kEsz = KT::kEsz;
     const char* kcb = reinterpret_cast<const char*>(a.kc) + (size_t)bk * a.ctx * hd * kEsz;
@@ -309,7 +314,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const char* canvas_base = ld_isv ? vb : kb;
     const int last_chunk = hd * kEsz / 16 - 1;   // kPad: chunks past it repeat it
     auto issue_stage = [&](int st, int buf) {
-        const int j0 = st * kStage + ld_tile * dgk::kKeys;
+        const int j0 = kbeg + st * kStage + ld_tile * dgk::kKeys;
+        if (j0 >= kend) return;              // the split's last stage holds one tile
         char* dst = tile_ptr(buf, ld_tile, ld_isv);
         const bool in_cache = j0 + dgk::kKeys <= a.ctx, in_canvas = j0 >= a.ctx;
         if ((in_cache || in_canvas) && j0 + dgk::kKeys <= kend) {   // one side of the seam
@@ -340,7 +346,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     };
 
     // The first stage's loads go out before the queries are fetched, so the two overlap.
-    if (!hi && st_begin < st_end) issue_stage(st_begin, 0);
+    if (!hi && nst > 0) issue_stage(0, 0);
     float qreg[HD / 2];
     if constexpr (kNormQ) {
         float* qs = smem + 2 * 2 * KT::kBytes / 4;
@@ -357,12 +363,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    for (int st = st_begin; st < st_end; ++st) {
-        const int buf = (st - st_begin) & 1;
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
         __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
-        if (!hi && st + 1 < st_end) issue_stage(st + 1, buf ^ 1);
-        const int t0 = st * kStage + hi * dgk::kKeys;
+        if (!hi && st + 1 < nst) issue_stage(st + 1, buf ^ 1);
+        const int t0 = kbeg + st * kStage + hi * dgk::kKeys;
         if (pair_active && t0 < kend) {
             f32x16 s;
             if constexpr (kKV == 0) {
