@@ -242,7 +242,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     // reuses the space at the end.
     constexpr int kStageFloats = 2 * 2 * 2 * KT::kBytes / 4;
     constexpr int kQStageEnd = 2 * 2 * KT::kBytes / 4 + kBlockQ * kQStride<HD>;
-    constexpr int kMergeFloats = kPairs * 64 * (TL::kGroups * 16 + 2);
+    constexpr int kMergeFloats = kPairs * 64 * (TL::kGroups * 16 + 2) + 2 * kBlockQ;  // + row indices
     constexpr int kA = kNormQ && kQStageEnd > kStageFloats ? kQStageEnd : kStageFloats;
     constexpr int kSmemFloats = kA > kMergeFloats ? kA : kMergeFloats;
     __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
@@ -400,16 +400,34 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     __syncthreads();  // every wave is done with the stage buffers; reuse them for the merge
     dgk::pair_merge<HD>(smem, pair, hi, pair_active, lane, m, lsum, o);
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (hi || !valid) return;
-    if (a.nsplit == 1) {
-        dgk::store_row<HD>(a.out + gq * hd, 1.0f / ltot, o, half, hd);
-    } else {
-        dgk::store_row<HD>(a.ws + ((size_t)split * a.nqtot + gq) * hd, 1.0f, o, half, hd);
-        if (half == 0) {
+    // The even wavefront of each pair restages its 32 merged rows row-major over its own merge
+    // scratch (the same LDS span: 64 * (HD/2 + 2) = 32 * (HD + 4) floats, read only by this
+    // wavefront), with the rows' global query indices beside the block.  The workgroup then
+    // writes the block out with 16 contiguous bytes per lane, whole rows per half-wavefront.
+    constexpr int kOStride = HD + 4;
+    static_assert(64 * (TL::kGroups * 16 + 2) == dgk::kQuery * kOStride, "row block overlays the merge scratch");
+    long long* rowg = reinterpret_cast<long long*>(smem + kPairs * dgk::kQuery * kOStride);
+    if (!hi) {
+        dgk::stage_row<HD>(smem + pair * dgk::kQuery * kOStride, l32,
+                           a.nsplit == 1 && valid ? 1.0f / ltot : 1.0f, o, half);
+        if (half == 0) rowg[pair * dgk::kQuery + l32] = valid ? (long long)gq : -1;
+        if (a.nsplit > 1 && valid && half == 0) {
             float* wm = a.ws + (size_t)a.nsplit * a.nqtot * hd;
             wm[(size_t)split * a.nqtot + gq] = m;
             wm[(size_t)(a.nsplit + split) * a.nqtot + gq] = ltot;
         }
+    }
+    __syncthreads();
+    float* obase = a.nsplit == 1 ? a.out : a.ws + (size_t)split * a.nqtot * hd;
+    constexpr int kChunksO = HD / 4;                       // 16-byte chunks per row
+    constexpr int kRowsPerPass = kWaves * 64 / kChunksO;
+#pragma unroll
+    for (int r0 = 0; r0 < kBlockQ; r0 += kRowsPerPass) {
+        const int rloc = r0 + tid / kChunksO, c = tid % kChunksO;
+        const long long g = rowg[rloc];
+        if (g < 0 || (kPad && 4 * c >= hd)) continue;
+        *reinterpret_cast<float4*>(obase + (size_t)g * hd + 4 * c) =
+            *reinterpret_cast<const float4*>(smem + rloc * kOStride + 4 * c);
     }
 }
 

@@ -211,6 +211,25 @@ __device__ inline void store_row(float* __restrict__ orow, float scale,
     }
 }
 
+// Writes o * scale for the lane's query as row l32 of a row-major block in LDS (`rows`, row
+// stride HD + 4 floats: consecutive rows start 4 banks apart, so the 16-byte writes of a
+// wavefront do not collide).
+template <int HD>
+__device__ inline void stage_row(float* __restrict__ rows, int l32, float scale,
+                                 const f32x16 (&o)[Tile<HD>::kGroups], int half) {
+    float* dst = rows + l32 * (HD + 4);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float* d = dst + out_elem<HD>(0, r, half);
+        if constexpr (HD == 128) {
+            *reinterpret_cast<float4*>(d) =
+                make_float4(o[0][r] * scale, o[1][r] * scale, o[2][r] * scale, o[3][r] * scale);
+        } else {
+            *reinterpret_cast<float2*>(d) = make_float2(o[0][r] * scale, o[1][r] * scale);
+        }
+    }
+}
+
 // Merges the softmax states of the two wavefronts of a pair (same 32 queries, disjoint keys):
 // the odd-tile wavefront (hi) hands (o, m, lsum) to the even-tile one through LDS scratch
 // `smem` (at least 4 * 64 * (hd/2 + 2) floats, not in use by anyone).  Every thread of the
