@@ -60,7 +60,8 @@ struct NormArgs {
 
 // kHD: the head dim when it is 128 or 64 (no per-lane guards), 0 for any other hd <= 128.  Lanes
 // past hd read an element that exists (element 0 of the row) and discard it by selection, so
-// the loads are not turned into divergent branches.
+// the loads are not turned into divergent branches.  The row, its weights and its cos|sin
+// entries are all loaded before any arithmetic: the wavefront waits for memory once.
 template <int kHD>
 __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restrict__ w,
                                     const float* __restrict__ cr, int hd_rt, unsigned flags,
@@ -69,11 +70,20 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = kHD ? true : e0 < hd;
     const bool v1 = kHD == 128 ? true : (kHD == 64 ? false : e1 < hd);
-    const float x0 = xr[v0 ? e0 : 0];
-    const float x1 = kHD == 64 ? 0.0f : xr[v1 ? e1 : 0];
+    const int i0 = v0 ? e0 : 0, i1 = v1 ? e1 : 0;
+    const bool norm = !(flags & DG_NORM_SKIP);
+    const bool weighted = norm && (flags & DG_NORM_WEIGHTED);
+    const bool rope = (flags & DG_NORM_ROPE) != 0;
+    const float x0 = xr[i0];
+    const float x1 = kHD == 64 ? 0.0f : xr[i1];
+    const float w0 = weighted ? w[i0] : 1.0f;
+    const float w1 = weighted && kHD != 64 ? w[i1] : 1.0f;
+    const float c0 = rope ? cr[i0] : 0.0f, s0v = rope ? cr[hd + i0] : 0.0f;
+    const float c1 = rope && kHD != 64 ? cr[i1] : 0.0f;
+    const float s1v = rope && kHD != 64 ? cr[hd + i1] : 0.0f;
     float y0 = v0 ? x0 : 0.0f;
     float y1 = v1 ? x1 : 0.0f;
-    if (!(flags & DG_NORM_SKIP)) {
+    if (norm) {
         const float ss = wave_sum(y0 * y0 + y1 * y1);
         const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
         y0 *= inv;
@@ -82,14 +92,12 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
             if (v0) vr[e0] = y0;
             if (v1) vr[e1] = y1;
         }
-        if (flags & DG_NORM_WEIGHTED) {
-            const float w0 = w[v0 ? e0 : 0];
-            const float w1 = kHD == 64 ? 0.0f : w[v1 ? e1 : 0];
+        if (weighted) {
             y0 *= w0;
             y1 *= w1;
         }
     }
-    if (flags & DG_NORM_ROPE) {
+    if (rope) {
         const int half = hd >> 1;
         // partner of element e is e + half (e < half, enters negated) or e - half
         const int p0 = e0 < half ? e0 + half : e0 - half;
@@ -108,9 +116,6 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
             q0 = p0 >= 64 ? b0 : a0;
             q1 = p1 >= 64 ? b1 : a1;
         }
-        const float c0 = cr[v0 ? e0 : 0], s0v = cr[hd + (v0 ? e0 : 0)];
-        const float c1 = kHD == 64 ? 0.0f : cr[v1 ? e1 : 0];
-        const float s1v = kHD == 64 ? 0.0f : cr[hd + (v1 ? e1 : 0)];
         const float rot0 = e0 < half ? -q0 : q0;
         const float rot1 = e1 < half ? -q1 : q1;
         if (v0) xr[e0] = y0 * c0 + rot0 * s0v;
@@ -126,10 +131,19 @@ template <int kHD>
 __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
     long long u = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    int s = 0;
-    while (s < a.nseg && u >= a.seg[s].rows) u -= a.seg[s++].rows;  // wave-uniform
-    if (s >= a.nseg) return;
-    const NormSeg& g = a.seg[s];
+    // The segment is found with constant indices into the arguments, so its fields come from
+    // scalar loads (a computed index would read them through per-lane memory loads).
+    NormSeg g = a.seg[0];
+    if (u >= g.rows) {
+        u -= g.rows;
+        if (a.nseg < 2) return;
+        g = a.seg[1];
+        if (u >= g.rows) {
+            u -= g.rows;
+            if (a.nseg < 3 || u >= a.seg[2].rows) return;
+            g = a.seg[2];
+        }
+    }
     const int t = (int)((u / g.heads) % a.T);
     const float* cr = (g.flags & DG_NORM_ROPE) ? a.cs + (size_t)t * 2 * a.hd : nullptr;
     headnorm_row<kHD>(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane,
