@@ -26,17 +26,27 @@ namespace {
 using dgk::f32x16;
 constexpr int HD = 64;
 constexpr int kWaves = 8;
-// A workgroup of 8 wavefronts is kQGroups = 8 / kParts query groups of 32 times kParts
-// wavefronts per group, each taking every kParts-th key tile: 2 x 4 for large grids (64
-// queries per workgroup, 4-way key split), 4 x 2 for small ones (128 queries, 2-way), where
-// fewer, longer-running workgroups amortise their prologue and merge.
-template <int kParts>
+// A workgroup of kWavesT wavefronts is kQGroups = kWavesT / kParts query groups of 32 times
+// kParts wavefronts per group, each taking every kParts-th key tile:
+//  * 2 x 4 for large grids (8 wavefronts, 64 queries, 4-way key split);
+//  * 4 x 2 for small ones (8 wavefronts, 128 queries, 2-way), where fewer, longer-running
+//    workgroups amortise their prologue and merge;
+//  * 4 x 1 for small grids of at most 16 rows of at most 32, such as 14x14 windows (4
+//    wavefronts, 128 queries, no key split; row tiles only, as every wavefront takes every
+//    tile): with its height-bias table cut to 16 rows a workgroup needs 40 KiB
+//    of LDS, so three fit on a CU beside each other and the windows' workgroups run in one
+//    round, each CU's matrix pipes kept busy by whichever workgroup is not waiting.  Used
+//    when the launch has more workgroups than the GPU has CUs.
+template <int kParts, int kWavesT = 8>
 struct RelShape {
-    static constexpr int kQGroups = 8 / kParts;
+    static constexpr int kQGroups = kWavesT / kParts;
     static constexpr int kBlockQ = kQGroups * dgk::kQuery;
+    static constexpr int kTabRows = kWavesT == 4 ? 16 : 64;   // height-bias table rows (>= gh)
 };
 constexpr int kMaxGrid = 64;                  // gh, gw <= 64
-constexpr int kSmallGrid = 512;               // grids of at most this many tokens use 4 x 2
+constexpr int kSmallGrid = 512;               // grids of at most this many tokens use 4 x 2 (or 4 x 1)
+constexpr int kSmallRows = 16;                // ... and 4 x 1 when gh is at most this
+constexpr int kCUs = 256;                     // compute units of the target GPU
 
 struct RelArgs {
     const float* qkv;  // [nwin][n][3W]
@@ -186,14 +196,16 @@ __host__ __device__ inline Tiling make_tiling(int gh, int gw) {
 
 // kFull: every tile holds 32 keys (no padding slots, no short last tile); kOneShift: the height
 // bias takes one MFMA step (at most two grid rows per tile).
-template <bool kFull, bool kOneShift, int kParts>
-__global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
+template <bool kFull, bool kOneShift, int kParts, int kWavesT>
+__global__ void __launch_bounds__(64 * kWavesT)
+    __attribute__((amdgpu_waves_per_eu(kWavesT == 4 ? 3 : 1))) relpos_flash_kernel(RelArgs a) {
     using TL = dgk::Tile<HD>;
-    constexpr int kQGroups = RelShape<kParts>::kQGroups;
-    constexpr int kBlockQ = RelShape<kParts>::kBlockQ;
+    constexpr int kQGroups = RelShape<kParts, kWavesT>::kQGroups;
+    constexpr int kBlockQ = RelShape<kParts, kWavesT>::kBlockQ;
+    constexpr int kTabRows = RelShape<kParts, kWavesT>::kTabRows;
     // staging: [buffer][tile][K, V] and bias tables [group][ky][query] (dh)
     __shared__ __attribute__((aligned(16))) float smem[2 * kParts * 2 * TL::kFloats];
-    __shared__ float tab[kQGroups * kMaxGrid * dgk::kQuery];
+    __shared__ float tab[kQGroups * kTabRows * dgk::kQuery];
     auto tile_ptr = [&](int buf, int tile, int isv) {
         return smem + ((buf * kParts + tile) * 2 + isv) * TL::kFloats;
     };
@@ -205,7 +217,8 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    // wavefronts w and w+4 share a SIMD: the same group, parts p and p + kParts/2
+    // in the 8-wavefront shapes wavefronts w and w+4 share a SIMD: the same group, parts p and
+    // p + kParts/2
     const int grp = wave & (kQGroups - 1), part = wave / kQGroups;
     const size_t rs = (size_t)3 * a.W;  // qkv row stride (floats)
     const Tiling tl = make_tiling(a.gh, a.gw);
@@ -217,7 +230,7 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     const float* qrow = qkvw + (size_t)(valid ? qi : 0) * rs + head * HD;
     const bool active = qfirst < a.n;
     const bool bias = a.rh != nullptr;
-    float* dh_tab = tab + grp * kMaxGrid * dgk::kQuery;   // [ky][query]
+    float* dh_tab = tab + grp * kTabRows * dgk::kQuery;   // [ky][query]
 
     // Where the lane's 16 score slots sit in its tiles (the same in every tile of this wave).
     const int parity = part & 1;                           // half-row tiles: which half
@@ -278,8 +291,9 @@ __global__ void __launch_bounds__(512) relpos_flash_kernel(RelArgs a) {
     auto tile_start = [&](int t) { return (t >> a.tsh) * a.ta + (t & a.tmsk) * a.tb; };
     auto tile_len = [&](int t) { return min(a.tl0 + (t & a.tmsk) * a.td, a.n - tile_start(t)); };
 
-    // Loads: the four wavefronts with part < 2 (one per SIMD) issue each stage's 64 wave-wide
-    // loads -- K and V of 4 tiles -- while their SIMD partners keep the matrix pipe busy.  A
+    // Loads: the four wavefronts with part < 2 (one per SIMD) issue each stage's wave-wide
+    // loads -- K and V of kParts tiles -- while their SIMD partners keep the matrix pipe busy
+    // (in the 4 x 1 shape every wavefront issues, and the partners are other workgroups').  A
     // full 32-key tile is a scalar row base plus loop-invariant lane offsets; a shorter one
     // repeats its last key in the padding rows.
     constexpr int kLoadsPerWave = 2 * kParts * TL::kLoadsPerTile / 4;
@@ -377,6 +391,14 @@ extern "C" size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, in
 
 namespace {
 
+template <int kParts, int kWavesT>
+auto pick_flash(bool full, bool one) {
+    return full ? (one ? relpos_flash_kernel<true, true, kParts, kWavesT>
+                       : relpos_flash_kernel<true, false, kParts, kWavesT>)
+                : (one ? relpos_flash_kernel<false, true, kParts, kWavesT>
+                       : relpos_flash_kernel<false, false, kParts, kWavesT>);
+}
+
 int relpos_call(const char* fn, const float* qkv, const float* rh, const float* rw, float* out,
                 int nwin, int gh, int gw, int heads, int hd, float scale, void* workspace,
                 size_t workspace_bytes, void* stream) {
@@ -416,10 +438,16 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(out) |
          reinterpret_cast<uintptr_t>(rh) | reinterpret_cast<uintptr_t>(rw)) & 15)
         return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
-    const bool small = n <= kSmallGrid;   // 4 x 2 workgroups for small grids
+    const bool small = n <= kSmallGrid;              // 4 x 2 workgroups for small grids
+    static_assert(RelShape<1, 4>::kBlockQ == RelShape<2>::kBlockQ, "small shapes share a block");
     const long long kbq = small ? RelShape<2>::kBlockQ : RelShape<4>::kBlockQ;
     const long long qblocks = (n + kbq - 1) / kbq;
     const long long nblocks = qblocks * heads * nwin;
+    // 4 x 1 for small grids of few rows cut into row tiles (gw <= 32; a wavefront of that shape
+    // takes every tile, and the half-row tiling needs each wavefront to see one half only),
+    // when there are more workgroups than CUs: with fewer, the 4 x 2 shape's key split halves
+    // each workgroup's time.
+    const bool rows16 = small && gh <= kSmallRows && gw <= 32 && nblocks > kCUs;
     if (nblocks > 0x7fffffffLL || (long long)nwin * heads * (gh + gw) > 0x1fffffffLL)
         return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     RelArgs a;
@@ -450,11 +478,9 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     }
     const bool full = tl.half_rows ? gw == 64 : (tl.kpt == dgk::kKeys && gh % tl.rpt == 0);
     const bool one = tl.nshift == 1;
-    auto* kern = small ? (full ? (one ? relpos_flash_kernel<true, true, 2> : relpos_flash_kernel<true, false, 2>)
-                               : (one ? relpos_flash_kernel<false, true, 2> : relpos_flash_kernel<false, false, 2>))
-                       : (full ? (one ? relpos_flash_kernel<true, true, 4> : relpos_flash_kernel<true, false, 4>)
-                               : (one ? relpos_flash_kernel<false, true, 4> : relpos_flash_kernel<false, false, 4>));
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.nblocks), dim3(512), 0, s, a);
+    auto* kern = rows16 ? pick_flash<1, 4>(full, one) : small ? pick_flash<2, 8>(full, one)
+                                                             : pick_flash<4, 8>(full, one);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.nblocks), dim3(rows16 ? 256 : 512), 0, s, a);
     return dg::launch_status(fn);
 }
 

@@ -341,7 +341,10 @@ def test_dg_layer_stack_every_element(norm_mode):
                                               # several rows, one-column grids
                                               (6, 33, 2, True), (5, 47, 1, True), (3, 63, 2, True),
                                               (7, 17, 1, True), (9, 10, 2, True), (11, 3, 1, True),
-                                              (20, 2, 1, True), (33, 1, 1, True), (13, 14, 2, False)])
+                                              (20, 2, 1, True), (33, 1, 1, True), (13, 14, 2, False),
+                                              # the 4-wavefront shape's limits (512 tokens, 16
+                                              # rows of at most 32) and one row past them
+                                              (16, 32, 2, True), (17, 30, 1, True)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
 def test_relpos_small(gh, gw, heads, bias, use_ws):
     c = synth.relpos_case(gh, gw, heads, 64, seed=gh * 100 + gw, bias=bias, table_std=0.3)
@@ -374,7 +377,10 @@ def oracle_windows(c):
 @pytest.mark.parametrize("nwin,gh,gw,heads,bias", [(3, 5, 7, 2, True), (25, 14, 14, 2, True),
                                                    (4, 8, 8, 3, True), (2, 3, 32, 1, True),
                                                    (5, 1, 1, 1, True), (3, 14, 14, 2, False),
-                                                   (2, 12, 64, 1, True), (3, 9, 47, 1, True)])
+                                                   (2, 12, 64, 1, True), (3, 9, 47, 1, True),
+                                                   # more workgroups than CUs: the 4-wavefront
+                                                   # shape, on ragged grids
+                                                   (130, 5, 7, 2, True), (90, 11, 13, 3, False)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
 def test_relpos_windows_small(nwin, gh, gw, heads, bias, use_ws):
     c = synth.windows_case(nwin, gh, gw, heads, 64, seed=nwin * 1000 + gh * 10 + gw, bias=bias,
