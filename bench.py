@@ -41,11 +41,38 @@ CSRC = os.path.join(ROOT, "gqa_flash_attention_dg_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed (string and character
+    literals kept as written), so that an edit of comments alone keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout excluded): the profiles' traffic
+    records are used only while it matches the one they were measured on."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

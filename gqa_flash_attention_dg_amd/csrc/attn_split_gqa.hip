@@ -14,18 +14,20 @@
 // pair hold the same 32 queries and take alternate 32-key tiles, so the block walks the keys in
 // stages of 64.  Each stage's K and V tiles are fetched once into LDS for all 128 queries with
 // direct global->LDS loads, double-buffered so the next stage streams in while this one is
-// computed; the cache/canvas seam is resolved per key row when the load addresses are formed.
+// computed; a tile lying wholly in the cache or wholly in the canvas is addressed from a scalar
+// base, and only a tile across the seam (or the end of the keys) forms per-row addresses.
 // Scores and the value product run on f32 MFMA (flash_core.hpp).  At the end each pair merges
-// its two partial softmax states through LDS.
+// its two partial softmax states through LDS, and the workgroup writes its rows out whole.
 //
 // dg_attn_split_gqa_qnorm takes the raw q projection instead and applies the q dispatch of
-// DG_HEADNORM_ROPE (RMSNorm, weight, NeoX rope) to each query vector in registers while loading
-// it, so q never makes the extra round trip through HBM; q itself is left unchanged.
+// DG_HEADNORM_ROPE (RMSNorm, weight, NeoX rope) to the workgroup's query vectors as it stages
+// them in LDS before the first stage, so q never makes the extra round trip through HBM; q
+// itself is left unchanged.
 //
-// Shapes with too few workgroups to fill the GPU also split the key range across workgroups
-// ("split-KV"): each writes an unnormalised partial (max, denominator, output) to the caller's
-// workspace and a second kernel merges them.  Workgroups that share K/V are placed on the same
-// XCD so its L2 serves the re-reads.
+// Shapes with too few workgroups to fill the GPU also split the key range, in whole 32-key
+// tiles, across workgroups ("split-KV"): each writes an unnormalised partial (max,
+// denominator, output) to the caller's workspace and a second kernel merges them.  Workgroups
+// that share K/V are placed on the same XCD so its L2 serves the re-reads.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
