@@ -9,15 +9,16 @@
 // SAM blocks that the page's encoder cost model counts (25 windows of 14 x 14 tokens) are the
 // same attention run independently per window with shared tables: a batch of grids.
 //
-// With a workspace, relpos_bias_kernel first writes the hoisted bias rows (dh, dw: 64 floats
-// per (window, head, query) each, in log2 units), as the page's DHDW step does; without one,
+// With a workspace, a bias pass first writes the hoisted bias rows (dh: gh floats, dw: gw
+// floats per (window, head, query), in log2 units), as the page's DHDW step does; without one,
 // each attention workgroup forms the dot products of its own queries in a prologue.  The
-// attention is the f32-MFMA flash loop of flash_core.hpp.  A workgroup is 2 groups of 32
-// queries x 4 wavefronts; the 4 wavefronts of a group take every 4th 32-key tile (stages of
-// 128 keys, double-buffered direct global->LDS tiles) and merge their softmax states at the
-// end.  The bias enters each score through the MFMA accumulator's starting value where the
-// grid width allows (see relpos_flash_kernel).  64-query workgroups give 768 workgroups at the
-// 64x64-grid, 12-head shape: three full rounds on 256 CUs.
+// attention is the f32-MFMA flash loop of flash_core.hpp.  For large grids a workgroup is 2
+// groups of 32 queries x 4 wavefronts; the 4 wavefronts of a group take every 4th 32-key tile
+// (stages of 128 keys, double-buffered direct global->LDS tiles) and merge their softmax
+// states at the end.  Small grids use the shapes of RelShape.  The bias enters each score
+// through the MFMA accumulator's starting value (see relpos_flash_kernel).  64-query
+// workgroups give 768 workgroups at the 64x64-grid, 12-head shape: three full rounds on 256
+// CUs.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
