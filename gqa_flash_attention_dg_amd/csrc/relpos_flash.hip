@@ -205,7 +205,10 @@ __global__ void __launch_bounds__(64 * kWavesT)
     constexpr int kBlockQ = RelShape<kParts, kWavesT>::kBlockQ;
     constexpr int kTabRows = RelShape<kParts, kWavesT>::kTabRows;
     // staging: [buffer][tile][K, V] and bias tables [group][ky][query] (dh)
-    __shared__ __attribute__((aligned(16))) float smem[2 * kParts * 2 * TL::kFloats];
+    constexpr int kOStride = HD + 4;   // row stride of the output rows restaged at the end
+    constexpr int kStageFloats = 2 * kParts * 2 * TL::kFloats;
+    constexpr int kSmemFloats = kStageFloats > kBlockQ * kOStride ? kStageFloats : kBlockQ * kOStride;
+    __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
     __shared__ float tab[kQGroups * kTabRows * dgk::kQuery];
     auto tile_ptr = [&](int buf, int tile, int isv) {
         return smem + ((buf * kParts + tile) * 2 + isv) * TL::kFloats;
@@ -373,8 +376,22 @@ __global__ void __launch_bounds__(64 * kWavesT)
     __syncthreads();
     dgk::group_merge<HD>(smem, grp, part, kParts, active, lane, m, lsum, o);
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (part != 0 || !valid) return;
-    dgk::store_row<HD>(a.out + ((size_t)win * a.n + qi) * a.W + head * HD, 1.0f / ltot, o, half);
+    // The merged rows are restaged row-major in LDS (after every part-0 wavefront has read the
+    // merge scratch) and written with 16 contiguous bytes per lane: whole 256-byte rows rather
+    // than 8-byte pieces spread over 32 rows per instruction.
+    __syncthreads();
+    if (part == 0) dgk::stage_row<HD>(smem + grp * dgk::kQuery * kOStride, l32, valid ? 1.0f / ltot : 0.0f, o, half);
+    __syncthreads();
+    constexpr int kChunksO = HD / 4;
+    constexpr int kRowsPerPass = 64 * kWavesT / kChunksO;
+#pragma unroll
+    for (int r0 = 0; r0 < kBlockQ; r0 += kRowsPerPass) {
+        const int rloc = r0 + tid / kChunksO, c = tid % kChunksO;
+        const int q = qb * kBlockQ + rloc;
+        if (q < a.n)
+            *reinterpret_cast<float4*>(a.out + ((size_t)win * a.n + q) * a.W + head * HD + 4 * c) =
+                *reinterpret_cast<const float4*>(smem + rloc * kOStride + 4 * c);
+    }
 }
 
 }  // namespace
