@@ -129,10 +129,12 @@ class SplitWork:
         self.q, self.k, self.v = d(c.q), d(c.k), d(c.v)
         self.out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
         self.flops, self.attn_bytes, self.norm_bytes = split_counts(c, norm_mode)
-        if kv16:  # K/V read as 16-bit values; the per-step pack reads and writes canvas k, v
+        if kv16:  # K/V read as 16-bit values; the canvas twins are written by the one-launch
+            # norm (2 bytes per element) or by a pack pass (4 read + 2 written)
             kvn = c.B * c.T * c.nkv * c.hd
             self.attn_bytes -= 2 * (2 * kvn + 2 * c.B * c.nkv * c.ctx * c.hd)
-            self.norm_bytes += 2 * kvn * (4 + 2)
+            fused = norm_mode == "one_launch" and c.normed
+            self.norm_bytes += 2 * kvn * (2 if fused else 4 + 2)
         self.bound = "mfma" if self.flops / self.attn_bytes > 20 else "hbm"
 
     def config(self):
@@ -143,8 +145,11 @@ class SplitWork:
 
     def step_name(self):
         if getattr(self, "kv16", None):
-            return ("dg_qkv_headnorm_rope(q, k, v) + dg_pack_kv16(k), dg_pack_kv16(v) + "
-                    "dg_attn_split_gqa_kv16 (%s K/V)" % self.kv16)
+            if self.norm_mode == "one_launch" and getattr(self.c, "normed", True):
+                return ("dg_qkv_headnorm_rope_kv16(q, k, v -> k16, v16) + "
+                        "dg_attn_split_gqa_kv16 (%s K/V)" % self.kv16)
+            return ("norms as --norm %s + dg_pack_kv16(k), dg_pack_kv16(v) + "
+                    "dg_attn_split_gqa_kv16 (%s K/V)" % (self.norm_mode, self.kv16))
         if not getattr(self.c, "normed", True):
             return "dg_attn_split_gqa"
         return {"one_launch": "dg_qkv_headnorm_rope(q, k, v) + dg_attn_split_gqa",
@@ -153,14 +158,17 @@ class SplitWork:
 
     def step(self, ev=None):
         normed_q = self.c.normed and self.norm_mode == "in_attention"
-        if self.c.normed:
+        fused16 = self.kv16 and self.c.normed and self.norm_mode == "one_launch"
+        if fused16:   # one launch: the norms and the 16-bit twins of k and v
+            self.blk.norm_qkv_kv16(self.q, self.k, self.v)
+        elif self.c.normed:
             if self.norm_mode == "in_attention":
                 self.blk.norm_qkv(None, self.k, self.v)
             elif self.norm_mode == "one_launch":
                 self.blk.norm_qkv(self.q, self.k, self.v)
             else:
                 self.blk.norm(self.q, self.k, self.v)
-        if self.kv16:
+        if self.kv16 and not fused16:
             self.blk.pack_canvas(self.k, self.v)
         if ev:
             ev[0].record()

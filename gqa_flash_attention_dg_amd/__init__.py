@@ -21,6 +21,7 @@ DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
 DG_KV_F16, DG_KV_BF16 = 1, 2
 
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
+           "dg_qkv_headnorm_rope_kv16",
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
            "dg_attn_split_gqa_kv16",
            "relpos_flash_attn_workspace_size", "relpos_flash_attn",
@@ -51,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.dg_headnorm_rope.argtypes = [vp, vp, vp, I, I, I, I, U, F, vp]
         L.dg_qkv_headnorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, U, F, vp]
         L.dg_pack_kv16.argtypes = [vp, vp, Z, I, vp]
+        L.dg_qkv_headnorm_rope_kv16.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, U,
+                                                F, I, vp]
         L.dg_attn_split_gqa_kv16.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, I, vp,
                                              Z, vp]
         L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -65,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.relpos_flash_attn_windows_workspace_size.restype = Z
         L.relpos_flash_attn_windows.argtypes = [vp, vp, vp, vp, I, I, I, I, I, F, vp, Z, vp]
         for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
+                     "dg_qkv_headnorm_rope_kv16",
                      "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "dg_attn_split_gqa_kv16",
                      "relpos_flash_attn",
                      "relpos_flash_attn_windows"):
@@ -162,6 +166,22 @@ def dg_qkv_headnorm_rope(q, wq, k, wk, v, cs, batch: int, T: int, nh: int, nkv: 
         _ptr(k, "k", nk), _ptr(wk, "wk", hd if need_w and k is not None else 0),
         _ptr(v, "v", nk), _ptr(cs, "cs", T * 2 * hd if need_cs else 0),
         batch, T, nh, nkv, hd, flags, float(eps), _stream(stream)))
+
+
+def dg_qkv_headnorm_rope_kv16(q, wq, k, wk, v, cs, k16, v16, batch: int, T: int, nh: int,
+                              nkv: int, hd: int, flags: int, eps: float, kv_format: int,
+                              stream=None) -> None:
+    _nonneg(batch=batch, T=T, nh=nh, nkv=nkv, hd=hd)
+    need_w = (flags & DG_NORM_WEIGHTED) and not (flags & DG_NORM_SKIP)
+    need_cs = (flags & DG_NORM_ROPE) and (q is not None or k is not None)
+    nq, nk = batch * T * nh * hd, batch * T * nkv * hd
+    _check(lib().dg_qkv_headnorm_rope_kv16(
+        _ptr(q, "q", nq), _ptr(wq, "wq", hd if need_w and q is not None else 0),
+        _ptr(k, "k", nk), _ptr(wk, "wk", hd if need_w and k is not None else 0),
+        _ptr(v, "v", nk), _ptr(cs, "cs", T * 2 * hd if need_cs else 0),
+        _ptr16(k16, "k16", nk if k is not None else 0),
+        _ptr16(v16, "v16", nk if v is not None else 0),
+        batch, T, nh, nkv, hd, flags, float(eps), int(kv_format), _stream(stream)))
 
 
 def dg_pack_kv16(src, dst, n: int, format: int, stream=None) -> None:

@@ -24,7 +24,7 @@ import torch
 from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K,
                DG_NORM_WEIGHTED, dg_attn_split_gqa, dg_attn_split_gqa_kv16,
                dg_attn_split_gqa_qnorm, dg_attn_split_gqa_workspace_size, dg_headnorm_rope,
-               dg_pack_kv16, dg_qkv_headnorm_rope, dg_rope_table)
+               dg_pack_kv16, dg_qkv_headnorm_rope, dg_qkv_headnorm_rope_kv16, dg_rope_table)
 
 KV_FORMATS = {"f16": DG_KV_F16, "bf16": DG_KV_BF16}
 
@@ -50,8 +50,9 @@ class CanvasBlock:
     says.  k_eq_v: the layer has no v projection; each step's v buffer is written with the
     weightless norm of the raw k (its input contents are ignored).
     kv16: None (f32 K/V) or "f16" / "bf16": the cache is packed once into 16-bit twins here, each
-    step packs its normalised canvas k and v, and the attention widens them to f32 as it reads
-    them (the q norm then runs in the one-launch norm, not inside attention).
+    step's one-launch norm also writes 16-bit twins of its normalised canvas k and v (with
+    "separate" norms a pack pass writes them), and the attention widens them to f32 as it
+    reads them (the q norm then runs in the norm launch, not inside attention).
     """
 
     def __init__(self, B, T, ctx, nh, nkv, hd, kc=None, vc=None, wq=None, wk=None, *,
@@ -123,6 +124,12 @@ class CanvasBlock:
                                 DG_NORM_WEIGHTED | DG_NORM_ROPE, self.eps, self.scale,
                                 self.causal, self.ws, self.ws_bytes)
 
+    def norm_qkv_kv16(self, q, k, v):
+        """norm_qkv that also writes the 16-bit twins of the normalised k and v (kv16 blocks)."""
+        flags = DG_NORM_WEIGHTED | DG_NORM_ROPE | (DG_NORM_V_FROM_K if self.k_eq_v else 0)
+        dg_qkv_headnorm_rope_kv16(q, self.wq, k, self.wk, v, self.cs, self.k16, self.v16, self.B,
+                                  self.T, self.nh, self.nkv, self.hd, flags, self.eps, self.kv16)
+
     def pack_canvas(self, k, v):
         """16-bit twins of this step's normed canvas k and v (kv16 blocks)."""
         nk = self.B * self.T * self.nkv * self.hd
@@ -147,6 +154,10 @@ class CanvasBlock:
         if self.normed and self.norm_mode == "in_attention":
             self.norm_qkv(None, k, v)
             self.attend_qnorm(q, k, v, out)
+            return
+        if self.normed and self.norm_mode == "one_launch" and self.kv16:
+            self.norm_qkv_kv16(q, k, v)
+            self.attend_kv16(q, out)
             return
         if self.normed and self.norm_mode == "one_launch":
             self.norm_qkv(q, k, v)

@@ -5,20 +5,12 @@
 // before the unchanged f32 math.  This is that pack pass, for IEEE binary16 or bfloat16, both
 // rounded to nearest with ties to even.  HBM-bound: each thread turns 8 floats (two 16-byte
 // loads) into one 16-byte store.
-#include "dg_common.hpp"
+#include "kv16.hpp"
 
 namespace {
 
-__device__ inline uint32_t to_f16(float f) {
-    const _Float16 h = static_cast<_Float16>(f);   // v_cvt_f16_f32: IEEE round to nearest even
-    return __builtin_bit_cast(uint16_t, h);
-}
-
-__device__ inline uint32_t to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (u >> 16) | 0x40u;  // NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                                    // RNE
-}
+using dg::to_bf16;
+using dg::to_f16;
 
 template <int kFmt>
 __device__ inline uint32_t pack2(float a, float b) {

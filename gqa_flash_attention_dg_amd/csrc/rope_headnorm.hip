@@ -12,7 +12,7 @@
 // the rotate-half partner is either in the same lane (hd = 128) or one lane shuffle away.  One
 // launch can cover the rows of q, k and v together (dg_qkv_headnorm_rope): at canvas sizes
 // the three calls are launch-bound.
-#include "dg_common.hpp"
+#include "kv16.hpp"
 
 namespace {
 
@@ -48,6 +48,8 @@ struct NormSeg {
     int heads;
     unsigned flags;
     float* vout;      // k_eq_v: also write the weightless norm of the raw rows here, or NULL
+    uint16_t* x16;    // 16-bit twin of the output rows (format NormArgs::fmt16), or NULL
+    uint16_t* vout16; // 16-bit twin of vout, or NULL
 };
 
 struct NormArgs {
@@ -56,6 +58,7 @@ struct NormArgs {
     const float* cs;  // [T, 2*hd], shared by every segment that ropes
     int T, hd;
     float eps;
+    int fmt16;        // DG_KV_F16 or DG_KV_BF16 when a segment has twins
 };
 
 // kHD: the head dim when it is 128 or 64 (no per-lane guards), 0 for any other hd <= 128.  Lanes
@@ -65,7 +68,9 @@ struct NormArgs {
 template <int kHD>
 __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restrict__ w,
                                     const float* __restrict__ cr, int hd_rt, unsigned flags,
-                                    float eps, int lane, float* __restrict__ vr) {
+                                    float eps, int lane, float* __restrict__ vr,
+                                    uint16_t* __restrict__ xr16, uint16_t* __restrict__ vr16,
+                                    int fmt16) {
     const int hd = kHD ? kHD : hd_rt;
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = kHD ? true : e0 < hd;
@@ -91,6 +96,10 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
         if (vr) {  // the v-norm of the same raw rows: weightless, un-roped
             if (v0) vr[e0] = y0;
             if (v1) vr[e1] = y1;
+            if (vr16) {
+                if (v0) vr16[e0] = dg::to_kv16(y0, fmt16);
+                if (v1) vr16[e1] = dg::to_kv16(y1, fmt16);
+            }
         }
         if (weighted) {
             y0 *= w0;
@@ -118,11 +127,14 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
         }
         const float rot0 = e0 < half ? -q0 : q0;
         const float rot1 = e1 < half ? -q1 : q1;
-        if (v0) xr[e0] = y0 * c0 + rot0 * s0v;
-        if (v1) xr[e1] = y1 * c1 + rot1 * s1v;
-    } else {
-        if (v0) xr[e0] = y0;
-        if (v1) xr[e1] = y1;
+        y0 = y0 * c0 + rot0 * s0v;
+        y1 = y1 * c1 + rot1 * s1v;
+    }
+    if (v0) xr[e0] = y0;
+    if (v1) xr[e1] = y1;
+    if (xr16) {  // the 16-bit twin, rounded as dg_pack_kv16 rounds
+        if (v0) xr16[e0] = dg::to_kv16(y0, fmt16);
+        if (v1) xr16[e1] = dg::to_kv16(y1, fmt16);
     }
 }
 
@@ -147,7 +159,9 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     const int t = (int)((u / g.heads) % a.T);
     const float* cr = (g.flags & DG_NORM_ROPE) ? a.cs + (size_t)t * 2 * a.hd : nullptr;
     headnorm_row<kHD>(g.x + (size_t)u * a.hd, g.w, cr, a.hd, g.flags, a.eps, lane,
-                      g.vout ? g.vout + (size_t)u * a.hd : nullptr);
+                      g.vout ? g.vout + (size_t)u * a.hd : nullptr,
+                      g.x16 ? g.x16 + (size_t)u * a.hd : nullptr,
+                      g.vout16 ? g.vout16 + (size_t)u * a.hd : nullptr, a.fmt16);
 }
 
 }  // namespace
@@ -226,10 +240,13 @@ extern "C" int dg_headnorm_rope(float* x, const float* w, const float* cs, int b
     return launch_norm(fn, a, stream);
 }
 
-extern "C" int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, float* v,
-                                    const float* cs, int batch, int T, int nh, int nkv, int hd,
-                                    unsigned flags, float eps, void* stream) {
-    const char* fn = "dg_qkv_headnorm_rope";
+namespace {
+
+// Shared body of dg_qkv_headnorm_rope and dg_qkv_headnorm_rope_kv16 (k16/v16 NULL and fmt16 0
+// for the former).
+int qkv_norm_call(const char* fn, float* q, const float* wq, float* k, const float* wk, float* v,
+                  const float* cs, void* k16, void* v16, int fmt16, int batch, int T, int nh,
+                  int nkv, int hd, unsigned flags, float eps, void* stream) {
     if (nh < 0 || nkv < 0) return dg::fail(DG_EINVAL, "%s: negative size (nh %d, nkv %d)", fn, nh, nkv);
     const bool v_from_k = (flags & DG_NORM_V_FROM_K) != 0;
     flags &= ~DG_NORM_V_FROM_K;
@@ -245,33 +262,63 @@ extern "C" int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const f
     const bool need_w = (flags & DG_NORM_WEIGHTED) && !(flags & DG_NORM_SKIP);
     const bool need_cs = (flags & DG_NORM_ROPE) != 0;
     const bool do_q = q && nq > 0, do_k = k && nk > 0, do_v = v && nk > 0;
+    if (fmt16 && ((do_k && !k16) || (do_v && !v16)))
+        return dg::fail(DG_EINVAL, "%s: k16 and v16 are needed for the given k and v", fn);
     if (!do_q && !do_k && !do_v) return dg::ok();
     if (need_w && ((do_q && !wq) || (do_k && !wk)))
         return dg::fail(DG_EINVAL, "%s: WEIGHTED set but wq or wk is NULL", fn);
     if (need_cs && (do_q || do_k) && !cs)
         return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
-    const dg::Span xs[3] = {dg::Span(do_q ? q : nullptr, nq * 4), dg::Span(do_k ? k : nullptr, nk * 4),
-                            dg::Span(do_v ? v : nullptr, nk * 4)};
+    const dg::Span xs[5] = {dg::Span(do_q ? q : nullptr, nq * 4), dg::Span(do_k ? k : nullptr, nk * 4),
+                            dg::Span(do_v ? v : nullptr, nk * 4),
+                            dg::Span(fmt16 && do_k ? k16 : nullptr, nk * 2),
+                            dg::Span(fmt16 && do_v ? v16 : nullptr, nk * 2)};
     const dg::Span ro[3] = {dg::Span(need_w && do_q ? wq : nullptr, (size_t)hd * 4),
                             dg::Span(need_w && do_k ? wk : nullptr, (size_t)hd * 4),
                             dg::Span(need_cs && (do_q || do_k) ? cs : nullptr, (size_t)T * 2 * hd * 4)};
-    for (int i = 0; i < 3; ++i) {
-        for (int j = i + 1; j < 3; ++j)
-            if (xs[i].overlaps(xs[j])) return dg::fail(DG_EINVAL, "%s: q, k and v overlap", fn);
+    for (int i = 0; i < 5; ++i) {
+        for (int j = i + 1; j < 5; ++j)
+            if (xs[i].overlaps(xs[j])) return dg::fail(DG_EINVAL, "%s: the outputs overlap", fn);
         for (int j = 0; j < 3; ++j)
-            if (xs[i].overlaps(ro[j])) return dg::fail(DG_EINVAL, "%s: wq, wk or cs overlaps q, k or v", fn);
+            if (xs[i].overlaps(ro[j])) return dg::fail(DG_EINVAL, "%s: wq, wk or cs overlaps an output", fn);
     }
+    uint16_t* k16p = fmt16 && do_k ? static_cast<uint16_t*>(k16) : nullptr;
+    uint16_t* v16p = fmt16 && do_v ? static_cast<uint16_t*>(v16) : nullptr;
     NormArgs a{};
     if (do_q)
-        a.seg[a.nseg++] = NormSeg{q, need_w ? wq : nullptr, (long long)batch * T * nh, nh, flags, nullptr};
+        a.seg[a.nseg++] = NormSeg{q, need_w ? wq : nullptr, (long long)batch * T * nh, nh, flags,
+                                  nullptr, nullptr, nullptr};
     if (do_k)
         a.seg[a.nseg++] = NormSeg{k, need_w ? wk : nullptr, (long long)batch * T * nkv, nkv, flags,
-                                  v_from_k ? v : nullptr};
+                                  v_from_k ? v : nullptr, k16p, v_from_k ? v16p : nullptr};
     if (do_v && !v_from_k)
-        a.seg[a.nseg++] = NormSeg{v, nullptr, (long long)batch * T * nkv, nkv, 0u, nullptr};
+        a.seg[a.nseg++] = NormSeg{v, nullptr, (long long)batch * T * nkv, nkv, 0u, nullptr, v16p,
+                                  nullptr};
     a.cs = need_cs ? cs : nullptr;
     a.T = T;
     a.hd = hd;
     a.eps = eps;
+    a.fmt16 = fmt16;
     return launch_norm(fn, a, stream);
+}
+
+}  // namespace
+
+extern "C" int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, float* v,
+                                    const float* cs, int batch, int T, int nh, int nkv, int hd,
+                                    unsigned flags, float eps, void* stream) {
+    return qkv_norm_call("dg_qkv_headnorm_rope", q, wq, k, wk, v, cs, nullptr, nullptr, 0, batch,
+                         T, nh, nkv, hd, flags, eps, stream);
+}
+
+extern "C" int dg_qkv_headnorm_rope_kv16(float* q, const float* wq, float* k, const float* wk,
+                                         float* v, const float* cs, void* k16, void* v16,
+                                         int batch, int T, int nh, int nkv, int hd,
+                                         unsigned flags, float eps, int kv_format, void* stream) {
+    const char* fn = "dg_qkv_headnorm_rope_kv16";
+    if (kv_format != DG_KV_F16 && kv_format != DG_KV_BF16)
+        return dg::fail(DG_EINVAL, "%s: kv_format must be DG_KV_F16 or DG_KV_BF16, got %d", fn,
+                        kv_format);
+    return qkv_norm_call(fn, q, wq, k, wk, v, cs, k16, v16, kv_format, batch, T, nh, nkv, hd,
+                         flags, eps, stream);
 }

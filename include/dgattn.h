@@ -125,6 +125,25 @@ int dg_qkv_headnorm_rope(float* q, const float* wq, float* k, const float* wk, f
 int dg_pack_kv16(const float* src, void* dst, size_t n, int format, void* stream);
 
 /*
+ * dg_qkv_headnorm_rope_kv16 -- dg_qkv_headnorm_rope that also writes 16-bit twins of the normed
+ * k and v, for dg_attn_split_gqa_kv16: the canvas step's norm launch and the pack pass of
+ * deepencoder_gpu.rs `flash_reg_kv16_src` in one launch.  q, k and v are normed in place
+ * exactly as dg_qkv_headnorm_rope does, and each twin element is the f32 result rounded as
+ * dg_pack_kv16 rounds it (bit-identical to packing the f32 outputs).
+ *   k16  out [batch, T, nkv*hd] 16-bit values; needed iff k is given
+ *   v16  out [batch, T, nkv*hd] 16-bit values; needed iff v is given (with DG_NORM_V_FROM_K
+ *        the twin of the v output)
+ *   kv_format  DG_KV_F16 or DG_KV_BF16
+ *   the other arguments as dg_qkv_headnorm_rope.
+ * Errors: as dg_qkv_headnorm_rope, plus DG_EINVAL for an unknown kv_format, a missing twin,
+ * or a twin that overlaps q, k, v, the other twin, a weight or the table.
+ */
+int dg_qkv_headnorm_rope_kv16(float* q, const float* wq, float* k, const float* wk, float* v,
+                              const float* cs, void* k16, void* v16, int batch, int T, int nh,
+                              int nkv, int hd, unsigned flags, float eps, int kv_format,
+                              void* stream);
+
+/*
  * dg_attn_split_gqa_workspace_size -- bytes of scratch that dg_attn_split_gqa can use to split
  * the key range of one call across more workgroups (partial results and their combine).
  * Returns 0 when the shape gains nothing from a split.  Arguments as for dg_attn_split_gqa;

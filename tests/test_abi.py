@@ -126,6 +126,30 @@ def test_qkv_headnorm_validation(L):
     assert _err(L) == ""
 
 
+def test_qkv_headnorm_kv16_validation(L):
+    f = L.dg_qkv_headnorm_rope_kv16
+    base = dict(q=FAKE, wq=FAKE + (1 << 24), k=FAKE + (2 << 24), wk=FAKE + (3 << 24),
+                v=FAKE + (4 << 24), cs=FAKE + (5 << 24), k16=FAKE + (6 << 24),
+                v16=FAKE + (7 << 24), batch=1, T=4, nh=4, nkv=2, hd=64, flags=3, eps=1e-6,
+                fmt=dg.DG_KV_BF16, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(fmt=0) == dg.DG_EINVAL                      # unknown format
+    assert call(fmt=3) == dg.DG_EINVAL
+    assert "kv_format" in _err(L)
+    assert call(k16=None) == dg.DG_EINVAL                   # k given without its twin
+    assert call(v16=None) == dg.DG_EINVAL                   # v given without its twin
+    assert call(k16=FAKE + (2 << 24) + 64) == dg.DG_EINVAL  # twin inside k
+    assert "overlap" in _err(L)
+    assert call(v16=FAKE + (6 << 24) + 32) == dg.DG_EINVAL  # twin inside the other twin
+    assert call(k16=FAKE + (5 << 24)) == dg.DG_EINVAL       # twin on the rope table
+    assert call(flags=16) == dg.DG_EINVAL                   # the checks of the plain entry
+    assert call(wq=None) == dg.DG_EINVAL
+    assert call(flags=3 | dg.DG_NORM_V_FROM_K, v=None) == dg.DG_EINVAL
+    assert call(q=None, k=None, v=None, k16=None, v16=None) == dg.DG_OK   # nothing to do
+    assert call(T=0) == dg.DG_OK
+    assert _err(L) == ""
+
+
 def test_attn_qnorm_validation(L):
     f = L.dg_attn_split_gqa_qnorm
     base = dict(q=FAKE, wq=FAKE + (1 << 24), cs=FAKE + (2 << 24), kc=FAKE + (3 << 24),

@@ -467,31 +467,113 @@ def test_attn_split_kv16(shape, use_ws, fmt, name):
 KV16_VS_F32 = {dg.DG_KV_F16: 2e-2, dg.DG_KV_BF16: 1.5e-1}
 
 
+# Half a 16-bit step, relative (normal range), and the absolute half step at the bottom of the
+# f16 subnormals: the rounding error of one pack.
+HALF_STEP16 = {dg.DG_KV_F16: (2.0 ** -11, 2.0 ** -25), dg.DG_KV_BF16: (2.0 ** -8, 0.0)}
+
+
+def decode16(h, fmt):
+    """16-bit bit patterns -> float64, by the formats' definitions (numpy's float16, or the
+    upper half of an f32 for bfloat16)."""
+    h = np.asarray(h).view(np.uint16)
+    if fmt == dg.DG_KV_F16:
+        return h.view(np.float16).astype(np.float64)
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_rounds_near(h, ref, fmt, what):
+    """Each 16-bit value is the rounding of a float within the f32 bar of `ref`: within half a
+    16-bit step of it, after the f32 tolerance."""
+    rel, ab = HALF_STEP16[fmt]
+    ref = np.asarray(ref, np.float64).ravel()
+    got = decode16(h, fmt).ravel()
+    bound = 2e-4 + 1e-4 * np.abs(ref) + rel * (np.abs(ref) + 2e-4 + 1e-4 * np.abs(ref)) + ab
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), "%s: %d of %d 16-bit values off by up to %.3e" % (
+        what, int((err > bound).sum()), err.size, float(err.max()))
+
+
+@pytest.mark.parametrize("fmt,name", KV_FMTS, ids=[n for _, n in KV_FMTS])
+@pytest.mark.parametrize("B,T,nh,nkv,hd,vfk", [(1, 16, 4, 2, 64, False), (2, 37, 6, 3, 128, False),
+                                                (1, 5, 2, 1, 24, False), (2, 19, 4, 2, 96, True)])
+def test_qkv_headnorm_rope_kv16(B, T, nh, nkv, hd, vfk, fmt, name):
+    """The norm launch that also writes 16-bit twins of k and v: its f32 outputs are those of
+    dg_qkv_headnorm_rope bit for bit and meet the oracle's norms at the f32 bar; the twins are
+    bit-identical to dg_pack_kv16 of those outputs and lie within half a 16-bit step of the
+    oracle's normed values; nothing is written past the twins."""
+    rng = np.random.default_rng(B * 1000 + T * 10 + hd + fmt)
+    q = (rng.standard_normal((B, T, nh * hd)) * 2.0).astype(np.float32)
+    k = (rng.standard_normal((B, T, nkv * hd)) * 0.5).astype(np.float32)
+    v = rng.standard_normal((B, T, nkv * hd)).astype(np.float32)
+    wq = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    wk = (1 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    cs = oracle.rope_table(30, T, hd, 10000.0)
+    flags = dg.DG_NORM_WEIGHTED | dg.DG_NORM_ROPE | (dg.DG_NORM_V_FROM_K if vfk else 0)
+    nk = B * T * nkv * hd
+    outs = []
+    for fused in (False, True):
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        if fused:
+            k16 = torch.full((nk + 8,), -1, dtype=torch.int16, device="cuda")   # guards
+            v16 = torch.full((nk + 8,), -1, dtype=torch.int16, device="cuda")
+            dg.dg_qkv_headnorm_rope_kv16(qd, dev(wq), kd, dev(wk), vd, dev(cs), k16, v16, B, T,
+                                         nh, nkv, hd, flags, 1e-6, fmt)
+        else:
+            dg.dg_qkv_headnorm_rope(qd, dev(wq), kd, dev(wk), vd, dev(cs), B, T, nh, nkv, hd,
+                                    flags, 1e-6)
+        outs.append((host(qd), host(kd), host(vd), kd, vd))
+    (q0, k0, v0, _, _), (q1, k1, v1, kd, vd) = outs
+    for a, b, what in ((q0, q1, "q"), (k0, k1, "k"), (v0, v1, "v")):
+        assert np.array_equal(a, b), "%s differs from dg_qkv_headnorm_rope" % what
+    base = flags & ~dg.DG_NORM_V_FROM_K
+    qref = oracle.headnorm_rope(q, wq, cs, nh, hd, base, 1e-6)
+    kref = oracle.headnorm_rope(k, wk, cs, nkv, hd, base, 1e-6)
+    vref = oracle.headnorm_rope(k if vfk else v, None, None, nkv, hd, 0, 1e-6)
+    assert_parity(q1, qref, "q")
+    assert_parity(k1, kref, "k")
+    assert_parity(v1, vref, "v")
+    for t16, f32d, ref, what in ((k16, kd, kref, "k16"), (v16, vd, vref, "v16")):
+        packed = torch.empty((nk,), dtype=torch.int16, device="cuda")
+        dg.dg_pack_kv16(f32d, packed, nk, fmt)
+        assert torch.equal(t16[:nk], packed), "%s differs from the pack pass" % what
+        assert bool(torch.all(t16[nk:] == -1)), "%s: written past the end" % what
+        assert_rounds_near(host(t16[:nk]), ref, fmt, what)
+
+
 @pytest.mark.parametrize("fmt,name", KV_FMTS, ids=[n for _, n in KV_FMTS])
 def test_canvas_step_kv16(fmt, name):
-    """DiffusionGemma-like step with 16-bit K/V: every packed value bit-exact against the
-    oracle's packing of the same f32 data, the attention at the f32 bar on those values, and the
-    distance from the all-f32 step within the stated bound."""
+    """DiffusionGemma-like step with 16-bit K/V, checked against the oracle's step:
+    - the normed q, k and v at the f32 bar;
+    - the cache twins: the un-roped values bit-exact against the oracle's packing of the same
+      input, and the roped keys and every canvas twin within half a 16-bit step of the
+      oracle's f32 values;
+    - the canvas twins, written by the norm launch, bit-identical to the pack pass applied
+      to the step's own f32 outputs;
+    - the output within the stated distance of the oracle's all-f32 step.
+    The attention on 16-bit values is held to the f32 bar in test_attn_split_kv16, on values the
+    oracle packed."""
     c = synth.dg_canvas_steps(1)
+    cs, kc_ref = oracle_prepare(c)
+    ref32, (qn_ref, kn_ref, vn_ref) = oracle_step(c, c.q, c.k, c.v, cs, kc_ref)
     blk16 = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, dev(c.kc), dev(c.vc), dev(c.wq),
                         dev(c.wk), eps=c.eps, theta=c.theta, rope_cache=True, kv16=name)
     q, k, v = dev(c.q), dev(c.k), dev(c.v)
     out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
     blk16.step(q, k, v, out)
-    kc_roped = host(blk16.kc)                       # the f32 cache after the set-up rope
-    assert np.array_equal(host(blk16.kc16).view(np.uint16), oracle.pack16(kc_roped, fmt).ravel())
+    assert_parity(host(q), qn_ref, "q")
+    assert_parity(host(k), kn_ref, "k")
+    assert_parity(host(v), vn_ref, "v")
     assert np.array_equal(host(blk16.vc16).view(np.uint16), oracle.pack16(c.vc, fmt).ravel())
-    kn, vn, qn = host(k), host(v), host(q)          # normed in place by the step
-    k16, v16 = host(blk16.k16).view(np.uint16), host(blk16.v16).view(np.uint16)
-    assert np.array_equal(k16, oracle.pack16(kn, fmt).ravel())
-    assert np.array_equal(v16, oracle.pack16(vn, fmt).ravel())
-    w = lambda h, shape: oracle.widen16(h, fmt).reshape(shape)
-    ref = oracle.attn_split_gqa(qn, w(host(blk16.kc16).view(np.uint16), c.kc.shape),
-                                w(host(blk16.vc16).view(np.uint16), c.vc.shape), w(k16, kn.shape),
-                                w(v16, vn.shape), c.nh, c.nkv, c.hd)
+    assert_rounds_near(host(blk16.kc16), kc_ref, fmt, "roped cache keys")
+    assert_rounds_near(host(blk16.k16), kn_ref, fmt, "canvas k")
+    assert_rounds_near(host(blk16.v16), vn_ref, fmt, "canvas v")
+    nk = blk16.k16.numel()
+    for t16, f32d, what in ((blk16.k16, k, "k"), (blk16.v16, v, "v")):
+        packed = torch.empty_like(t16)
+        dg.dg_pack_kv16(f32d, packed, nk, fmt)
+        assert torch.equal(t16, packed), "canvas %s twin differs from the pack pass" % what
     got = host(out)
-    assert_parity(got, ref, "kv16 canvas %s" % name)
-    ref32 = oracle.attn_split_gqa(qn, kc_roped, c.vc, kn, vn, c.nh, c.nkv, c.hd)
+    assert np.all(np.isfinite(got))
     dist = float(np.max(np.abs(got - ref32)))
     assert dist <= KV16_VS_F32[fmt], "%s storage moved the output by %.3e" % (name, dist)
     print("kv16 %s: max |out - f32 out| = %.3e" % (name, dist))
