@@ -80,9 +80,10 @@ constexpr int kBiasWaves = 4;
 
 // Lines of at most 16 queries against at most 16 table rows (windowed grids): one 16x16 tile
 // per line with v_mfma_f32_16x16x4f32, a quarter of the 32x32 tile's matrix work.  Lane l
-// supplies query row l%16 (A) and table row l%16 (B) at contraction index k = l/16, which
-// covers elements 16k..16k+15 over the 16 steps (4 contiguous float4 loads per operand); the
-// 4 accumulators hold queries 4*(l/16)+r of table row l%16.
+// supplies query row l%16 (A) and table row l%16 (B) at contraction index k = l/16; step
+// 4c+e contracts element 16c+4k+e, so in each of the 4 float4 loads per operand the 4 lanes
+// of a row read 64 contiguous bytes.  The 4 accumulators hold queries 4*(l/16)+r of table
+// row l%16.
 __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs a, float* __restrict__ dhw,
                                                                        long long ntasks) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -97,14 +98,14 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs 
     const int nr = is_h ? a.gh : a.gw;
     auto qidx = [&](int v) { return is_h ? line * a.gw + v : v * a.gw + (line - a.gh); };
     const size_t rs = (size_t)3 * a.W;
-    const float* qr = a.qkv + ((size_t)win * a.n + qidx(min(l16, nq - 1))) * rs + head * HD + 16 * kq;
+    const float* qr = a.qkv + ((size_t)win * a.n + qidx(min(l16, nq - 1))) * rs + head * HD + 4 * kq;
     const float* tr = (is_h ? a.rh + (size_t)line * a.gh * HD : a.rw + (size_t)(line - a.gh) * a.gw * HD) +
-                      (size_t)min(l16, nr - 1) * HD + 16 * kq;
+                      (size_t)min(l16, nr - 1) * HD + 4 * kq;
     float qv[16], tv[16];
 #pragma unroll
     for (int c = 0; c < 16; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(qr + c);
-        const float4 y = *reinterpret_cast<const float4*>(tr + c);
+        const float4 x = *reinterpret_cast<const float4*>(qr + 4 * c);
+        const float4 y = *reinterpret_cast<const float4*>(tr + 4 * c);
         qv[c] = x.x; qv[c + 1] = x.y; qv[c + 2] = x.z; qv[c + 3] = x.w;
         tv[c] = y.x; tv[c + 1] = y.y; tv[c + 2] = y.z; tv[c + 3] = y.w;
     }
