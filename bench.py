@@ -464,20 +464,23 @@ def main():
 
     # Default step counts from the wall time of a few probe steps (which count as warmup; the
     # first one, which loads the code objects, is not timed).
+    # With --graph a probe is one whole replay, so that each timed probe does a replay's work.
+    per = args.graph or 1
     nprobe, est = 0, None
     if args.warmup is None or args.steps is None:
-        nprobe = 4 if args.warmup is None else min(4, args.warmup)
-        if nprobe >= 2:
-            work.step()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(nprobe - 1):
+        nprobe = 4 * per if args.warmup is None else min(4 * per, args.warmup // per * per)
+        if nprobe >= 2 * per:
+            for _ in range(per):
                 work.step()
             torch.cuda.synchronize()
-            est = max((time.perf_counter() - t0) / (nprobe - 1), 1e-6)
+            t0 = time.perf_counter()
+            for _ in range(nprobe - per):
+                work.step()
+            torch.cuda.synchronize()
+            est = max((time.perf_counter() - t0) / (nprobe - per), 1e-6)
         if args.warmup is None:
             args.warmup = max(nprobe, min(5000, int(0.5 / est)))
-        elif nprobe < 2:
+        elif nprobe < 2 * per:
             nprobe = 0
         if args.steps is None:
             args.steps = max(20, min(2000, int(0.25 / est))) if est else 20
