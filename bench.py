@@ -91,7 +91,7 @@ def measured_traffic(kernel: str, workload: str):
 def split_counts(c, norm_mode="in_attention"):
     """Algorithmic flops and bytes of one attention launch and of the headnorm work: q, k and v
     each read and written once, or with the q norm inside attention only k and v (q is read by
-    the attention launch either way)."""
+    the attention launch either way), or none with all three norms inside attention."""
     if c.causal:
         pairs = c.B * c.nh * (c.T * c.ctx + c.T * (c.T + 1) // 2)
     else:
@@ -103,21 +103,21 @@ def split_counts(c, norm_mode="in_attention"):
     cache = c.B * c.nkv * c.ctx * c.hd
     attn_bytes = f32 * (q + 2 * kv + 2 * cache + q)
     qn = 0 if norm_mode == "in_attention" else q
-    norm_bytes = (f32 * 2 * (qn + 2 * kv)) if c.normed else 0
+    norm_bytes = (f32 * 2 * (qn + 2 * kv)) if c.normed and norm_mode != "fused" else 0
     return flops, attn_bytes, norm_bytes
 
 
 class SplitWork:
     dominant = "attn_split_gqa"
 
-    def __init__(self, name, case, norm_mode="in_attention", kv16=None):
+    def __init__(self, name, case, norm_mode="auto", kv16=None):
         import numpy as np
         import torch
         from gqa_flash_attention_dg_amd.canvas import CanvasBlock
 
-        if kv16 and norm_mode == "in_attention":
+        if kv16 and norm_mode in ("auto", "fused", "in_attention"):
             norm_mode = "one_launch"   # the 16-bit attention takes a normed q
-        self.name, self.c, self.norm_mode, self.kv16 = name, case, norm_mode, kv16
+        self.name, self.c, self.kv16 = name, case, kv16
         # ctx + T <= 8 runs the short-key-set kernel, longer key sets the tiled MFMA kernel
         self.dominant = "attn_small" if case.ctx + case.T <= 8 else "attn_split_gqa"
         d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -126,6 +126,7 @@ class SplitWork:
                                d(c.wk), eps=c.eps, theta=c.theta, scale=c.scale,
                                causal=c.causal, rope_cache=c.rope_cache, normed=c.normed,
                                norm_mode=norm_mode, kv16=kv16)
+        self.norm_mode = norm_mode = self.blk.norm_mode   # "auto" resolved by the block
         self.q, self.k, self.v = d(c.q), d(c.k), d(c.v)
         self.out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
         self.flops, self.attn_bytes, self.norm_bytes = split_counts(c, norm_mode)
@@ -152,15 +153,20 @@ class SplitWork:
                     "dg_attn_split_gqa_kv16 (%s K/V)" % (self.norm_mode, self.kv16))
         if not getattr(self.c, "normed", True):
             return "dg_attn_split_gqa"
-        return {"one_launch": "dg_qkv_headnorm_rope(q, k, v) + dg_attn_split_gqa",
-                "in_attention": "dg_qkv_headnorm_rope(k, v) + dg_attn_split_gqa_qnorm",
-                "separate": "dg_headnorm_rope x3 (q, k, v) + dg_attn_split_gqa"}[self.norm_mode]
+        names = {"fused": "dg_attn_split_gqa_qkvnorm (q, k, v norms inside attention)",
+                 "one_launch": "dg_qkv_headnorm_rope(q, k, v) + dg_attn_split_gqa",
+                 "in_attention": "dg_qkv_headnorm_rope(k, v) + dg_attn_split_gqa_qnorm",
+                 "separate": "dg_headnorm_rope x3 (q, k, v) + dg_attn_split_gqa"}
+        return " / ".join(names[m] for m in self.norm_mode.split("/"))
 
     def step(self, ev=None):
         normed_q = self.c.normed and self.norm_mode == "in_attention"
+        normed_all = self.c.normed and self.norm_mode == "fused"
         fused16 = self.kv16 and self.c.normed and self.norm_mode == "one_launch"
         if fused16:   # one launch: the norms and the 16-bit twins of k and v
             self.blk.norm_qkv_kv16(self.q, self.k, self.v)
+        elif normed_all:
+            pass      # every norm runs inside the attention launch
         elif self.c.normed:
             if self.norm_mode == "in_attention":
                 self.blk.norm_qkv(None, self.k, self.v)
@@ -174,6 +180,8 @@ class SplitWork:
             ev[0].record()
         if self.kv16:
             self.blk.attend_kv16(self.q, self.out)
+        elif normed_all:
+            self.blk.attend_qkvnorm(self.q, self.k, self.v, self.out)
         elif normed_q:
             self.blk.attend_qnorm(self.q, self.k, self.v, self.out)
         else:
@@ -217,12 +225,12 @@ class LayerStackWork:
     are timed together as the dominant kernel."""
     dominant = "attn_split_gqa"
 
-    def __init__(self, name, case, norm_mode="in_attention"):
+    def __init__(self, name, case, norm_mode="auto"):
         import numpy as np
         import torch
         from gqa_flash_attention_dg_amd.canvas import CanvasStack
 
-        self.name, self.c, self.norm_mode = name, case, norm_mode
+        self.name, self.c = name, case
         d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
         c = case
         self.stack = CanvasStack(c.B, c.T, c.nh, c.pos0, c.layers,
@@ -232,7 +240,9 @@ class LayerStackWork:
                                  eps=c.eps, scale=c.scale, norm_mode=norm_mode)
         self.io = []
         self.flops = self.attn_bytes = self.norm_bytes = 0
-        for l, p in zip(c.layers, c.per_layer):
+        modes = [blk.norm_mode for blk in self.stack.blocks]   # "auto" resolved per layer
+        self.norm_mode = modes[0] if len(set(modes)) == 1 else "/".join(modes)
+        for l, p, norm_mode in zip(c.layers, c.per_layer, modes):
             v = torch.empty((c.B, c.T, l.nkv * l.hd), device="cuda") if l.k_eq_v else d(p["v"])
             out = torch.empty((c.B, c.T, c.nh * l.hd), device="cuda")
             self.io.append((d(p["q"]), d(p["k"]), v, out))
@@ -241,7 +251,8 @@ class LayerStackWork:
             self.flops += 4 * l.hd * c.B * c.nh * c.T * (l.ctx + c.T)
             self.attn_bytes += 4 * (2 * q + 2 * kv + 2 * cache)
             qn = 0 if norm_mode == "in_attention" else q
-            self.norm_bytes += 4 * 2 * (qn + kv) + 4 * (kv if l.k_eq_v else 2 * kv)
+            if norm_mode != "fused":
+                self.norm_bytes += 4 * 2 * (qn + kv) + 4 * (kv if l.k_eq_v else 2 * kv)
         self.bound = "mfma"
 
     def config(self):
@@ -256,15 +267,20 @@ class LayerStackWork:
         blocks = self.stack.blocks
         for li, (q, k, v, out) in enumerate(self.io):
             blk = blocks[li]
-            if self.norm_mode == "in_attention":
+            mode = blk.norm_mode
+            if mode == "fused":
+                pass
+            elif mode == "in_attention":
                 blk.norm_qkv(None, k, v)
-            elif self.norm_mode == "one_launch":
+            elif mode == "one_launch":
                 blk.norm_qkv(q, k, v)
             else:
                 blk.norm(q, k, v)
             if ev:
                 ev[li][0].record()
-            if self.norm_mode == "in_attention":
+            if mode == "fused":
+                blk.attend_qkvnorm(q, k, v, out)
+            elif mode == "in_attention":
                 blk.attend_qnorm(q, k, v, out)
             else:
                 blk.attend(q, k, v, out)
@@ -377,7 +393,7 @@ class CopyWork:
         return None
 
 
-def make_work(name, norm_mode="in_attention", kv16=None):
+def make_work(name, norm_mode="auto", kv16=None):
     from gqa_flash_attention_dg_amd import synth
     if name == "long_cache":
         return SplitWork(name, synth.long_cache(), norm_mode, kv16)
@@ -409,9 +425,12 @@ def main():
     ap.add_argument("--workload", default="long_cache",
                     choices=["long_cache", "dg_canvas", "dg_layers", "tiny", "depformer",
                              "sam_relpos", "sam_windowed", "hbm_copy"])
-    ap.add_argument("--norm", default="in_attention",
-                    choices=["in_attention", "one_launch", "separate"],
-                    help="in_attention: k/v norms in one launch + q norm inside attention; "
+    ap.add_argument("--norm", default="auto",
+                    choices=["auto", "fused", "in_attention", "one_launch", "separate"],
+                    help="auto (default): fused when the attention splits its key range across "
+                         "workgroups, else in_attention; "
+                         "fused: q, k and v norms inside the attention launch; "
+                         "in_attention: k/v norms in one launch + q norm inside attention; "
                          "one_launch: q, k, v norms in one launch; separate: the page's three "
                          "headnorm dispatches")
     ap.add_argument("--graph", type=int, default=0, metavar="STEPS",

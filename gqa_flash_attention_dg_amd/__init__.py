@@ -23,7 +23,7 @@ DG_KV_F16, DG_KV_BF16 = 1, 2
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
            "dg_qkv_headnorm_rope_kv16",
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
-           "dg_attn_split_gqa_kv16",
+           "dg_attn_split_gqa_qkvnorm", "dg_attn_split_gqa_kv16",
            "relpos_flash_attn_workspace_size", "relpos_flash_attn",
            "relpos_flash_attn_windows_workspace_size", "relpos_flash_attn_windows",
            "dg_last_error")
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
         L.dg_attn_split_gqa_qnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, U,
                                               F, F, I, vp, Z, vp]
+        L.dg_attn_split_gqa_qkvnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I,
+                                                I, U, F, F, I, vp, Z, vp]
         L.relpos_flash_attn_workspace_size.argtypes = [I, I, I, I]
         L.relpos_flash_attn_workspace_size.restype = Z
         L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp, Z, vp]
@@ -69,8 +71,8 @@ def lib() -> ctypes.CDLL:
         L.relpos_flash_attn_windows.argtypes = [vp, vp, vp, vp, I, I, I, I, I, F, vp, Z, vp]
         for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
                      "dg_qkv_headnorm_rope_kv16",
-                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "dg_attn_split_gqa_kv16",
-                     "relpos_flash_attn",
+                     "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "dg_attn_split_gqa_qkvnorm",
+                     "dg_attn_split_gqa_kv16", "relpos_flash_attn",
                      "relpos_flash_attn_windows"):
             getattr(L, name).restype = I
         L.dg_last_error.argtypes = []
@@ -232,6 +234,23 @@ def dg_attn_split_gqa_qnorm(q, wq, cs, kc, vc, k, v, out, batch: int, T: int, ct
         _ptr(cs, "cs", T * 2 * hd if need_cs else 0), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
         _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq), batch, T, ctx, nh, nkv, hd,
         qflags, float(eps), float(scale), int(causal), ws, wsb, _stream(stream)))
+
+
+def dg_attn_split_gqa_qkvnorm(q, wq, k, wk, v, cs, kc, vc, out, batch: int, T: int, ctx: int,
+                              nh: int, nkv: int, hd: int, flags: int, eps: float, scale: float,
+                              causal: int, workspace=None, workspace_bytes: int = 0,
+                              stream=None) -> None:
+    _nonneg(batch=batch, T=T, ctx=ctx, nh=nh, nkv=nkv, hd=hd)
+    nq, nkvc, nc = batch * T * nh * hd, batch * T * nkv * hd, batch * nkv * ctx * hd
+    need_w = flags & DG_NORM_WEIGHTED
+    need_cs = flags & DG_NORM_ROPE
+    ws, wsb = _workspace(workspace, workspace_bytes)
+    _check(lib().dg_attn_split_gqa_qkvnorm(
+        _ptr(q, "q", nq), _ptr(wq, "wq", hd if need_w else 0), _ptr(k, "k", nkvc),
+        _ptr(wk, "wk", hd if need_w else 0), _ptr(v, "v", nkvc),
+        _ptr(cs, "cs", T * 2 * hd if need_cs else 0), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
+        _ptr(out, "out", nq), batch, T, ctx, nh, nkv, hd, flags, float(eps), float(scale),
+        int(causal), ws, wsb, _stream(stream)))
 
 
 def dg_attn_split_gqa_kv16(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int, nkv: int,

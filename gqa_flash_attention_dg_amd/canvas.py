@@ -9,8 +9,14 @@ attention over that layer's [cache | canvas].  A k_eq_v layer has no v projectio
 the raw k projection, normalised without weight or rope.
 
 Set-up work (rope tables, roping a cache that is stored un-roped) happens once per canvas
-block in the constructor; `step` is the per-denoising-step hot path.  Three ways to run the
-norms of a step (`norm_mode`):
+block in the constructor; `step` is the per-denoising-step hot path.  Four ways to run the
+norms of a step (`norm_mode`), plus "auto" (the default), which takes "fused" when the
+attention splits its key range across workgroups (each workgroup then sees at most a few
+canvas tiles, so normalising them in place costs less than a launch) and "in_attention"
+otherwise (a workgroup that walks the whole key range would norm every canvas tile itself):
+  "fused"         all three norms inside the attention launch: q as it is staged, the canvas
+                  k and v rows as their tiles land in on-chip memory (q, k and v are not
+                  written; a k_eq_v layer's v buffer is neither read nor written);
   "in_attention"  k and v normalised by one launch, the q norm and rope applied by the
                   attention kernel as it stages q (q is left un-normalised in memory);
   "one_launch"    q, k and v normalised in place by one launch, then plain attention;
@@ -23,12 +29,13 @@ import torch
 
 from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K,
                DG_NORM_WEIGHTED, dg_attn_split_gqa, dg_attn_split_gqa_kv16,
-               dg_attn_split_gqa_qnorm, dg_attn_split_gqa_workspace_size, dg_headnorm_rope,
+               dg_attn_split_gqa_qkvnorm, dg_attn_split_gqa_qnorm,
+               dg_attn_split_gqa_workspace_size, dg_headnorm_rope,
                dg_pack_kv16, dg_qkv_headnorm_rope, dg_qkv_headnorm_rope_kv16, dg_rope_table)
 
 KV_FORMATS = {"f16": DG_KV_F16, "bf16": DG_KV_BF16}
 
-NORM_MODES = ("in_attention", "one_launch", "separate")
+NORM_MODES = ("auto", "fused", "in_attention", "one_launch", "separate")
 
 
 def rope_table(pos0, T, hd, theta, device="cuda"):
@@ -57,11 +64,11 @@ class CanvasBlock:
 
     def __init__(self, B, T, ctx, nh, nkv, hd, kc=None, vc=None, wq=None, wk=None, *,
                  eps=1e-6, theta=10000.0, scale=1.0, causal=False, rope_cache=False,
-                 normed=True, norm_mode="in_attention", use_workspace=True, pos0=None, cs=None,
+                 normed=True, norm_mode="auto", use_workspace=True, pos0=None, cs=None,
                  k_eq_v=False, kv16=None, device="cuda"):
         if kv16 is not None and kv16 not in KV_FORMATS:
             raise ValueError("kv16 must be None, 'f16' or 'bf16'")
-        if kv16 is not None and norm_mode == "in_attention":
+        if kv16 is not None and norm_mode in ("auto", "fused", "in_attention"):
             norm_mode = "one_launch"
         if norm_mode not in NORM_MODES:
             raise ValueError("unknown norm_mode %r" % (norm_mode,))
@@ -97,6 +104,8 @@ class CanvasBlock:
             if use_workspace else 0
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
             if self.ws_bytes > 0 else None
+        if self.norm_mode == "auto":
+            self.norm_mode = "fused" if self.ws_bytes > 0 else "in_attention"
 
     def norm(self, q, k, v):
         """The page's per-step headnorm calls, in place on q, k and v (for a k_eq_v layer the
@@ -123,6 +132,14 @@ class CanvasBlock:
                                 self.T, self.ctx, self.nh, self.nkv, self.hd,
                                 DG_NORM_WEIGHTED | DG_NORM_ROPE, self.eps, self.scale,
                                 self.causal, self.ws, self.ws_bytes)
+
+    def attend_qkvnorm(self, q, k, v, out):
+        """Attention on the raw q, k and v, all three normalised inside the kernel (none of them
+        is written); a k_eq_v layer's v is the raw k."""
+        dg_attn_split_gqa_qkvnorm(q, self.wq, k, self.wk, k if self.k_eq_v else v, self.cs,
+                                  self.kc, self.vc, out, self.B, self.T, self.ctx, self.nh,
+                                  self.nkv, self.hd, DG_NORM_WEIGHTED | DG_NORM_ROPE, self.eps,
+                                  self.scale, self.causal, self.ws, self.ws_bytes)
 
     def norm_qkv_kv16(self, q, k, v):
         """norm_qkv that also writes the 16-bit twins of the normalised k and v (kv16 blocks)."""
@@ -151,6 +168,9 @@ class CanvasBlock:
 
     def step(self, q, k, v, out):
         """One canvas step: norms (when enabled), then attention into `out`."""
+        if self.normed and self.norm_mode == "fused":
+            self.attend_qkvnorm(q, k, v, out)
+            return
         if self.normed and self.norm_mode == "in_attention":
             self.norm_qkv(None, k, v)
             self.attend_qnorm(q, k, v, out)
@@ -200,7 +220,7 @@ class CanvasStack:
     """
 
     def __init__(self, B, T, nh, pos0, layers, caches, weights, *, theta_sliding, theta_full,
-                 eps=1e-6, scale=1.0, norm_mode="in_attention", use_workspace=True,
+                 eps=1e-6, scale=1.0, norm_mode="auto", use_workspace=True,
                  device="cuda"):
         self.layers = list(layers)
         tables = {}

@@ -57,8 +57,9 @@ struct SplitArgs {
     float qmul;        // scale * log2(e)
     int causal;
     const float* wq;   // q norm weight [hd] (qnorm entry with WEIGHTED)
+    const float* wk;   // k norm weight [hd] (qkvnorm entry with WEIGHTED)
     const float* cs;   // rope table [T, 2*hd] (qnorm entry with ROPE)
-    unsigned qflags;   // DG_NORM_* bits of the q norm
+    unsigned qflags;   // DG_NORM_* bits of the q norm (and of the k norm in the qkvnorm entry)
     float eps;
 };
 
@@ -224,6 +225,106 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
     }
 }
 
+// The k and v dispatches of DG_HEADNORM_ROPE on the canvas rows of one stage tile pair in LDS,
+// in place (dg_attn_split_gqa_qkvnorm): a K row gets the norm, the weight and the rope of its
+// canvas row (the q flags), a V row the weightless, un-roped norm.  Cache rows (key < ctx) are
+// stored normalised and left alone; rows past the end of the keys hold a copy of the last key
+// and are normalised like it.  L = HD/8 lanes share a row, lane c holding chunks c and c + L,
+// so for the exact widths the rope partner chunk (hd/2 away) is in the same lane; padded widths
+// read it back from the row, which the same wavefront wrote.  The 64 rows (32 K, then 32 V)
+// go in passes of 512/L rows (one at HD 64; at HD 128 the K rows, then the V rows, which need
+// no table loads), kept apart so that few registers are live beside the attention state.
+// Chunks past hd keep their raw copies (they meet zero query elements, or fill output
+// elements that are never stored).
+template <int HD, bool kPad>
+__device__ inline void norm_canvas_tile(const SplitArgs& a, float* __restrict__ kt,
+                                        float* __restrict__ vt, int j0, int kend, int wave,
+                                        int lane, int hd) {
+    constexpr int kChunks = HD / 4, L = HD / 8, kRowsPerPass = 512 / L;
+    const int c = lane % L;
+#pragma unroll 1
+    for (int r0 = 0; r0 < 2 * dgk::kKeys; r0 += kRowsPerPass) {
+        const int R = r0 + wave * (64 / L) + lane / L;
+        const bool isv = R >= dgk::kKeys;        // wave-uniform
+        const int trow = R % dgk::kKeys;
+        const int j = min(j0 + trow, kend - 1);
+        if (j < a.ctx) continue;                 // a cache row; its L lanes leave together
+        float* rowp = (isv ? vt : kt) + trow * HD;
+        const int sw = isv ? 0 : trow % kChunks; // K rows are stored chunk-swizzled
+        float4 x[2];
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int ch = c + L * k;
+            x[k] = !kPad || 4 * ch < hd ? *reinterpret_cast<const float4*>(rowp + 4 * (ch ^ sw))
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
+        }
+#pragma unroll
+        for (int m = 1; m < L; m <<= 1) ss += __shfl_xor(ss, m);
+        const float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
+        const bool weighted = !isv && (a.qflags & DG_NORM_WEIGHTED);
+        const bool rope = !isv && (a.qflags & DG_NORM_ROPE);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int ch = c + L * k;
+            const float4 w = weighted && (!kPad || 4 * ch < hd)
+                                 ? *reinterpret_cast<const float4*>(a.wk + 4 * ch)
+                                 : make_float4(1.f, 1.f, 1.f, 1.f);
+            x[k] = make_float4(x[k].x * inv * w.x, x[k].y * inv * w.y, x[k].z * inv * w.z,
+                               x[k].w * inv * w.w);
+        }
+        if (rope) {
+            const int half_hd = hd >> 1;
+            const float* cr = a.cs + (size_t)(j - a.ctx) * 2 * hd;
+            float4 part[2];
+            if constexpr (!kPad) {
+                part[0] = x[1];
+                part[1] = x[0];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int ch = c + L * k;
+                    if (4 * ch < hd) *reinterpret_cast<float4*>(rowp + 4 * (ch ^ sw)) = x[k];
+                }
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    float pv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * (c + L * k) + i;
+                        const int pe = e < half_hd ? e + half_hd : e - half_hd;
+                        pv[i] = e < hd ? rowp[4 * ((pe >> 2) ^ sw) + (pe & 3)] : 0.0f;
+                    }
+                    part[k] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int e0 = 4 * (c + L * k);
+                if (kPad && e0 >= hd) continue;
+                const float4 co = *reinterpret_cast<const float4*>(cr + e0);
+                const float4 si = *reinterpret_cast<const float4*>(cr + hd + e0);
+                const float y[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+                const float p[4] = {part[k].x, part[k].y, part[k].z, part[k].w};
+                const float cc[4] = {co.x, co.y, co.z, co.w}, sn[4] = {si.x, si.y, si.z, si.w};
+                float r[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float rot = e0 + i < half_hd ? -p[i] : p[i];
+                    r[i] = y[i] * cc[i] + rot * sn[i];
+                }
+                x[k] = make_float4(r[0], r[1], r[2], r[3]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int ch = c + L * k;
+            if (!kPad || 4 * ch < hd) *reinterpret_cast<float4*>(rowp + 4 * (ch ^ sw)) = x[k];
+        }
+    }
+}
+
 // Workgroup id -> logical id such that consecutive logical ids share an XCD (the hardware
 // deals workgroups to the 8 XCDs round robin).
 __device__ inline int xcd_remap(int bid, int n) {
@@ -235,7 +336,11 @@ __device__ inline int xcd_remap(int bid, int n) {
 // are zero past hd; key/value rows are loaded with their chunks past hd taken from a valid
 // chunk of the same row (finite values that meet zero query elements, and output elements
 // past hd that are never stored).
-template <int HD, bool kNormQ, bool kPad, int kKV>
+// kNormKV (with kNormQ): k and v arrive raw; each stage that holds canvas rows normalises them
+// in LDS (norm_canvas_tile) before they are read.  Split-KV then deals the tiles round robin
+// (split s takes tiles s, s + nsplit, ...), so the canvas tiles, and that work, spread evenly
+// over the splits instead of falling to the last ones.
+template <int HD, bool kNormQ, bool kNormKV, bool kPad, int kKV>
 __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     using TL = dgk::Tile<HD>;
     using KT = KVTile<HD, kKV>;
@@ -287,8 +392,19 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const int tile_begin = (int)((long long)split * ntile / a.nsplit);
     const int tile_end = (int)((long long)(split + 1) * ntile / a.nsplit);
     const int kbeg = tile_begin * dgk::kKeys;   // this split's keys: [kbeg, kend)
-    kend = min(kend, tile_end * dgk::kKeys);
-    const int nst = (tile_end - tile_begin + 1) / 2;
+    int ntl;                                    // tiles of this split
+    if constexpr (kNormKV) {                    // round robin: tiles split, split + nsplit, ...
+        ntl = split < ntile ? (ntile - split + a.nsplit - 1) / a.nsplit : 0;
+    } else {
+        kend = min(kend, tile_end * dgk::kKeys);
+        ntl = tile_end - tile_begin;
+    }
+    const int nst = (ntl + 1) / 2;
+    // First key of tile t (0 or 1) of stage st; a key at or past kend means the tile is absent.
+    auto key0 = [&](int st, int t) {
+        if constexpr (kNormKV) return (split + a.nsplit * (2 * st + t)) * dgk::kKeys;
+        else return kbeg + st * kStage + t * dgk::kKeys;
+    };
 
     constexpr int kEsz = KT::kEsz;
     const char* kcb = reinterpret_cast<const char*>(a.kc) + (size_t)bk * a.ctx * hd * kEsz;
@@ -316,7 +432,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     const char* canvas_base = ld_isv ? vb : kb;
     const int last_chunk = hd * kEsz / 16 - 1;   // kPad: chunks past it repeat it
     auto issue_stage = [&](int st, int buf) {
-        const int j0 = kbeg + st * kStage + ld_tile * dgk::kKeys;
+        const int j0 = key0(st, ld_tile);
         if (j0 >= kend) return;              // the split's last stage holds one tile
         char* dst = tile_ptr(buf, ld_tile, ld_isv);
         const bool in_cache = j0 + dgk::kKeys <= a.ctx, in_canvas = j0 >= a.ctx;
@@ -369,8 +485,26 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         const int buf = st & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
         __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
+        if constexpr (kNormKV) {
+            // Canvas rows are normalised in place before anyone reads them.  The next stage is
+            // issued after that, so the norm's weight and table loads do not queue behind it.
+            const int ja = key0(st, 0), jb = key0(st, 1);
+            const bool ca = ja < kend && ja + dgk::kKeys > a.ctx;
+            const bool cb = jb < kend && jb + dgk::kKeys > a.ctx;
+            if (ca || cb) {
+                if (ca)
+                    norm_canvas_tile<HD, kPad>(a, reinterpret_cast<float*>(tile_ptr(buf, 0, 0)),
+                                               reinterpret_cast<float*>(tile_ptr(buf, 0, 1)), ja,
+                                               kend, wave, lane, hd);
+                if (cb)
+                    norm_canvas_tile<HD, kPad>(a, reinterpret_cast<float*>(tile_ptr(buf, 1, 0)),
+                                               reinterpret_cast<float*>(tile_ptr(buf, 1, 1)), jb,
+                                               kend, wave, lane, hd);
+                __syncthreads();
+            }
+        }
         if (!hi && st + 1 < nst) issue_stage(st + 1, buf ^ 1);
-        const int t0 = kbeg + st * kStage + hi * dgk::kKeys;
+        const int t0 = key0(st, hi);
         if (pair_active && t0 < kend) {
             f32x16 s;
             if constexpr (kKV == 0) {
@@ -441,10 +575,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 // exchange within each group of 8 completes them, the 8-entry softmax runs in registers, and
 // each lane writes its segment of the output row.  All global accesses are contiguous per row.
 // Elements at or past hd (kPad) are zero.  With kNormQ the q norm runs on the lane's segment
-// (3 exchanges for the sum of squares) and the rope partner is read back from a staged row.
+// (3 exchanges for the sum of squares) and the rope partner is read back from a staged row;
+// with kNormKV the k and v norms of canvas key rows run the same way (the k rope partner is
+// read back from the key's own LDS row before the row is written).
 constexpr int kSmallKeys = 8;
 
-template <int HD, bool kNormQ, bool kPad, int kKV>
+template <int HD, bool kNormQ, bool kNormKV, bool kPad, int kKV>
 __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long units) {
     constexpr int SEG = HD / 8;
     constexpr int kRows = kNormQ ? 3 : 2;   // K, V (and the staged q) per wave
@@ -545,6 +681,54 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
     }
 #pragma unroll
     for (int e = 0; e < SEG; ++e) qr[e] *= a.qmul;
+    if constexpr (kNormKV) {
+        // Canvas key rows arrive raw: the k dispatch (norm, weight, rope at canvas row r - ctx)
+        // and the weightless v norm, on the lane's segment.  kr, vr are zero past hd.
+        const bool canvas_key = has_key && r >= a.ctx;   // the same for the 8 lanes of a row
+        float ssk = 0.0f, ssv = 0.0f;
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) {
+            ssk += kr[e] * kr[e];
+            ssv += vr[e] * vr[e];
+        }
+        ssk += __shfl_xor(ssk, 1);
+        ssk += __shfl_xor(ssk, 2);
+        ssk += __shfl_xor(ssk, 4);
+        ssv += __shfl_xor(ssv, 1);
+        ssv += __shfl_xor(ssv, 2);
+        ssv += __shfl_xor(ssv, 4);
+        if (canvas_key) {
+            const float invk = 1.0f / sqrtf(ssk / (float)hd + a.eps);
+            const float invv = 1.0f / sqrtf(ssv / (float)hd + a.eps);
+#pragma unroll
+            for (int e = 0; e < SEG; ++e) {
+                kr[e] *= invk;
+                if ((a.qflags & DG_NORM_WEIGHTED) && cseg + e < hd) kr[e] *= a.wk[cseg + e];
+                vr[e] *= invv;
+            }
+            if (a.qflags & DG_NORM_ROPE) {
+                float* krow = ks + r * HD;    // the key's own row, wave-private, written below
+#pragma unroll
+                for (int e = 0; e < SEG; ++e) krow[cseg + e] = kr[e];
+                const int half_hd = hd >> 1;
+                const float* cr = a.cs + (size_t)(r - a.ctx) * 2 * hd;
+                float part[SEG];
+#pragma unroll
+                for (int e = 0; e < SEG; ++e) {
+                    const int el = cseg + e;
+                    part[e] = el < hd ? krow[el < half_hd ? el + half_hd : el - half_hd] : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < SEG; ++e) {
+                    const int el = cseg + e;
+                    if (el < hd) {
+                        const float rot = el < half_hd ? -part[e] : part[e];
+                        kr[e] = kr[e] * cr[el] + rot * cr[hd + el];
+                    }
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int e = 0; e < SEG; e += 4) {
         *reinterpret_cast<float4*>(ks + r * HD + cseg + e) = make_float4(kr[e], kr[e + 1], kr[e + 2], kr[e + 3]);
@@ -683,38 +867,53 @@ namespace {
 using SplitKernel = void (*)(SplitArgs);
 using SmallKernel = void (*)(SplitArgs, long long);
 
-template <int HD, bool kNormQ, int kKV>
+// norm: 0 (k, v and q as given), 1 (q normalised in the kernel), 2 (q, k and v normalised in
+// the kernel).
+template <int HD, int kNorm, int kKV>
 SplitKernel split_variant(int hd) {
-    return hd == HD ? attn_split_gqa_kernel<HD, kNormQ, false, kKV>
-                    : attn_split_gqa_kernel<HD, kNormQ, true, kKV>;
+    return hd == HD ? attn_split_gqa_kernel<HD, kNorm >= 1, kNorm == 2, false, kKV>
+                    : attn_split_gqa_kernel<HD, kNorm >= 1, kNorm == 2, true, kKV>;
 }
 
-// kv: 0 (f32), DG_KV_F16 or DG_KV_BF16; the 16-bit variants take no in-kernel q norm.
-SplitKernel pick_split(int hd, bool normq, int kv) {
-    if (kv == DG_KV_F16) return hd > 64 ? split_variant<128, false, DG_KV_F16>(hd) : split_variant<64, false, DG_KV_F16>(hd);
-    if (kv == DG_KV_BF16) return hd > 64 ? split_variant<128, false, DG_KV_BF16>(hd) : split_variant<64, false, DG_KV_BF16>(hd);
-    if (hd > 64) return normq ? split_variant<128, true, 0>(hd) : split_variant<128, false, 0>(hd);
-    return normq ? split_variant<64, true, 0>(hd) : split_variant<64, false, 0>(hd);
+template <int HD>
+SplitKernel split_norm_variant(int hd, int norm) {
+    return norm == 2 ? split_variant<HD, 2, 0>(hd) : norm == 1 ? split_variant<HD, 1, 0>(hd)
+                                                               : split_variant<HD, 0, 0>(hd);
 }
 
-template <int HD, bool kNormQ, int kKV>
+// kv: 0 (f32), DG_KV_F16 or DG_KV_BF16; the 16-bit variants take no in-kernel norm.
+SplitKernel pick_split(int hd, int norm, int kv) {
+    if (kv == DG_KV_F16) return hd > 64 ? split_variant<128, 0, DG_KV_F16>(hd) : split_variant<64, 0, DG_KV_F16>(hd);
+    if (kv == DG_KV_BF16) return hd > 64 ? split_variant<128, 0, DG_KV_BF16>(hd) : split_variant<64, 0, DG_KV_BF16>(hd);
+    return hd > 64 ? split_norm_variant<128>(hd, norm) : split_norm_variant<64>(hd, norm);
+}
+
+template <int HD, int kNorm, int kKV>
 SmallKernel small_variant(int hd) {
-    return hd == HD ? attn_small_kernel<HD, kNormQ, false, kKV> : attn_small_kernel<HD, kNormQ, true, kKV>;
+    return hd == HD ? attn_small_kernel<HD, kNorm >= 1, kNorm == 2, false, kKV>
+                    : attn_small_kernel<HD, kNorm >= 1, kNorm == 2, true, kKV>;
 }
 
-SmallKernel pick_small(int hd, bool normq, int kv) {
-    if (kv == DG_KV_F16) return hd > 64 ? small_variant<128, false, DG_KV_F16>(hd) : small_variant<64, false, DG_KV_F16>(hd);
-    if (kv == DG_KV_BF16) return hd > 64 ? small_variant<128, false, DG_KV_BF16>(hd) : small_variant<64, false, DG_KV_BF16>(hd);
-    if (hd > 64) return normq ? small_variant<128, true, 0>(hd) : small_variant<128, false, 0>(hd);
-    return normq ? small_variant<64, true, 0>(hd) : small_variant<64, false, 0>(hd);
+template <int HD>
+SmallKernel small_norm_variant(int hd, int norm) {
+    return norm == 2 ? small_variant<HD, 2, 0>(hd) : norm == 1 ? small_variant<HD, 1, 0>(hd)
+                                                               : small_variant<HD, 0, 0>(hd);
 }
 
-// Shared body of both attention entry points.  `normq` selects the q-norm variant, whose extra
-// arguments (wq, cs, qflags, eps) were validated by the caller.
+SmallKernel pick_small(int hd, int norm, int kv) {
+    if (kv == DG_KV_F16) return hd > 64 ? small_variant<128, 0, DG_KV_F16>(hd) : small_variant<64, 0, DG_KV_F16>(hd);
+    if (kv == DG_KV_BF16) return hd > 64 ? small_variant<128, 0, DG_KV_BF16>(hd) : small_variant<64, 0, DG_KV_BF16>(hd);
+    return hd > 64 ? small_norm_variant<128>(hd, norm) : small_norm_variant<64>(hd, norm);
+}
+
+// Shared body of the attention entry points.  `norm` selects the in-kernel norms (0 none, 1 q,
+// 2 q, k and v), whose extra arguments (wq, wk, cs, qflags, eps) were validated by the caller.
 int attn_call(const char* fn, const float* q, const void* kc, const void* vc, const void* k,
               const void* v, float* out, int batch, int T, int ctx, int nh, int nkv, int hd,
               float scale, int causal, void* workspace, size_t workspace_bytes, void* stream,
-              bool normq, const float* wq, const float* cs, unsigned qflags, float eps, int kv) {
+              int norm, const float* wq, const float* wk, const float* cs, unsigned qflags,
+              float eps, int kv) {
+    const bool normq = norm >= 1;
     if (batch < 0 || T < 0 || ctx < 0 || nh < 0 || nkv < 0)
         return dg::fail(DG_EINVAL, "%s: negative size (batch %d, T %d, ctx %d, nh %d, nkv %d)", fn,
                         batch, T, ctx, nh, nkv);
@@ -754,20 +953,21 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
         p.ws_bytes = 0;
     }
     const dg::Span so(out, nq * 4);
-    const dg::Span ins[8] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * esz), dg::Span(v, nkvc * esz),
+    const dg::Span ins[9] = {dg::Span(q, nq * 4), dg::Span(k, nkvc * esz), dg::Span(v, nkvc * esz),
                              dg::Span(ncache ? kc : nullptr, ncache * esz),
                              dg::Span(ncache ? vc : nullptr, ncache * esz),
                              dg::Span(normq ? wq : nullptr, (size_t)hd * 4),
+                             dg::Span(norm == 2 ? wk : nullptr, (size_t)hd * 4),
                              dg::Span(normq ? cs : nullptr, (size_t)T * 2 * hd * 4),
                              dg::Span(p.nsplit > 1 ? workspace : nullptr, p.ws_bytes)};
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 9; ++i)
         if (so.overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: out overlaps an input or the workspace", fn);
-    for (int i = 0; i < 7; ++i)
-        if (ins[7].overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: workspace overlaps an input", fn);
-    // The kernels read and write these with 16-byte vector accesses.
-    const void* vec[8] = {q, k, v, out, ncache ? kc : nullptr, ncache ? vc : nullptr,
-                          normq ? wq : nullptr, normq ? cs : nullptr};
     for (int i = 0; i < 8; ++i)
+        if (ins[8].overlaps(ins[i])) return dg::fail(DG_EINVAL, "%s: workspace overlaps an input", fn);
+    // The kernels read and write these with 16-byte vector accesses.
+    const void* vec[9] = {q, k, v, out, ncache ? kc : nullptr, ncache ? vc : nullptr,
+                          normq ? wq : nullptr, norm == 2 ? wk : nullptr, normq ? cs : nullptr};
+    for (int i = 0; i < 9; ++i)
         if (reinterpret_cast<uintptr_t>(vec[i]) & 15)
             return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
     const long long nblocks = (long long)batch * nkv * p.qblocks * p.nsplit;
@@ -786,6 +986,7 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
     a.qmul = scale * dgk::kLog2e;
     a.causal = causal;
     a.wq = normq ? wq : nullptr;
+    a.wk = norm == 2 ? wk : nullptr;
     a.cs = normq ? cs : nullptr;
     a.qflags = normq ? qflags : 0u;
     a.eps = eps;
@@ -794,10 +995,10 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
         const long long units = (long long)batch * nh;
         const long long blocks = (units + 3) / 4;
         if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
-        hipLaunchKernelGGL(pick_small(hd, normq, kv), dim3((unsigned)blocks), dim3(256), 0, s, a, units);
+        hipLaunchKernelGGL(pick_small(hd, norm, kv), dim3((unsigned)blocks), dim3(256), 0, s, a, units);
         return dg::launch_status(fn);
     }
-    hipLaunchKernelGGL(pick_split(hd, normq, kv), dim3((unsigned)nblocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(pick_split(hd, norm, kv), dim3((unsigned)nblocks), dim3(512), 0, s, a);
     if (p.nsplit > 1) {
         const size_t total = (size_t)batch * T * nh;
         const size_t threads = total * (hd / 4);
@@ -815,7 +1016,8 @@ extern "C" int dg_attn_split_gqa(const float* q, const float* kc, const float* v
                                  int nkv, int hd, float scale, int causal, void* workspace,
                                  size_t workspace_bytes, void* stream) {
     return attn_call("dg_attn_split_gqa", q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale,
-                     causal, workspace, workspace_bytes, stream, false, nullptr, nullptr, 0u, 0.0f, 0);
+                     causal, workspace, workspace_bytes, stream, 0, nullptr, nullptr, nullptr, 0u,
+                     0.0f, 0);
 }
 
 extern "C" int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs,
@@ -835,8 +1037,31 @@ extern "C" int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const fl
     if (!empty && need_w && !wq) return dg::fail(DG_EINVAL, "%s: WEIGHTED set but wq is NULL", fn);
     if (!empty && need_cs && !cs) return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
     return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal,
-                     workspace, workspace_bytes, stream, true, need_w ? wq : nullptr,
+                     workspace, workspace_bytes, stream, 1, need_w ? wq : nullptr, nullptr,
                      need_cs ? cs : nullptr, qflags, eps, 0);
+}
+
+extern "C" int dg_attn_split_gqa_qkvnorm(const float* q, const float* wq, const float* k,
+                                         const float* wk, const float* v, const float* cs,
+                                         const float* kc, const float* vc, float* out, int batch,
+                                         int T, int ctx, int nh, int nkv, int hd, unsigned flags,
+                                         float eps, float scale, int causal, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    const char* fn = "dg_attn_split_gqa_qkvnorm";
+    if (flags & ~(DG_NORM_WEIGHTED | DG_NORM_ROPE))
+        return dg::fail(DG_EINVAL, "%s: flag bits 0x%x not accepted (WEIGHTED and ROPE only)", fn,
+                        flags);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return dg::fail(DG_EINVAL, "%s: eps must be finite and >= 0", fn);
+    const bool need_w = (flags & DG_NORM_WEIGHTED) != 0;
+    const bool need_cs = (flags & DG_NORM_ROPE) != 0;
+    const bool empty = batch == 0 || T == 0;
+    if (!empty && need_w && (!wq || !wk))
+        return dg::fail(DG_EINVAL, "%s: WEIGHTED set but wq or wk is NULL", fn);
+    if (!empty && need_cs && !cs) return dg::fail(DG_EINVAL, "%s: ROPE set but cs is NULL", fn);
+    return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal,
+                     workspace, workspace_bytes, stream, 2, need_w ? wq : nullptr,
+                     need_w ? wk : nullptr, need_cs ? cs : nullptr, flags, eps, 0);
 }
 
 extern "C" int dg_attn_split_gqa_kv16(const float* q, const void* kc, const void* vc, const void* k,
@@ -847,5 +1072,5 @@ extern "C" int dg_attn_split_gqa_kv16(const float* q, const void* kc, const void
     if (kv_format != DG_KV_F16 && kv_format != DG_KV_BF16)
         return dg::fail(DG_EINVAL, "%s: kv_format must be DG_KV_F16 or DG_KV_BF16, got %d", fn, kv_format);
     return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal, workspace,
-                     workspace_bytes, stream, false, nullptr, nullptr, 0u, 0.0f, kv_format);
+                     workspace_bytes, stream, 0, nullptr, nullptr, nullptr, 0u, 0.0f, kv_format);
 }

@@ -209,6 +209,32 @@ int dg_attn_split_gqa_qnorm(const float* q, const float* wq, const float* cs, co
                             size_t workspace_bytes, void* stream);
 
 /*
+ * dg_attn_split_gqa_qkvnorm -- dg_attn_split_gqa on the RAW q, k and v projections of a canvas
+ * step: the three headnorm dispatches of `canvas_forward` (diffusion_gemma_gpu.rs, kernel
+ * DG_HEADNORM_ROPE: q weighted + roped, k weighted + roped, v the weightless, un-roped norm)
+ * run inside the attention launch.  q is normalised as dg_attn_split_gqa_qnorm does it; each
+ * canvas key/value row is normalised in on-chip memory after it is loaded, by every workgroup
+ * that reads it.  The result equals dg_qkv_headnorm_rope(q, wq, k, wk, v, cs, ..., flags, eps)
+ * followed by dg_attn_split_gqa, up to rounding; q, k and v are NOT modified.  A layer whose v
+ * is the raw k projection (the page's k_eq_v layers) passes k as v.
+ *   q       [batch, T, nh*hd] raw queries;   wq [hd], read iff WEIGHTED
+ *   k       [batch, T, nkv*hd] raw canvas keys;   wk [hd], read iff WEIGHTED
+ *   v       [batch, T, nkv*hd] raw canvas values (may be the same pointer as k)
+ *   cs      [T, 2*hd] rope table (row t = canvas row t, for q and k); read iff ROPE
+ *   kc, vc  the cache, stored normalised (and its keys roped), as for dg_attn_split_gqa
+ *   flags   DG_NORM_WEIGHTED and/or DG_NORM_ROPE, applied to q and k;  eps >= 0
+ *   every other argument as dg_attn_split_gqa (same workspace size function).
+ * Errors: as dg_attn_split_gqa, plus DG_EINVAL for flag bits other than WEIGHTED and ROPE, a
+ * negative or non-finite eps, a needed wq, wk or cs that is NULL, or out overlapping wq, wk
+ * or cs.
+ */
+int dg_attn_split_gqa_qkvnorm(const float* q, const float* wq, const float* k, const float* wk,
+                              const float* v, const float* cs, const float* kc, const float* vc,
+                              float* out, int batch, int T, int ctx, int nh, int nkv, int hd,
+                              unsigned flags, float eps, float scale, int causal,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dg_attn_split_gqa_kv16 -- dg_attn_split_gqa with keys and values stored in 16 bits (the
  * page's kv16 twin, §8(f)-style reduced-precision K/V storage): kc, vc, k and v hold f16 or
  * bf16 values (`kv_format`), in the same layouts as dg_attn_split_gqa's f32 tensors.  Every

@@ -170,6 +170,30 @@ def test_attn_qnorm_validation(L):
     assert call(T=0) == dg.DG_OK
 
 
+def test_attn_qkvnorm_validation(L):
+    f = L.dg_attn_split_gqa_qkvnorm
+    base = dict(q=FAKE, wq=FAKE + (1 << 24), k=FAKE + (2 << 24), wk=FAKE + (3 << 24),
+                v=FAKE + (4 << 24), cs=FAKE + (5 << 24), kc=FAKE + (6 << 24),
+                vc=FAKE + (7 << 24), out=FAKE + (8 << 24), batch=1, T=16, ctx=32, nh=4, nkv=2,
+                hd=64, flags=3, eps=1e-6, scale=1.0, causal=0, ws=None, wsb=0, stream=None)
+    call = lambda **kw: f(*[{**base, **kw}[k] for k in base])
+    assert call(flags=4) == dg.DG_EINVAL                    # SKIP is not accepted here
+    assert call(flags=8) == dg.DG_EINVAL                    # nor V_FROM_K (pass k as v)
+    assert call(eps=float("nan")) == dg.DG_EINVAL
+    assert call(wq=None) == dg.DG_EINVAL
+    assert call(wk=None) == dg.DG_EINVAL
+    assert call(cs=None) == dg.DG_EINVAL
+    assert call(out=FAKE + (3 << 24)) == dg.DG_EINVAL       # out overlaps wk
+    assert call(out=FAKE + (2 << 24) + 256) == dg.DG_EINVAL # out overlaps the canvas keys
+    assert call(out=FAKE + (5 << 24) + 512) == dg.DG_EINVAL # out overlaps the rope table
+    assert call(hd=66) == dg.DG_EUNSUPPORTED
+    assert call(nh=3) == dg.DG_EINVAL
+    assert call(wk=FAKE + (3 << 24) + 4) == dg.DG_EINVAL     # misaligned wk
+    assert "aligned" in _err(L)
+    assert call(T=0, wq=None, wk=None, cs=None) == dg.DG_OK
+    assert call(flags=0, T=0) == dg.DG_OK
+
+
 def test_attn_alignment_validation(L):
     f = L.dg_attn_split_gqa
     assert f(FAKE, FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24) + 8, FAKE + (4 << 24),

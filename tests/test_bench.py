@@ -86,3 +86,6 @@ def test_split_counts_match_brute_force(B, T, ctx, nh, nkv, hd, causal):
     assert nb_sep == 4 * 2 * (q + 2 * kv)
     _, _, nb_none = bench.split_counts(_case(B, T, ctx, nh, nkv, hd, causal, normed=False))
     assert nb_none == 0
+    # with every norm inside attention nothing makes a separate round trip
+    f2, a2, nb_fused = bench.split_counts(_case(B, T, ctx, nh, nkv, hd, causal), "fused")
+    assert (f2, a2, nb_fused) == (flops, attn_bytes, 0)

@@ -223,6 +223,94 @@ def test_attn_split_qnorm_flags(shape, flags):
     assert_parity(host(out), ref, "qnorm flags=%d %s" % (flags, shape))
 
 
+def qkvnorm_case(shape, flags, seed, k_eq_v=False):
+    """A split case whose q, k and v are raw projections, with the q and k weights and the rope
+    table; the reference is the oracle's three headnorms, then its attention."""
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=seed, scale=scale, causal=causal)
+    rng = np.random.default_rng(seed + 13)
+    q = (rng.standard_normal(c.q.shape) * 3.0).astype(np.float32)   # raw projection scales
+    k = (rng.standard_normal(c.k.shape) * 2.0 + 0.3).astype(np.float32)
+    v = k.copy() if k_eq_v else (rng.standard_normal(c.v.shape) * 1.5 - 0.2).astype(np.float32)
+    wq = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    wk = (1 + 0.2 * rng.standard_normal(hd)).astype(np.float32)
+    cs = oracle.rope_table(ctx, T, hd, 10000.0)
+    qn = oracle.headnorm_rope(q, wq, cs, nh, hd, flags, 1e-6)
+    kn = oracle.headnorm_rope(k, wk, cs, nkv, hd, flags, 1e-6)
+    vn = oracle.headnorm_rope(v, None, None, nkv, hd, 0, 1e-6)
+    ref = oracle.attn_split_gqa(qn, c.kc, c.vc, kn, vn, nh, nkv, hd, scale, causal)
+    return c, (q, wq, k, wk, v, cs), ref
+
+
+def run_qkvnorm(c, raw, flags, ws=None, nbytes=0, v_is_k=False):
+    q, wq, k, wk, v, cs = raw
+    out = torch.full((c.B, c.T, c.nh * c.hd), float("nan"), device="cuda")
+    qd, kd = dev(q), dev(k)
+    vd = kd if v_is_k else dev(v)
+    dg.dg_attn_split_gqa_qkvnorm(qd, dev(wq) if flags & 1 else None, kd,
+                                 dev(wk) if flags & 1 else None, vd,
+                                 dev(cs) if flags & 2 else None, dev(c.kc), dev(c.vc), out, c.B,
+                                 c.T, c.ctx, c.nh, c.nkv, c.hd, flags, 1e-6, c.scale,
+                                 int(c.causal), ws, nbytes)
+    got = host(out)
+    assert np.array_equal(host(qd), q) and np.array_equal(host(kd), k), "inputs must stay raw"
+    if not v_is_k:
+        assert np.array_equal(host(vd), v), "inputs must stay raw"
+    return got
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["unsplit", "ws"])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "B%d_T%d_ctx%d_h%d_kv%d_hd%d_c%d" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], s[7]))
+def test_attn_split_qkvnorm_small(shape, use_ws):
+    """q, k and v normed (and q, k roped) inside the attention kernel == the three headnorms,
+    then attention; q, k and v are left unchanged."""
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    flags = dg.DG_NORM_WEIGHTED | dg.DG_NORM_ROPE
+    c, raw, ref = qkvnorm_case(shape, flags, seed=5 * T + ctx)
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd) if use_ws else (None, 0)
+    assert_parity(run_qkvnorm(c, raw, flags, ws, nbytes), ref, "qkvnorm %s ws=%d" % (shape, nbytes))
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", [(1, 40, 90, 4, 2, 128, 1.0, False), (2, 6, 2, 4, 2, 64, 0.5, True),
+                                   (1, 70, 0, 8, 2, 64, 0.3, True), (1, 33, 20, 4, 2, 80, 1.0, False),
+                                   (1, 4, 3, 2, 1, 20, 1.0, False), (1, 64, 2000, 4, 2, 96, 1.0, False)],
+                         ids=["hd128", "short-set", "causal-hd64", "hd80", "short-set-hd20",
+                              "split-kv-hd96"])
+def test_attn_split_qkvnorm_flags(shape, flags):
+    B, T, ctx, nh, nkv, hd, scale, causal = shape
+    c, raw, ref = qkvnorm_case(shape, flags, seed=17 + flags)
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
+    assert_parity(run_qkvnorm(c, raw, flags, ws, nbytes), ref, "qkvnorm flags=%d %s" % (flags, shape))
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 2000, 4, 2, 128), (2, 40, 700, 8, 8, 64),
+                                   (1, 256, 1024, 16, 8, 128), (1, 3, 5000, 2, 1, 64),
+                                   (1, 64, 2000, 4, 2, 96), (1, 250, 1000, 16, 8, 128),
+                                   (1, 100, 165, 8, 4, 128)])
+def test_attn_split_qkvnorm_split_kv(shape):
+    """Split-KV with the tiles dealt round robin to the splits (canvas tiles spread over them,
+    a seam tile across cache and canvas when ctx is not a multiple of 32)."""
+    B, T, ctx, nh, nkv, hd = shape
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
+    assert nbytes > 0, "this shape is expected to take the split-KV path"
+    c, raw, ref = qkvnorm_case((B, T, ctx, nh, nkv, hd, 1.0, False), 3, seed=ctx + T)
+    assert_parity(run_qkvnorm(c, raw, 3, ws, nbytes), ref, "qkvnorm split-kv %s" % (shape,))
+    assert_parity(run_qkvnorm(c, raw, 3), ref, "qkvnorm unsplit %s" % (shape,))
+
+
+@pytest.mark.parametrize("shape", [(1, 40, 90, 4, 2, 128, 1.0, False), (2, 5, 3, 4, 2, 128, 1.0, False),
+                                   (1, 64, 2000, 4, 2, 96, 1.0, False)],
+                         ids=["hd128", "short-set", "split-kv-hd96"])
+def test_attn_split_qkvnorm_k_eq_v(shape):
+    """A k_eq_v layer passes its raw k as v: v = the weightless norm of the raw k."""
+    B, T, ctx, nh, nkv, hd = shape[:6]
+    c, raw, ref = qkvnorm_case(shape, 3, seed=23, k_eq_v=True)
+    ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
+    assert_parity(run_qkvnorm(c, raw, 3, ws, nbytes, v_is_k=True), ref, "qkvnorm k_eq_v %s" % (shape,))
+
+
 def test_attn_split_zero_canvas_is_noop_and_nonfinite_free():
     out = torch.full((1, 4, 128), 7.0, device="cuda")
     q = torch.zeros(1, 4, 128, device="cuda")
@@ -259,7 +347,7 @@ def run_block(case, steps=None, norm_mode="in_attention"):
     return blk, outs
 
 
-NORM_MODES = ["in_attention", "one_launch", "separate"]
+NORM_MODES = ["fused", "in_attention", "one_launch", "separate"]
 
 
 @pytest.mark.parametrize("norm_mode", NORM_MODES)
@@ -281,7 +369,7 @@ def test_dg_canvas_48_steps(norm_mode):
         assert_parity(outs[s], ref, "dg step %d" % s)
 
 
-@pytest.mark.parametrize("norm_mode", ["in_attention", "one_launch"])
+@pytest.mark.parametrize("norm_mode", ["fused", "in_attention", "one_launch"])
 def test_long_cache_every_element(norm_mode):
     c = synth.long_cache()
     _, (got,) = run_block(c, norm_mode=norm_mode)
@@ -581,7 +669,7 @@ def test_canvas_step_kv16(fmt, name):
 
 # ----------------------------------------------------------------------------- HIP graphs
 
-@pytest.mark.parametrize("norm_mode", ["in_attention", "one_launch"])
+@pytest.mark.parametrize("norm_mode", ["fused", "in_attention", "one_launch"])
 def test_canvas_step_graph_replays(norm_mode):
     """A canvas step captured as a HIP graph: every replay (with fresh inputs copied in place,
     eager launches and synchronisations in between) equals the eager step on the same inputs."""
@@ -635,8 +723,9 @@ SWEEP = _sweep_shapes(40, seed=2024)
 
 @pytest.mark.parametrize("i", range(len(SWEEP)))
 def test_split_shape_sweep(i):
-    """Each random shape through all three attention entry points: plain (with and without the
-    split-KV workspace), q norm inside attention, and 16-bit K/V."""
+    """Each random shape through all four attention entry points: plain (with and without the
+    split-KV workspace), q norm inside attention, all three norms inside attention, and 16-bit
+    K/V."""
     shape = SWEEP[i]
     B, T, ctx, nh, nkv, hd, scale, causal = shape
     c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=100 + i, scale=scale, causal=causal)
@@ -655,6 +744,8 @@ def test_split_shape_sweep(i):
                                dev(cq.v), out, B, T, ctx, nh, nkv, hd, flags, 1e-6, scale,
                                int(causal), ws, nbytes)
     assert_parity(host(out), refq, "sweep qnorm %d %s" % (i, shape))
+    ck, raw, refk = qkvnorm_case(shape, flags, seed=400 + i)
+    assert_parity(run_qkvnorm(ck, raw, flags, ws, nbytes), refk, "sweep qkvnorm %d %s" % (i, shape))
     fmt = dg.DG_KV_BF16 if i % 2 else dg.DG_KV_F16
     c16, pk, wd = kv16_case(shape, fmt, seed=300 + i)
     ref16 = oracle.attn_split_gqa(c16.q, wd["kc"], wd["vc"], wd["k"], wd["v"], nh, nkv, hd, scale,
