@@ -56,6 +56,8 @@ class CanvasBlock:
     ctx positions just before pos0.  normed: normalise q, k and v in each step, as `norm_mode`
     says.  k_eq_v: the layer has no v projection; each step's v buffer is written with the
     weightless norm of the raw k (its input contents are ignored).
+    workspace: an optional GPU tensor to use as the split-KV scratch (e.g. one shared by the
+    layers of a stack, which run one after another on one stream); one is allocated otherwise.
     kv16: None (f32 K/V) or "f16" / "bf16": the cache is packed once into 16-bit twins here, each
     step's one-launch norm also writes 16-bit twins of its normalised canvas k and v (with
     "separate" norms a pack pass writes them), and the attention widens them to f32 as it
@@ -65,7 +67,7 @@ class CanvasBlock:
     def __init__(self, B, T, ctx, nh, nkv, hd, kc=None, vc=None, wq=None, wk=None, *,
                  eps=1e-6, theta=10000.0, scale=1.0, causal=False, rope_cache=False,
                  normed=True, norm_mode="auto", use_workspace=True, pos0=None, cs=None,
-                 k_eq_v=False, kv16=None, device="cuda"):
+                 k_eq_v=False, kv16=None, workspace=None, device="cuda"):
         if kv16 is not None and kv16 not in KV_FORMATS:
             raise ValueError("kv16 must be None, 'f16' or 'bf16'")
         if kv16 is not None and norm_mode in ("auto", "fused", "in_attention"):
@@ -102,8 +104,13 @@ class CanvasBlock:
             self.k16, self.v16 = half(nk), half(nk)
         self.ws_bytes = dg_attn_split_gqa_workspace_size(B, T, ctx, nh, nkv, hd) \
             if use_workspace else 0
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
-            if self.ws_bytes > 0 else None
+        if self.ws_bytes > 0 and workspace is not None:
+            if workspace.numel() * workspace.element_size() < self.ws_bytes:
+                raise ValueError("workspace holds fewer than the %d bytes needed" % self.ws_bytes)
+            self.ws = workspace
+        else:
+            self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
+                if self.ws_bytes > 0 else None
         if self.norm_mode == "auto":
             self.norm_mode = "fused" if self.ws_bytes > 0 else "in_attention"
 
@@ -233,12 +240,22 @@ class CanvasStack:
             if len({l.hd for l in self.layers if l.sliding == sliding}) > 1:
                 raise ValueError("all layers of one type share one head dim (one rope table)")
         self.tables = tables
+        # Layers of one shape share a split-KV scratch (they run in order on one stream): the
+        # partials then land in the lines the last such layer's combine read on the same XCD.
+        self.ws = {}
+        if use_workspace:
+            for l in self.layers:
+                key = (l.ctx, l.nkv, l.hd)
+                need = dg_attn_split_gqa_workspace_size(B, T, l.ctx, nh, l.nkv, l.hd)
+                if key not in self.ws and need > 0:
+                    self.ws[key] = torch.empty(need, dtype=torch.uint8, device=device)
         self.blocks = []
         for l, (kc, vc), (wq, wk) in zip(self.layers, caches, weights):
             self.blocks.append(CanvasBlock(
                 B, T, l.ctx, nh, l.nkv, l.hd, kc, vc, wq, wk, eps=eps, scale=scale,
                 norm_mode=norm_mode, use_workspace=use_workspace, pos0=pos0,
-                cs=tables[(l.sliding, l.hd)], k_eq_v=l.k_eq_v, device=device))
+                cs=tables[(l.sliding, l.hd)], k_eq_v=l.k_eq_v,
+                workspace=self.ws.get((l.ctx, l.nkv, l.hd)), device=device))
 
     def step(self, li, q, k, v, out):
         """Layer li's attention for this canvas step (q, k, v are its projections; for a

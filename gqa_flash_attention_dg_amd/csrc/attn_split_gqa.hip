@@ -784,15 +784,33 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
 // One thread per 4 output elements (hd is a multiple of 4).  Splits are taken 8 at a time with
 // all their loads issued together, and the running maximum is folded in as it grows (the
 // same rescaling as the online softmax), so no pass waits for a previous one.
+// With `local`, threads are numbered (batch, kv head, query vector of the group, chunk) and
+// workgroups are placed as the attention kernel placed its own, so each kv head's partials
+// are merged on the XCD whose workgroups wrote them (the launch sets it only when both grids
+// divide evenly into the 8 XCDs and each kv head fills whole workgroups).
 __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restrict__ ws,
                                                             float* __restrict__ out,
-                                                            size_t total, int nsplit, int hd) {
+                                                            size_t total, int nsplit, int hd,
+                                                            int T, int G, int nkv, int local) {
     constexpr int kBatch = 8;
     const int c4 = hd / 4;
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total * c4) return;
-    const size_t gq = idx / c4;
-    const int c = (int)(idx % c4) * 4;
+    size_t gq;
+    int c;
+    if (local) {
+        const size_t idx = (size_t)xcd_remap(blockIdx.x, gridDim.x) * blockDim.x + threadIdx.x;
+        if (idx >= total * c4) return;
+        const size_t per_bk = (size_t)T * G * c4;
+        const size_t bk = idx / per_bk, rem = idx % per_bk;
+        const int qv = (int)(rem / c4);
+        c = (int)(rem % c4) * 4;
+        const size_t b = bk / nkv, kv = bk % nkv;
+        gq = (b * T + qv / G) * ((size_t)nkv * G) + kv * G + qv % G;
+    } else {
+        const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (idx >= total * c4) return;
+        gq = idx / c4;
+        c = (int)(idx % c4) * 4;
+    }
     const float* wm = ws + (size_t)nsplit * total * hd;
     const float* wl = wm + (size_t)nsplit * total;
     float M = -INFINITY, L = 0.0f;
@@ -1003,8 +1021,10 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
         const size_t total = (size_t)batch * T * nh;
         const size_t threads = total * (hd / 4);
         const unsigned blocks = (unsigned)((threads + 255) / 256);
+        const int local = nblocks % 8 == 0 && blocks % 8 == 0 &&
+                          ((size_t)T * a.G * (hd / 4)) % 256 == 0;
         hipLaunchKernelGGL(split_combine_kernel, dim3(blocks), dim3(256), 0, s, (const float*)a.ws,
-                           out, total, p.nsplit, hd);
+                           out, total, p.nsplit, hd, T, a.G, nkv, local);
     }
     return dg::launch_status(fn);
 }
