@@ -78,6 +78,11 @@ __device__ inline int xcd_remap(int bid, int n) {
 // dh [nwin][heads][n][gh], then dw [nwin][heads][n][gw].
 constexpr int kBiasWaves = 4;
 
+// Both bias kernels number their workgroups through xcd_remap over a grid padded to a multiple
+// of 8 (the padding workgroups have no task), so the rows of one (window, head) are written on
+// the XCD whose attention workgroups read them: writing lines that another XCD's L2 has just
+// read was measured to be the slow case for the split-KV workspace.
+//
 // Lines of at most 16 queries against at most 16 table rows (windowed grids): one 16x16 tile
 // per line with v_mfma_f32_16x16x4f32, a quarter of the 32x32 tile's matrix work.  Lane l
 // supplies query row l%16 (A) and table row l%16 (B) at contraction index k = l/16; step
@@ -88,7 +93,8 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs 
                                                                        long long ntasks) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
-    const long long task = (long long)blockIdx.x * kBiasWaves + (threadIdx.x >> 6);
+    const long long task =
+        (long long)xcd_remap(blockIdx.x, gridDim.x) * kBiasWaves + (threadIdx.x >> 6);
     if (task >= ntasks) return;  // wave-uniform; task = unit * (gh + gw) + line
     const int line = (int)(task % (a.gh + a.gw));
     const int unit = (int)(task / (a.gh + a.gw));
@@ -125,7 +131,8 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs 
 __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias_kernel(RelArgs a, float* __restrict__ dhw,
                                                                      long long ntasks) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
-    const long long task = (long long)blockIdx.x * kBiasWaves + (threadIdx.x >> 6);
+    const long long task =
+        (long long)xcd_remap(blockIdx.x, gridDim.x) * kBiasWaves + (threadIdx.x >> 6);
     if (task >= ntasks) return;  // wave-uniform
     // task = ((unit * (gh + gw) + line) * 2 + qt) * 2 + rt, unit = win * heads + head
     const int rt = (int)(task & 1), qt = (int)((task >> 1) & 1);
@@ -487,7 +494,8 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     if (use_ws) {
         const bool b16 = gh <= 16 && gw <= 16;   // every line fits one 16x16 tile
         const long long ntasks = (long long)nwin * heads * (gh + gw) * (b16 ? 1 : 4);
-        const dim3 grid((unsigned)((ntasks + kBiasWaves - 1) / kBiasWaves));
+        const long long nbias = (ntasks + kBiasWaves - 1) / kBiasWaves;
+        const dim3 grid((unsigned)((nbias + 7) / 8 * 8));   // a multiple of 8 for xcd_remap
         if (b16)
             hipLaunchKernelGGL(relpos_bias16_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
                                static_cast<float*>(workspace), ntasks);

@@ -159,9 +159,14 @@ def test_attn_split_small(shape, use_ws):
 
 @pytest.mark.parametrize("shape", [(1, 64, 2000, 4, 2, 128), (2, 40, 700, 8, 8, 64),
                                    (1, 256, 1024, 16, 8, 128), (1, 3, 5000, 2, 1, 64),
-                                   (1, 64, 2000, 4, 2, 96)])
+                                   (1, 64, 2000, 4, 2, 96), (2, 256, 1024, 16, 8, 128),
+                                   (3, 128, 900, 8, 2, 64), (1, 250, 1000, 16, 8, 128)])
 def test_attn_split_kv_partials_and_combine(shape):
-    """Shapes with few workgroups split the key range across workgroups and merge partials."""
+    """Shapes with few workgroups split the key range across workgroups and merge partials.
+    The combine runs in XCD order (one kv head's partials per XCD) where both grids divide
+    over the 8 XCDs and a kv head fills whole combine workgroups -- here at the 128-wide head
+    dims with T*G*hd/4 a multiple of 256, batches of 1 to 3 -- and in plain order otherwise
+    (T 250, T 40, T 3)."""
     B, T, ctx, nh, nkv, hd = shape
     ws, nbytes = workspace_for(B, T, ctx, nh, nkv, hd)
     assert nbytes > 0, "this shape is expected to take the split-KV path"
@@ -288,7 +293,8 @@ def test_attn_split_qkvnorm_flags(shape, flags):
 @pytest.mark.parametrize("shape", [(1, 64, 2000, 4, 2, 128), (2, 40, 700, 8, 8, 64),
                                    (1, 256, 1024, 16, 8, 128), (1, 3, 5000, 2, 1, 64),
                                    (1, 64, 2000, 4, 2, 96), (1, 250, 1000, 16, 8, 128),
-                                   (1, 100, 165, 8, 4, 128)])
+                                   (1, 100, 165, 8, 4, 128), (2, 256, 1024, 16, 8, 128),
+                                   (3, 128, 900, 8, 2, 64)])
 def test_attn_split_qkvnorm_split_kv(shape):
     """Split-KV with the tiles dealt round robin to the splits (canvas tiles spread over them,
     a seam tile across cache and canvas when ctx is not a multiple of 32)."""
