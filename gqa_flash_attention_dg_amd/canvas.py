@@ -10,10 +10,10 @@ the raw k projection, normalised without weight or rope.
 
 Set-up work (rope tables, roping a cache that is stored un-roped) happens once per canvas
 block in the constructor; `step` is the per-denoising-step hot path.  Four ways to run the
-norms of a step (`norm_mode`), plus "auto" (the default), which takes "fused" when the
-attention splits its key range across workgroups (each workgroup then sees at most a few
-canvas tiles, so normalising them in place costs less than a launch) and "in_attention"
-otherwise (a workgroup that walks the whole key range would norm every canvas tile itself):
+norms of a step (`norm_mode`), plus "auto" (the default), which takes "fused" when each
+attention workgroup meets at most AUTO_FUSED_TILES canvas tiles of 32 keys (a split key
+range, or a short canvas: normalising them in place costs less than a launch) and
+"in_attention" otherwise (a workgroup that walks many canvas tiles would norm each itself):
   "fused"         all three norms inside the attention launch: q as it is staged, the canvas
                   k and v rows as their tiles land in on-chip memory (q, k and v are not
                   written; a k_eq_v layer's v buffer is neither read nor written);
@@ -36,6 +36,9 @@ from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM
 KV_FORMATS = {"f16": DG_KV_F16, "bf16": DG_KV_BF16}
 
 NORM_MODES = ("auto", "fused", "in_attention", "one_launch", "separate")
+# Canvas tiles per attention workgroup up to which "auto" norms k and v inside the kernel:
+# measured faster at 1 tile (a split key range, or a canvas of at most 32 rows), slower at 8.
+AUTO_FUSED_TILES = 2
 
 
 def rope_table(pos0, T, hd, theta, device="cuda"):
@@ -112,7 +115,11 @@ class CanvasBlock:
             self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
                 if self.ws_bytes > 0 else None
         if self.norm_mode == "auto":
-            self.norm_mode = "fused" if self.ws_bytes > 0 else "in_attention"
+            # the workspace holds nsplit partials of (hd + 2) floats per query vector
+            nsplit = max(1, self.ws_bytes // (B * T * nh * (hd + 2) * 4))
+            tiles = (T + 31) // 32                       # canvas tiles of 32 keys
+            per_wg = (tiles + nsplit - 1) // nsplit      # ... met by one workgroup
+            self.norm_mode = "fused" if per_wg <= AUTO_FUSED_TILES else "in_attention"
 
     def norm(self, q, k, v):
         """The page's per-step headnorm calls, in place on q, k and v (for a k_eq_v layer the
