@@ -325,12 +325,7 @@ __device__ inline void norm_canvas_tile(const SplitArgs& a, float* __restrict__ 
     }
 }
 
-// Workgroup id -> logical id such that consecutive logical ids share an XCD (the hardware
-// deals workgroups to the 8 XCDs round robin).
-__device__ inline int xcd_remap(int bid, int n) {
-    if ((n & 7) != 0) return bid;
-    return (bid & 7) * (n >> 3) + (bid >> 3);
-}
+using dg::xcd_remap;
 
 // kPad: the head dim hd is narrower than the HD-wide tile (hd < HD, a multiple of 4).  Queries
 // are zero past hd; key/value rows are loaded with their chunks past hd taken from a valid

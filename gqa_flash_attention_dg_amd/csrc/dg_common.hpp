@@ -1,5 +1,6 @@
-// dg_common.hpp -- host-side helpers shared by the entry points of libdgattn.so:
-// the per-thread error message, argument checks and launch-error capture.
+// dg_common.hpp -- helpers shared by the entry points and kernels of libdgattn.so: the
+// per-thread error message, argument checks, launch-error capture, and the XCD placement of
+// workgroups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,6 +37,14 @@ inline bool mul_ok(size_t& acc, long long f) {
     if (f != 0 && acc > (SIZE_MAX / 8) / static_cast<size_t>(f)) return false;
     acc *= static_cast<size_t>(f);
     return true;
+}
+
+// Workgroup id -> logical id such that consecutive logical ids share an XCD: the hardware deals
+// the workgroups of a launch to the 8 XCDs round robin (workgroup b runs on XCD b % 8), so
+// logical id l runs on XCD l / (n / 8).  A grid that is not a multiple of 8 keeps its order.
+__device__ inline int xcd_remap(int bid, int n) {
+    if ((n & 7) != 0) return bid;
+    return (bid & 7) * (n >> 3) + (bid >> 3);
 }
 
 inline int launch_status(const char* what) {

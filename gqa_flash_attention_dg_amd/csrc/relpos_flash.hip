@@ -63,10 +63,7 @@ struct RelArgs {
     int tsh, ta, tmsk, tb, tl0, td, ntiles;
 };
 
-__device__ inline int xcd_remap(int bid, int n) {
-    if ((n & 7) != 0) return bid;
-    return (bid & 7) * (n >> 3) + (bid >> 3);
-}
+using dg::xcd_remap;
 
 // Bias rows in log2 units, the page's DHDW step, as small matrix products on MFMA.  A "line"
 // is one grid row qy (its gw queries against the gh table rows Rh[qy, :]) or one grid column qx

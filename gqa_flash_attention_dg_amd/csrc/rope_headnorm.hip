@@ -59,6 +59,7 @@ struct NormArgs {
     int T, hd;
     float eps;
     int fmt16;        // DG_KV_F16 or DG_KV_BF16 when a segment has twins
+    int kvmajor;      // exactly k and v of one shape: rows taken in (b*heads + h, k|v, t) order
 };
 
 // kHD: the head dim when it is 128 or 64 (no per-lane guards), 0 for any other hd <= 128.  Lanes
@@ -139,14 +140,30 @@ __device__ inline void headnorm_row(float* __restrict__ xr, const float* __restr
 }
 
 // Rows of all segments are numbered consecutively (segment 0 first); each wavefront takes one.
+// With kvmajor (the k and v of a canvas step) rows go in (batch * heads + head, k|v, token)
+// order instead, with workgroups placed by xcd_remap: the attention kernel reads the canvas
+// rows of each (batch, kv head) on one XCD, and the norm then rewrites them on that XCD too
+// (writing lines that another XCD has just read is the slow case).
 template <int kHD>
 __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
-    long long u = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    long long u;
     // The segment is found with constant indices into the arguments, so its fields come from
     // scalar loads (a computed index would read them through per-lane memory loads).
     NormSeg g = a.seg[0];
-    if (u >= g.rows) {
+    if (a.kvmajor) {
+        const long long r =
+            (long long)dg::xcd_remap(blockIdx.x, gridDim.x) * kRowsPerBlock + (threadIdx.x >> 6);
+        if (r >= 2 * g.rows) return;
+        const long long bh = r / (2 * a.T);
+        const int rem = (int)(r % (2 * a.T));
+        const int t = rem % a.T;
+        if (rem >= a.T) g = a.seg[1];
+        u = ((bh / g.heads) * a.T + t) * g.heads + bh % g.heads;
+    } else {
+        u = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    }
+    if (!a.kvmajor && u >= g.rows) {
         u -= g.rows;
         if (a.nseg < 2) return;
         g = a.seg[1];
@@ -299,6 +316,7 @@ int qkv_norm_call(const char* fn, float* q, const float* wq, float* k, const flo
     a.hd = hd;
     a.eps = eps;
     a.fmt16 = fmt16;
+    a.kvmajor = !do_q && do_k && do_v && !v_from_k;   // two segments of nkv heads, T rows each
     return launch_norm(fn, a, stream);
 }
 
