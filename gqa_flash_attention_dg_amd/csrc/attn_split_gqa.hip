@@ -157,9 +157,16 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
         w[k] = weighted && e0 < hd ? *reinterpret_cast<const float4*>(a.wq + e0)
                                    : make_float4(1.f, 1.f, 1.f, 1.f);
     }
+    // Lane group g (8 lanes) takes vectors kPasses*g + pass, consecutive vectors in successive
+    // passes: with an even G they are heads of one canvas row, and the row's cos|sin entries,
+    // loaded in the first pass, serve the next as well (half the table reads of the burst
+    // that opens every workgroup).
+    constexpr int kPasses = kBlockQ / (8 * kWaves);
+    float4 co[kPerLane], si[kPerLane];
+    int cs_row = -1;   // canvas row whose entries co/si hold
 #pragma unroll 1
-    for (int pass = 0; pass < kBlockQ / (8 * kWaves); ++pass) {
-        const int vloc = (pass * kWaves + wave) * 8 + sub;
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int vloc = (wave * 8 + sub) * kPasses + pass;
         const int qv = qb * kBlockQ + vloc;
         const bool valid = qv < nq;
         const int row = valid ? qv / a.G : 0;
@@ -190,7 +197,18 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
 #pragma unroll
             for (int k = 0; k < kPerLane; ++k)
                 *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) = x[k];
-            const float* cr = a.cs + (size_t)row * 2 * hd;
+            if (row != cs_row) {   // the same for the 8 lanes of a vector
+                const float* cr = a.cs + (size_t)row * 2 * hd;
+#pragma unroll
+                for (int k = 0; k < kPerLane; ++k) {
+                    const int e0 = 4 * (c + 8 * k);
+                    co[k] = e0 < hd ? *reinterpret_cast<const float4*>(cr + e0)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+                    si[k] = e0 < hd ? *reinterpret_cast<const float4*>(cr + hd + e0)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                cs_row = row;
+            }
             float part[kPerLane][4];
 #pragma unroll
             for (int k = 0; k < kPerLane; ++k)
@@ -204,10 +222,9 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
             for (int k = 0; k < kPerLane; ++k) {
                 const int e0 = 4 * (c + 8 * k);
                 if (e0 < hd) {
-                    const float4 co = *reinterpret_cast<const float4*>(cr + e0);
-                    const float4 si = *reinterpret_cast<const float4*>(cr + hd + e0);
                     const float y[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-                    const float cc[4] = {co.x, co.y, co.z, co.w}, sn[4] = {si.x, si.y, si.z, si.w};
+                    const float cc[4] = {co[k].x, co[k].y, co[k].z, co[k].w};
+                    const float sn[4] = {si[k].x, si[k].y, si[k].z, si[k].w};
                     float r[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
