@@ -41,6 +41,17 @@ NORM_MODES = ("auto", "fused", "in_attention", "one_launch", "separate")
 AUTO_FUSED_TILES = 2
 
 
+def auto_norm_mode(B, T, nh, hd, ws_bytes):
+    """The norm mode "auto" stands for, given the split-KV workspace size of the attention call
+    (0 when it does not split): "fused" when one attention workgroup meets at most
+    AUTO_FUSED_TILES canvas tiles of 32 keys, "in_attention" otherwise."""
+    # the workspace holds nsplit partials of (hd + 2) floats per query vector
+    nsplit = max(1, ws_bytes // (B * T * nh * (hd + 2) * 4)) if B * T * nh > 0 else 1
+    tiles = (T + 31) // 32                       # canvas tiles of 32 keys
+    per_wg = (tiles + nsplit - 1) // nsplit      # ... met by one workgroup
+    return "fused" if per_wg <= AUTO_FUSED_TILES else "in_attention"
+
+
 def rope_table(pos0, T, hd, theta, device="cuda"):
     """[T, 2*hd] cos|sin table for positions pos0..pos0+T-1 (one launch)."""
     cs = torch.empty((T, 2 * hd), dtype=torch.float32, device=device)
@@ -115,11 +126,7 @@ class CanvasBlock:
             self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
                 if self.ws_bytes > 0 else None
         if self.norm_mode == "auto":
-            # the workspace holds nsplit partials of (hd + 2) floats per query vector
-            nsplit = max(1, self.ws_bytes // (B * T * nh * (hd + 2) * 4))
-            tiles = (T + 31) // 32                       # canvas tiles of 32 keys
-            per_wg = (tiles + nsplit - 1) // nsplit      # ... met by one workgroup
-            self.norm_mode = "fused" if per_wg <= AUTO_FUSED_TILES else "in_attention"
+            self.norm_mode = auto_norm_mode(B, T, nh, hd, self.ws_bytes)
 
     def norm(self, q, k, v):
         """The page's per-step headnorm calls, in place on q, k and v (for a k_eq_v layer the
