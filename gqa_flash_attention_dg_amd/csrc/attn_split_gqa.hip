@@ -128,6 +128,22 @@ __device__ inline void accumulate_pv16(const char* __restrict__ vs, int l32, int
     }
 }
 
+// Sum of v over each aligned group of N lanes (N = 8 or 16), left in every lane of the group,
+// with DPP lane moves within the lanes' own registers: two quad permutes (lane ^ 1, lane ^ 2),
+// then the mirror within 8 lanes and, for 16, within 16.  Each step adds a value and its
+// partner's in the same order on both sides, so every lane of a group ends with the same sum.
+// (A lane shuffle goes through the LDS crossbar and waits out its latency at every step.)
+template <int N>
+__device__ inline float group_sum(float v) {
+    static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if constexpr (N == 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // Row stride (floats) of the normalised queries staged in LDS: HD + 4 keeps the 16-byte
 // operand reads (32 lanes on 32 different rows) free of bank conflicts.
 template <int HD>
@@ -182,9 +198,7 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
             ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
         }
-        ss += __shfl_xor(ss, 1);
-        ss += __shfl_xor(ss, 2);
-        ss += __shfl_xor(ss, 4);
+        ss = group_sum<8>(ss);
         const float inv = norm ? (valid ? 1.0f / sqrtf(ss / (float)hd + a.eps) : 0.0f) : 1.0f;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
@@ -277,8 +291,7 @@ __device__ inline void norm_canvas_tile(const SplitArgs& a, float* __restrict__ 
                                         : make_float4(0.f, 0.f, 0.f, 0.f);
             ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
         }
-#pragma unroll
-        for (int m = 1; m < L; m <<= 1) ss += __shfl_xor(ss, m);
+        ss = group_sum<L>(ss);
         const float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
         const bool weighted = !isv && (a.qflags & DG_NORM_WEIGHTED);
         const bool rope = !isv && (a.qflags & DG_NORM_ROPE);
@@ -497,9 +510,10 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         const int buf = st & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
         __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
+        if (!hi && st + 1 < nst) issue_stage(st + 1, buf ^ 1);
         if constexpr (kNormKV) {
-            // Canvas rows are normalised in place before anyone reads them.  The next stage is
-            // issued after that, so the norm's weight and table loads do not queue behind it.
+            // Canvas rows are normalised in place before anyone reads them (the next stage's
+            // loads, issued just before, stream in meanwhile).
             const int ja = key0(st, 0), jb = key0(st, 1);
             const bool ca = ja < kend && ja + dgk::kKeys > a.ctx;
             const bool cb = jb < kend && jb + dgk::kKeys > a.ctx;
@@ -515,7 +529,6 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
                 __syncthreads();
             }
         }
-        if (!hi && st + 1 < nst) issue_stage(st + 1, buf ^ 1);
         const int t0 = key0(st, hi);
         if (pair_active && t0 < kend) {
             f32x16 s;
@@ -657,9 +670,7 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < SEG; ++e) ss += qr[e] * qr[e];
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
+            ss = group_sum<8>(ss);
             const float inv = has_q ? 1.0f / sqrtf(ss / (float)hd + a.eps) : 0.0f;
 #pragma unroll
             for (int e = 0; e < SEG; ++e) {
@@ -703,12 +714,8 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
             ssk += kr[e] * kr[e];
             ssv += vr[e] * vr[e];
         }
-        ssk += __shfl_xor(ssk, 1);
-        ssk += __shfl_xor(ssk, 2);
-        ssk += __shfl_xor(ssk, 4);
-        ssv += __shfl_xor(ssv, 1);
-        ssv += __shfl_xor(ssv, 2);
-        ssv += __shfl_xor(ssv, 4);
+        ssk = group_sum<8>(ssk);
+        ssv = group_sum<8>(ssv);
         if (canvas_key) {
             const float invk = 1.0f / sqrtf(ssk / (float)hd + a.eps);
             const float invv = 1.0f / sqrtf(ssv / (float)hd + a.eps);
@@ -756,9 +763,7 @@ __global__ void __launch_bounds__(256) attn_small_kernel(SplitArgs a, long long 
             const float4 k4 = *reinterpret_cast<const float4*>(ks + j * HD + cseg + e);
             d += qr[e] * k4.x + qr[e + 1] * k4.y + qr[e + 2] * k4.z + qr[e + 3] * k4.w;
         }
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        d += __shfl_xor(d, 4);
+        d = group_sum<8>(d);
         const bool visible = j < S && !(a.causal && j >= a.ctx && j - a.ctx > r);
         sc[j] = visible ? d : -INFINITY;
     }
