@@ -65,6 +65,10 @@ struct RelArgs {
 
 using dg::xcd_remap;
 
+// Reads the height-bias table in LDS (a separate array that the direct-to-LDS loads never
+// write).
+__device__ inline float tab_read(const float* __restrict__ tab, int i) { return tab[i]; }
+
 // Bias rows in log2 units, the page's DHDW step, as small matrix products on MFMA.  A "line"
 // is one grid row qy (its gw queries against the gh table rows Rh[qy, :]) or one grid column qx
 // (its gh queries against Rw[qx, :]); its output is [queries x table rows] = Q_line T^T with a
@@ -345,24 +349,45 @@ __global__ void __launch_bounds__(64 * kWavesT)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // stage st has landed everywhere, stage st-1 is consumed (and the
                           // bias tables are complete before the first use)
-        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
         const int t = st * kParts + part;
+        // The height-bias table values of this tile (one per step; a row tile has at most 8 rows,
+        // so at most 4 steps).  An LDS read issued after the next stage's loads makes the
+        // compiler wait for all of them (s_waitcnt vmcnt(0)) before the tile's first K read, so
+        // the issuing wavefront stalls until its next stage has landed.  In the 4 x 1 shape,
+        // where every wavefront issues, the values are read before the loads go out (measured:
+        // SAM windows 65.0 -> 64.1 us); in the 8-wavefront shapes the issuing wavefront's SIMD
+        // partner covers the stall, and reading early measured slower (64 x 64: 450 -> 454 us).
+        constexpr int kMaxShift = 4;
+        float dhv[kMaxShift] = {0.0f, 0.0f, 0.0f, 0.0f};
+        auto read_dh = [&]() {
+            if (!(active && t < a.ntiles)) return;
+            const int row0 = tl.half_rows ? (t >> 1) : t * tl.rpt;
+            if (kOneShift) {
+                dhv[0] = tab_read(dh_tab, min(row0 + (tl.half_rows ? 0 : half), a.gh - 1) * dgk::kQuery + l32);
+            } else {
+#pragma unroll
+                for (int ms = 0; ms < kMaxShift; ++ms) {
+                    const int ky = row0 + 2 * ms + half;
+                    if (ms < tl.nshift && ky < a.gh) dhv[ms] = tab_read(dh_tab, ky * dgk::kQuery + l32);
+                }
+            }
+        };
+        if constexpr (kParts == 1) read_dh();
+        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
+        if constexpr (kParts != 1) read_dh();
         if (active && t < a.ntiles) {
             const float ref = dgk::ref_of(m);
             const int row0 = tl.half_rows ? (t >> 1) : t * tl.rpt;
             f32x16 s;
             if (kOneShift) {
-                const int ky = min(row0 + (tl.half_rows ? 0 : half), a.gh - 1);
-                s = __builtin_amdgcn_mfma_f32_32x32x2f32(aone, dh_tab[ky * dgk::kQuery + l32] - ref,
-                                                         dwreg, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(aone, dhv[0] - ref, dwreg, 0, 0, 0);
             } else {
                 s = dwreg;
-                for (int ms = 0; ms < tl.nshift; ++ms) {
-                    const int ky = row0 + 2 * ms + half;
-                    const float bv = (ky < a.gh ? dh_tab[ky * dgk::kQuery + l32] : 0.0f) - ref;
-                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(arow == 2 * ms + half ? 1.0f : 0.0f, bv, s,
-                                                             0, 0, 0);
-                }
+#pragma unroll
+                for (int ms = 0; ms < kMaxShift; ++ms)
+                    if (ms < tl.nshift)
+                        s = __builtin_amdgcn_mfma_f32_32x32x2f32(arow == 2 * ms + half ? 1.0f : 0.0f,
+                                                                 dhv[ms] - ref, s, 0, 0, 0);
             }
             s = dgk::scores_from<HD>(tile_ptr(buf, part, 0), l32, half, qreg, s);
             if (!kFull) {
