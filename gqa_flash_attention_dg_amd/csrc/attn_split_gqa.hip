@@ -24,6 +24,15 @@
 // them in LDS before the first stage, so q never makes the extra round trip through HBM; q
 // itself is left unchanged.
 //
+// dg_attn_split_gqa_qkvnorm also takes the raw k and v projections: the k dispatch (norm,
+// weight, rope) and the weightless v dispatch run on each canvas tile after it lands in LDS and
+// before any wavefront reads it, so neither makes a round trip through HBM either.  Its splits
+// deal the key tiles round robin, which spreads the canvas tiles (and their norm work) over the
+// workgroups of a kv head.
+//
+// The 16-bit K/V variants read cache and canvas rows stored as f16 or bf16 and widen each
+// element as it is read from LDS; the arithmetic is the same f32 MFMA path.
+//
 // Shapes with too few workgroups to fill the GPU also split the key range, in whole 32-key
 // tiles, across workgroups ("split-KV"): each writes an unnormalised partial (max,
 // denominator, output) to the caller's workspace and a second kernel merges them.  Workgroups
