@@ -84,6 +84,41 @@ struct KVTile {
     static constexpr int kLoadsPerTile = dgk::kKeys / kRowsPerLoad;
 };
 
+// Where the key rows of a K tile sit in LDS.  f32 tiles at HD 128 are padded: wave-wide load i
+// fills key rows i and i + 16 (512 bytes each) and loads start 1040 bytes apart.  Chunk c of
+// rows 0..15 (likewise of rows 16..31) then lies in 16 different 16-byte bank groups, so the 32
+// lanes reading one chunk of 32 rows do not collide, and a lane's K reads are its row base
+// plus a constant: no per-chunk address arithmetic.  The other tiles (HD 64, whose loads hold
+// four rows each, and 16-bit rows) are plain row-major with each row's 16-byte chunks
+// permuted, chunk c of row k at position c ^ (k mod chunks-per-row).
+template <int HD, int kKV>
+struct KLayout {
+    using KT = KVTile<HD, kKV>;
+    static constexpr bool kPadded = HD == 128 && kKV == 0;
+    static constexpr int kLoadBytes = kPadded ? 1040 : 1024;
+    static constexpr int kSlotBytes = KT::kLoadsPerTile * kLoadBytes;   // one K or V tile slot
+    // Byte offset of key row `trow` (and of its chunk 0) in a K tile.
+    __device__ static int row(int trow) {
+        return kPadded ? (trow & 15) * kLoadBytes + (trow >> 4) * 512 : trow * HD * KT::kEsz;
+    }
+};
+
+// dgk::scores_from on a padded f32 K tile: the lane's chunks 2g + half are 32 bytes apart.
+template <int HD>
+__device__ inline f32x16 scores_padded(const char* __restrict__ ks, int l32, int half,
+                                       const float (&qreg)[HD / 2], f32x16 s) {
+    const float* kr = reinterpret_cast<const float*>(ks + KLayout<HD, 0>::row(l32)) + 4 * half;
+#pragma unroll
+    for (int g = 0; g < HD / 8; ++g) {
+        const float4 kf = *reinterpret_cast<const float4*>(kr + 8 * g);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qreg[4 * g + 0], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qreg[4 * g + 1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qreg[4 * g + 2], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qreg[4 * g + 3], s, 0, 0, 0);
+    }
+    return s;
+}
+
 template <int kKV>
 __device__ inline float lo16(uint32_t w) {
     if constexpr (kKV == DG_KV_BF16) return __uint_as_float(w << 16);
@@ -289,8 +324,10 @@ __device__ inline void norm_canvas_tile(const SplitArgs& a, float* __restrict__ 
         const int trow = R % dgk::kKeys;
         const int j = min(j0 + trow, kend - 1);
         if (j < a.ctx) continue;                 // a cache row; its L lanes leave together
-        float* rowp = (isv ? vt : kt) + trow * HD;
-        const int sw = isv ? 0 : trow % kChunks; // K rows are stored chunk-swizzled
+        using KL = KLayout<HD, 0>;
+        float* rowp = isv ? vt + trow * HD : kt + KL::row(trow) / 4;
+        // K rows of unpadded tiles are stored chunk-swizzled
+        const int sw = isv || KL::kPadded ? 0 : trow % kChunks;
         float4 x[2];
         float ss = 0.0f;
 #pragma unroll
@@ -381,15 +418,16 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     // [buffer][tile of the stage][K, V]; with kNormQ the normalised queries are staged over
     // buffer 1 (free until the second stage is issued) and a little past it; the pair merge
     // reuses the space at the end.
-    constexpr int kStageFloats = 2 * 2 * 2 * KT::kBytes / 4;
-    constexpr int kQStageEnd = 2 * 2 * KT::kBytes / 4 + kBlockQ * kQStride<HD>;
+    using KL = KLayout<HD, kKV>;
+    constexpr int kStageFloats = 2 * 2 * 2 * KL::kSlotBytes / 4;
+    constexpr int kQStageEnd = 2 * 2 * KL::kSlotBytes / 4 + kBlockQ * kQStride<HD>;
     constexpr int kMergeFloats = kPairs * 64 * (TL::kGroups * 16 + 2) + 2 * kBlockQ;  // + row indices
     constexpr int kA = kNormQ && kQStageEnd > kStageFloats ? kQStageEnd : kStageFloats;
     constexpr int kSmemFloats = kA > kMergeFloats ? kA : kMergeFloats;
     __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
     const int hd = kPad ? a.hd : HD;
     auto tile_ptr = [&](int buf, int tile, int isv) {
-        return reinterpret_cast<char*>(smem) + ((buf * 2 + tile) * 2 + isv) * KT::kBytes;
+        return reinterpret_cast<char*>(smem) + ((buf * 2 + tile) * 2 + isv) * KL::kSlotBytes;
     };
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks);
@@ -469,6 +507,10 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         const int j0 = key0(st, ld_tile);
         if (j0 >= kend) return;              // the split's last stage holds one tile
         char* dst = tile_ptr(buf, ld_tile, ld_isv);
+        // A padded K tile takes rows i and i + 16 in load i (KLayout); V tiles and unpadded K
+        // tiles take rows 2i, 2i + 1 (HD 128) or 4i..4i + 3 (HD 64).
+        const bool padk = KL::kPadded && !ld_isv;
+        const int load_bytes = padk ? KL::kLoadBytes : 1024;
         const bool in_cache = j0 + dgk::kKeys <= a.ctx, in_canvas = j0 >= a.ctx;
         if ((in_cache || in_canvas) && j0 + dgk::kKeys <= kend) {   // one side of the seam
             const char* b = in_cache ? cache_base + (size_t)j0 * rstride_c
@@ -476,23 +518,23 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             const unsigned rs = in_cache ? rstride_c : rstride_v;
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int trow = i * R + rsub;
-                int chunk = ld_isv ? pos : (pos ^ (trow % KT::kChunks));
+                const int trow = padk ? i + KT::kLoadsPerTile * rsub : i * R + rsub;
+                int chunk = ld_isv || KL::kPadded ? pos : (pos ^ (trow % KT::kChunks));
                 if (kPad) chunk = min(chunk, last_chunk);
                 __builtin_amdgcn_global_load_lds(b + ((unsigned)trow * rs + 16u * chunk),
-                                                 (dgk::lds_void*)(dst + i * 1024), 16, 0, 0);
+                                                 (dgk::lds_void*)(dst + i * load_bytes), 16, 0, 0);
             }
         } else {                           // straddles the seam or the end: per-row addresses
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
-                const int trow = i * R + rsub;
+                const int trow = padk ? i + KT::kLoadsPerTile * rsub : i * R + rsub;
                 const int j = min(j0 + trow, kend - 1);
-                int chunk = ld_isv ? pos : (pos ^ (trow % KT::kChunks));
+                int chunk = ld_isv || KL::kPadded ? pos : (pos ^ (trow % KT::kChunks));
                 if (kPad) chunk = min(chunk, last_chunk);
                 const char* p = (j < a.ctx ? cache_base + (size_t)j * rstride_c
                                            : canvas_base + (size_t)(j - a.ctx) * rstride_v) +
                                 16u * chunk;
-                __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)(dst + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(p, (dgk::lds_void*)(dst + i * load_bytes), 16, 0, 0);
             }
         }
     };
@@ -501,7 +543,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     if (!hi && nst > 0) issue_stage(0, 0);
     float qreg[HD / 2];
     if constexpr (kNormQ) {
-        float* qs = smem + 2 * 2 * KT::kBytes / 4;
+        float* qs = smem + 2 * 2 * KL::kSlotBytes / 4;
         stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
         __syncthreads();
         dgk::load_q<HD>(qs + (pair * dgk::kQuery + l32) * kQStride<HD>, true, half, 1.0f, qreg);
@@ -542,8 +584,15 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         if (pair_active && t0 < kend) {
             f32x16 s;
             if constexpr (kKV == 0) {
-                s = dgk::scores<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 0)), l32, half,
-                                    qreg, -dgk::ref_of(m));
+                if constexpr (KL::kPadded) {
+                    const float shift = -dgk::ref_of(m);
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
+                                                             f32x16{}, 0, 0, 0);
+                    s = scores_padded<HD>(tile_ptr(buf, hi, 0), l32, half, qreg, s);
+                } else {
+                    s = dgk::scores<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 0)), l32,
+                                        half, qreg, -dgk::ref_of(m));
+                }
             } else {
                 const float shift = -dgk::ref_of(m);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
