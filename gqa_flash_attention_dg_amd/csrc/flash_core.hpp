@@ -25,7 +25,8 @@
 // 16-byte direct global->LDS loads (global_load_lds_dwordx4: lane i of an instruction lands at
 // base + 16*i).  K rows are stored with their 16-byte chunks permuted, chunk c of key row k at
 // position c ^ (k mod chunks-per-row), which makes the 32 lanes reading 32 different K rows hit
-// distinct banks.
+// distinct banks.  (The split-GQA kernel's f32 tiles at hd 128 use a padded layout of their own,
+// with no permutation; the helpers here serve the rel-pos kernel and its other tiles.)
 #pragma once
 
 #include <hip/hip_runtime.h>
