@@ -19,11 +19,12 @@ LIB_PATH = os.path.join(HERE, "libdgattn.so")
 DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
 DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
 DG_KV_F16, DG_KV_BF16 = 1, 2
+DG_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
            "dg_qkv_headnorm_rope_kv16",
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
-           "dg_attn_split_gqa_qkvnorm", "dg_attn_split_gqa_kv16",
+           "dg_attn_split_gqa_qkvnorm", "dg_attn_split_gqa_kv16", "dg_attn_split_gqa_noalloc",
            "relpos_flash_attn_workspace_size", "relpos_flash_attn",
            "relpos_flash_attn_windows_workspace_size", "relpos_flash_attn_windows",
            "dg_last_error")
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
         L.dg_attn_split_gqa_workspace_size.restype = Z
         L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
+        L.dg_attn_split_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp]
         L.dg_attn_split_gqa_qnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, U,
                                               F, F, I, vp, Z, vp]
         L.dg_attn_split_gqa_qkvnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I,
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
         for name in ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
                      "dg_qkv_headnorm_rope_kv16",
                      "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "dg_attn_split_gqa_qkvnorm",
-                     "dg_attn_split_gqa_kv16", "relpos_flash_attn",
+                     "dg_attn_split_gqa_kv16", "dg_attn_split_gqa_noalloc", "relpos_flash_attn",
                      "relpos_flash_attn_windows"):
             getattr(L, name).restype = I
         L.dg_last_error.argtypes = []
@@ -218,6 +220,16 @@ def dg_attn_split_gqa(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: in
                                    _ptr(k, "k", nkvc), _ptr(v, "v", nkvc), _ptr(out, "out", nq),
                                    batch, T, ctx, nh, nkv, hd, float(scale), int(causal), ws,
                                    wsb, _stream(stream)))
+
+
+def dg_attn_split_gqa_noalloc(q, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int,
+                              nkv: int, hd: int, scale: float, causal: int, stream=None) -> None:
+    _nonneg(batch=batch, T=T, ctx=ctx, nh=nh, nkv=nkv, hd=hd)
+    nq, nkvc, nc = batch * T * nh * hd, batch * T * nkv * hd, batch * nkv * ctx * hd
+    _check(lib().dg_attn_split_gqa_noalloc(_ptr(q, "q", nq), _ptr(kc, "kc", nc), _ptr(vc, "vc", nc),
+                                           _ptr(k, "k", nkvc), _ptr(v, "v", nkvc),
+                                           _ptr(out, "out", nq), batch, T, ctx, nh, nkv, hd,
+                                           float(scale), int(causal), _stream(stream)))
 
 
 def dg_attn_split_gqa_qnorm(q, wq, cs, kc, vc, k, v, out, batch: int, T: int, ctx: int, nh: int,

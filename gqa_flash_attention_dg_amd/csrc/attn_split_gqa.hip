@@ -37,6 +37,8 @@
 // tiles, across workgroups ("split-KV"): each writes an unnormalised partial (max,
 // denominator, output) to the caller's workspace and a second kernel merges them.  Workgroups
 // that share K/V are placed on the same XCD so its L2 serves the re-reads.
+#include <mutex>
+
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
@@ -944,6 +946,48 @@ Plan plan(int batch, int T, int ctx, int nh, int nkv, int hd, int causal) {
     return p;
 }
 
+// The static split-KV scratch of dg_attn_split_gqa_noalloc: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory; its device address on each GPU comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = DG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that runs `stream`, which must be the current
+// device (the address is looked up with that device current).
+int scratch_for_stream(const char* fn, void* stream, void** out) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return dg::fail(DG_ELAUNCH, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess)
+            return dg::fail(DG_ELAUNCH, "%s: hipStreamGetDevice: %s", fn, hipGetErrorString(e));
+        if (sdev != cur)
+            return dg::fail(DG_EINVAL, "%s: the stream belongs to device %d, the current device is %d",
+                            fn, (int)sdev, cur);
+    }
+    if (cur < 0 || cur >= kMaxDevices)
+        return dg::fail(DG_EUNSUPPORTED, "%s: device %d is beyond the %d the library tracks", fn,
+                        cur, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[cur]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return dg::fail(DG_ELAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn,
+                            cur, hipGetErrorString(e));
+        g_scratch_ptr[cur] = ptr;
+    }
+    *out = g_scratch_ptr[cur];
+    return DG_OK;
+}
+
 }  // namespace
 
 extern "C" size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int nkv,
@@ -1001,11 +1045,13 @@ SmallKernel pick_small(int hd, int norm, int kv) {
 
 // Shared body of the attention entry points.  `norm` selects the in-kernel norms (0 none, 1 q,
 // 2 q, k and v), whose extra arguments (wq, wk, cs, qflags, eps) were validated by the caller.
+// With `use_scratch` the split-KV partials go to the library's static device scratch (the
+// caller passes no workspace); a shape whose partials exceed it is refused.
 int attn_call(const char* fn, const float* q, const void* kc, const void* vc, const void* k,
               const void* v, float* out, int batch, int T, int ctx, int nh, int nkv, int hd,
               float scale, int causal, void* workspace, size_t workspace_bytes, void* stream,
               int norm, const float* wq, const float* wk, const float* cs, unsigned qflags,
-              float eps, int kv) {
+              float eps, int kv, bool use_scratch = false) {
     const bool normq = norm >= 1;
     if (batch < 0 || T < 0 || ctx < 0 || nh < 0 || nkv < 0)
         return dg::fail(DG_EINVAL, "%s: negative size (batch %d, T %d, ctx %d, nh %d, nkv %d)", fn,
@@ -1038,6 +1084,16 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
     if (!q || !k || !v || !out) return dg::fail(DG_EINVAL, "%s: q, k, v and out must be non-NULL", fn);
     if (ncache > 0 && (!kc || !vc)) return dg::fail(DG_EINVAL, "%s: kc/vc NULL with ctx %d > 0", fn, ctx);
     Plan p = plan(batch, T, ctx, nh, nkv, hd, causal);
+    if (use_scratch && p.nsplit > 1) {
+        if (p.ws_bytes > kScratchBytes)
+            return dg::fail(DG_EUNSUPPORTED,
+                            "%s: this shape needs %zu bytes of split-KV scratch, more than the "
+                            "%zu bytes of the library's static scratch (use dg_attn_split_gqa "
+                            "with a workspace)", fn, p.ws_bytes, kScratchBytes);
+        const int st = scratch_for_stream(fn, stream, &workspace);
+        if (st != DG_OK) return st;
+        workspace_bytes = kScratchBytes;
+    }
     if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes)) {
         if (workspace)
             return dg::fail(DG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed",
@@ -1168,4 +1224,13 @@ extern "C" int dg_attn_split_gqa_kv16(const float* q, const void* kc, const void
         return dg::fail(DG_EINVAL, "%s: kv_format must be DG_KV_F16 or DG_KV_BF16, got %d", fn, kv_format);
     return attn_call(fn, q, kc, vc, k, v, out, batch, T, ctx, nh, nkv, hd, scale, causal, workspace,
                      workspace_bytes, stream, 0, nullptr, nullptr, nullptr, 0u, 0.0f, kv_format);
+}
+
+extern "C" int dg_attn_split_gqa_noalloc(const float* q, const float* kc, const float* vc,
+                                         const float* k, const float* v, float* out, int batch,
+                                         int T, int ctx, int nh, int nkv, int hd, float scale,
+                                         int causal, void* stream) {
+    return attn_call("dg_attn_split_gqa_noalloc", q, kc, vc, k, v, out, batch, T, ctx, nh, nkv,
+                     hd, scale, causal, nullptr, 0, stream, 0, nullptr, nullptr, nullptr, 0u,
+                     0.0f, 0, true);
 }

@@ -251,6 +251,32 @@ int dg_attn_split_gqa_kv16(const float* q, const void* kc, const void* vc, const
                            int hd, float scale, int causal, int kv_format, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch behind dg_attn_split_gqa_noalloc, one copy per GPU. */
+#define DG_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * dg_attn_split_gqa_noalloc -- dg_attn_split_gqa for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): it
+ * takes no workspace and allocates nothing.  Where dg_attn_split_gqa would split the key range
+ * across workgroups, the partial results go to a static device array of
+ * DG_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a caller workspace; the same
+ * kernels run with the same launch plan, so the result is bit-identical to dg_attn_split_gqa
+ * given a workspace of dg_attn_split_gqa_workspace_size() bytes.
+ *   Every argument as dg_attn_split_gqa.  `stream` must belong to the current device (NULL is
+ *   the current device's legacy default stream).
+ *   The scratch is one array per GPU, shared by every call on that GPU and held until the
+ *   process ends; each call writes every partial it reads, so nothing needs clearing between
+ *   calls.  Calls that overlap in time on one GPU (other streams, other threads, other
+ *   processes' contexts excepted) RACE on it: order them on one stream.
+ * Errors: as dg_attn_split_gqa; DG_EUNSUPPORTED when the shape's split partials need more than
+ * DG_NOALLOC_SCRATCH_BYTES (dg_attn_split_gqa_workspace_size() tells how many it needs);
+ * DG_EINVAL when `stream` belongs to another device than the current one; DG_ELAUNCH when the
+ * runtime cannot report the current device or the scratch's address.
+ */
+int dg_attn_split_gqa_noalloc(const float* q, const float* kc, const float* vc, const float* k,
+                              const float* v, float* out, int batch, int T, int ctx, int nh,
+                              int nkv, int hd, float scale, int causal, void* stream);
+
 /*
  * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn can use to hold the
  * hoisted bias rows, the page's DHDW buffers: dh [heads][n][gh] then dw [heads][n][gw], i.e.

@@ -1,0 +1,93 @@
+"""dg_attn_split_gqa_noalloc: the entry point that allocates nothing.
+
+It runs the kernels of dg_attn_split_gqa with the split-KV partials in the library's static
+device scratch.  Through the C ABI, its output must equal dg_attn_split_gqa's (given a
+workspace) on two calls in a row, the second with a smaller input, and stay within the f32
+parity bar of the oracle-checked entry point.  A shape whose partials exceed the scratch is
+refused before any launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_flash_attention_dg_amd as dg
+from gqa_flash_attention_dg_amd import synth
+from helpers import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _inputs(B, T, ctx, nh, nkv, hd, seed):
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=seed, normed=False)
+    kc = _dev(c.kc) if ctx > 0 else None
+    vc = _dev(c.vc) if ctx > 0 else None
+    return c, _dev(c.q), kc, vc, _dev(c.k), _dev(c.v)
+
+
+def _with_workspace(c, q, kc, vc, k, v, scale, causal):
+    out = torch.empty_like(q)
+    need = dg.dg_attn_split_gqa_workspace_size(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+    dg.dg_attn_split_gqa(q, kc, vc, k, v, out, c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, scale, causal,
+                         ws, need)
+    return out, need
+
+
+def test_noalloc_matches_workspace_entry_twice():
+    torch.cuda.set_device(0)
+    shapes = [(1, 256, 1024, 16, 8, 128, 1.0, 0),   # DiffusionGemma-like step: split key range
+              (1, 40, 300, 8, 4, 96, 0.5, 0)]       # then a smaller one (padded head dim)
+    for i, (B, T, ctx, nh, nkv, hd, scale, causal) in enumerate(shapes):
+        print("noalloc call %d: B%d T%d ctx%d nh%d nkv%d hd%d" % (i, B, T, ctx, nh, nkv, hd),
+              flush=True)
+        c, q, kc, vc, k, v = _inputs(B, T, ctx, nh, nkv, hd, seed=10 + i)
+        ref, need = _with_workspace(c, q, kc, vc, k, v, scale, causal)
+        assert 0 < need <= dg.DG_NOALLOC_SCRATCH_BYTES, need   # both shapes use the scratch
+        out = torch.full_like(q, float("nan"))
+        dg.dg_attn_split_gqa_noalloc(q, kc, vc, k, v, out, B, T, ctx, nh, nkv, hd, scale, causal)
+        torch.cuda.synchronize()
+        got, want = out.cpu().numpy(), ref.cpu().numpy()
+        assert_parity(got, want, "noalloc call %d" % i)
+        # same kernels, same plan, same partials: bit-identical
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "call %d" % i
+
+
+def test_noalloc_unsplit_shape():
+    # a shape that fills the GPU without a split uses no scratch at all
+    torch.cuda.set_device(0)
+    c, q, kc, vc, k, v = _inputs(2, 64, 96, 64, 16, 64, seed=3)
+    ref, need = _with_workspace(c, q, kc, vc, k, v, 0.125, 1)
+    out = torch.empty_like(q)
+    dg.dg_attn_split_gqa_noalloc(q, kc, vc, k, v, out, c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, 0.125, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref.cpu().numpy())
+
+
+def test_noalloc_refuses_oversize_partials():
+    # find a shape whose split partials need more than the static scratch holds
+    torch.cuda.set_device(0)
+    shape = None
+    for nkv in range(1, 33):
+        for qb in range(1, 512):
+            T, B, ctx, hd = 128 * qb, 1, 256, 128
+            need = dg.dg_attn_split_gqa_workspace_size(B, T, ctx, nkv, nkv, hd)
+            if need > dg.DG_NOALLOC_SCRATCH_BYTES:
+                shape = (B, T, ctx, nkv, nkv, hd)
+                break
+        if shape:
+            break
+    if shape is None:
+        pytest.skip("no shape on this device needs more split-KV scratch than the static array")
+    B, T, ctx, nh, nkv, hd = shape
+    c, q, kc, vc, k, v = _inputs(B, T, ctx, nh, nkv, hd, seed=4)
+    out = torch.zeros_like(q)
+    with pytest.raises(dg.DgError) as e:
+        dg.dg_attn_split_gqa_noalloc(q, kc, vc, k, v, out, B, T, ctx, nh, nkv, hd, 1.0, 0)
+    assert e.value.status == dg.DG_EUNSUPPORTED
+    assert "static scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert float(out.abs().max()) == 0.0    # nothing launched, nothing written
