@@ -334,6 +334,93 @@ def test_attn_split_long_cache_spot_rows_against_f64():
     assert worst < 5e-5, worst
 
 
+def test_attn_split_is_invariant_to_which_keys_sit_in_cache_or_canvas():
+    """Bidirectional attention sees one key set: redistributing the S = ctx + T key/value rows
+    between the cache and the canvas (each kept in its own layout, K and V rows moved
+    together, the same redistribution for every kv head) leaves every output unchanged up to
+    the summation order."""
+    B, T, ctx, nh, nkv, hd = 2, 6, 11, 4, 2, 64
+    c = synth.split_case(B, T, ctx, nh, nkv, hd, seed=21)
+    S = ctx + T
+    # the key list of each (b, kv) in the page's order: cache rows, then canvas rows
+    K = np.concatenate([c.kc, c.k.reshape(B, T, nkv, hd).transpose(0, 2, 1, 3)], axis=2)
+    V = np.concatenate([c.vc, c.v.reshape(B, T, nkv, hd).transpose(0, 2, 1, 3)], axis=2)
+    a = oracle.attn_split_gqa(c.q, c.kc, c.vc, c.k, c.v, nh, nkv, hd)
+    for seed in range(3):
+        perm = np.random.default_rng(seed).permutation(S)
+        Kp, Vp = K[:, :, perm], V[:, :, perm]
+        kc2, vc2 = np.ascontiguousarray(Kp[:, :, :ctx]), np.ascontiguousarray(Vp[:, :, :ctx])
+        k2 = np.ascontiguousarray(Kp[:, :, ctx:].transpose(0, 2, 1, 3).reshape(B, T, nkv * hd))
+        v2 = np.ascontiguousarray(Vp[:, :, ctx:].transpose(0, 2, 1, 3).reshape(B, T, nkv * hd))
+        assert not np.array_equal(k2, c.k)       # some keys really moved between the two
+        b = oracle.attn_split_gqa(c.q, kc2, vc2, k2, v2, nh, nkv, hd)
+        assert np.max(np.abs(a - b)) < 1e-6, seed
+
+
+def _split_rows_f64(q, kc, vc, k, v, nh, nkv, hd, T, rows):
+    """Exact float64 attention of the sampled flattened rows b*T + i, all heads."""
+    G = nh // nkv
+    ref = {}
+    for r in rows:
+        b, i = divmod(int(r), T)
+        for h in range(nh):
+            kv = h // G
+            sl = slice(kv * hd, (kv + 1) * hd)
+            Kx = np.concatenate([kc[b, kv], k[b, :, sl]]).astype(np.float64)
+            Vx = np.concatenate([vc[b, kv], v[b, :, sl]]).astype(np.float64)
+            sc = Kx @ q[b, i, h * hd:(h + 1) * hd].astype(np.float64)
+            p = np.exp(sc - sc.max())
+            ref[(b, i, h)] = (p / p.sum()) @ Vx
+    return ref
+
+
+def test_attn_split_dg_canvas_spot_rows_against_f64():
+    """The oracle's own f32 error at the DiffusionGemma-like step's full shape (T 256, ctx 1024,
+    16/8 heads, hd 128) with its real inputs: a roped cache, normed and roped q and k, the
+    weightless v norm.  16 sampled canvas rows, all heads, against exact float64: within a
+    quarter of the parity bar's absolute part (2e-4)."""
+    c = synth.dg_canvas_steps(1)
+    cs = oracle.rope_table(c.ctx, c.T, c.hd, c.theta)
+    csc = oracle.rope_table(0, c.ctx, c.hd, c.theta)
+    kc = oracle.headnorm_rope(c.kc.reshape(c.nkv, c.ctx, c.hd), None, csc, 1, c.hd,
+                              oracle.NORM_ROPE | oracle.NORM_SKIP, 0.0).reshape(c.kc.shape)
+    q = oracle.headnorm_rope(c.q, c.wq, cs, c.nh, c.hd, 3, c.eps)
+    k = oracle.headnorm_rope(c.k, c.wk, cs, c.nkv, c.hd, 3, c.eps)
+    v = oracle.headnorm_rope(c.v, None, None, c.nkv, c.hd, 0, c.eps)
+    rows = np.sort(np.random.default_rng(11).choice(c.T, size=16, replace=False)).astype(np.int64)
+    out = oracle.attn_split_gqa(q, kc, c.vc, k, v, c.nh, c.nkv, c.hd, 1.0, False, rows=rows)
+    ref = _split_rows_f64(q, kc, c.vc, k, v, c.nh, c.nkv, c.hd, c.T, rows)
+    worst = max(float(np.max(np.abs(out[b, i, h * c.hd:(h + 1) * c.hd] - want)))
+                for (b, i, h), want in ref.items())
+    assert worst < 5e-5, worst
+
+
+def test_relpos_sam_global_spot_rows_against_f64():
+    """The oracle's own f32 error at the SAM rel-pos shape (64 x 64 grid, 12 heads, hd 64, scale
+    1/8) with bias-augmented scores: 16 sampled query rows, all heads, against the exact
+    float64 score definition (scale*q.k + q.Rh[qy,ky] + q.Rw[qx,kx]), within a quarter of the
+    parity bar's absolute part (2e-4)."""
+    c = synth.sam_global()
+    n, W, hd = c.gh * c.gw, c.heads * c.hd, c.hd
+    rows = np.sort(np.random.default_rng(12).choice(n, size=16, replace=False)).astype(np.int64)
+    out = oracle.relpos_attn(c.qkv, c.rh, c.rw, c.gh, c.gw, c.heads, hd, c.scale, rows=rows)
+    qkv = c.qkv.astype(np.float64)
+    rh, rw = c.rh.astype(np.float64), c.rw.astype(np.float64)
+    ky, kx = np.divmod(np.arange(n), c.gw)
+    worst = 0.0
+    for i in rows:
+        qy, qx = divmod(int(i), c.gw)
+        for h in range(c.heads):
+            qv = qkv[i, h * hd:(h + 1) * hd]
+            Kh = qkv[:, W + h * hd:W + (h + 1) * hd]
+            Vh = qkv[:, 2 * W + h * hd:2 * W + (h + 1) * hd]
+            sc = c.scale * (Kh @ qv) + (rh[qy] @ qv)[ky] + (rw[qx] @ qv)[kx]
+            p = np.exp(sc - sc.max())
+            want = (p / p.sum()) @ Vh
+            worst = max(worst, float(np.max(np.abs(out[i, h * hd:(h + 1) * hd] - want))))
+    assert worst < 5e-5, worst
+
+
 # ----------------------------------------------------------------------------- rel-pos attention
 
 def test_relpos_golden():
