@@ -17,10 +17,18 @@ sustained load) and K about a quarter second; both are reported.  A second pass 
 times each launch of the dominant call with its own events (kept out of the first pass: an
 event pair between launches adds a few microseconds to a step).
 
+A third pass records an event at every step boundary (median and minimum step time), and
+--cold N times N more steps one at a time, each after a read of a 512 MiB buffer has evicted
+the L2s and the MALL.  The DiffusionGemma-like workload cycles through 48 pre-staged denoising
+steps (fresh canvas q, k, v each step, one fixed cache).  Before the main workload, the
+workloads named by --also (default: the other configurations) are measured the same way with
+time-based step counts and reported under "also".
+
 Prints ONE JSON line: metric/value/unit (algorithmic TFLOP/s of the step, or GB/s for the
-HBM-bound depformer workload), roofline of the dominant kernel against MI355X peaks, and the
-oracle timed on the host cores over a bounded sample of the same workload (a reported
-baseline, not the target).  Parity of this launch configuration is the GPU tests' job.
+HBM-bound depformer workload), roofline of the dominant kernel against MI355X peaks, timing
+statistics, and the oracle timed on the host cores over a bounded sample of the same workload
+(a reported baseline, not the target; with the host CPU's model and the threads it used).
+Parity of this launch configuration is the GPU tests' job.
 """
 from __future__ import annotations
 
@@ -127,7 +135,12 @@ class SplitWork:
                                causal=c.causal, rope_cache=c.rope_cache, normed=c.normed,
                                norm_mode=norm_mode, kv16=kv16)
         self.norm_mode = norm_mode = self.blk.norm_mode   # "auto" resolved by the block
-        self.q, self.k, self.v = d(c.q), d(c.k), d(c.v)
+        # Canvas inputs of every pre-staged denoising step (one set unless the case holds
+        # several); step i of a run reads set i mod len(sets), against the fixed cache.
+        draws = c.steps if c.steps else [{"q": c.q, "k": c.k, "v": c.v}]
+        self.sets = [(d(st["q"]), d(st["k"]), d(st["v"])) for st in draws]
+        self.q, self.k, self.v = self.sets[0]
+        self.t = 0
         self.out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
         self.flops, self.attn_bytes, self.norm_bytes = split_counts(c, norm_mode)
         if kv16:  # K/V read as 16-bit values; the canvas twins are written by the one-launch
@@ -140,9 +153,12 @@ class SplitWork:
 
     def config(self):
         c = self.c
-        return {"workload": c.name, "batch": c.B, "T": c.T, "ctx": c.ctx, "nh": c.nh,
-                "nkv": c.nkv, "hd": c.hd, "scale": c.scale, "causal": bool(c.causal),
-                "step": self.step_name()}
+        cfg = {"workload": c.name, "batch": c.B, "T": c.T, "ctx": c.ctx, "nh": c.nh,
+               "nkv": c.nkv, "hd": c.hd, "scale": c.scale, "causal": bool(c.causal),
+               "step": self.step_name()}
+        if len(self.sets) > 1:
+            cfg["staged_steps"] = len(self.sets)
+        return cfg
 
     def step_name(self):
         if getattr(self, "kv16", None):
@@ -160,6 +176,8 @@ class SplitWork:
         return " / ".join(names[m] for m in self.norm_mode.split("/"))
 
     def step(self, ev=None):
+        self.q, self.k, self.v = self.sets[self.t % len(self.sets)]
+        self.t += 1
         normed_q = self.c.normed and self.norm_mode == "in_attention"
         normed_all = self.c.normed and self.norm_mode == "fused"
         fused16 = self.kv16 and self.c.normed and self.norm_mode == "one_launch"
@@ -398,7 +416,7 @@ def make_work(name, norm_mode="auto", kv16=None):
     if name == "long_cache":
         return SplitWork(name, synth.long_cache(), norm_mode, kv16)
     if name == "dg_canvas":
-        return SplitWork(name, synth.dg_canvas_steps(1), norm_mode, kv16)
+        return SplitWork(name, synth.dg_canvas_steps(48), norm_mode, kv16)
     if name == "tiny":
         return SplitWork(name, synth.tiny_canvas_step(), norm_mode)
     if name == "depformer":
@@ -412,6 +430,171 @@ def make_work(name, norm_mode="auto", kv16=None):
     if name == "hbm_copy":
         return CopyWork(name)
     raise SystemExit("unknown workload %s" % name)
+
+
+def host_cpu_model() -> str:
+    """Model name of the host CPU (from /proc/cpuinfo), or what the platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _stats(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"mean": sum(xs) / n, "median": med, "min": xs[0]}
+
+
+def attach_graph(work, nsteps):
+    """Replace work.step by replays of a HIP graph of `nsteps` consecutive canvas steps (split-GQA
+    workloads); the events of a replay are split evenly over its steps."""
+    from gqa_flash_attention_dg_amd.canvas import CanvasGraph
+    sets = [work.sets[j % len(work.sets)] for j in range(nsteps)]
+    cg = CanvasGraph(work.blk, [s[0] for s in sets], [s[1] for s in sets], [s[2] for s in sets],
+                     work.out, steps=nsteps)
+    work.graph = nsteps
+    state = {"n": 0}
+
+    def graph_step(ev=None):
+        if state["n"] % nsteps == 0:
+            if ev:
+                ev[0].record()
+            cg.replay()
+            if ev:
+                ev[1].record()
+        elif ev:
+            ev[0].record()
+            ev[1].record()
+        state["n"] += 1
+    work.step = graph_step
+    work.graph_state = state
+
+
+def run(work, steps=None, warmup=None, cold=0):
+    """Times `work` on the GPU.  W untimed warmup steps, then three passes of K steps:
+    pass 1 times all K steps between two events (nothing queued between their launches) and
+    gives the mean step time; pass 2 puts an event pair around each launch of the dominant
+    call; pass 3 records one event at every step boundary, for the median and minimum step.
+    With `cold` > 0, that many more steps each follow a read of a 512 MiB buffer that evicts
+    the L2s and the MALL, and are timed alone."""
+    import torch
+    per = getattr(work, "graph", 0) or 1
+    nprobe = 0
+    if warmup is None or steps is None:
+        # default counts from the wall time of a few probe steps (which count as warmup; the
+        # first, which loads the code objects, is not timed); with a graph a probe is a replay
+        nprobe = 4 * per if warmup is None else min(4 * per, warmup // per * per)
+        est = None
+        if nprobe >= 2 * per:
+            for _ in range(per):
+                work.step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(nprobe - per):
+                work.step()
+            torch.cuda.synchronize()
+            est = max((time.perf_counter() - t0) / (nprobe - per), 1e-6)
+        else:
+            nprobe = 0
+        if warmup is None:
+            warmup = max(nprobe, min(5000, int(0.5 / est)))
+        if steps is None:
+            steps = max(20, min(2000, int(0.25 / est))) if est else 20
+            steps = -(-steps // per) * per
+    for _ in range(warmup - nprobe):
+        work.step()
+    torch.cuda.synchronize()
+    reset = lambda: getattr(work, "graph_state", {}).update(n=0)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # pass 1
+    reset()
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(steps):
+        work.step()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / steps
+    # pass 2
+    reset()
+    nev = len(work.io) if isinstance(work, LayerStackWork) else 0
+    evs = [[(ev(), ev()) for _ in range(nev)] if nev else (ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        work.step(evs[i])
+    torch.cuda.synchronize()
+    if nev:
+        kern_ms = [sum(a.elapsed_time(b) for a, b in st) for st in evs]
+    else:
+        kern_ms = [a.elapsed_time(b) for a, b in evs]
+    # pass 3 (per-step boundaries; a graph replay is one boundary per replay)
+    reset()
+    marks = [ev() for _ in range(steps // per + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for i in range(steps):
+        work.step()
+        if (i + 1) % per == 0:
+            marks[(i + 1) // per].record()
+    torch.cuda.synchronize()
+    step_ms = [marks[j].elapsed_time(marks[j + 1]) / per for j in range(len(marks) - 1)]
+    r = {"steps": steps, "warmup": warmup, "ms_step": ms_step, "kern_ms": kern_ms,
+         "step_ms": step_ms}
+    if cold > 0:
+        flush = torch.ones((512 << 20) // 4, device="cuda")
+        cold_ms = []
+        for _ in range(cold):
+            # Reading 512 MiB leaves other lines in the L2s and the MALL.  The step's launches
+            # queue behind that read, so the events time the step alone, with no host gap.
+            flush.sum()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(per):
+                work.step()
+            b.record()
+            torch.cuda.synchronize()
+            cold_ms.append(a.elapsed_time(b) / per)
+        del flush
+        r["cold_ms"] = cold_ms
+    return r
+
+
+def rates(work, r):
+    """value/unit of the step and the roofline of the dominant kernel from run()'s times."""
+    kern_avg = sum(r["kern_ms"]) / len(r["kern_ms"])
+    step_bytes = work.attn_bytes + work.norm_bytes
+    if work.bound == "mfma":
+        achieved = work.flops / (kern_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_MFMA, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_F32_MFMA}
+        per_ms = lambda ms: work.flops / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    else:
+        achieved = work.attn_bytes / (kern_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM}
+        per_ms = lambda ms: step_bytes / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+    roof["kernel"] = work.dominant
+    roof["avg_launch_ms"] = kern_avg
+    timing = {"step_ms": _stats(r["step_ms"]), "dominant_ms": _stats(r["kern_ms"])}
+    timing["step_ms"]["mean_first_pass"] = r["ms_step"]
+    if "cold_ms" in r:
+        cold = _stats(r["cold_ms"])
+        timing["cold"] = dict(cold, value_at_median=per_ms(cold["median"]), runs=len(r["cold_ms"]))
+        timing["warm_value_at_median"] = per_ms(timing["step_ms"]["median"])
+    return per_ms(r["ms_step"]), unit, roof, timing
+
+
+ALSO_DEFAULT = "dg_canvas,sam_relpos,sam_windowed,depformer"
 
 
 def main():
@@ -440,6 +623,12 @@ def main():
     ap.add_argument("--kv16", default=None, choices=["f16", "bf16"],
                     help="long_cache / dg_canvas: keys and values stored in 16 bits, widened to "
                          "f32 inside attention")
+    ap.add_argument("--cold", type=int, default=10,
+                    help="extra steps of the main workload timed one at a time after the L2s "
+                         "and the MALL are evicted (0 = skip)")
+    ap.add_argument("--also", default=ALSO_DEFAULT,
+                    help="comma-separated workloads measured first, in the same run, with "
+                         "default step counts and reported under 'also' ('' = none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle wall time for the CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -456,116 +645,50 @@ def main():
     dg.lib()
     torch.cuda.set_device(0)
 
+    # The main workload's inputs are staged first, so that no host-side input generation
+    # separates the other configurations' runs from its timed steps.
     work = make_work(args.workload, norm_mode=args.norm, kv16=args.kv16)
+    # The other configurations next, each with its own time-based warmup and step counts.
+    also = {}
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        w = make_work(name)
+        r = run(w)
+        value, unit, roof, timing = rates(w, r)
+        also[name] = {"value": value, "unit": unit, "ms_per_step": r["ms_step"],
+                      "steps": r["steps"], "warmup": r["warmup"], "step": w.config()["step"],
+                      "workload": w.config()["workload"],
+                      "roofline": {k: roof[k] for k in ("kernel", "bound", "achieved", "unit",
+                                                        "frac", "avg_launch_ms")},
+                      "timing": timing}
+        del w, r
+        torch.cuda.empty_cache()
+
     if args.graph:
         if not isinstance(work, SplitWork):
             raise SystemExit("--graph applies to the split-GQA workloads")
-        from gqa_flash_attention_dg_amd.canvas import CanvasGraph
         if args.steps is not None and args.steps % args.graph:
             raise SystemExit("--steps must be a multiple of --graph")
-        cg = CanvasGraph(work.blk, work.q, work.k, work.v, work.out, steps=args.graph)
-        work.graph = args.graph
-        steps_run = [0]
-
-        def graph_step(ev=None, _cg=cg, _k=args.graph):
-            # one replay every _k steps; the events of a replay are split evenly over its steps
-            if steps_run[0] % _k == 0:
-                if ev:
-                    ev[0].record()
-                _cg.replay()
-                if ev:
-                    ev[1].record()
-            elif ev:
-                ev[0].record()
-                ev[1].record()
-            steps_run[0] += 1
-        work.step = graph_step
-
-    # Default step counts from the wall time of a few probe steps (which count as warmup; the
-    # first one, which loads the code objects, is not timed).
-    # With --graph a probe is one whole replay, so that each timed probe does a replay's work.
-    per = args.graph or 1
-    nprobe, est = 0, None
-    if args.warmup is None or args.steps is None:
-        nprobe = 4 * per if args.warmup is None else min(4 * per, args.warmup // per * per)
-        if nprobe >= 2 * per:
-            for _ in range(per):
-                work.step()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(nprobe - per):
-                work.step()
-            torch.cuda.synchronize()
-            est = max((time.perf_counter() - t0) / (nprobe - per), 1e-6)
-        if args.warmup is None:
-            args.warmup = max(nprobe, min(5000, int(0.5 / est)))
-        elif nprobe < 2 * per:
-            nprobe = 0
-        if args.steps is None:
-            args.steps = max(20, min(2000, int(0.25 / est))) if est else 20
-            if args.graph:
-                args.steps = -(-args.steps // args.graph) * args.graph
-    for _ in range(args.warmup - nprobe):
-        work.step()
-    torch.cuda.synchronize()
-    if args.graph:
-        steps_run[0] = 0   # the timed steps start on a replay boundary
-    nev = len(work.io) if isinstance(work, LayerStackWork) else 0
-    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    # Pass 1 (value, ms_per_step): K steps with nothing between their launches.
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        work.step()
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    # Pass 2 (roofline): K more steps with events around each launch of the dominant call.  An
-    # event pair between launches costs a few microseconds of queue time on this stack, so the
-    # step time is not taken from this pass.
-    if args.graph:
-        steps_run[0] = 0
-    evs = [[mk() for _ in range(nev)] if nev else mk() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        work.step(evs[i])
-    torch.cuda.synchronize()
-    if nev:
-        kern_ms = [sum(a.elapsed_time(b) for a, b in step) for step in evs]
-    else:
-        kern_ms = [a.elapsed_time(b) for a, b in evs]
-    kern_avg = sum(kern_ms) / len(kern_ms)
-
-    step_bytes = work.attn_bytes + work.norm_bytes
-    if work.bound == "mfma":
-        achieved = work.flops / (kern_avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_MFMA, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_F32_MFMA}
-        value, unit = work.flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
-    else:
-        achieved = work.attn_bytes / (kern_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM}
-        value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
-    roof["kernel"] = work.dominant
-    roof["avg_launch_ms"] = kern_avg
+        attach_graph(work, args.graph)
+    r = run(work, args.steps, args.warmup, cold=args.cold)
+    value, unit, roof, timing = rates(work, r)
     roof["traffic"] = measured_traffic(work.dominant, work.name + (
         "_kv16" + args.kv16 if getattr(args, "kv16", None) else ""))
 
     cpu = None
     if args.cpu_budget > 0:
         cpu = work.cpu_baseline(args.cpu_budget)
+        if cpu is not None:
+            cpu["cpu_model"] = host_cpu_model()
 
+    step_bytes = work.attn_bytes + work.norm_bytes
     rec = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": r["steps"],
+        "warmup": r["warmup"], "ms_per_step": r["ms_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": dict(work.config(), **({"hip_graph_steps": work.graph} if getattr(work, "graph", 0) else {})),
         "step_flops": work.flops, "step_hbm_bytes_algorithmic": step_bytes,
-        "step_hbm_gbps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
-        "roofline": roof, "cpu_baseline": cpu,
+        "step_hbm_gbps_algorithmic": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
+        "roofline": roof, "timing": timing, "cpu_baseline": cpu, "also": also,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)

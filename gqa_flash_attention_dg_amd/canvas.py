@@ -210,21 +210,27 @@ class CanvasBlock:
 class CanvasGraph:
     """`steps` canvas steps of a CanvasBlock captured as one HIP graph (through
     torch.cuda.CUDAGraph): the steps' launches (norms, attention, split-KV combine; no memset or
-    host work) replay with one submission.  The graph is bound to the q, k, v and out tensors given at capture; a
-    caller refreshes their contents in place between replays."""
+    host work) replay with one submission.  The graph is bound to the tensors given at capture:
+    q, k and v are either single tensors, used by every step, or lists of `steps` tensors, one
+    set per step (e.g. pre-staged denoising steps); a caller refreshes their contents in place
+    between replays."""
 
     def __init__(self, blk, q, k, v, out, warmup=2, steps=1):
-        self.blk, self.io, self.steps = blk, (q, k, v, out), steps
+        per = lambda x: list(x) if isinstance(x, (list, tuple)) else [x] * steps
+        qs, ks, vs = per(q), per(k), per(v)
+        if not len(qs) == len(ks) == len(vs) == steps:
+            raise ValueError("q, k and v lists must hold one tensor per step")
+        self.blk, self.io, self.steps = blk, (qs, ks, vs, out), steps
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):      # launch once outside capture (loads the code objects)
             for _ in range(warmup):
-                blk.step(q, k, v, out)
+                blk.step(qs[0], ks[0], vs[0], out)
         torch.cuda.current_stream().wait_stream(side)
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            for _ in range(steps):   # `steps` consecutive steps on the same buffers
-                blk.step(q, k, v, out)
+            for i in range(steps):   # `steps` consecutive steps, step i on set i
+                blk.step(qs[i], ks[i], vs[i], out)
 
     def replay(self):
         self.graph.replay()

@@ -106,3 +106,13 @@ def test_auto_norm_mode_counts_canvas_tiles_per_workgroup():
     assert auto_norm_mode(1, 64, 8, 64, 0) == "fused"                       # 2 tiles, unsplit
     assert auto_norm_mode(1, 65, 8, 64, 0) == "in_attention"                # 3 tiles
     assert auto_norm_mode(0, 16, 4, 64, 0) == "fused"                       # empty: no launch
+
+
+def test_stats_mean_median_min():
+    assert bench._stats([3.0, 1.0, 2.0]) == {"mean": 2.0, "median": 2.0, "min": 1.0}
+    assert bench._stats([4.0, 1.0, 2.0, 3.0]) == {"mean": 2.5, "median": 2.5, "min": 1.0}
+
+
+def test_host_cpu_model_is_named():
+    m = bench.host_cpu_model()
+    assert isinstance(m, str) and m and m != "unknown"
