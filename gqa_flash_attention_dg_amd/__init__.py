@@ -20,10 +20,18 @@ DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
 DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
 DG_KV_F16, DG_KV_BF16 = 1, 2
 DG_NOALLOC_SCRATCH_BYTES = 32 << 20
+DG_KERNEL_NONE, DG_KERNEL_SMALL, DG_KERNEL_TILE32, DG_KERNEL_TILE16 = 0, 1, 2, 3
+
+
+class AttnPlan(ctypes.Structure):
+    """dg_attn_plan: how a split-GQA attention call is launched."""
+    _fields_ = [("kernel", ctypes.c_int), ("query_block", ctypes.c_int), ("nsplit", ctypes.c_int),
+                ("workgroups", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t)]
 
 EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack_kv16",
            "dg_qkv_headnorm_rope_kv16",
-           "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm",
+           "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa_plan", "dg_attn_split_gqa",
+           "dg_attn_split_gqa_qnorm",
            "dg_attn_split_gqa_qkvnorm", "dg_attn_split_gqa_kv16", "dg_attn_split_gqa_noalloc",
            "relpos_flash_attn_workspace_size", "relpos_flash_attn",
            "relpos_flash_attn_windows_workspace_size", "relpos_flash_attn_windows",
@@ -59,6 +67,8 @@ def lib() -> ctypes.CDLL:
                                              Z, vp]
         L.dg_attn_split_gqa_workspace_size.argtypes = [I, I, I, I, I, I]
         L.dg_attn_split_gqa_workspace_size.restype = Z
+        L.dg_attn_split_gqa_plan.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(AttnPlan)]
+        L.dg_attn_split_gqa_plan.restype = I
         L.dg_attn_split_gqa.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, Z, vp]
         L.dg_attn_split_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp]
         L.dg_attn_split_gqa_qnorm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, U,
@@ -197,6 +207,15 @@ def dg_pack_kv16(src, dst, n: int, format: int, stream=None) -> None:
 def dg_attn_split_gqa_workspace_size(batch: int, T: int, ctx: int, nh: int, nkv: int,
                                      hd: int) -> int:
     return int(lib().dg_attn_split_gqa_workspace_size(batch, T, ctx, nh, nkv, hd))
+
+
+def dg_attn_split_gqa_plan(batch: int, T: int, ctx: int, nh: int, nkv: int, hd: int,
+                           causal: int = 0, kv_format: int = 0, cus: int = 0) -> AttnPlan:
+    """The launch plan of a split-GQA attention call (cus = 0: the current device's CUs)."""
+    p = AttnPlan()
+    _check(lib().dg_attn_split_gqa_plan(batch, T, ctx, nh, nkv, hd, int(causal), int(kv_format),
+                                        int(cus), ctypes.byref(p)))
+    return p
 
 
 def _workspace(workspace, workspace_bytes):

@@ -11,9 +11,9 @@ the raw k projection, normalised without weight or rope.
 Set-up work (rope tables, roping a cache that is stored un-roped) happens once per canvas
 block in the constructor; `step` is the per-denoising-step hot path.  Four ways to run the
 norms of a step (`norm_mode`), plus "auto" (the default), which takes "fused" when each
-attention workgroup meets at most AUTO_FUSED_TILES canvas tiles of 32 keys (a split key
-range, or a short canvas: normalising them in place costs less than a launch) and
-"in_attention" otherwise (a workgroup that walks many canvas tiles would norm each itself):
+attention workgroup meets at most AUTO_FUSED_KEYS canvas keys (a split key range, or a short
+canvas: normalising them in place costs less than a launch) and "in_attention" otherwise (a
+workgroup that walks many canvas tiles would norm each itself):
   "fused"         all three norms inside the attention launch: q as it is staged, the canvas
                   k and v rows as their tiles land in on-chip memory (q, k and v are not
                   written; a k_eq_v layer's v buffer is neither read nor written);
@@ -27,8 +27,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K,
-               DG_NORM_WEIGHTED, dg_attn_split_gqa, dg_attn_split_gqa_kv16,
+from . import (DG_KERNEL_TILE16, DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP,
+               DG_NORM_V_FROM_K, DG_NORM_WEIGHTED, dg_attn_split_gqa, dg_attn_split_gqa_kv16,
+               dg_attn_split_gqa_plan,
                dg_attn_split_gqa_qkvnorm, dg_attn_split_gqa_qnorm,
                dg_attn_split_gqa_workspace_size, dg_headnorm_rope,
                dg_pack_kv16, dg_qkv_headnorm_rope, dg_qkv_headnorm_rope_kv16, dg_rope_table)
@@ -36,20 +37,26 @@ from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM
 KV_FORMATS = {"f16": DG_KV_F16, "bf16": DG_KV_BF16}
 
 NORM_MODES = ("auto", "fused", "in_attention", "one_launch", "separate")
-# Canvas tiles per attention workgroup up to which "auto" norms k and v inside the kernel:
-# measured faster at 1 tile (a split key range, or a canvas of at most 32 rows), slower at 8.
-AUTO_FUSED_TILES = 2
+# Canvas keys per attention workgroup up to which "auto" norms k and v inside the kernel:
+# measured faster at one 32-key tile (a split key range, or a canvas of at most 32 rows), and
+# with the 16-key-tile kernel at four 16-key tiles; slower at 8 tiles of 32.
+AUTO_FUSED_KEYS = 64
 
 
-def auto_norm_mode(B, T, nh, hd, ws_bytes):
-    """The norm mode "auto" stands for, given the split-KV workspace size of the attention call
-    (0 when it does not split): "fused" when one attention workgroup meets at most
-    AUTO_FUSED_TILES canvas tiles of 32 keys, "in_attention" otherwise."""
-    # the workspace holds nsplit partials of (hd + 2) floats per query vector
-    nsplit = max(1, ws_bytes // (B * T * nh * (hd + 2) * 4)) if B * T * nh > 0 else 1
-    tiles = (T + 31) // 32                       # canvas tiles of 32 keys
-    per_wg = (tiles + nsplit - 1) // nsplit      # ... met by one workgroup
-    return "fused" if per_wg <= AUTO_FUSED_TILES else "in_attention"
+def auto_norm_mode(B, T, ctx, nh, nkv, hd, causal=False, cus=0, split=True):
+    """The norm mode "auto" stands for: "fused" when one attention workgroup of the call's
+    launch plan (dg_attn_split_gqa_plan; cus = 0: the current device) meets at most
+    AUTO_FUSED_KEYS canvas keys, "in_attention" otherwise.  Splits deal the canvas tiles round
+    robin, so a workgroup meets about T / nsplit of them; causal calls do not split, nor do
+    calls without a workspace (split=False)."""
+    if B * T * nh == 0:
+        return "fused"
+    p = dg_attn_split_gqa_plan(B, T, ctx, nh, nkv, hd, int(causal), 0, cus)
+    tile = 16 if p.kernel == DG_KERNEL_TILE16 else 32
+    nsplit = p.nsplit if split else 1
+    tiles = (T + tile - 1) // tile                   # canvas tiles
+    per_wg = (tiles + nsplit - 1) // nsplit          # ... met by one workgroup
+    return "fused" if per_wg * tile <= AUTO_FUSED_KEYS else "in_attention"
 
 
 def rope_table(pos0, T, hd, theta, device="cuda"):
@@ -126,7 +133,8 @@ class CanvasBlock:
             self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) \
                 if self.ws_bytes > 0 else None
         if self.norm_mode == "auto":
-            self.norm_mode = auto_norm_mode(B, T, nh, hd, self.ws_bytes)
+            self.norm_mode = auto_norm_mode(B, T, ctx, nh, nkv, hd, causal,
+                                            split=self.ws_bytes > 0)
 
     def norm(self, q, k, v):
         """The page's per-step headnorm calls, in place on q, k and v (for a k_eq_v layer the

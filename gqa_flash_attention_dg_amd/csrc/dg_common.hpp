@@ -1,6 +1,6 @@
 // dg_common.hpp -- helpers shared by the entry points and kernels of libdgattn.so: the
-// per-thread error message, argument checks, launch-error capture, and the XCD placement of
-// workgroups.
+// per-thread error message, argument checks, launch-error capture, the device topology and the
+// XCD placement of workgroups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,12 +39,28 @@ inline bool mul_ok(size_t& acc, long long f) {
     return true;
 }
 
+// Compute units and XCDs (accelerator dies, each with its own L2) of the current device, read
+// from the runtime once per device and cached.  Without a device to ask (a host with no GPU)
+// it returns an MI355X's 256 CUs in 8 XCDs.
+struct Topology {
+    int cus;
+    int xcds;
+};
+Topology device_topology();
+
 // Workgroup id -> logical id such that consecutive logical ids share an XCD: the hardware deals
-// the workgroups of a launch to the 8 XCDs round robin (workgroup b runs on XCD b % 8), so
-// logical id l runs on XCD l / (n / 8).  A grid that is not a multiple of 8 keeps its order.
-__device__ inline int xcd_remap(int bid, int n) {
-    if ((n & 7) != 0) return bid;
-    return (bid & 7) * (n >> 3) + (bid >> 3);
+// the workgroups of a launch to the device's XCDs round robin (workgroup b runs on XCD
+// b % nxcd), so logical id l runs on XCD l / (n / nxcd).  A bijection of [0, n); a grid that
+// is not a multiple of nxcd keeps its order.
+__host__ __device__ inline int xcd_remap(int bid, int n, int nxcd) {
+    if (nxcd <= 1) return bid;
+    if ((nxcd & (nxcd - 1)) == 0) {   // a power of two (8, or 4 and 1 on a partitioned MI355X)
+        const int sh = __builtin_ctz(nxcd);
+        if (n & (nxcd - 1)) return bid;
+        return (bid & (nxcd - 1)) * (n >> sh) + (bid >> sh);
+    }
+    if (n % nxcd != 0) return bid;
+    return (bid % nxcd) * (n / nxcd) + bid / nxcd;
 }
 
 inline int launch_status(const char* what) {

@@ -17,8 +17,8 @@
 // (stages of 128 keys, double-buffered direct global->LDS tiles) and merge their softmax
 // states at the end.  Small grids use the shapes of RelShape.  The bias enters each score
 // through the MFMA accumulator's starting value (see relpos_flash_kernel).  64-query
-// workgroups give 768 workgroups at the 64x64-grid, 12-head shape: three full rounds on 256
-// CUs.
+// workgroups give 768 workgroups at the 64x64-grid, 12-head shape: three full rounds on an
+// MI355X's 256 CUs.
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
@@ -47,7 +47,6 @@ struct RelShape {
 constexpr int kMaxGrid = 64;                  // gh, gw <= 64
 constexpr int kSmallGrid = 512;               // grids of at most this many tokens use 4 x 2 (or 4 x 1)
 constexpr int kSmallRows = 16;                // ... and 4 x 1 when gh is at most this
-constexpr int kCUs = 256;                     // compute units of the target GPU
 
 struct RelArgs {
     const float* qkv;  // [nwin][n][3W]
@@ -57,6 +56,7 @@ struct RelArgs {
     float* out;        // [nwin][n][W]
     int n, gh, gw, heads, W, nwin;
     int qblocks, nblocks;
+    int nxcd;    // XCDs of the device (workgroup placement)
     float qmul;  // scale * log2(e)
     // key tiling (see make_tiling): tile t starts at key (t >> tsh) * ta + (t & tmsk) * tb and
     // holds min(tl0 + (t & tmsk) * td, n - start) keys
@@ -80,7 +80,7 @@ __device__ inline float tab_read(const float* __restrict__ tab, int i) { return 
 constexpr int kBiasWaves = 4;
 
 // Both bias kernels number their workgroups through xcd_remap over a grid padded to a multiple
-// of 8 (the padding workgroups have no task), so the rows of one (window, head) are written on
+// of the XCD count (the padding workgroups have no task), so the rows of one (window, head) are written on
 // the XCD whose attention workgroups read them: writing lines that another XCD's L2 has just
 // read was measured to be the slow case for the split-KV workspace.
 //
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs 
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
     const long long task =
-        (long long)xcd_remap(blockIdx.x, gridDim.x) * kBiasWaves + (threadIdx.x >> 6);
+        (long long)xcd_remap(blockIdx.x, gridDim.x, a.nxcd) * kBiasWaves + (threadIdx.x >> 6);
     if (task >= ntasks) return;  // wave-uniform; task = unit * (gh + gw) + line
     const int line = (int)(task % (a.gh + a.gw));
     const int unit = (int)(task / (a.gh + a.gw));
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias_kernel(RelArgs a,
                                                                      long long ntasks) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
     const long long task =
-        (long long)xcd_remap(blockIdx.x, gridDim.x) * kBiasWaves + (threadIdx.x >> 6);
+        (long long)xcd_remap(blockIdx.x, gridDim.x, a.nxcd) * kBiasWaves + (threadIdx.x >> 6);
     if (task >= ntasks) return;  // wave-uniform
     // task = ((unit * (gh + gw) + line) * 2 + qt) * 2 + rt, unit = win * heads + head
     const int rt = (int)(task & 1), qt = (int)((task >> 1) & 1);
@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(64 * kWavesT)
         return smem + ((buf * kParts + tile) * 2 + isv) * TL::kFloats;
     };
 
-    const int lid = xcd_remap(blockIdx.x, a.nblocks);
+    const int lid = xcd_remap(blockIdx.x, a.nblocks, a.nxcd);
     const int qb = lid % a.qblocks;
     const int unit = lid / a.qblocks;          // win * heads + head
     const int head = unit % a.heads, win = unit / a.heads;
@@ -495,7 +495,8 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     // takes every tile, and the half-row tiling needs each wavefront to see one half only),
     // when there are more workgroups than CUs: with fewer, the 4 x 2 shape's key split halves
     // each workgroup's time.
-    const bool rows16 = small && gh <= kSmallRows && gw <= 32 && nblocks > kCUs;
+    const dg::Topology topo = dg::device_topology();
+    const bool rows16 = small && gh <= kSmallRows && gw <= 32 && nblocks > topo.cus;
     if (nblocks > 0x7fffffffLL || (long long)nwin * heads * (gh + gw) > 0x1fffffffLL)
         return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     RelArgs a;
@@ -504,6 +505,7 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     a.n = (int)n; a.gh = gh; a.gw = gw; a.heads = heads; a.W = (int)W; a.nwin = nwin;
     a.qblocks = (int)qblocks;
     a.nblocks = (int)nblocks;
+    a.nxcd = topo.xcds;
     a.qmul = scale * dgk::kLog2e;
     const Tiling tl = make_tiling(gh, gw);
     a.ntiles = tl.ntiles;
@@ -517,7 +519,8 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
         const bool b16 = gh <= 16 && gw <= 16;   // every line fits one 16x16 tile
         const long long ntasks = (long long)nwin * heads * (gh + gw) * (b16 ? 1 : 4);
         const long long nbias = (ntasks + kBiasWaves - 1) / kBiasWaves;
-        const dim3 grid((unsigned)((nbias + 7) / 8 * 8));   // a multiple of 8 for xcd_remap
+        const long long nx = topo.xcds;
+        const dim3 grid((unsigned)((nbias + nx - 1) / nx * nx));   // whole XCD rounds for xcd_remap
         if (b16)
             hipLaunchKernelGGL(relpos_bias16_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
                                static_cast<float*>(workspace), ntasks);

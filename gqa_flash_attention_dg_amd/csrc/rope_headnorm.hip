@@ -60,6 +60,7 @@ struct NormArgs {
     float eps;
     int fmt16;        // DG_KV_F16 or DG_KV_BF16 when a segment has twins
     int kvmajor;      // exactly k and v of one shape: rows taken in (b*heads + h, k|v, t) order
+    int nxcd;         // XCDs of the device (kvmajor workgroup placement)
 };
 
 // kHD: the head dim when it is 128 or 64 (no per-lane guards), 0 for any other hd <= 128.  Lanes
@@ -153,7 +154,7 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
     NormSeg g = a.seg[0];
     if (a.kvmajor) {
         const long long r =
-            (long long)dg::xcd_remap(blockIdx.x, gridDim.x) * kRowsPerBlock + (threadIdx.x >> 6);
+            (long long)dg::xcd_remap(blockIdx.x, gridDim.x, a.nxcd) * kRowsPerBlock + (threadIdx.x >> 6);
         if (r >= 2 * g.rows) return;
         const long long bh = r / (2 * a.T);
         const int rem = (int)(r % (2 * a.T));
@@ -220,6 +221,7 @@ int launch_norm(const char* fn, NormArgs& a, void* stream) {
     if (rows == 0) return dg::ok();
     const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many rows", fn);
+    a.nxcd = dg::device_topology().xcds;
     auto* kern = a.hd == 128 ? headnorm_rope_kernel<128>
                              : (a.hd == 64 ? headnorm_rope_kernel<64> : headnorm_rope_kernel<0>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);

@@ -16,9 +16,11 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  Work is
  *     enqueued on it asynchronously; nothing synchronises inside the library.  The caller
  *     keeps every buffer alive until the stream has passed the launch.
- *   - Every argument is validated on the host before any HIP call.  On failure the call
- *     returns a negative status, launches nothing, writes nothing, and records a message
- *     that dg_last_error() returns (per calling thread).  The library never aborts or prints.
+ *   - Every argument is validated on the host before any work is enqueued; the only runtime
+ *     calls made before validation completes are read-only queries of the current device (its
+ *     compute-unit and XCD counts, which size the launch plans).  On failure the call returns
+ *     a negative status, launches nothing, writes nothing, and records a message that
+ *     dg_last_error() returns (per calling thread).  The library never aborts or prints.
  *   - A call whose output is empty (T == 0, batch == 0, n == 0) returns DG_OK and launches
  *     nothing.
  *   - Calls on one stream run in order; calls that write the same buffer from different
@@ -145,11 +147,43 @@ int dg_qkv_headnorm_rope_kv16(float* q, const float* wq, float* k, const float* 
 
 /*
  * dg_attn_split_gqa_workspace_size -- bytes of scratch that dg_attn_split_gqa can use to split
- * the key range of one call across more workgroups (partial results and their combine).
- * Returns 0 when the shape gains nothing from a split.  Arguments as for dg_attn_split_gqa;
- * returns 0 for any argument dg_attn_split_gqa would reject.
+ * the key range of one call across more workgroups (partial results and their combine), on the
+ * current device (its compute-unit count sets the split; see dg_attn_split_gqa_plan).  Enough
+ * for the f32 and the 16-bit K/V entry points alike.  Returns 0 when the shape gains nothing
+ * from a split.  Arguments as for dg_attn_split_gqa; returns 0 for any argument
+ * dg_attn_split_gqa would reject.
  */
 size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int nkv, int hd);
+
+/* Attention kernels a launch plan can name (dg_attn_plan.kernel). */
+#define DG_KERNEL_NONE 0     /* empty output: nothing is launched */
+#define DG_KERNEL_SMALL 1    /* ctx + T <= 8: one wavefront per (batch entry, q head) */
+#define DG_KERNEL_TILE32 2   /* 32-key tiles, 128 query vectors per workgroup */
+#define DG_KERNEL_TILE16 3   /* 16-key tiles, 64 query vectors per workgroup (64 < hd <= 128,
+                                f32 K/V, shapes too small to fill the device otherwise) */
+
+/* How a split-GQA attention call is launched (see dg_attn_split_gqa_plan). */
+typedef struct dg_attn_plan {
+    int kernel;              /* DG_KERNEL_* */
+    int query_block;         /* query vectors per workgroup (0 for DG_KERNEL_SMALL) */
+    int nsplit;              /* key-range splits (1 = unsplit) */
+    long long workgroups;    /* attention workgroups launched */
+    size_t workspace_bytes;  /* split-KV scratch the call uses (0 when unsplit) */
+} dg_attn_plan;
+
+/*
+ * dg_attn_split_gqa_plan -- the launch plan of the dg_attn_split_gqa family for a shape on a
+ * device with `cus` compute units (0 = the current device's count): which kernel runs, the
+ * workgroups and the key-range splits.  The split count targets one workgroup per compute unit
+ * and keeps at least two 64-key stages per split; causal calls do not split.  For sizing a
+ * workspace ahead of time for another device, and for inspection.  kv_format is 0 for f32 K/V,
+ * or DG_KV_F16 / DG_KV_BF16.  The plan of the actual call also depends on the workspace given
+ * (none: unsplit).
+ * Errors: DG_EINVAL for a NULL plan, negative sizes, nkv < 1, nh % nkv != 0, cus < 0, causal
+ * not 0/1 or an unknown kv_format; DG_EUNSUPPORTED for hd not a multiple of 4 in [4, 128].
+ */
+int dg_attn_split_gqa_plan(int batch, int T, int ctx, int nh, int nkv, int hd, int causal,
+                           int kv_format, int cus, dg_attn_plan* plan);
 
 /*
  * dg_attn_split_gqa -- GQA flash attention over the split key/value set [cache | canvas].

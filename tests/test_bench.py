@@ -91,21 +91,22 @@ def test_split_counts_match_brute_force(B, T, ctx, nh, nkv, hd, causal):
     assert (f2, a2, nb_fused) == (flops, attn_bytes, 0)
 
 
-def test_auto_norm_mode_counts_canvas_tiles_per_workgroup():
-    """'auto' norms k and v inside attention when a workgroup meets at most 2 canvas tiles (the
-    key range split over workgroups, or a short canvas), else keeps the k/v norm launch.  The
-    workspace sizes are those dg_attn_split_gqa_workspace_size returns for each shape:
-    nsplit partials of (hd + 2) floats per query vector."""
+def test_auto_norm_mode_counts_canvas_keys_per_workgroup():
+    """'auto' norms k and v inside attention when one workgroup of the launch plan meets at most
+    64 canvas keys (the key range split over workgroups, or a short canvas), else keeps the k/v
+    norm launch.  Plans are taken for a 256-CU device; causal calls and calls without a
+    workspace do not split."""
     from gqa_flash_attention_dg_amd.canvas import auto_norm_mode
-    ws = lambda B, T, nh, hd, nsplit: nsplit * B * T * nh * (hd + 2) * 4 if nsplit > 1 else 0
-    assert auto_norm_mode(1, 16, 4, 64, 0) == "fused"                       # tiny: 1 tile
-    assert auto_norm_mode(1, 256, 16, 128, ws(1, 256, 16, 128, 8)) == "fused"   # 8 tiles / 8
-    assert auto_norm_mode(1, 256, 16, 128, ws(1, 256, 16, 128, 6)) == "fused"   # 2 per split
-    assert auto_norm_mode(1, 256, 16, 128, ws(1, 256, 16, 128, 2)) == "in_attention"  # 4
-    assert auto_norm_mode(4, 256, 32, 128, 0) == "in_attention"             # long cache: 8
-    assert auto_norm_mode(1, 64, 8, 64, 0) == "fused"                       # 2 tiles, unsplit
-    assert auto_norm_mode(1, 65, 8, 64, 0) == "in_attention"                # 3 tiles
-    assert auto_norm_mode(0, 16, 4, 64, 0) == "fused"                       # empty: no launch
+    m = lambda *a, **k: auto_norm_mode(*a, cus=256, **k)
+    assert m(1, 16, 32, 4, 2, 64) == "fused"                       # tiny: 1 tile
+    assert m(1, 256, 1024, 16, 8, 128) == "fused"                  # 8 tiles over 8 splits
+    assert m(1, 256, 512, 16, 8, 128) == "fused"                   # 16-key tiles, 4 per split
+    assert m(4, 256, 8192, 32, 8, 128) == "in_attention"           # long cache: unsplit
+    assert m(1, 64, 0, 8, 8, 64) == "fused"                        # 2 tiles, unsplit
+    assert m(1, 65, 0, 8, 8, 64) == "in_attention"                 # 3 tiles, unsplit
+    assert m(1, 256, 1024, 16, 8, 128, causal=True) == "in_attention"   # causal: no split
+    assert m(1, 256, 1024, 16, 8, 128, split=False) == "in_attention"   # no workspace
+    assert m(0, 16, 32, 4, 2, 64) == "fused"                       # empty: no launch
 
 
 def test_stats_mean_median_min():

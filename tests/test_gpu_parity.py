@@ -177,8 +177,10 @@ def test_attn_split_kv_partials_and_combine(shape):
             1.0, 0]
     dg.dg_attn_split_gqa(*args, ws, nbytes)
     assert_parity(host(out), ref, "split-kv %s" % (shape,))
+    need = dg.dg_attn_split_gqa_plan(B, T, ctx, nh, nkv, hd).workspace_bytes
+    assert 0 < need <= nbytes
     with pytest.raises(dg.DgError):          # a workspace that is too small is refused
-        dg.dg_attn_split_gqa(*args, ws, nbytes - 4)
+        dg.dg_attn_split_gqa(*args, ws, need - 4)
 
 
 def qnorm_case(shape, qflags, seed):

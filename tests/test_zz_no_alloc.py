@@ -45,7 +45,8 @@ def test_noalloc_matches_workspace_entry_twice():
         print("noalloc call %d: B%d T%d ctx%d nh%d nkv%d hd%d" % (i, B, T, ctx, nh, nkv, hd),
               flush=True)
         c, q, kc, vc, k, v = _inputs(B, T, ctx, nh, nkv, hd, seed=10 + i)
-        ref, need = _with_workspace(c, q, kc, vc, k, v, scale, causal)
+        ref, _ = _with_workspace(c, q, kc, vc, k, v, scale, causal)
+        need = dg.dg_attn_split_gqa_plan(B, T, ctx, nh, nkv, hd, causal).workspace_bytes
         assert 0 < need <= dg.DG_NOALLOC_SCRATCH_BYTES, need   # both shapes use the scratch
         out = torch.full_like(q, float("nan"))
         dg.dg_attn_split_gqa_noalloc(q, kc, vc, k, v, out, B, T, ctx, nh, nkv, hd, scale, causal)
@@ -68,21 +69,21 @@ def test_noalloc_unsplit_shape():
 
 
 def test_noalloc_refuses_oversize_partials():
-    # find a shape whose split partials need more than the static scratch holds
+    # find a shape whose split partials (the f32 plan) need more than the static scratch holds
     torch.cuda.set_device(0)
     shape = None
-    for nkv in range(1, 33):
-        for qb in range(1, 512):
-            T, B, ctx, hd = 128 * qb, 1, 256, 128
-            need = dg.dg_attn_split_gqa_workspace_size(B, T, ctx, nkv, nkv, hd)
-            if need > dg.DG_NOALLOC_SCRATCH_BYTES:
-                shape = (B, T, ctx, nkv, nkv, hd)
+    for hd in (128, 64):
+        for T in range(64, 64 * 512, 64):
+            p = dg.dg_attn_split_gqa_plan(1, T, 256, 1, 1, hd)
+            if p.workspace_bytes > dg.DG_NOALLOC_SCRATCH_BYTES:
+                shape = (1, T, 256, 1, 1, hd)
                 break
         if shape:
             break
     if shape is None:
         pytest.skip("no shape on this device needs more split-KV scratch than the static array")
     B, T, ctx, nh, nkv, hd = shape
+    print("oversize shape: B%d T%d ctx%d nh%d nkv%d hd%d" % shape, flush=True)
     c, q, kc, vc, k, v = _inputs(B, T, ctx, nh, nkv, hd, seed=4)
     out = torch.zeros_like(q)
     with pytest.raises(dg.DgError) as e:
