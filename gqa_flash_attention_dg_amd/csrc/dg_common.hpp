@@ -63,6 +63,22 @@ __host__ __device__ inline int xcd_remap(int bid, int n, int nxcd) {
     return (bid % nxcd) * (n / nxcd) + bid / nxcd;
 }
 
+// Sum of v over each aligned group of N lanes (N = 8 or 16), left in every lane of the group,
+// with DPP lane moves within the lanes' own registers: two quad permutes (lane ^ 1, lane ^ 2),
+// then the mirror within 8 lanes and, for 16, within 16.  Each step adds a value and its
+// partner's in the same order on both sides, so every lane of a group ends with the same sum.
+// (A lane shuffle goes through the LDS crossbar and waits out its latency at every step.)
+template <int N>
+__device__ inline float group_sum(float v) {
+    static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if constexpr (N == 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 inline int launch_status(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DG_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -6,12 +6,13 @@
 // builds for positions seq_len + t.
 //
 // Both are HBM-bound.  The page runs one 128-thread workgroup per (token, head) with shared
-// memory trees, and dispatches q, k and v separately; here one 64-lane wavefront owns one
-// (token, head) row: lane l holds elements l and l+64, so every global access is one coalesced
-// 256-byte wave load/store, the sum of squares is a wave butterfly (no LDS, no barrier), and
-// the rotate-half partner is either in the same lane (hd = 128) or one lane shuffle away.  One
-// launch can cover the rows of q, k and v together (dg_qkv_headnorm_rope): at canvas sizes
-// the three calls are launch-bound.
+// memory trees, and dispatches q, k and v separately.  Here, for hd 64 and 128, hd/8 lanes own
+// one (token, head) row, each with two 16-byte chunks hd/2 apart, so a wavefront streams 4 or 8
+// rows with 16-byte accesses, the rope partner of every element is in the same lane, and the
+// sum of squares is a DPP sum within the row's lanes (no LDS, no barrier).  Other head dims take
+// one 64-lane wavefront per row (lane l holds elements l and l+64; the rope partner is one lane
+// shuffle away).  One launch can cover the rows of q, k and v together
+// (dg_qkv_headnorm_rope): at canvas sizes the three calls are launch-bound.
 #include "kv16.hpp"
 
 namespace {
@@ -61,6 +62,8 @@ struct NormArgs {
     int fmt16;        // DG_KV_F16 or DG_KV_BF16 when a segment has twins
     int kvmajor;      // exactly k and v of one shape: rows taken in (b*heads + h, k|v, t) order
     int nxcd;         // XCDs of the device (kvmajor workgroup placement)
+    int kvgroup;      // 16-byte kernel, kvmajor: (b, head) pairs per XCD, rows taken in
+                      // (group, k|v, t, pair) order; 0: the (b*heads + h, k|v, t) order
 };
 
 // kHD: the head dim when it is 128 or 64 (no per-lane guards), 0 for any other hd <= 128.  Lanes
@@ -182,6 +185,135 @@ __global__ void __launch_bounds__(256) headnorm_rope_kernel(NormArgs a) {
                       g.vout16 ? g.vout16 + (size_t)u * a.hd : nullptr, a.fmt16);
 }
 
+// hd 64 and 128: 16-byte accesses.  A row is taken by L lanes, lane c holding chunks c, c + L,
+// ... (4 floats each); chunks hd/2 apart share a lane, so the rope partner of each element is
+// in the same lane, and a 64-lane wavefront takes 64/L rows at once.  The sum of squares is a DPP sum over
+// the row's L lanes.  Row numbering and placement as in headnorm_rope_kernel.
+template <int HD>
+struct V4 {
+    static constexpr int L = HD / 8;              // lanes per row
+    static constexpr int kRowsPerWave = 64 / L;
+    static constexpr int kRowsPerBlock = 4 * kRowsPerWave;
+};
+
+__device__ inline uint2 pack4_kv16(float4 v, int fmt) {
+    return make_uint2((uint32_t)dg::to_kv16(v.x, fmt) | ((uint32_t)dg::to_kv16(v.y, fmt) << 16),
+                      (uint32_t)dg::to_kv16(v.z, fmt) | ((uint32_t)dg::to_kv16(v.w, fmt) << 16));
+}
+
+__device__ inline float4 scale4(float4 v, float s) { return make_float4(v.x * s, v.y * s, v.z * s, v.w * s); }
+__device__ inline float4 mul4(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
+
+template <int HD>
+__device__ inline void headnorm_row_v4(float* __restrict__ xr, const float* __restrict__ w,
+                                       const float* __restrict__ cr, unsigned flags, float eps,
+                                       int c, float* __restrict__ vr, uint16_t* __restrict__ xr16,
+                                       uint16_t* __restrict__ vr16, int fmt16) {
+    constexpr int L = V4<HD>::L;
+    constexpr int K = HD / (4 * L);   // chunks per lane: c + L*k; chunk k pairs with k + K/2
+    const bool norm = !(flags & DG_NORM_SKIP);
+    const bool weighted = norm && (flags & DG_NORM_WEIGHTED);
+    const bool rope = (flags & DG_NORM_ROPE) != 0;
+    const float4 one = make_float4(1.f, 1.f, 1.f, 1.f), zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 x[K], wv[K], co[K], si[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int ch = c + L * k;
+        x[k] = reinterpret_cast<const float4*>(xr)[ch];
+        wv[k] = weighted ? reinterpret_cast<const float4*>(w)[ch] : one;
+        co[k] = rope ? reinterpret_cast<const float4*>(cr)[ch] : zero;
+        si[k] = rope ? reinterpret_cast<const float4*>(cr + HD)[ch] : zero;
+    }
+    if (norm) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
+        ss = dg::group_sum<L>(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)HD + eps);
+#pragma unroll
+        for (int k = 0; k < K; ++k) x[k] = scale4(x[k], inv);
+        if (vr) {  // the v-norm of the same raw rows: weightless, un-roped
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                reinterpret_cast<float4*>(vr)[c + L * k] = x[k];
+                if (vr16) reinterpret_cast<uint2*>(vr16)[c + L * k] = pack4_kv16(x[k], fmt16);
+            }
+        }
+        if (weighted) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) x[k] = mul4(x[k], wv[k]);
+        }
+    }
+    if (rope) {   // chunk k of the first half pairs with chunk k + K/2 of the second
+#pragma unroll
+        for (int k = 0; k < K / 2; ++k) {
+            const float4 y0 = x[k], y1 = x[k + K / 2];
+            const float4 c0 = co[k], s0 = si[k], c1 = co[k + K / 2], s1 = si[k + K / 2];
+            x[k] = make_float4(y0.x * c0.x - y1.x * s0.x, y0.y * c0.y - y1.y * s0.y,
+                               y0.z * c0.z - y1.z * s0.z, y0.w * c0.w - y1.w * s0.w);
+            x[k + K / 2] = make_float4(y1.x * c1.x + y0.x * s1.x, y1.y * c1.y + y0.y * s1.y,
+                                       y1.z * c1.z + y0.z * s1.z, y1.w * c1.w + y0.w * s1.w);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        reinterpret_cast<float4*>(xr)[c + L * k] = x[k];
+        if (xr16)   // the 16-bit twin, rounded as dg_pack_kv16 rounds
+            reinterpret_cast<uint2*>(xr16)[c + L * k] = pack4_kv16(x[k], fmt16);
+    }
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) headnorm_rope_v4_kernel(NormArgs a) {
+    using S = V4<HD>;
+    const int lane = threadIdx.x & 63, sub = lane / S::L, c = lane % S::L;
+    const long long r0 = (long long)(a.kvmajor ? dg::xcd_remap(blockIdx.x, gridDim.x, a.nxcd)
+                                               : (int)blockIdx.x) * S::kRowsPerBlock +
+                         (threadIdx.x >> 6) * S::kRowsPerWave + sub;
+    long long u;
+    NormSeg g = a.seg[0];   // constant indices: the segment's fields come from scalar loads
+    if (a.kvmajor) {
+        if (r0 >= 2 * g.rows) return;                  // the whole row group of L lanes
+        if (a.kvgroup > 0) {
+            // The (b, head) pairs of one XCD (as the attention places them) go token by token,
+            // the pairs of a token next to each other: adjacent heads are adjacent rows in
+            // memory, so a wavefront's rows are contiguous runs instead of rows 4 KiB apart.
+            const long long per = 2LL * a.T * a.kvgroup;
+            const long long grp = r0 / per, rem = r0 % per;
+            const long long half = (long long)a.T * a.kvgroup;
+            if (rem >= half) g = a.seg[1];
+            const long long r2 = rem % half;
+            const int t = (int)(r2 / a.kvgroup);
+            const long long bh = grp * a.kvgroup + r2 % a.kvgroup;
+            u = ((bh / g.heads) * a.T + t) * g.heads + bh % g.heads;
+        } else {
+            const long long bh = r0 / (2 * a.T);
+            const int rem = (int)(r0 % (2 * a.T));
+            const int t = rem % a.T;
+            if (rem >= a.T) g = a.seg[1];
+            u = ((bh / g.heads) * a.T + t) * g.heads + bh % g.heads;
+        }
+    } else {
+        u = r0;
+        if (u >= g.rows) {
+            u -= g.rows;
+            if (a.nseg < 2) return;
+            g = a.seg[1];
+            if (u >= g.rows) {
+                u -= g.rows;
+                if (a.nseg < 3 || u >= a.seg[2].rows) return;
+                g = a.seg[2];
+            }
+        }
+    }
+    const int t = (int)((u / g.heads) % a.T);
+    const float* cr = (g.flags & DG_NORM_ROPE) ? a.cs + (size_t)t * 2 * HD : nullptr;
+    headnorm_row_v4<HD>(g.x + (size_t)u * HD, g.w, cr, g.flags, a.eps, c,
+                        g.vout ? g.vout + (size_t)u * HD : nullptr,
+                        g.x16 ? g.x16 + (size_t)u * HD : nullptr,
+                        g.vout16 ? g.vout16 + (size_t)u * HD : nullptr, a.fmt16);
+}
+
 }  // namespace
 
 extern "C" int dg_rope_table(float* cs, int pos0, int T, int hd, double theta, void* stream) {
@@ -219,11 +351,28 @@ int launch_norm(const char* fn, NormArgs& a, void* stream) {
     long long rows = 0;
     for (int i = 0; i < a.nseg; ++i) rows += a.seg[i].rows;
     if (rows == 0) return dg::ok();
-    const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many rows", fn);
     a.nxcd = dg::device_topology().xcds;
-    auto* kern = a.hd == 128 ? headnorm_rope_kernel<128>
-                             : (a.hd == 64 ? headnorm_rope_kernel<64> : headnorm_rope_kernel<0>);
+    // hd 64 and 128 take the 16-byte kernel when every tensor is 16-byte aligned
+    bool v4 = a.hd == 128 || a.hd == 64;
+    uintptr_t al = reinterpret_cast<uintptr_t>(a.cs);
+    for (int i = 0; i < a.nseg; ++i)
+        al |= reinterpret_cast<uintptr_t>(a.seg[i].x) | reinterpret_cast<uintptr_t>(a.seg[i].w) |
+              reinterpret_cast<uintptr_t>(a.seg[i].vout) | reinterpret_cast<uintptr_t>(a.seg[i].x16) |
+              reinterpret_cast<uintptr_t>(a.seg[i].vout16);
+    if (al & 15) v4 = false;
+    const int per = !v4 ? kRowsPerBlock : a.hd == 128 ? V4<128>::kRowsPerBlock : V4<64>::kRowsPerBlock;
+    const long long blocks = (rows + per - 1) / per;
+    a.kvgroup = 0;
+    if (v4 && a.kvmajor) {   // whole XCDs of whole workgroups: the grouped order applies
+        const long long pairs = a.seg[0].rows / a.T;     // (b, head) pairs
+        const long long nx = a.nxcd;
+        if (pairs % nx == 0 && (2LL * a.T * (pairs / nx)) % per == 0)
+            a.kvgroup = (int)(pairs / nx);
+    }
+    if (blocks > 0x7fffffffLL) return dg::fail(DG_EUNSUPPORTED, "%s: too many rows", fn);
+    auto* kern = v4 ? (a.hd == 128 ? headnorm_rope_v4_kernel<128> : headnorm_rope_v4_kernel<64>)
+                    : a.hd == 128 ? headnorm_rope_kernel<128>
+                                  : (a.hd == 64 ? headnorm_rope_kernel<64> : headnorm_rope_kernel<0>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
     return dg::launch_status(fn);
 }
