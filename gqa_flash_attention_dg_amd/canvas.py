@@ -196,7 +196,15 @@ class CanvasBlock:
                           self.nkv, self.hd, self.scale, self.causal, self.ws, self.ws_bytes)
 
     def step(self, q, k, v, out):
-        """One canvas step: norms (when enabled), then attention into `out`."""
+        """One canvas step: norms (when enabled), then attention into `out`.
+
+        What the step leaves in the caller's buffers depends on the norm mode (a normed block):
+          "fused"         q, k and v are read only and keep their raw contents; a k_eq_v
+                          layer's v buffer is neither read nor written;
+          "in_attention"  k holds the normed, weighted, roped k and v the weightless norm of v
+                          (k_eq_v: of the raw k); q keeps its raw contents;
+          "one_launch", "separate"  as "in_attention", and q holds the normed, weighted, roped q.
+        `out` is written in every mode."""
         if self.normed and self.norm_mode == "fused":
             self.attend_qkvnorm(q, k, v, out)
             return
@@ -286,6 +294,8 @@ class CanvasStack:
                 workspace=self.ws.get((l.ctx, l.nkv, l.hd)), device=device))
 
     def step(self, li, q, k, v, out):
-        """Layer li's attention for this canvas step (q, k, v are its projections; for a
-        k_eq_v layer v is an output buffer)."""
+        """Layer li's attention for this canvas step (q, k, v are its projections; a k_eq_v
+        layer ignores v's contents).  Which of q, k and v are left normed depends on the layer's
+        norm mode, as CanvasBlock.step says; with "fused" (what "auto" picks at the
+        DiffusionGemma-like shapes) none of them is written, and a k_eq_v layer's v neither."""
         self.blocks[li].step(q, k, v, out)

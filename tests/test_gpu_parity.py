@@ -367,6 +367,37 @@ def test_tiny_canvas_step_every_element(norm_mode):
     assert_parity(got, ref, "tiny canvas step")
 
 
+@pytest.mark.parametrize("k_eq_v", [False, True], ids=["plain", "k_eq_v"])
+@pytest.mark.parametrize("norm_mode", NORM_MODES)
+def test_canvas_step_leaves_buffers_as_documented(norm_mode, k_eq_v):
+    """After one step, q, k and v hold what CanvasBlock.step documents for the mode: raw
+    contents where the norm ran inside attention (a k_eq_v layer's v untouched under "fused"),
+    else the page's normed rows (v: the weightless norm of v, or of the raw k for k_eq_v)."""
+    c = synth.split_case(1, 40, 70, 8, 2, 128, seed=31)
+    blk = CanvasBlock(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, dev(c.kc), dev(c.vc), dev(c.wq),
+                      dev(c.wk), eps=c.eps, theta=c.theta, norm_mode=norm_mode, k_eq_v=k_eq_v)
+    sentinel = np.full_like(c.v, 7.0)
+    q, k = dev(c.q), dev(c.k)
+    v = dev(sentinel if k_eq_v else c.v)
+    out = torch.empty((c.B, c.T, c.nh * c.hd), device="cuda")
+    blk.step(q, k, v, out)
+    got_q, got_k, got_v = host(q), host(k), host(v)
+    cs = oracle.rope_table(c.ctx, c.T, c.hd, c.theta)
+    nq = oracle.headnorm_rope(c.q, c.wq, cs, c.nh, c.hd, 3, c.eps)
+    nk = oracle.headnorm_rope(c.k, c.wk, cs, c.nkv, c.hd, 3, c.eps)
+    nv = oracle.headnorm_rope(c.k if k_eq_v else c.v, None, None, c.nkv, c.hd, 0, c.eps)
+    if norm_mode == "fused":
+        assert np.array_equal(got_q, c.q) and np.array_equal(got_k, c.k)
+        assert np.array_equal(got_v, sentinel if k_eq_v else c.v)
+        return
+    assert_parity(got_k, nk, "k after %s" % norm_mode)
+    assert_parity(got_v, nv, "v after %s" % norm_mode)
+    if norm_mode == "in_attention":
+        assert np.array_equal(got_q, c.q)
+    else:
+        assert_parity(got_q, nq, "q after %s" % norm_mode)
+
+
 @pytest.mark.parametrize("norm_mode", NORM_MODES)
 def test_dg_canvas_48_steps(norm_mode):
     c = synth.dg_canvas_steps(48)
