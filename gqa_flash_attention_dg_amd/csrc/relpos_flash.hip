@@ -61,6 +61,9 @@ struct RelArgs {
     // key tiling (see make_tiling): tile t starts at key (t >> tsh) * ta + (t & tmsk) * tb and
     // holds min(tl0 + (t & tmsk) * td, n - start) keys
     int tsh, ta, tmsk, tb, tl0, td, ntiles;
+    // small grids (gh, gw <= 16): bias row layout [dh (gh4 floats) | dw] with stride brs floats,
+    // and 16-query tiles per (window, head)
+    int gh4, brs, qtiles;
 };
 
 using dg::xcd_remap;
@@ -89,25 +92,33 @@ constexpr int kBiasWaves = 4;
 // supplies query row l%16 (A) and table row l%16 (B) at contraction index k = l/16; step
 // 4c+e contracts element 16c+4k+e, so in each of the 4 float4 loads per operand the 4 lanes
 // of a row read 64 contiguous bytes.  The 4 accumulators hold queries 4*(l/16)+r of table
-// row l%16.
+// row l%16.  One wavefront per line (measured fastest: two or four lines per wavefront, with
+// their loads in flight together, took 12.0 and 14.7 us against 10.3 for the SAM windows).
+// The output is one row per (window, head, query), dh then dw, each part padded to a multiple
+// of 4 floats (the layout relpos_win_kernel reads); the head is the fastest-varying task
+// index, so the wavefronts running together read the q slices of all heads of the same tokens,
+// which lie next to each other in each qkv row.
 __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs a, float* __restrict__ dhw,
-                                                                       long long ntasks) {
+                                                                       int ntasks) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
-    const long long task =
-        (long long)xcd_remap(blockIdx.x, gridDim.x, a.nxcd) * kBiasWaves + (threadIdx.x >> 6);
-    if (task >= ntasks) return;  // wave-uniform; task = unit * (gh + gw) + line
-    const int line = (int)(task % (a.gh + a.gw));
-    const int unit = (int)(task / (a.gh + a.gw));
-    const int head = unit % a.heads, win = unit / a.heads;
-    const bool is_h = line < a.gh;
-    const int nq = is_h ? a.gw : a.gh;
-    const int nr = is_h ? a.gh : a.gw;
-    auto qidx = [&](int v) { return is_h ? line * a.gw + v : v * a.gw + (line - a.gh); };
+    const int task = xcd_remap(blockIdx.x, gridDim.x, a.nxcd) * kBiasWaves +
+                     __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (task >= ntasks) return;  // wave-uniform; task = (win * (gh + gw) + line) * heads + head
+    const int head = task % a.heads;
+    const int wl = task / a.heads;
+    const int line = wl % (a.gh + a.gw), win = wl / (a.gh + a.gw);
+    const int unit = win * a.heads + head;
+    // line < gh: grid row `line` (gw queries) against rh[line] (gh rows); else grid column
+    // p = line - gh (gh queries) against rw[p] (gw rows)
+    const bool col = line >= a.gh;
+    const int p = col ? line - a.gh : line;
+    const int nq = col ? a.gh : a.gw, nr = col ? a.gw : a.gh;
+    auto qidx = [&](int v) { return col ? v * a.gw + p : p * a.gw + v; };
     const size_t rs = (size_t)3 * a.W;
     const float* qr = a.qkv + ((size_t)win * a.n + qidx(min(l16, nq - 1))) * rs + head * HD + 4 * kq;
-    const float* tr = (is_h ? a.rh + (size_t)line * a.gh * HD : a.rw + (size_t)(line - a.gh) * a.gw * HD) +
-                      (size_t)min(l16, nr - 1) * HD + 4 * kq;
+    const float* tr = (col ? a.rw + ((size_t)p * a.gw + min(l16, nr - 1)) * HD
+                           : a.rh + ((size_t)p * a.gh + min(l16, nr - 1)) * HD) + 4 * kq;
     float qv[16], tv[16];
 #pragma unroll
     for (int c = 0; c < 16; c += 4) {
@@ -118,14 +129,14 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs 
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s], tv[s], acc, 0, 0, 0);
+    for (int st = 0; st < 16; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[st], tv[st], acc, 0, 0, 0);
     if (l16 >= nr) return;
-    float* base = dhw + (is_h ? (size_t)unit * a.n * a.gh
-                              : (size_t)a.nwin * a.heads * a.n * a.gh + (size_t)unit * a.n * a.gw);
+    // one row of gh4 + gw4 floats per (window, head, query): dh at 0, dw at gh4
+    float* base = dhw + (size_t)unit * a.n * a.brs + (col ? a.gh4 : 0) + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int v = 4 * kq + r;   // accumulator r: query on the line
-        if (v < nq) base[(size_t)qidx(v) * nr + l16] = acc[r] * dgk::kLog2e;
+        if (v < nq) base[(size_t)qidx(v) * a.brs] = acc[r] * dgk::kLog2e;
     }
 }
 
@@ -170,6 +181,341 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias_kernel(RelArgs a,
     for (int r = 0; r < 16; ++r) {
         const int v = qt * 32 + dgk::key_of(r, half);   // accumulator row r: query on the line
         if (v < nq) base[(size_t)qidx(v) * nr + rrow] = acc[r] * dgk::kLog2e;
+    }
+}
+
+// Small grids (gh, gw <= 16: the SAM windows) on v_mfma_f32_16x16x4f32.  One wavefront owns
+// one (window, head, 16-query tile) and runs on its own: no LDS staging of K or V and no
+// barriers, so wavefronts of any tile and window fill a SIMD and the launch balances at tile
+// granularity (a 14x14 window is 13 tiles; 300 window-heads would not balance over 256 CUs).
+//
+// Scores are S^T = K Q^T per 16-key tile: lane (n = l%16, g = l/16) holds query n and, in
+// accumulator r, key 16t + 4r + g.  The K rows are fed to the matrix rows in that order (matrix
+// row 4g + r takes key 16t + 4r + g), so the output step O^T += V^T P^T contracts in its step r
+// exactly the four keys 16t + 4r .. 16t + 4r + 3, with the lane's own register r as the B
+// operand: a key set of n keys needs ceil(n / 4) steps, not a multiple of 16.  Output row m of
+// head-dim tile h is head element 4m + h, so each lane reads 16 contiguous bytes of a V row per
+// step and writes 16 contiguous bytes of an output row per register.  Contraction order of the
+// scores: step 4c + e, lane group g, element 16c + 4g + e (one 16-byte K read per 4 steps).
+//
+// The bias of every (query, key) pair the lane holds is formed once, before the key loop: the
+// wavefront expands its 16 queries' dh/dw rows into a [key][query] table in LDS (dh[ky] +
+// dw[kx], -inf past the last key) and each lane reads its 4 * NT values into registers, where
+// they start the score accumulators.  The padding keys of the last tile so carry -inf and need
+// no mask.  K and V are read with buffer loads (the tile offset in a scalar register), two tiles
+// ahead of their use.  Softmax reference: scores stay in log2 units, the reference
+// stays 0 while the running maximum lies within +-kHeadroom (no subtraction at all) and moves
+// only when a score would overflow exp2 or the first tile's maximum is far below 0.
+constexpr int kWinGrid = 16;       // grids with gh, gw <= 16 take the 16x16 path
+namespace win {
+constexpr int kWaves = 4;          // wavefronts per workgroup (independent tasks)
+constexpr int kQT = 16;            // queries per wavefront
+constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw 32-bit buffer descriptor (gfx9 family)
+// The bias-row layout of a query with no bias (dh and dw all zero, never written): read in
+// place of the rows when the call has no tables, so the loads are the same either way.  Not
+// const, so it shares the global address space with the workspace and the loads stay global
+// loads (a flat load would make every wait a wait for all loads).
+__device__ __attribute__((aligned(16))) float kZeroRow[2 * 16];
+}  // namespace win
+
+// NT is the exact number of 16-key tiles (ceil(n / 16)), so only the last tile has runtime
+// conditions.  Two wavefronts per SIMD cap the kernel at 256 VGPRs, which keeps every MFMA
+// operand and accumulator in VGPRs (no copies to and from accumulation registers).
+//
+// The grid holds as many wavefronts as run at once and each takes tasks gw, gw + G, ... (G
+// wavefronts in the grid).  A wavefront loads the next task's bias rows and Q three tiles
+// before the end of the current one, and its first two K/V tiles in place of the current
+// task's tiles NT + 0 and NT + 1: only the first task of each wavefront waits for memory
+// before its first tile (measured with one task per wavefront, that wait was about 10 us of a
+// wavefront's 17 us, all wavefronts waiting at once).
+template <int NT>
+__global__ void __launch_bounds__(64 * win::kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+    relpos_win_kernel(RelArgs a, int ntasks) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    // one spare 16-key tile per table takes the writes of columns past the grid's width
+    __shared__ __attribute__((aligned(16))) float ebuf[win::kWaves][(NT + 1) * 16 * win::kQT];
+    // the wavefront index is uniform: every task quantity below lives in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    // Tasks are split into one contiguous range per XCD (workgroup b runs on XCD b % nxcd), so
+    // the wavefronts streaming one window's K/V share an L2; within its XCD's range a wavefront
+    // takes every (wavefronts per XCD)-th task.  (Taking the next free task from a per-XCD
+    // atomic counter instead was measured 1.5x slower.)
+    const int per = (int)gridDim.x / a.nxcd;   // workgroups per XCD (the grid is a multiple)
+    const int lid = xcd_remap(blockIdx.x, gridDim.x, a.nxcd);
+    const int xcd = lid / per, wpx = per * win::kWaves;
+    const int range = (ntasks + a.nxcd - 1) / a.nxcd;
+    const int lo = xcd * range, hi = min(lo + range, ntasks);
+    int task = lo + (lid % per) * win::kWaves + wave;
+    if (task >= hi) return;   // wave-uniform; no barrier below
+    const int n = a.n;
+    const unsigned rsb = 12u * (unsigned)a.W;           // qkv row stride in bytes
+    const int krow = 4 * (l16 & 3) + (l16 >> 2);        // matrix row l16 takes key 16t + krow
+    const unsigned koff = (unsigned)krow * rsb + 16u * kq;
+    const unsigned voff = (unsigned)kq * rsb + 16u * l16;
+    constexpr bool kCross = NT >= 2;                     // next task's tiles 0, 1 prefetched
+
+    // A task is (window, 16-query tile, head), numbered (w * qtiles + qt) * heads + head: the
+    // heads of one query tile run together.
+    struct Task {
+        int w, head, qt;
+        __amdgpu_buffer_rsrc_t rsrc;   // this window's qkv rows
+        int kb, vb;                    // byte offsets of this head's k and v in a row
+    };
+    auto decode = [&](int tk) {
+        Task T;
+        T.head = tk % a.heads;
+        const int wq = tk / a.heads;
+        T.qt = wq % a.qtiles;
+        T.w = wq / a.qtiles;
+        T.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.qkv + (size_t)T.w * n * 3 * a.W), 0,
+                                                   (int)((unsigned)n * rsb), (int)win::kRsrcWord3);
+        T.kb = (a.W + T.head * HD) * 4;
+        T.vb = (2 * a.W + T.head * HD) * 4;
+        return T;
+    };
+    // This lane's bias-row values -- dh[0..gh) of its query and dw at kx = kq + 4i, the columns
+    // it expands -- and its Q values (B operand of the scores, in log2 units).  Rows past the
+    // window read row 0 and are zeroed.
+    // Every load here and in load_k / load_v is unconditional (addresses clamped into range), so
+    // the compiler can count exactly which loads a wait needs and never waits for later ones.
+    auto load_head = [&](const Task& T, float (&dhr)[kWinGrid], float (&dwv)[4], float (&qreg)[16]) {
+        const int qn = T.qt * win::kQT + l16;
+        const bool qvalid = qn < n;
+        // without bias rows, a row of zeros in the same layout
+        const bool bias = a.dhw != nullptr;
+        const float* br = bias ? a.dhw + ((size_t)(T.w * a.heads + T.head) * n + (qvalid ? qn : 0)) * a.brs
+                               : win::kZeroRow;
+        const int clast = (bias ? a.brs : 2 * kWinGrid) - 4;
+#pragma unroll
+        for (int c = 0; c < kWinGrid / 4; ++c) {
+            // dh[4c .. 4c+3]; past gh4 this reads other values of the row, never used
+            const float4 v = *reinterpret_cast<const float4*>(br + min(4 * c, clast));
+            dhr[4 * c] = v.x; dhr[4 * c + 1] = v.y; dhr[4 * c + 2] = v.z; dhr[4 * c + 3] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dwv[i] = br[a.gh4 + min(kq + 4 * i, a.gw - 1)];
+        const float* qr = a.qkv + ((size_t)T.w * n + (qvalid ? qn : 0)) * 3 * a.W + T.head * HD + 4 * kq;
+        const float z = qvalid ? a.qmul : 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 v = *reinterpret_cast<const float4*>(qr + 16 * c);
+            qreg[4 * c + 0] = v.x * z;
+            qreg[4 * c + 1] = v.y * z;
+            qreg[4 * c + 2] = v.z * z;
+            qreg[4 * c + 3] = v.w * z;
+        }
+    };
+    auto load_k = [&](const Task& T, int t, f32x4 (&kf)[4]) {
+        if (t < NT - 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kf[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      T.rsrc, (int)koff, T.kb + 16 * t * (int)rsb + 64 * c, 0));
+        } else {   // the last tile: rows past the last key repeat it (their bias is -inf)
+            const unsigned o = (unsigned)min(16 * t + krow, n - 1) * rsb + 16u * kq;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                kf[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      T.rsrc, (int)o, T.kb + 64 * c, 0));
+        }
+    };
+    auto load_v = [&](const Task& T, int t, f32x4 (&vf)[4]) {
+        if (t < NT - 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vf[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      T.rsrc, (int)voff, T.vb + (16 * t + 4 * r) * (int)rsb, 0));
+        } else {   // keys past the last one read the last (their probability is 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const unsigned o = (unsigned)min(16 * t + 4 * r + kq, n - 1) * rsb + 16u * l16;
+                vf[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(T.rsrc, (int)o, T.vb, 0));
+            }
+        }
+    };
+
+    // Loads complete in issue order: bias rows and Q first, then K and V of the first two tiles
+    // (two tiles ahead of their use: the wavefronts of one (window, head) stream the same tiles
+    // at about the same time, so a tile's first read goes to HBM for all of them).
+    Task T = decode(task);
+    float dhr[kWinGrid], dwv[4], qreg[16];
+    load_head(T, dhr, dwv, qreg);
+    f32x4 kcur[4], vcur[4], k1[4], v1[4];
+    load_k(T, 0, kcur);
+    load_v(T, 0, vcur);
+    if (NT > 1) {
+        load_k(T, 1, k1);
+        load_v(T, 1, v1);
+    }
+    // The bias of every (query, key) pair of the task, E[key][query] in this wavefront's LDS:
+    // the lane writes its query's keys ky * gw + kx for kx = kq + 4i, and -inf past the last key
+    // (so the padding keys of the last tile need no mask).  The lane's own 4 keys of tile t,
+    // 16t + 4r + kq, are read back one tile ahead and start the score accumulators.
+    float* const E = ebuf[wave];
+    float* const col = E + kq * win::kQT + l16;   // E[kq][l16]; key j is j * kQT floats further
+    // Straight-line writes: a column kq + 4i at or past gw lands on a later key of the table
+    // (row ky + 1 or beyond), which is written afterwards in program order -- by a later row or,
+    // past the last row, by the -inf padding or in the spare tile -- so no write needs a guard.
+    auto build_e = [&](const float (&dh)[kWinGrid], const float (&dw)[4]) {
+        // LDS operations of one wavefront complete in issue order; the fences keep the
+        // compiler's order (earlier reads of E before these writes, these before later reads)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int ky = 0; ky < kWinGrid; ++ky) {
+            if (ky < a.gh) {   // wave-uniform
+                float* row = col + ky * a.gw * win::kQT;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) row[4 * i * win::kQT] = dh[ky] + dw[i];
+            }
+        }
+        for (int j = n + kq; j < 16 * NT; j += 4) E[j * win::kQT + l16] = -INFINITY;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto read_bias = [&](int t) {
+        f32x4 bv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bv[r] = col[(16 * t + 4 * r) * win::kQT];
+        return bv;
+    };
+    build_e(dhr, dwv);
+    f32x4 bnext = read_bias(0);
+    constexpr float kH = dgk::kHeadroom;
+    const float kBig = __builtin_exp2f(kH);
+
+    int nxt = task + wpx;
+    while (true) {
+        const bool has_next = nxt < hi;
+        const Task N = decode(has_next ? nxt : task);
+
+        f32x4 o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) o[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Scores come out of the MFMAs relative to the reference `ref` (E holds bias - ref), so
+        // exp2 takes them as they are.  The first tile sets the reference from its maximum (0
+        // while that lies within +-kH: nothing to subtract, and the row's largest term is at
+        // least 2^-kH); later tiles keep it unless a probability exceeds 2^kH, seen from the
+        // tile's sum, which the denominator needs anyway.  Such a tile is redone from its maximum.
+        float m = -INFINITY, ref = 0.0f, lsum = 0.0f;
+        // New reference from the tile's scores (relative to `ref`); rescales o and lsum, and moves
+        // the current scores, the next tile's bias (in registers) and the later tiles' bias (the
+        // lane's own entries of E) to the new reference.
+        auto rebase = [&](int t, f32x4& sc) {
+            float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float m_new = fmaxf(m, ref + tmax);
+            const float nref = (m_new == -INFINITY || fabsf(m_new) <= kH) ? 0.0f : m_new;
+            const float d = nref - ref;
+            const float corr = m == -INFINITY ? 0.0f : dgk::fast_exp2(-d);
+            lsum *= corr;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) o[h] *= corr;
+            sc -= d;
+            if (t + 1 < NT) bnext -= d;
+            if (t + 2 < NT && __any(d != 0.0f)) {
+                for (int u = t + 2; u < NT; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) col[(16 * u + 4 * r) * win::kQT] -= d;
+            }
+            m = m_new;
+            ref = nref;
+        };
+
+        float dhr_n[kWinGrid], dwv_n[4], qreg_n[16];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f32x4 k2[4], v2[4];
+            constexpr int kLast = NT - 1;
+            const bool more = t < kLast, more2 = t + 1 < kLast;
+            // k2/v2 take the next task's tile 0 or 1 (the last task reloads its own; unused)
+            const bool cross = kCross && !more2;
+            if (t == 0) {
+                load_head(N, dhr_n, dwv_n, qreg_n);   // the next task's bias rows and Q
+            }
+            if (more2) load_k(T, t + 2, k2);
+            else if (cross) load_k(N, t + 2 - NT, k2);
+            f32x4 sc = bnext;
+            if (more) bnext = read_bias(t + 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].x, qreg[4 * c + 0], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].y, qreg[4 * c + 1], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].z, qreg[4 * c + 2], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].w, qreg[4 * c + 3], sc, 0, 0, 0);
+            }
+            if (more2) load_v(T, t + 2, v2);
+            else if (cross) load_v(N, t + 2 - NT, v2);
+            if (t == 0) rebase(t, sc);
+            f32x4 p;
+            auto exps = [&]() {
+                p[0] = dgk::fast_exp2(sc[0]);
+                p[1] = dgk::fast_exp2(sc[1]);
+                p[2] = dgk::fast_exp2(sc[2]);
+                p[3] = dgk::fast_exp2(sc[3]);
+            };
+            exps();
+            float psum = (p[0] + p[1]) + (p[2] + p[3]);
+            if (t > 0 && __any(!(psum <= kBig))) {   // a score above the headroom (or inf)
+                rebase(t, sc);
+                exps();
+                psum = (p[0] + p[1]) + (p[2] + p[3]);
+            }
+            lsum += psum;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (t < kLast || r == 0 || 16 * t + 4 * r < n) {   // a step with no key is skipped
+                    o[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].x, p[r], o[0], 0, 0, 0);
+                    o[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].y, p[r], o[1], 0, 0, 0);
+                    o[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].z, p[r], o[2], 0, 0, 0);
+                    o[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].w, p[r], o[3], 0, 0, 0);
+                }
+            }
+            if (t == kLast) {   // this task is done with E: the next task's table (the last
+                                // task rebuilds its own, unused)
+                build_e(dhr_n, dwv_n);
+                bnext = read_bias(0);
+            }
+            if (more || cross) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    kcur[c] = k1[c];
+                    vcur[c] = v1[c];
+                }
+            }
+            if (more2 || cross) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    k1[c] = k2[c];
+                    v1[c] = v2[c];
+                }
+            }
+        }
+
+        float ltot = lsum + __shfl_xor(lsum, 16);
+        ltot += __shfl_xor(ltot, 32);
+        const int qn = T.qt * win::kQT + l16;
+        if (qn < n) {
+            const float inv = 1.0f / ltot;
+            float* orow = a.out + ((size_t)T.w * n + qn) * a.W + T.head * HD + 16 * kq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<float4*>(orow + 4 * r) =
+                    make_float4(o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv);
+        }
+        if (!has_next) break;
+        task = nxt;
+        nxt += wpx;
+        T = N;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qreg[i] = qreg_n[i];
+        if (!kCross) {
+            load_k(T, 0, kcur);
+            load_v(T, 0, vcur);
+        }
     }
 }
 
@@ -426,11 +772,21 @@ __global__ void __launch_bounds__(64 * kWavesT)
 
 }  // namespace
 
+namespace {
+// Grids whose lines fit one 16x16 tile take the 16-query wavefront kernel.
+bool win_grid(int gh, int gw) { return gh <= kWinGrid && gw <= kWinGrid; }
+int round4(int x) { return (x + 3) & ~3; }
+// Floats per (window, head, query) of bias rows: dh then dw, each padded to 4 floats for the
+// 16x16 path; unpadded otherwise.
+int bias_row_floats(int gh, int gw) { return win_grid(gh, gw) ? round4(gh) + round4(gw) : gh + gw; }
+
+}  // namespace
+
 extern "C" size_t relpos_flash_attn_windows_workspace_size(int nwin, int gh, int gw, int heads,
                                                           int hd) {
     if (nwin < 1 || gh < 1 || gw < 1 || heads < 1 || hd != HD || gh > kMaxGrid || gw > kMaxGrid)
         return 0;
-    return (size_t)nwin * heads * gh * gw * (gh + gw) * sizeof(float);
+    return (size_t)nwin * heads * gh * gw * bias_row_floats(gh, gw) * sizeof(float);
 }
 
 extern "C" size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd) {
@@ -486,6 +842,10 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(out) |
          reinterpret_cast<uintptr_t>(rh) | reinterpret_cast<uintptr_t>(rw)) & 15)
         return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
+    const bool use_win = win_grid(gh, gw) && (use_ws || !rh);
+    if (use_win && (size_t)n * 12 * W > 0x7fffffffu)
+        return dg::fail(DG_EUNSUPPORTED, "%s: a window of %lld tokens x %zu floats exceeds 2 GiB", fn, n,
+                        3 * W);
     const bool small = n <= kSmallGrid;              // 4 x 2 workgroups for small grids
     static_assert(RelShape<1, 4>::kBlockQ == RelShape<2>::kBlockQ, "small shapes share a block");
     const long long kbq = small ? RelShape<2>::kBlockQ : RelShape<4>::kBlockQ;
@@ -514,19 +874,44 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     } else {
         a.tsh = 0; a.ta = tl.kpt; a.tmsk = 0; a.tb = 0; a.tl0 = tl.kpt; a.td = 0;
     }
+    a.gh4 = round4(gh);
+    a.brs = bias_row_floats(gh, gw);
+    a.qtiles = (int)((n + win::kQT - 1) / win::kQT);
     hipStream_t s = (hipStream_t)stream;
+    if (use_win) {
+        const long long ntasks = (long long)nwin * heads * a.qtiles;
+        if (ntasks > 0x7fffffffLL)
+            return dg::fail(DG_EUNSUPPORTED, "%s: too many tasks", fn);
+        // as many workgroups as run at once (two per CU: 2 wavefronts per SIMD), each
+        // wavefront looping over tasks; a multiple of the XCD count for xcd_remap
+        const long long nx = topo.xcds;
+        const long long want = (ntasks + win::kWaves - 1) / win::kWaves;
+        const long long cap = 2LL * topo.cus;
+        const long long nwg = ((want < cap ? want : cap) + nx - 1) / nx * nx;
+        if (use_ws) {
+            const long long nbt = (long long)nwin * heads * (gh + gw);
+            const long long nbias = (nbt + kBiasWaves - 1) / kBiasWaves;
+            const dim3 bgrid((unsigned)((nbias + nx - 1) / nx * nx));
+            hipLaunchKernelGGL(relpos_bias16_kernel, bgrid, dim3(64 * kBiasWaves), 0, s, a,
+                               static_cast<float*>(workspace), (int)nbt);
+        }
+        const dim3 grid((unsigned)nwg);
+        static void (*const kWin[16])(RelArgs, int) = {
+            relpos_win_kernel<1>,  relpos_win_kernel<2>,  relpos_win_kernel<3>,  relpos_win_kernel<4>,
+            relpos_win_kernel<5>,  relpos_win_kernel<6>,  relpos_win_kernel<7>,  relpos_win_kernel<8>,
+            relpos_win_kernel<9>,  relpos_win_kernel<10>, relpos_win_kernel<11>, relpos_win_kernel<12>,
+            relpos_win_kernel<13>, relpos_win_kernel<14>, relpos_win_kernel<15>, relpos_win_kernel<16>};
+        auto* wk = kWin[(n + 15) / 16 - 1];
+        hipLaunchKernelGGL(wk, grid, dim3(64 * win::kWaves), 0, s, a, (int)ntasks);
+        return dg::launch_status(fn);
+    }
     if (use_ws) {
-        const bool b16 = gh <= 16 && gw <= 16;   // every line fits one 16x16 tile
-        const long long ntasks = (long long)nwin * heads * (gh + gw) * (b16 ? 1 : 4);
+        const long long ntasks = (long long)nwin * heads * (gh + gw) * 4;
         const long long nbias = (ntasks + kBiasWaves - 1) / kBiasWaves;
         const long long nx = topo.xcds;
         const dim3 grid((unsigned)((nbias + nx - 1) / nx * nx));   // whole XCD rounds for xcd_remap
-        if (b16)
-            hipLaunchKernelGGL(relpos_bias16_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
-                               static_cast<float*>(workspace), ntasks);
-        else
-            hipLaunchKernelGGL(relpos_bias_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
-                               static_cast<float*>(workspace), ntasks);
+        hipLaunchKernelGGL(relpos_bias_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
+                           static_cast<float*>(workspace), ntasks);
     }
     const bool full = tl.half_rows ? gw == 64 : (tl.kpt == dgk::kKeys && gh % tl.rpt == 0);
     const bool one = tl.nshift == 1;

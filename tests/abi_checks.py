@@ -222,7 +222,8 @@ def check_relpos_windows_validation(L):
     assert call(out=FAKE + 4 * 8 * 8 * 3 * 128 * 4 - 16) == dg.DG_EINVAL   # inside the last window
     assert call(ws=FAKE + (4 << 26), wsb=1024) == dg.DG_EINVAL             # too small for 4 windows
     assert call(nwin=0) == dg.DG_OK
-    assert L.relpos_flash_attn_windows_workspace_size(25, 14, 14, 12, 64) == 25 * 12 * 196 * 28 * 4
+    # grids of at most 16 x 16: dh and dw rows each padded to 4 floats (14 -> 16)
+    assert L.relpos_flash_attn_windows_workspace_size(25, 14, 14, 12, 64) == 25 * 12 * 196 * 32 * 4
     assert L.relpos_flash_attn_windows_workspace_size(0, 14, 14, 12, 64) == 0
 
 
