@@ -33,7 +33,7 @@ EXPORTS = ("dg_rope_table", "dg_headnorm_rope", "dg_qkv_headnorm_rope", "dg_pack
            "dg_attn_split_gqa_workspace_size", "dg_attn_split_gqa_plan", "dg_attn_split_gqa",
            "dg_attn_split_gqa_qnorm",
            "dg_attn_split_gqa_qkvnorm", "dg_attn_split_gqa_kv16", "dg_attn_split_gqa_noalloc",
-           "relpos_flash_attn_workspace_size", "relpos_flash_attn",
+           "relpos_flash_attn_workspace_size", "relpos_flash_attn", "relpos_flash_attn_ws",
            "relpos_flash_attn_windows_workspace_size", "relpos_flash_attn_windows",
            "dg_last_error")
 
@@ -77,7 +77,8 @@ def lib() -> ctypes.CDLL:
                                                 I, U, F, F, I, vp, Z, vp]
         L.relpos_flash_attn_workspace_size.argtypes = [I, I, I, I]
         L.relpos_flash_attn_workspace_size.restype = Z
-        L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp, Z, vp]
+        L.relpos_flash_attn.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp]
+        L.relpos_flash_attn_ws.argtypes = [vp, vp, vp, vp, I, I, I, I, F, vp, Z, vp]
         L.relpos_flash_attn_windows_workspace_size.argtypes = [I, I, I, I, I]
         L.relpos_flash_attn_windows_workspace_size.restype = Z
         L.relpos_flash_attn_windows.argtypes = [vp, vp, vp, vp, I, I, I, I, I, F, vp, Z, vp]
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
                      "dg_qkv_headnorm_rope_kv16",
                      "dg_attn_split_gqa", "dg_attn_split_gqa_qnorm", "dg_attn_split_gqa_qkvnorm",
                      "dg_attn_split_gqa_kv16", "dg_attn_split_gqa_noalloc", "relpos_flash_attn",
+                     "relpos_flash_attn_ws",
                      "relpos_flash_attn_windows"):
             getattr(L, name).restype = I
         L.dg_last_error.argtypes = []
@@ -301,13 +303,22 @@ def relpos_flash_attn_workspace_size(gh: int, gw: int, heads: int, hd: int) -> i
 
 
 def relpos_flash_attn(qkv, rh, rw, out, gh: int, gw: int, heads: int, hd: int, scale: float,
-                      workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+                      stream=None) -> None:
+    _nonneg(gh=gh, gw=gw, heads=heads, hd=hd)
+    n, W = gh * gw, heads * hd
+    _check(lib().relpos_flash_attn(_ptr(qkv, "qkv", n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
+                                   _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", n * W),
+                                   gh, gw, heads, hd, float(scale), _stream(stream)))
+
+
+def relpos_flash_attn_ws(qkv, rh, rw, out, gh: int, gw: int, heads: int, hd: int, scale: float,
+                         workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     _nonneg(gh=gh, gw=gw, heads=heads, hd=hd)
     n, W = gh * gw, heads * hd
     ws, wsb = _workspace(workspace, workspace_bytes)
-    _check(lib().relpos_flash_attn(_ptr(qkv, "qkv", n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
-                                   _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", n * W),
-                                   gh, gw, heads, hd, float(scale), ws, wsb, _stream(stream)))
+    _check(lib().relpos_flash_attn_ws(_ptr(qkv, "qkv", n * 3 * W), _ptr(rh, "rh", gh * gh * hd),
+                                      _ptr(rw, "rw", gw * gw * hd), _ptr(out, "out", n * W),
+                                      gh, gw, heads, hd, float(scale), ws, wsb, _stream(stream)))
 
 
 def relpos_flash_attn_windows_workspace_size(nwin: int, gh: int, gw: int, heads: int,

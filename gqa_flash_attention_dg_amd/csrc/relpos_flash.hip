@@ -932,8 +932,14 @@ extern "C" int relpos_flash_attn_windows(const float* qkv, const float* rh, cons
 }
 
 extern "C" int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out,
-                                 int gh, int gw, int heads, int hd, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 int gh, int gw, int heads, int hd, float scale, void* stream) {
     return relpos_call("relpos_flash_attn", qkv, rh, rw, out, 1, gh, gw, heads, hd, scale,
+                       nullptr, 0, stream);
+}
+
+extern "C" int relpos_flash_attn_ws(const float* qkv, const float* rh, const float* rw, float* out,
+                                    int gh, int gw, int heads, int hd, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return relpos_call("relpos_flash_attn_ws", qkv, rh, rw, out, 1, gh, gw, heads, hd, scale,
                        workspace, workspace_bytes, stream);
 }

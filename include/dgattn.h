@@ -312,14 +312,6 @@ int dg_attn_split_gqa_noalloc(const float* q, const float* kc, const float* vc, 
                               int nkv, int hd, float scale, int causal, void* stream);
 
 /*
- * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn can use to hold the
- * hoisted bias rows, the page's DHDW buffers: dh [heads][n][gh] then dw [heads][n][gw], i.e.
- * heads * n * (gh + gw) * 4 bytes with n = gh * gw.  Returns 0 for arguments relpos_flash_attn
- * would reject.
- */
-size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
-
-/*
  * relpos_flash_attn -- windowless vision attention with the decomposed relative-position bias,
  * flash style (no [heads, n, n] buffer).  Follows deepencoder_gpu.rs: kernel SAM_SCORES
  * (score definition), kernel DHDW (the bias dot products hoisted out of the n^2 loop), the
@@ -331,39 +323,56 @@ size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
  *   Token i is at grid cell (qy, qx) = (i / gw, i % gw).  For every head and query i:
  *     s_j = scale*<q_i, k_j> + <q_i, rh[qy, ky_j]> + <q_i, rw[qx, kx_j]>  (bias on unscaled q)
  *     out[i, h*hd:(h+1)*hd] = sum_j softmax(s)_j v_j
- *   scale      finite float (1/sqrt(hd) in the page's SAM block).
- *   workspace  optional device scratch of at least relpos_flash_attn_workspace_size() bytes,
- *              16-byte aligned: the bias rows are then computed once per (head, query) by a
- *              first kernel, as the page's DHDW step does; NULL/0 computes them inside each
- *              attention workgroup instead (same results up to rounding, slower).  Must not
- *              overlap any input or `out`.
- *   Every tensor pointer must be 16-byte aligned.
+ *   scale  finite float (1/sqrt(hd) in the page's SAM block).
+ *   Every tensor pointer must be 16-byte aligned.  The library allocates nothing, so without a
+ *   workspace the bias dot products are formed inside each attention workgroup for its own
+ *   queries; relpos_flash_attn_ws takes a workspace for them instead.
  * Errors: DG_EINVAL for gh, gw or heads < 0, exactly one of rh/rw NULL, a NULL qkv/out with
  * n > 0, a non-finite scale, overlapping buffers, a tensor pointer that is not 16-byte
- * aligned, a misaligned or too small workspace;
+ * aligned;
  * DG_EUNSUPPORTED for hd != 64 (the page's kernel fixes hd to its 64-wide workgroup) or gh or
  * gw above 64.
  */
 int relpos_flash_attn(const float* qkv, const float* rh, const float* rw, float* out, int gh,
-                      int gw, int heads, int hd, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      int gw, int heads, int hd, float scale, void* stream);
+
+/*
+ * relpos_flash_attn_workspace_size -- bytes of scratch relpos_flash_attn_ws uses to hold the
+ * hoisted bias rows, the page's DHDW buffers dh [heads][n][gh] and dw [heads][n][gw]: per
+ * (head, query) gh + gw floats, each part padded to a multiple of 4 floats when gh and gw are
+ * at most 16; n = gh * gw.  Returns 0 for arguments relpos_flash_attn_ws would reject.
+ */
+size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
+
+/*
+ * relpos_flash_attn_ws -- relpos_flash_attn with a caller workspace for the bias rows: a first
+ * kernel computes them once per (head, query), as the page's DHDW step does, and the attention
+ * reads them.  Same results as relpos_flash_attn up to rounding; faster.
+ *   workspace  device scratch of at least relpos_flash_attn_workspace_size() bytes, 16-byte
+ *              aligned, not overlapping any input or `out` (NULL/0: as relpos_flash_attn).
+ * Errors: as relpos_flash_attn, plus DG_EINVAL for a misaligned or too small workspace.
+ */
+int relpos_flash_attn_ws(const float* qkv, const float* rh, const float* rw, float* out, int gh,
+                         int gw, int heads, int hd, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * relpos_flash_attn_windows_workspace_size -- as relpos_flash_attn_workspace_size for a batch of
- * nwin windows: nwin * heads * n * (gh + gw) * 4 bytes; 0 for arguments the call would reject.
+ * nwin windows (nwin times as many rows); 0 for arguments the call would reject.
  */
 size_t relpos_flash_attn_windows_workspace_size(int nwin, int gh, int gw, int heads, int hd);
 
 /*
- * relpos_flash_attn_windows -- relpos_flash_attn over a batch of independent windows sharing
+ * relpos_flash_attn_windows -- relpos_flash_attn_ws over a batch of independent windows sharing
  * the tables: the windowed SAM blocks of deepencoder_gpu.rs's encoder (its cost model: 25
  * windows of 14 x 14 tokens; a 64 x 64 map padded to 70 x 70).  Window partitioning and its
  * padding belong to the caller, whose qkv already holds the padded tokens.
  *   qkv  [nwin, gh*gw, 3*heads*hd]   window w's tokens, each row q | k | v as in relpos_flash_attn
  *   out  [nwin, gh*gw, heads*hd]
- *   rh, rw, gh, gw, heads, hd, scale, workspace as relpos_flash_attn (workspace size from
- *   relpos_flash_attn_windows_workspace_size).  Each window is exactly one relpos_flash_attn.
- * Errors: as relpos_flash_attn, plus DG_EINVAL for nwin < 0.  nwin == 0 is a no-op.
+ *   rh, rw, gh, gw, heads, hd, scale, workspace as relpos_flash_attn_ws (workspace size from
+ *   relpos_flash_attn_windows_workspace_size; NULL/0 forms the bias inside the attention).
+ *   Each window is exactly one relpos_flash_attn.
+ * Errors: as relpos_flash_attn_ws, plus DG_EINVAL for nwin < 0.  nwin == 0 is a no-op.
  */
 int relpos_flash_attn_windows(const float* qkv, const float* rh, const float* rw, float* out,
                               int nwin, int gh, int gw, int heads, int hd, float scale,

@@ -186,7 +186,17 @@ def check_attn_alignment_validation(L):
 
 
 def check_relpos_validation(L):
-    f = L.relpos_flash_attn
+    # the form without a workspace
+    g = L.relpos_flash_attn
+    base0 = dict(qkv=FAKE, rh=FAKE + (1 << 26), rw=FAKE + (2 << 26), out=FAKE + (3 << 26),
+                 gh=8, gw=8, heads=2, hd=64, scale=0.125, stream=None)
+    call0 = lambda **kw: g(*[{**base0, **kw}[k] for k in base0])
+    assert call0(hd=32) == dg.DG_EUNSUPPORTED
+    assert call0(rw=None) == dg.DG_EINVAL
+    assert call0(out=FAKE + 4) == dg.DG_EINVAL
+    assert call0(gw=0) == dg.DG_OK
+    # the form with a workspace
+    f = L.relpos_flash_attn_ws
     base = dict(qkv=FAKE, rh=FAKE + (1 << 26), rw=FAKE + (2 << 26), out=FAKE + (3 << 26),
                 gh=8, gw=8, heads=2, hd=64, scale=0.125, ws=None, wsb=0, stream=None)
     call = lambda **kw: f(*[{**base, **kw}[k] for k in base])

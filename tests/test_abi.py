@@ -60,10 +60,51 @@ def test_argument_checks_without_a_gpu(isolated_results, name):
     assert isolated_results.get(name) == "ok", isolated_results.get(name)
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+def prototypes():
+    """{name: (return type, [parameter types])} of every function include/dgattn.h declares,
+    with parameter names dropped and spacing normalised (`const float*`)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    out = {}
+    for ret, name, params in re.findall(
+            r"^\s*((?:const\s+)?\w+\s*\*?)\s*(\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.M | re.S):
+        types = []
+        for p in (x.strip() for x in params.split(",")):
+            if p == "void" or not p:
+                continue
+            p = re.sub(r"\s+", " ", p.replace("*", " * ")).strip()
+            words = p.split(" ")
+            if words[-1] != "*" and len(words) > 1:
+                words = words[:-1]                      # drop the parameter name
+            types.append(" ".join(words).replace(" *", "*"))
+        out[name] = (re.sub(r"\s+", " ", ret.replace("*", " *")).strip().replace(" *", "*"), types)
+    return out
+
+
+# The boundary calls in the form the method's hot path is specified with: headnorm + rope in
+# place, split-GQA attention with an optional split-KV workspace, rel-pos attention (no
+# workspace), and the error message.
+BOUNDARY = {
+    "dg_headnorm_rope": ("int", ["float*", "const float*", "const float*", "int", "int", "int",
+                                 "int", "unsigned", "float", "void*"]),
+    "dg_attn_split_gqa_workspace_size": ("size_t", ["int"] * 6),
+    "dg_attn_split_gqa": ("int", ["const float*"] * 5 + ["float*"] + ["int"] * 6 +
+                          ["float", "int", "void*", "size_t", "void*"]),
+    "relpos_flash_attn": ("int", ["const float*"] * 3 + ["float*"] + ["int"] * 4 +
+                          ["float", "void*"]),
+    "dg_last_error": ("const char*", []),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BOUNDARY))
+def test_header_keeps_the_boundary_prototypes(name):
+    assert prototypes()[name] == BOUNDARY[name]
+
+
+def test_binding_argument_counts_match_the_header(L):
+    for name, (_, params) in prototypes().items():
+        argtypes = getattr(L, name).argtypes
+        assert argtypes is not None and len(argtypes) == len(params), (name, argtypes, params)
 
 
 def test_binding_refuses_bad_tensors_before_the_call():

@@ -479,8 +479,11 @@ def test_relpos_small(gh, gw, heads, bias, use_ws):
     out = torch.full((gh * gw, heads * 64), float("nan"), device="cuda")
     nbytes = dg.relpos_flash_attn_workspace_size(gh, gw, heads, 64) if use_ws else 0
     ws = torch.full((max(nbytes, 4) // 4,), float("nan"), device="cuda") if use_ws else None
-    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, gh, gw, heads, 64, c.scale,
-                         ws, nbytes)
+    if use_ws:
+        dg.relpos_flash_attn_ws(dev(c.qkv), dev(c.rh), dev(c.rw), out, gh, gw, heads, 64, c.scale,
+                                ws, nbytes)
+    else:
+        dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, gh, gw, heads, 64, c.scale)
     assert_parity(host(out), ref, "relpos %dx%d ws=%d" % (gh, gw, nbytes))
 
 
@@ -489,7 +492,8 @@ def test_sam_global_every_element():
     out = torch.empty((4096, 768), device="cuda")
     nbytes = dg.relpos_flash_attn_workspace_size(64, 64, 12, 64)
     ws = torch.empty((nbytes // 4,), device="cuda")
-    dg.relpos_flash_attn(dev(c.qkv), dev(c.rh), dev(c.rw), out, 64, 64, 12, 64, c.scale, ws, nbytes)
+    dg.relpos_flash_attn_ws(dev(c.qkv), dev(c.rh), dev(c.rw), out, 64, 64, 12, 64, c.scale, ws,
+                            nbytes)
     got = host(out)
     ref = oracle.relpos_attn(c.qkv, c.rh, c.rw, 64, 64, 12, 64, c.scale)   # every element
     assert_parity(got, ref, "sam global")
