@@ -529,6 +529,12 @@ __global__ void __launch_bounds__(64 * win::kWaves) __attribute__((amdgpu_waves_
 // score accumulator, with -inf at padding slots (which masks them for free), and the height
 // bias dh[q][ky] - ref rides in ceil(rpt / 2) extra MFMA steps: step m contracts over the two
 // rows 2m and 2m+1 of the tile, with A one-hot on the key's row within the tile.
+// A compile-time double-buffer index.
+template <int B>
+struct BufC {
+    static constexpr int value = B;
+};
+
 struct Tiling {
     int half_rows;   // 1: half-row tiles; 0: row tiles
     int rpt;         // grid rows per tile (row tiles)
@@ -552,7 +558,9 @@ __host__ __device__ inline Tiling make_tiling(int gh, int gw) {
 
 // kFull: every tile holds 32 keys (no padding slots, no short last tile); kOneShift: the height
 // bias takes one MFMA step (at most two grid rows per tile).
-template <bool kFull, bool kOneShift, int kParts, int kWavesT>
+// kPatch: the workgroup's 64 queries are an 8 x 8 patch of the grid (both sides multiples of
+// 8, half-row tiles) and the workgroup forms their bias rows itself on MFMA (see below).
+template <bool kFull, bool kOneShift, int kParts, int kWavesT, bool kPatch = false>
 __global__ void __launch_bounds__(64 * kWavesT)
     __attribute__((amdgpu_waves_per_eu(kWavesT == 4 ? 3 : 1))) relpos_flash_kernel(RelArgs a) {
     using TL = dgk::Tile<HD>;
@@ -582,8 +590,13 @@ __global__ void __launch_bounds__(64 * kWavesT)
     const size_t rs = (size_t)3 * a.W;  // qkv row stride (floats)
     const Tiling tl = make_tiling(a.gh, a.gw);
 
+    static_assert(!kPatch || kBlockQ == 64, "a patch is 64 queries");
+    // patch mode: query p of the workgroup (p = 32 grp + l32) is patch cell (p / 8, p % 8)
+    const int pxn = a.gw >> 3;
+    const int py0 = kPatch ? 8 * (qb / pxn) : 0, px0 = kPatch ? 8 * (qb % pxn) : 0;
+    auto patch_token = [&](int p) { return (py0 + (p >> 3)) * a.gw + px0 + (p & 7); };
     const int qfirst = qb * kBlockQ + grp * dgk::kQuery;
-    const int qi = qfirst + l32;
+    const int qi = kPatch ? patch_token(grp * dgk::kQuery + l32) : qfirst + l32;
     const bool valid = qi < a.n;
     const float* qkvw = a.qkv + (size_t)win * a.n * rs;   // this window's rows
     const float* qrow = qkvw + (size_t)(valid ? qi : 0) * rs + head * HD;
@@ -603,7 +616,73 @@ __global__ void __launch_bounds__(64 * kWavesT)
     // Prologue: the dh rows of this group's queries (all ky) into LDS, and the lane's dw terms.
     f32x16 dwreg;
     const int qx = valid ? qi % a.gw : 0, qy = valid ? qi / a.gw : 0;
-    if (bias && active && a.dhw) {
+    if (kPatch && bias) {
+        // The bias rows of the patch as small matrix products on v_mfma_f32_16x16x4f32:
+        // wavefront w takes patch row w (8 queries of grid row py0 + w against rh[py0 + w]) and
+        // patch column w (8 queries of grid column px0 + w against rw[px0 + w]).  A line's
+        // product D^T = T Q^T has 16 table rows per tile (up to 4 tiles) and 16 columns, the 8
+        // queries twice (columns n and n + 8 alike).  Lane l supplies table row l%16 (A) and
+        // query l%8 (B) at contraction index k = l/16; step 4c+e contracts element 16c+4k+e.
+        // Accumulator i holds table row 4*(l/16)+i of the tile for query (l%16) % 8.  Row
+        // products go to the dh tables; column products to a [query][kx] table in the second
+        // stage buffer (free until stage 1), from which each lane then takes its dw terms.
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const int l16 = lane & 15, kq = lane >> 4;
+        float* dwt = smem + 2 * kParts * TL::kFloats;   // [64 queries][kDwStride]
+        constexpr int kDwStride = 64 + 4;
+        float qb_h[16], qb_w[16];
+        const int qh = (py0 + wave) * a.gw + px0 + (l16 & 7);        // row segment's query
+        const int qv = (py0 + (l16 & 7)) * a.gw + px0 + wave;        // column segment's query
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 x = *reinterpret_cast<const float4*>(qkvw + (size_t)qh * rs + head * HD + 16 * c + 4 * kq);
+            const float4 y = *reinterpret_cast<const float4*>(qkvw + (size_t)qv * rs + head * HD + 16 * c + 4 * kq);
+            qb_h[4 * c] = x.x; qb_h[4 * c + 1] = x.y; qb_h[4 * c + 2] = x.z; qb_h[4 * c + 3] = x.w;
+            qb_w[4 * c] = y.x; qb_w[4 * c + 1] = y.y; qb_w[4 * c + 2] = y.z; qb_w[4 * c + 3] = y.w;
+        }
+        // One table tile at a time: loading all eight tiles of both lines up front made the
+        // prologue slower (14.9 against 11.9 us per workgroup), every workgroup of a round
+        // asking for its tables at once.
+        auto line = [&](const float* table, int nrows, const float (&qv_)[16], auto put) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                if (16 * kt < nrows) {
+                    const float* tr = table + (size_t)min(16 * kt + l16, nrows - 1) * HD + 4 * kq;
+                    float tv[16];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float4 t = *reinterpret_cast<const float4*>(tr + 16 * c);
+                        tv[4 * c] = t.x; tv[4 * c + 1] = t.y; tv[4 * c + 2] = t.z; tv[4 * c + 3] = t.w;
+                    }
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 16; ++st)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[st], qv_[st], acc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * kt + 4 * kq + i;
+                        if (l16 < 8 && row < nrows) put(row, acc[i] * dgk::kLog2e);
+                    }
+                }
+            }
+        };
+        // patch row `wave`: queries p = 8 wave + c, in group p / 32 at index p % 32
+        line(a.rh + (size_t)(py0 + wave) * a.gh * HD, a.gh, qb_h, [&](int ky, float v) {
+            const int p = 8 * wave + l16;
+            tab[((p >> 5) * kTabRows + ky) * dgk::kQuery + (p & 31)] = v;
+        });
+        // patch column `wave`: queries p = 8 r + wave
+        line(a.rw + (size_t)(px0 + wave) * a.gw * HD, a.gw, qb_w, [&](int kx, float v) {
+            dwt[(8 * l16 + wave) * kDwStride + kx] = v;
+        });
+        __syncthreads();
+        const int p = grp * dgk::kQuery + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = dgk::key_of(r, half);
+            dwreg[r] = i < tlen_w ? dwt[p * kDwStride + min(kx0 + i, a.gw - 1)] : -INFINITY;
+        }
+    } else if (bias && active && a.dhw) {
         const float* dhq = a.dhw + ((size_t)unit * a.n + (valid ? qi : 0)) * a.gh;
         const float* dwq = a.dhw + (size_t)a.nwin * a.heads * a.n * a.gh +
                            ((size_t)unit * a.n + (valid ? qi : 0)) * a.gw;
@@ -652,30 +731,49 @@ __global__ void __launch_bounds__(64 * kWavesT)
 
     // Loads: the four wavefronts with part < 2 (one per SIMD) issue each stage's wave-wide
     // loads -- K and V of kParts tiles -- while their SIMD partners keep the matrix pipe busy
-    // (in the 4 x 1 shape every wavefront issues, and the partners are other workgroups').  A
-    // full 32-key tile is a scalar row base plus loop-invariant lane offsets; a shorter one
+    // (in the 4 x 1 shape every wavefront issues, and the partners are other workgroups').  They
+    // are buffer loads straight into LDS: the window's qkv rows are one buffer, the lane's
+    // offset within a full tile is loop-invariant (a row rsub of its 4-row group and a 16-byte
+    // chunk, K's chunks permuted as the reads expect) and the tile, the 4-row group and the k
+    // or v column are a scalar offset, so a load costs no vector instruction.  A shorter tile
     // repeats its last key in the padding rows.
     constexpr int kLoadsPerWave = 2 * kParts * TL::kLoadsPerTile / 4;
     constexpr int R = TL::kRowsPerLoad;
+    static_assert(TL::kChunks == 16 && R == 4, "the offsets below assume hd 64");
     const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
-    const char* kbase = reinterpret_cast<const char*>(qkvw + a.W + head * HD);
-    const char* vbase = reinterpret_cast<const char*>(qkvw + 2 * (size_t)a.W + head * HD);
     const unsigned rsb = (unsigned)(rs * 4);
-    auto issue_stage = [&](int st, int buf) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(qkvw), 0, (int)((unsigned)a.n * rsb), (int)win::kRsrcWord3);
+    const int colk = (a.W + head * HD) * 4, colv = (2 * a.W + head * HD) * 4;
+    // lane offsets of full-tile loads: row rsub of load ld's 4 rows; K's chunk pos ^ (row % 16)
+    // depends on ld % 4 only (row = 4 * ld + rsub < 32)
+    unsigned koffs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) koffs[j] = (unsigned)rsub * rsb + 16u * (pos ^ (4 * j + rsub));
+    const unsigned voffs = (unsigned)rsub * rsb + 16u * pos;
+    auto issue_stage = [&](int st, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) {
             const int L = wave * kLoadsPerWave + i;
             const int tpart = L / TL::kLoadsPerTile, ld = L % TL::kLoadsPerTile;
             const int tile = tpart >> 1, isv = tpart & 1;
-            const int trow = ld * R + rsub;
-            const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
             // a tile past the last one reloads keys that exist (its results are never used)
             const int t = min(st * kParts + tile, a.ntiles - 1);
             const int j0 = tile_start(t);
-            const char* b = (isv ? vbase : kbase) + (size_t)j0 * rsb;
-            const unsigned off = kFull ? (unsigned)trow * rsb + coff
-                                       : (unsigned)min(trow, tile_len(t) - 1) * rsb + coff;
-            __builtin_amdgcn_global_load_lds(b + off, (dgk::lds_void*)(tile_ptr(buf, tile, isv) + ld * 256), 16, 0, 0);
+            unsigned off;
+            int soff;
+            if (kFull) {
+                off = isv ? voffs : koffs[i % 4];   // ld % 4 == i % 4 in every shape
+                soff = (isv ? colv : colk) + (j0 + R * ld) * (int)rsb;
+            } else {
+                const int trow = ld * R + rsub;
+                const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
+                off = (unsigned)min(trow, tile_len(t) - 1) * rsb + coff;
+                soff = (isv ? colv : colk) + j0 * (int)rsb;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (dgk::lds_void*)(tile_ptr(buf, tile, isv) + ld * 256), 16, (int)off, soff, 0, 0);
         }
     };
 
@@ -689,9 +787,11 @@ __global__ void __launch_bounds__(64 * kWavesT)
     float m = -INFINITY, lsum = 0.0f;
 
     const int nstage = (a.ntiles + kParts - 1) / kParts;
-    if (wave < 4) issue_stage(0, 0);
-    for (int st = 0; st < nstage; ++st) {
-        const int buf = st & 1;
+    if (wave < 4) issue_stage(0, BufC<0>{});
+    // One stage; the stage loop is unrolled by two so that the buffer index is a constant and
+    // the LDS reads of a tile take immediate offsets.
+    auto stage = [&](int st, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // stage st has landed everywhere, stage st-1 is consumed (and the
                           // bias tables are complete before the first use)
@@ -719,7 +819,7 @@ __global__ void __launch_bounds__(64 * kWavesT)
             }
         };
         if constexpr (kParts == 1) read_dh();
-        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, buf ^ 1);
+        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, BufC<buf ^ 1>{});
         if constexpr (kParts != 1) read_dh();
         if (active && t < a.ntiles) {
             const float ref = dgk::ref_of(m);
@@ -747,6 +847,10 @@ __global__ void __launch_bounds__(64 * kWavesT)
             dgk::softmax_update<HD>(s, m, lsum, o);
             dgk::accumulate_pv<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
         }
+    };
+    for (int st = 0; st < nstage; st += 2) {
+        stage(st, BufC<0>{});
+        if (st + 1 < nstage) stage(st + 1, BufC<1>{});
     }
 
     __syncthreads();
@@ -763,7 +867,7 @@ __global__ void __launch_bounds__(64 * kWavesT)
 #pragma unroll
     for (int r0 = 0; r0 < kBlockQ; r0 += kRowsPerPass) {
         const int rloc = r0 + tid / kChunksO, c = tid % kChunksO;
-        const int q = qb * kBlockQ + rloc;
+        const int q = kPatch ? patch_token(rloc) : qb * kBlockQ + rloc;
         if (q < a.n)
             *reinterpret_cast<float4*>(a.out + ((size_t)win * a.n + q) * a.W + head * HD + 4 * c) =
                 *reinterpret_cast<const float4*>(smem + rloc * kOStride + 4 * c);
@@ -803,6 +907,10 @@ auto pick_flash(bool full, bool one) {
                        : relpos_flash_kernel<false, false, kParts, kWavesT>);
 }
 
+// Grids whose attention workgroups form their own bias rows from an 8 x 8 patch of queries:
+// large grids (64-query workgroups) cut into half-row tiles with both sides multiples of 8.
+bool patch_grid(int gh, int gw) { return gh * gw > kSmallGrid && gw > 32 && gh % 8 == 0 && gw % 8 == 0; }
+
 int relpos_call(const char* fn, const float* qkv, const float* rh, const float* rw, float* out,
                 int nwin, int gh, int gw, int heads, int hd, float scale, void* workspace,
                 size_t workspace_bytes, void* stream) {
@@ -830,7 +938,8 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     if (workspace && workspace_bytes < need)
         return dg::fail(DG_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
                         workspace_bytes, need);
-    const bool use_ws = workspace && rh;
+    const bool patch = rh && patch_grid(gh, gw);   // bias rows formed inside the attention
+    const bool use_ws = workspace && rh && !patch;
     const dg::Span so(out, ntok * W * 4);
     const dg::Span sq(qkv, ntok * 3 * W * 4), sh(rh, (size_t)gh * gh * HD * 4),
         sw(rw, (size_t)gw * gw * HD * 4), sws(use_ws ? workspace : nullptr, need);
@@ -915,8 +1024,11 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     }
     const bool full = tl.half_rows ? gw == 64 : (tl.kpt == dgk::kKeys && gh % tl.rpt == 0);
     const bool one = tl.nshift == 1;
-    auto* kern = rows16 ? pick_flash<1, 4>(full, one) : small ? pick_flash<2, 8>(full, one)
-                                                             : pick_flash<4, 8>(full, one);
+    auto* kern = patch  ? (full ? relpos_flash_kernel<true, true, 4, 8, true>
+                                : relpos_flash_kernel<false, true, 4, 8, true>)
+               : rows16 ? pick_flash<1, 4>(full, one)
+               : small  ? pick_flash<2, 8>(full, one)
+                        : pick_flash<4, 8>(full, one);
     hipLaunchKernelGGL(kern, dim3((unsigned)a.nblocks), dim3(rows16 ? 256 : 512), 0, s, a);
     return dg::launch_status(fn);
 }

@@ -347,7 +347,10 @@ size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
 /*
  * relpos_flash_attn_ws -- relpos_flash_attn with a caller workspace for the bias rows: a first
  * kernel computes them once per (head, query), as the page's DHDW step does, and the attention
- * reads them.  Same results as relpos_flash_attn up to rounding; faster.
+ * reads them.  Same results as relpos_flash_attn up to rounding; faster.  Grids of more than
+ * 512 tokens whose sides are multiples of 8 and whose width is above 32 (the SAM global 64 x
+ * 64 map) form the bias rows inside the attention from 8 x 8 patches of queries either way, and
+ * leave the workspace unused.
  *   workspace  device scratch of at least relpos_flash_attn_workspace_size() bytes, 16-byte
  *              aligned, not overlapping any input or `out` (NULL/0: as relpos_flash_attn).
  * Errors: as relpos_flash_attn, plus DG_EINVAL for a misaligned or too small workspace.

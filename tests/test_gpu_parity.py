@@ -471,7 +471,10 @@ def test_dg_layer_stack_every_element(norm_mode):
                                               (20, 2, 1, True), (33, 1, 1, True), (13, 14, 2, False),
                                               # the 4-wavefront shape's limits (512 tokens, 16
                                               # rows of at most 32) and one row past them
-                                              (16, 32, 2, True), (17, 30, 1, True)])
+                                              (16, 32, 2, True), (17, 30, 1, True),
+                                              # 8 x 8 query patches forming their own bias
+                                              # rows, with partial (width 40, 48) tiles
+                                              (16, 40, 2, True), (24, 48, 1, True)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
 def test_relpos_small(gh, gw, heads, bias, use_ws):
     c = synth.relpos_case(gh, gw, heads, 64, seed=gh * 100 + gw, bias=bias, table_std=0.3)
@@ -511,7 +514,9 @@ def oracle_windows(c):
                                                    (2, 12, 64, 1, True), (3, 9, 47, 1, True),
                                                    # more workgroups than CUs: the 4-wavefront
                                                    # shape, on ragged grids
-                                                   (130, 5, 7, 2, True), (90, 11, 13, 3, False)])
+                                                   (130, 5, 7, 2, True), (90, 11, 13, 3, False),
+                                                   # 8 x 8 query patches
+                                                   (2, 16, 48, 1, True)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
 def test_relpos_windows_small(nwin, gh, gw, heads, bias, use_ws):
     c = synth.windows_case(nwin, gh, gw, heads, 64, seed=nwin * 1000 + gh * 10 + gw, bias=bias,
