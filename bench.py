@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -74,11 +75,33 @@ def _code_tokens(text: str) -> str:
     return " ".join("".join(out).split())
 
 
-def source_hash() -> str:
-    """Hash of the kernel sources' code (comments and layout excluded): the profiles' traffic
-    records are used only while it matches the one they were measured on."""
+# The source file each measured kernel family is built from; its local includes are followed.
+KERNEL_SOURCES = {"attn_split_gqa": "attn_split_gqa.hip", "attn_small": "attn_split_gqa.hip",
+                  "relpos_flash": "relpos_flash.hip", "hbm_copy": None}
+
+
+def _source_files(kernel):
+    """Names under CSRC that kernel's code comes from: its file and, transitively, every
+    `#include "..."` found there (all files when kernel is None)."""
+    if kernel is None:
+        return sorted(os.listdir(CSRC))
+    todo, seen = [KERNEL_SOURCES[kernel]] if KERNEL_SOURCES[kernel] else [], set()
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            todo += re.findall(r'^\s*#\s*include\s*"([^"]+)"', f.read(), flags=re.M)
+    return sorted(seen)
+
+
+def source_hash(kernel=None) -> str:
+    """Hash of a kernel family's source code (comments and layout excluded; every kernel
+    source when kernel is None): a profile's traffic record is used only while the hash of the
+    kernel it measured matches the one it was taken on."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in _source_files(kernel):
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode() + b"\0" + _code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
@@ -91,7 +114,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -689,7 +712,7 @@ def main():
         "step_flops": work.flops, "step_hbm_bytes_algorithmic": step_bytes,
         "step_hbm_gbps_algorithmic": step_bytes / (r["ms_step"] * 1e-3) / 1e9,
         "roofline": roof, "timing": timing, "cpu_baseline": cpu, "also": also,
-        "source_hash": source_hash(),
+        "source_hash": source_hash(work.dominant),
     }
     print(json.dumps(rec), flush=True)
 

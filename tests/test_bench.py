@@ -47,9 +47,32 @@ def test_source_hash_follows_code_not_comments(tmp_path, monkeypatch):
     assert bench.source_hash() != h0   # a new file is part of the kernel sources
 
 
+def test_source_hash_per_kernel_follows_its_file_and_includes(tmp_path, monkeypatch):
+    d = tmp_path / "csrc"
+    d.mkdir()
+    (d / "common.hpp").write_text("int shared = 0;\n")
+    (d / "attn_split_gqa.hip").write_text('#include "common.hpp"\n__global__ void a() {}\n')
+    (d / "relpos_flash.hip").write_text('#include "common.hpp"\n__global__ void r() {}\n')
+    monkeypatch.setattr(bench, "CSRC", str(d))
+    a0, r0 = bench.source_hash("attn_split_gqa"), bench.source_hash("relpos_flash")
+    assert bench.source_hash("attn_small") == a0          # built from the same file
+    (d / "relpos_flash.hip").write_text('#include "common.hpp"\n\n__global__  void r()  {}  // r\n')
+    assert bench.source_hash("relpos_flash") == r0        # layout and comments only
+    (d / "relpos_flash.hip").write_text('#include "common.hpp"\n__global__ void r(int) {}\n')
+    assert bench.source_hash("relpos_flash") != r0
+    assert bench.source_hash("attn_split_gqa") == a0      # the other kernel's record stays valid
+    (d / "common.hpp").write_text("int shared = 1;\n")
+    assert bench.source_hash("attn_split_gqa") != a0      # a shared include changes both
+    (d / "unrelated.hip").write_text("__global__ void u() {}\n")
+    a1 = bench.source_hash("attn_split_gqa")
+    (d / "unrelated.hip").write_text("__global__ void u(int) {}\n")
+    assert bench.source_hash("attn_split_gqa") == a1
+    assert bench.source_hash("hbm_copy") == bench.source_hash("hbm_copy")   # no source of ours
+
+
 def test_traffic_record_used_only_on_matching_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    rec = {"source_hash": bench.source_hash(), "hbm_bytes_per_launch": 12345.0}
+    rec = {"source_hash": bench.source_hash("attn_split_gqa"), "hbm_bytes_per_launch": 12345.0}
     (tmp_path / "traffic_attn_split_gqa_w.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("attn_split_gqa", "w") == 12345.0
     rec["source_hash"] = "0" * 16
