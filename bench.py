@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s and HBM GB/s (% of MI355X roofline) per canvas step"
 PEAK_F32_MFMA = 157.3      # TFLOP/s, dense f32 matrix
+PEAK_BF16_MFMA = 2500.0    # TFLOP/s, dense bf16 matrix
 PEAK_HBM = 8000.0          # GB/s
 CSRC = os.path.join(ROOT, "gqa_flash_attention_dg_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -173,6 +174,11 @@ class SplitWork:
             fused = norm_mode == "one_launch" and c.normed
             self.norm_bytes += 2 * kvn * (2 if fused else 4 + 2)
         self.bound = "mfma" if self.flops / self.attn_bytes > 20 else "hbm"
+        if kv16 == "bf16":
+            # every product runs as three bf16 MFMA products (the f32 operand split in three
+            # exact bf16 terms), so the ceiling for the algorithmic flops is a third of bf16's
+            self.mfma_peak = PEAK_BF16_MFMA / 3
+            self.mfma_peak_name = "bf16 MFMA / 3 (three bf16 products per f32 product)"
 
     def config(self):
         c = self.c
@@ -596,8 +602,10 @@ def rates(work, r):
     step_bytes = work.attn_bytes + work.norm_bytes
     if work.bound == "mfma":
         achieved = work.flops / (kern_avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F32_MFMA, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_F32_MFMA}
+        peak = getattr(work, "mfma_peak", PEAK_F32_MFMA)
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak,
+                "peak_of": getattr(work, "mfma_peak_name", "f32 MFMA")}
         per_ms = lambda ms: work.flops / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
     else:

@@ -81,8 +81,8 @@ class CanvasBlock:
     layers of a stack, which run one after another on one stream); one is allocated otherwise.
     kv16: None (f32 K/V) or "f16" / "bf16": the cache is packed once into 16-bit twins here, each
     step's one-launch norm also writes 16-bit twins of its normalised canvas k and v (with
-    "separate" norms a pack pass writes them), and the attention widens them to f32 as it
-    reads them (the q norm then runs in the norm launch, not inside attention).
+    "separate" norms a pack pass writes them), and the attention reads the 16-bit twins
+    (dg_attn_split_gqa_kv16; the q norm then runs in the norm launch, not inside attention).
     """
 
     def __init__(self, B, T, ctx, nh, nkv, hd, kc=None, vc=None, wq=None, wk=None, *,

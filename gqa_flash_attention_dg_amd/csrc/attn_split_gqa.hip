@@ -30,8 +30,9 @@
 // deal the key tiles round robin, which spreads the canvas tiles (and their norm work) over the
 // workgroups of a kv head.
 //
-// The 16-bit K/V variants read cache and canvas rows stored as f16 or bf16 and widen each
-// element as it is read from LDS; the arithmetic is the same f32 MFMA path.
+// The 16-bit K/V variants read cache and canvas rows stored as f16 or bf16.  f16 elements are
+// widened to f32 as they are read from LDS and run the f32 MFMA path; bf16 tiles run both
+// products on the bf16 matrix pipe, with the f32 operand taken as three bf16 terms.
 //
 // Shapes with too few workgroups to fill the GPU also split the key range, in whole 32-key
 // tiles, across workgroups ("split-KV"): each writes an unnormalised partial (max,
@@ -75,8 +76,8 @@ struct SplitArgs {
 };
 
 // K/V element storage: 0 = f32, DG_KV_F16, DG_KV_BF16.  16-bit tiles are loaded into LDS as
-// they are stored (half the bytes of a stage) and widened to f32 in registers as the MFMA
-// operands are read, so the arithmetic is the f32 arithmetic of the f32 path.
+// they are stored (half the bytes of a stage).  f16 operands are widened to f32 in registers as
+// they are read, so that arithmetic is the f32 path's; bf16 tiles feed bf16 MFMAs directly.
 template <int HD, int kKV>
 struct KVTile {
     static constexpr int kEsz = kKV ? 2 : 4;                  // bytes per element
@@ -172,6 +173,178 @@ __device__ inline void accumulate_pv16(const char* __restrict__ vs, int l32, int
             o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(hi16<kKV>(w), p[r], o[1], 0, 0, 0);
         }
     }
+}
+
+// bf16 K/V on the bf16 matrix pipe.  A product of two bf16 values is exact in f32, and an f32
+// value x is the sum of three bf16 values to within 2^-27 |x|: hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid), rounding to nearest (both differences are exact: each is a multiple
+// of x's last significand bit and at most 2^-9 of the value it is taken from).  So with x = q
+// (scores) or x = p (the value product) each MFMA step runs three v_mfma_f32_32x32x16_bf16, one
+// per term, with exact products and the sums in f32: the f32 path's arithmetic up to a 2^-27
+// relative change of one operand and the summation order, at about a fifth of the matrix-pipe
+// time of v_mfma_f32_32x32x2f32 on the same tile.  The k-slots a lane supplies are the same for
+// the A and the B operand, so which 8 of the 16 a lane half holds does not matter; the 32x32
+// accumulator layout is that of the f32 instruction.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// The weight pairs (-1, 0) and (0, -1) of split_bf16x3, as register values: the empty asm keeps
+// the compiler from encoding them as an inline constant, which the hardware would widen as an
+// f32 constant rather than place in the low half.
+struct SplitWeights {
+    bf16x2 n0, n1;
+    __device__ SplitWeights() {
+        unsigned w0 = 0x0000bf80u, w1 = 0xbf800000u;
+        asm volatile("" : "+s"(w0), "+s"(w1));
+        n0 = __builtin_bit_cast(bf16x2, w0);
+        n1 = __builtin_bit_cast(bf16x2, w1);
+    }
+};
+
+// The three terms of x0 and x1, each pair packed in one dword (x0 in the low half).  The
+// differences come from v_dot2c_f32_bf16 with weights (-1, 0) and (0, -1): x - term in one
+// instruction, exact since the result is representable.
+__device__ inline void split_bf16x3(float x0, float x1, const SplitWeights& w, unsigned& hi,
+                                    unsigned& mid, unsigned& lo) {
+    const bf16x2 n0 = w.n0, n1 = w.n1;
+    const bf16x2 h = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, n0, x0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, n1, x1, false);
+    const bf16x2 m = __builtin_convertvector((f32x2){r0, r1}, bf16x2);
+    const float t0 = __builtin_amdgcn_fdot2_f32_bf16(m, n0, r0, false);
+    const float t1 = __builtin_amdgcn_fdot2_f32_bf16(m, n1, r1, false);
+    const bf16x2 l = __builtin_convertvector((f32x2){t0, t1}, bf16x2);
+    hi = __builtin_bit_cast(unsigned, h);
+    mid = __builtin_bit_cast(unsigned, m);
+    lo = __builtin_bit_cast(unsigned, l);
+}
+
+// The lane's query operand in three bf16 terms: step st, k-slot e of lane half `half` is head
+// element 16*st + 8*half + e, times mul; elements at or past lim (a multiple of 4) are zero.
+template <int HD>
+struct QSplit {
+    u32x4 h[HD / 16], m[HD / 16], l[HD / 16];
+};
+
+template <int HD>
+__device__ inline void load_q_bf16x3(const float* __restrict__ qrow, bool valid, int half,
+                                     float mul, QSplit<HD>& q, int lim) {
+    const SplitWeights w;
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        float x[8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int d0 = 16 * st + 8 * half + 4 * c;
+            const float4 v = valid && d0 < lim ? *reinterpret_cast<const float4*>(qrow + d0)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            x[4 * c + 0] = v.x * mul;
+            x[4 * c + 1] = v.y * mul;
+            x[4 * c + 2] = v.z * mul;
+            x[4 * c + 3] = v.w * mul;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            unsigned th, tm, tl;
+            split_bf16x3(x[2 * i], x[2 * i + 1], w, th, tm, tl);
+            q.h[st][i] = th;
+            q.m[st][i] = tm;
+            q.l[st][i] = tl;
+        }
+    }
+}
+
+// S^T += K Q^T from a bf16 K tile (rows of HD elements, 16-byte chunks swizzled as in
+// scores_from16): step st reads chunk 2*st + half of the lane's key row, 8 elements at once.
+template <int HD>
+__device__ inline f32x16 scores_bf16x3(const char* __restrict__ ks, int l32, int half,
+                                       const QSplit<HD>& q, f32x16 s) {
+    const char* kr = ks + l32 * HD * 2;
+    const int sw = l32 % (HD / 8);
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        const bf16x8 k = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * ((2 * st + half) ^ sw)));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(q.h[st]), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(q.m[st]), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(q.l[st]), s, 0, 0, 0);
+    }
+    return s;
+}
+
+// bf16 V tiles sit in LDS row-major with each row's 16-byte chunks permuted, chunk c of key row
+// k at position c ^ vswz(k): the 8 rows a wavefront's transposed reads touch at once (4 per
+// lane half) then cover all 64 banks twice instead of 16 banks eight times.
+template <int HD>
+__device__ inline int vswz(int row) {
+    return HD == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// O^T += V^T P^T from a bf16 V tile.  Step st takes the 16 keys whose probabilities are the
+// lane's registers p[8*st .. 8*st + 7] (keys dgk::key_of(r, half)), so the B operand is those
+// registers split in three.  The A operand of output group t holds, for the lane's head element
+// 32*t + l32, the same 16 keys; two ds_read_b64_tr_b16 fetch it straight from the row-major tile.
+// That instruction hands out, within each 16 lanes, element j%4 of the 8 bytes addressed by lane
+// 4*e + j/4 as element e of lane j: so lane 4*e + c of a 16-lane group addresses key row
+// (4*half + e) (plus 8 for the second read) at head elements 32*t + 16*((lane/16)%2) + 4*c.
+// Output rows are therefore head elements 32*t + key_of(r, half): stage_row_blocked.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int HD>
+__device__ inline void vtr_offsets(int lane, int (&off)[dgk::Tile<HD>::kGroups]) {
+    const int j = lane & 15, e = j >> 2, c = j & 3, sg = (lane >> 4) & 1, half = lane >> 5;
+    const int row = 4 * half + e;
+#pragma unroll
+    for (int t = 0; t < dgk::Tile<HD>::kGroups; ++t)
+        off[t] = row * HD * 2 + 16 * ((4 * t + 2 * sg + (c >> 1)) ^ vswz<HD>(row)) + 8 * (c & 1);
+}
+
+template <int HD>
+__device__ inline void accumulate_pv_bf16x3(const char* __restrict__ vs, const int (&off)[dgk::Tile<HD>::kGroups],
+                                            const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
+    constexpr int G = dgk::Tile<HD>::kGroups;
+    const SplitWeights w;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        u32x4 bh, bm, bl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            unsigned th, tm, tl;
+            split_bf16x3(p[8 * st + 2 * i], p[8 * st + 2 * i + 1], w, th, tm, tl);
+            bh[i] = th;
+            bm[i] = tm;
+            bl[i] = tl;
+        }
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            const char* r0 = vs + st * 16 * HD * 2 + off[t];
+            const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0));
+            const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0 + 8 * HD * 2));
+            const uint2 u0 = __builtin_bit_cast(uint2, x0), u1 = __builtin_bit_cast(uint2, x1);
+            const bf16x8 av = as_bf16x8(u32x4{u0.x, u0.y, u1.x, u1.y});
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bh), o[t], 0, 0, 0);
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bm), o[t], 0, 0, 0);
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bl), o[t], 0, 0, 0);
+        }
+    }
+}
+
+// dgk::stage_row for the bf16 path's output layout (row m of group t is head element 32*t + m).
+template <int HD>
+__device__ inline void stage_row_blocked(float* __restrict__ rows, int l32, float scale,
+                                         const f32x16 (&o)[dgk::Tile<HD>::kGroups], int half) {
+    float* dst = rows + l32 * (HD + 4) + 4 * half;
+#pragma unroll
+    for (int t = 0; t < dgk::Tile<HD>::kGroups; ++t)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4*>(dst + 32 * t + 8 * rb) =
+                make_float4(o[t][4 * rb] * scale, o[t][4 * rb + 1] * scale,
+                            o[t][4 * rb + 2] * scale, o[t][4 * rb + 3] * scale);
 }
 
 using dg::group_sum;
@@ -468,6 +641,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     };
 
     constexpr int kEsz = KT::kEsz;
+    constexpr bool kBf16 = kKV == DG_KV_BF16;    // both contractions on the bf16 pipe
     const char* kcb = reinterpret_cast<const char*>(a.kc) + (size_t)bk * a.ctx * hd * kEsz;
     const char* vcb = reinterpret_cast<const char*>(a.vc) + (size_t)bk * a.ctx * hd * kEsz;
     const size_t cstride = (size_t)a.nkv * hd;   // canvas row stride, elements
@@ -508,7 +682,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 #pragma unroll
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int trow = padk ? i + KT::kLoadsPerTile * rsub : i * R + rsub;
-                int chunk = ld_isv || KL::kPadded ? pos : (pos ^ (trow % KT::kChunks));
+                int chunk = ld_isv ? (kBf16 ? pos ^ vswz<HD>(trow) : pos)
+                                   : (KL::kPadded ? pos : (pos ^ (trow % KT::kChunks)));
                 if (kPad) chunk = min(chunk, last_chunk);
                 __builtin_amdgcn_global_load_lds(b + ((unsigned)trow * rs + 16u * chunk),
                                                  (dgk::lds_void*)(dst + i * load_bytes), 16, 0, 0);
@@ -518,7 +693,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int trow = padk ? i + KT::kLoadsPerTile * rsub : i * R + rsub;
                 const int j = min(j0 + trow, kend - 1);
-                int chunk = ld_isv || KL::kPadded ? pos : (pos ^ (trow % KT::kChunks));
+                int chunk = ld_isv ? (kBf16 ? pos ^ vswz<HD>(trow) : pos)
+                                   : (KL::kPadded ? pos : (pos ^ (trow % KT::kChunks)));
                 if (kPad) chunk = min(chunk, last_chunk);
                 const char* p = (j < a.ctx ? cache_base + (size_t)j * rstride_c
                                            : canvas_base + (size_t)(j - a.ctx) * rstride_v) +
@@ -530,8 +706,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 
     // The first stage's loads go out before the queries are fetched, so the two overlap.
     if (!hi && nst > 0) issue_stage(0, 0);
-    float qreg[HD / 2];
-    if constexpr (kNormQ) {
+    float qreg[kBf16 ? 1 : HD / 2];
+    QSplit<kBf16 ? HD : 16> q3;
+    if constexpr (kBf16) {
+        static_assert(!kNormQ, "16-bit K/V take normalised q");
+        load_q_bf16x3<HD>(a.q + gq * hd, valid, half, a.qmul, q3, hd);
+    } else if constexpr (kNormQ) {
         float* qs = smem + 2 * 2 * KL::kSlotBytes / 4;
         stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
         __syncthreads();
@@ -545,6 +725,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
+    int voff[TL::kGroups];   // bf16 V: the lane's transposed-read offsets
+    if constexpr (kBf16) vtr_offsets<HD>(lane, voff);
 
     for (int st = 0; st < nst; ++st) {
         const int buf = st & 1;
@@ -586,7 +768,10 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
                 const float shift = -dgk::ref_of(m);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
                                                          f32x16{}, 0, 0, 0);
-                s = scores_from16<HD, kKV>(tile_ptr(buf, hi, 0), l32, half, qreg, s);
+                if constexpr (kBf16)
+                    s = scores_bf16x3<HD>(tile_ptr(buf, hi, 0), l32, half, q3, s);
+                else
+                    s = scores_from16<HD, kKV>(tile_ptr(buf, hi, 0), l32, half, qreg, s);
             }
             const bool need_mask =
                 t0 + dgk::kKeys > kend || (a.causal && t0 + dgk::kKeys - 1 - a.ctx > row_min);
@@ -600,6 +785,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             dgk::softmax_update<HD>(s, m, lsum, o);
             if constexpr (kKV == 0)
                 dgk::accumulate_pv<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 1)), l32, half, s, o);
+            else if constexpr (kBf16)
+                accumulate_pv_bf16x3<HD>(tile_ptr(buf, hi, 1), voff, s, o);
             else
                 accumulate_pv16<HD, kKV>(tile_ptr(buf, hi, 1), l32, half, s, o);
         }
@@ -616,8 +803,11 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     static_assert(64 * (TL::kGroups * 16 + 2) == dgk::kQuery * kOStride, "row block overlays the merge scratch");
     long long* rowg = reinterpret_cast<long long*>(smem + kPairs * dgk::kQuery * kOStride);
     if (!hi) {
-        dgk::stage_row<HD>(smem + pair * dgk::kQuery * kOStride, l32,
-                           a.nsplit == 1 && valid ? 1.0f / ltot : 1.0f, o, half);
+        const float oscale = a.nsplit == 1 && valid ? 1.0f / ltot : 1.0f;
+        if constexpr (kBf16)
+            stage_row_blocked<HD>(smem + pair * dgk::kQuery * kOStride, l32, oscale, o, half);
+        else
+            dgk::stage_row<HD>(smem + pair * dgk::kQuery * kOStride, l32, oscale, o, half);
         if (half == 0) rowg[pair * dgk::kQuery + l32] = valid ? (long long)gq : -1;
         if (a.nsplit > 1 && valid && half == 0) {
             float* wm = a.ws + (size_t)a.nsplit * a.nqtot * hd;

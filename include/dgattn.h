@@ -270,11 +270,15 @@ int dg_attn_split_gqa_qkvnorm(const float* q, const float* wq, const float* k, c
 
 /*
  * dg_attn_split_gqa_kv16 -- dg_attn_split_gqa with keys and values stored in 16 bits (the
- * page's kv16 twin, §8(f)-style reduced-precision K/V storage): kc, vc, k and v hold f16 or
- * bf16 values (`kv_format`), in the same layouts as dg_attn_split_gqa's f32 tensors.  Every
- * value is widened exactly to f32 and the arithmetic is that of dg_attn_split_gqa, so the
- * result equals dg_attn_split_gqa on the widened values up to rounding.  Stage tiles in LDS are
- * half the bytes; the widening costs vector instructions per tile.
+ * page's kv16 twin, reduced-precision K/V storage): kc, vc, k and v hold f16 or bf16 values
+ * (`kv_format`), in the same layouts as dg_attn_split_gqa's f32 tensors.  The result equals
+ * dg_attn_split_gqa on the widened values up to rounding:
+ *   f16   each value is widened exactly to f32 and runs the f32 MFMA arithmetic;
+ *   bf16  both products run on the bf16 matrix pipe: the f32 operand (q for the scores, the
+ *         probabilities for the value product) is taken as three bf16 terms whose sum is
+ *         within 2^-27 of it, each product of two bf16 values is exact in f32, and all sums
+ *         are f32 -- at about a fifth of the f32 MFMA time.
+ * Stage tiles in LDS are half the bytes of f32 ones.
  *   hd must be a multiple of 8 (16-byte rows of 16-bit values); q and out are f32.
  *   Other arguments, the workspace and its size function as dg_attn_split_gqa.
  * Errors: as dg_attn_split_gqa, plus DG_EINVAL for an unknown kv_format and DG_EUNSUPPORTED

@@ -715,6 +715,30 @@ def test_canvas_step_kv16(fmt, name):
     print("kv16 %s: max |out - f32 out| = %.3e" % (name, dist))
 
 
+@pytest.mark.parametrize("fmt,name", KV_FMTS, ids=[n for _, n in KV_FMTS])
+def test_long_cache_kv16_every_element(fmt, name):
+    """The 16-bit attention at the long cache's full size (B 4, T 256, ctx 8192, 32/8 heads, hd
+    128) in the launch configuration of the canvas block: q, k, v normed and the cache keys
+    roped by the oracle, K/V packed by the oracle, every output element against the oracle's
+    attention on the widened values at the f32 bar."""
+    c = synth.long_cache()
+    cs, kc = oracle_prepare(c)
+    qn = oracle.headnorm_rope(c.q, c.wq, cs, c.nh, c.hd, 3, c.eps)
+    kn = oracle.headnorm_rope(c.k, c.wk, cs, c.nkv, c.hd, 3, c.eps)
+    vn = oracle.headnorm_rope(c.v, None, None, c.nkv, c.hd, 0, c.eps)
+    pk = {"kc": oracle.pack16(kc, fmt), "vc": oracle.pack16(c.vc, fmt),
+          "k": oracle.pack16(kn, fmt), "v": oracle.pack16(vn, fmt)}
+    wd = {n: oracle.widen16(h, fmt) for n, h in pk.items()}
+    out = torch.full((c.B, c.T, c.nh * c.hd), float("nan"), device="cuda")
+    ws, nbytes = workspace_for(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd)
+    dg.dg_attn_split_gqa_kv16(dev(qn), dev16(pk["kc"]), dev16(pk["vc"]), dev16(pk["k"]),
+                              dev16(pk["v"]), out, c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, c.scale,
+                              int(c.causal), fmt, ws, nbytes)
+    ref = oracle.attn_split_gqa(qn, wd["kc"], wd["vc"], wd["k"], wd["v"], c.nh, c.nkv, c.hd,
+                                c.scale, c.causal)
+    assert_parity(host(out), ref, "long cache kv16 %s" % name)
+
+
 # ----------------------------------------------------------------------------- HIP graphs
 
 @pytest.mark.parametrize("norm_mode", ["fused", "in_attention", "one_launch"])
