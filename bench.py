@@ -46,6 +46,38 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s and HBM GB/s (% of MI355X roofline) per canvas step"
 PEAK_F32_MFMA = 157.3      # TFLOP/s, dense f32 matrix
 PEAK_BF16_MFMA = 2500.0    # TFLOP/s, dense bf16 matrix
+
+
+def mfma_ceiling(plan_kernel, kv16=None):
+    """(TFLOP/s of algorithmic flops, description) that bound the split-GQA kernel a plan names.
+    The 32-key tile kernel forms each f32 product from bf16 matrix products: six for f32 K/V
+    (both operands in three bf16 terms), three for bf16 K/V (q and p in three terms); the other
+    kernels, and f16 K/V, use f32 MFMA."""
+    from gqa_flash_attention_dg_amd import DG_KERNEL_TILE32
+    if plan_kernel != DG_KERNEL_TILE32 or kv16 == "f16":
+        return PEAK_F32_MFMA, "f32 MFMA"
+    if kv16 == "bf16":
+        return PEAK_BF16_MFMA / 3, "bf16 MFMA / 3 (three bf16 products per f32 product)"
+    return PEAK_BF16_MFMA / 6, "bf16 MFMA / 6 (six bf16 products per f32 product)"
+
+
+ARITH = {
+    "f32 MFMA": "f32 (f32 MFMA)",
+    "bf16 MFMA / 6 (six bf16 products per f32 product)":
+        "f32 operands as three bf16 terms each; every product as six exact bf16 MFMA products "
+        "summed in f32 (within 2^-25 of the f32 product)",
+    "bf16 MFMA / 3 (three bf16 products per f32 product)":
+        "bf16 K/V; q and p as three bf16 terms; exact bf16 MFMA products summed in f32",
+}
+
+
+def combined_ceiling(parts):
+    """Ceiling of a step made of launches [(flops, (peak, name))]: total flops over the sum of
+    each launch's minimum time."""
+    flops = sum(f for f, _ in parts)
+    tmin = sum(f / pk for f, (pk, _) in parts)
+    names = sorted(set(n for _, (_, n) in parts))
+    return flops / tmin, " + ".join(names)
 PEAK_HBM = 8000.0          # GB/s
 CSRC = os.path.join(ROOT, "gqa_flash_attention_dg_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -174,11 +206,10 @@ class SplitWork:
             fused = norm_mode == "one_launch" and c.normed
             self.norm_bytes += 2 * kvn * (2 if fused else 4 + 2)
         self.bound = "mfma" if self.flops / self.attn_bytes > 20 else "hbm"
-        if kv16 == "bf16":
-            # every product runs as three bf16 MFMA products (the f32 operand split in three
-            # exact bf16 terms), so the ceiling for the algorithmic flops is a third of bf16's
-            self.mfma_peak = PEAK_BF16_MFMA / 3
-            self.mfma_peak_name = "bf16 MFMA / 3 (three bf16 products per f32 product)"
+        from gqa_flash_attention_dg_amd import DG_KV_BF16, DG_KV_F16, dg_attn_split_gqa_plan
+        fmt = {None: 0, "f16": DG_KV_F16, "bf16": DG_KV_BF16}[kv16]
+        plan = dg_attn_split_gqa_plan(c.B, c.T, c.ctx, c.nh, c.nkv, c.hd, int(c.causal), fmt)
+        self.mfma_peak, self.mfma_peak_name = mfma_ceiling(plan.kernel, kv16)
 
     def config(self):
         c = self.c
@@ -285,8 +316,10 @@ class LayerStackWork:
                                  [(d(p["wq"]), d(p["wk"])) for p in c.per_layer],
                                  theta_sliding=c.theta_sliding, theta_full=c.theta_full,
                                  eps=c.eps, scale=c.scale, norm_mode=norm_mode)
+        from gqa_flash_attention_dg_amd import dg_attn_split_gqa_plan
         self.io = []
         self.flops = self.attn_bytes = self.norm_bytes = 0
+        parts = []
         modes = [blk.norm_mode for blk in self.stack.blocks]   # "auto" resolved per layer
         self.norm_mode = modes[0] if len(set(modes)) == 1 else "/".join(modes)
         for l, p, norm_mode in zip(c.layers, c.per_layer, modes):
@@ -295,12 +328,16 @@ class LayerStackWork:
             self.io.append((d(p["q"]), d(p["k"]), v, out))
             q, kv = c.B * c.T * c.nh * l.hd, c.B * c.T * l.nkv * l.hd
             cache = c.B * l.nkv * l.ctx * l.hd
-            self.flops += 4 * l.hd * c.B * c.nh * c.T * (l.ctx + c.T)
+            lflops = 4 * l.hd * c.B * c.nh * c.T * (l.ctx + c.T)
+            self.flops += lflops
+            plan = dg_attn_split_gqa_plan(c.B, c.T, l.ctx, c.nh, l.nkv, l.hd, 0, 0)
+            parts.append((lflops, mfma_ceiling(plan.kernel)))
             self.attn_bytes += 4 * (2 * q + 2 * kv + 2 * cache)
             qn = 0 if norm_mode == "in_attention" else q
             if norm_mode != "fused":
                 self.norm_bytes += 4 * 2 * (qn + kv) + 4 * (kv if l.k_eq_v else 2 * kv)
         self.bound = "mfma"
+        self.mfma_peak, self.mfma_peak_name = combined_ceiling(parts)
 
     def config(self):
         c = self.c
@@ -689,7 +726,8 @@ def main():
                       "steps": r["steps"], "warmup": r["warmup"], "step": w.config()["step"],
                       "workload": w.config()["workload"],
                       "roofline": {k: roof[k] for k in ("kernel", "bound", "achieved", "unit",
-                                                        "frac", "avg_launch_ms")},
+                                                        "peak", "frac", "avg_launch_ms")
+                                   if k in roof},
                       "timing": timing}
         del w, r
         torch.cuda.empty_cache()
@@ -716,6 +754,8 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": r["steps"],
         "warmup": r["warmup"], "ms_per_step": r["ms_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "arith": "; ".join(ARITH.get(n, n) for n in
+                           getattr(work, "mfma_peak_name", "f32 MFMA").split(" + ")),
         "config": dict(work.config(), **({"hip_graph_steps": work.graph} if getattr(work, "graph", 0) else {})),
         "step_flops": work.flops, "step_hbm_bytes_algorithmic": step_bytes,
         "step_hbm_gbps_algorithmic": step_bytes / (r["ms_step"] * 1e-3) / 1e9,

@@ -16,7 +16,9 @@
 // direct global->LDS loads, double-buffered so the next stage streams in while this one is
 // computed; a tile lying wholly in the cache or wholly in the canvas is addressed from a scalar
 // base, and only a tile across the seam (or the end of the keys) forms per-row addresses.
-// Scores and the value product run on f32 MFMA (flash_core.hpp).  At the end each pair merges
+// Scores and the value product run on the bf16 matrix pipe with each f32 operand split in three
+// bf16 terms (six products per f32 product; kF32OnBf16 below; the f32-MFMA pieces of
+// flash_core.hpp remain for the switch).  At the end each pair merges
 // its two partial softmax states through LDS, and the workgroup writes its rows out whole.
 //
 // dg_attn_split_gqa_qnorm takes the raw q projection instead and applies the q dispatch of
@@ -273,6 +275,120 @@ __device__ inline f32x16 scores_bf16x3(const char* __restrict__ ks, int l32, int
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(q.l[st]), s, 0, 0, 0);
     }
     return s;
+}
+
+// f32 K/V on the bf16 pipe.  With both operands split in three terms, a = ah + am + al and
+// b = bh + bm + bl, the product a*b is taken as the six terms down to order 2^-18 (ah*bh,
+// ah*bm, am*bh, ah*bl, al*bh, am*bm); the three dropped ones (am*bl, al*bm, al*bl) and the
+// splits' own 2^-27 leave each product within about 2^-25 of its value, inside f32's rounding
+// of a product (2^-24), so the result stays on the f32 bar.  Six v_mfma_f32_32x32x16_bf16 per
+// step are 2.7 times less matrix-pipe time than v_mfma_f32_32x32x2f32; the splitting costs
+// vector instructions instead (7 per pair of values).
+constexpr bool kF32OnBf16 = true;
+
+// The leading products go to `c`, the five smaller ones to `d`: kept apart, the corrections
+// are summed at their own magnitude (about 2^-8 of c's), so only the leading chain rounds at
+// the full magnitude of the result.
+__device__ inline void mfma_bf16x6(u32x4 ah, u32x4 am, u32x4 al, u32x4 bh, u32x4 bm, u32x4 bl,
+                                   f32x16& c, f32x16& d) {
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(am), as_bf16x8(bm), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bh), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bl), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(am), as_bf16x8(bh), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bm), d, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bh), c, 0, 0, 0);
+}
+
+// Splits 8 f32 values into the three bf16x8 operands of one MFMA step.
+__device__ inline void split8(const float (&x)[8], const SplitWeights& w, u32x4& h, u32x4& m,
+                              u32x4& l) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        unsigned th, tm, tl;
+        split_bf16x3(x[2 * i], x[2 * i + 1], w, th, tm, tl);
+        h[i] = th;
+        m[i] = tm;
+        l[i] = tl;
+    }
+}
+
+// The query operand in three terms from the f32 layout of dgk::load_q: step st, k-slot e is
+// qreg[8*st + e], head element 16*st + 8*(e/4) + 4*half + e%4.
+template <int HD>
+__device__ inline void split_q_bf16x3(const float (&qreg)[HD / 2], QSplit<HD>& q) {
+    const SplitWeights w;
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = qreg[8 * st + e];
+        split8(x, w, q.h[st], q.m[st], q.l[st]);
+    }
+}
+
+// S^T += K Q^T from an f32 K tile (padded or swizzled layout): step st reads the lane's head
+// elements 16*st + 4*half + 0..3 and 16*st + 8 + 4*half + 0..3 of its key row.
+template <int HD, bool kPadded>
+__device__ inline f32x16 scores_f32_bf16x6(const char* __restrict__ ks, int l32, int half,
+                                           const QSplit<HD>& q, f32x16 s) {
+    const SplitWeights w;
+    const float* kr = kPadded ? reinterpret_cast<const float*>(ks + KLayout<HD, 0>::row(l32)) + 4 * half
+                              : reinterpret_cast<const float*>(ks) + l32 * HD;
+    const int sw = l32 % (HD / 4);
+    f32x16 d = {};
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        float4 k0, k1;
+        if constexpr (kPadded) {
+            k0 = *reinterpret_cast<const float4*>(kr + 16 * st);
+            k1 = *reinterpret_cast<const float4*>(kr + 16 * st + 8);
+        } else {
+            k0 = *reinterpret_cast<const float4*>(kr + 4 * ((4 * st + half) ^ sw));
+            k1 = *reinterpret_cast<const float4*>(kr + 4 * ((4 * st + 2 + half) ^ sw));
+        }
+        const float x[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        u32x4 kh, km, kl;
+        split8(x, w, kh, km, kl);
+        mfma_bf16x6(kh, km, kl, q.h[st], q.m[st], q.l[st], s, d);
+        __builtin_amdgcn_sched_barrier(0);   // keep the K reads of later steps from piling up
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += d[r];
+    return s;
+}
+
+// O^T += V^T P^T from an f32 V tile (plain rows, the dgk::accumulate_pv layout: output row m
+// of group t is head element m*G + t): step st takes keys dgk::key_of(8*st + e, half).
+template <int HD>
+__device__ inline void accumulate_pv_f32_bf16x6(const float* __restrict__ vs, int l32, int half,
+                                                const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
+    constexpr int G = dgk::Tile<HD>::kGroups;
+    const SplitWeights w;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[8 * st + e];
+        u32x4 bh, bm, bl;
+        split8(x, w, bh, bm, bl);
+        // two output groups at a time (8-byte reads), so that 16 V values are live, not 32
+#pragma unroll
+        for (int tp = 0; tp < G; tp += 2) {
+            float v0[8], v1[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float2 f = *reinterpret_cast<const float2*>(
+                    vs + dgk::key_of(8 * st + e, half) * HD + l32 * G + tp);
+                v0[e] = f.x;
+                v1[e] = f.y;
+            }
+            u32x4 ah, am, al;
+            split8(v0, w, ah, am, al);
+            mfma_bf16x6(ah, am, al, bh, bm, bl, o[tp], o[tp]);
+            split8(v1, w, ah, am, al);
+            mfma_bf16x6(ah, am, al, bh, bm, bl, o[tp + 1], o[tp + 1]);
+        }
+    }
 }
 
 // bf16 V tiles sit in LDS row-major with each row's 16-byte chunks permuted, chunk c of key row
@@ -706,8 +822,9 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 
     // The first stage's loads go out before the queries are fetched, so the two overlap.
     if (!hi && nst > 0) issue_stage(0, 0);
+    constexpr bool kEmu = kKV == 0 && kF32OnBf16;   // f32 K/V on the bf16 pipe
     float qreg[kBf16 ? 1 : HD / 2];
-    QSplit<kBf16 ? HD : 16> q3;
+    QSplit<(kBf16 || kEmu) ? HD : 16> q3;
     if constexpr (kBf16) {
         static_assert(!kNormQ, "16-bit K/V take normalised q");
         load_q_bf16x3<HD>(a.q + gq * hd, valid, half, a.qmul, q3, hd);
@@ -719,6 +836,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     } else {
         dgk::load_q<HD>(a.q + gq * hd, valid, half, a.qmul, qreg, hd);
     }
+    if constexpr (kEmu) split_q_bf16x3<HD>(qreg, q3);
     f32x16 o[TL::kGroups];
 #pragma unroll
     for (int t = 0; t < TL::kGroups; ++t)
@@ -754,7 +872,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         const int t0 = key0(st, hi);
         if (pair_active && t0 < kend) {
             f32x16 s;
-            if constexpr (kKV == 0) {
+            if constexpr (kEmu) {
+                const float shift = -dgk::ref_of(m);
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
+                                                         f32x16{}, 0, 0, 0);
+                s = scores_f32_bf16x6<HD, KL::kPadded>(tile_ptr(buf, hi, 0), l32, half, q3, s);
+            } else if constexpr (kKV == 0) {
                 if constexpr (KL::kPadded) {
                     const float shift = -dgk::ref_of(m);
                     s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
@@ -783,7 +906,9 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
                 }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            if constexpr (kKV == 0)
+            if constexpr (kEmu)
+                accumulate_pv_f32_bf16x6<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 1)), l32, half, s, o);
+            else if constexpr (kKV == 0)
                 dgk::accumulate_pv<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 1)), l32, half, s, o);
             else if constexpr (kBf16)
                 accumulate_pv_bf16x3<HD>(tile_ptr(buf, hi, 1), voff, s, o);

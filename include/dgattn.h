@@ -210,6 +210,11 @@ int dg_attn_split_gqa_plan(int batch, int T, int ctx, int nh, int nkv, int hd, i
  *   torch allocations are).
  *   hd         any multiple of 4 up to 128 (the page allows hd <= 128); heads narrower than
  *              64 or 128 run in the 64- or 128-wide kernel with zero padding.
+ * Arithmetic: in the 32-key tile kernel each f32 operand is taken as three bf16 terms (sum
+ * within 2^-27 of it) and each product q.k and p.v as the six leading bf16 x bf16 products,
+ * each exact in f32, summed in f32 on the bf16 matrix pipe: every product is within about
+ * 2^-25 of its value (f32 rounds a product to 2^-24), and the large score terms are summed
+ * apart from the small ones.  The short-key-set and 16-key tile kernels use f32 arithmetic.
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
  * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, a tensor pointer
  * that is not 16-byte aligned, or a workspace pointer that is misaligned or has
