@@ -13,13 +13,14 @@
 // so they are contiguous in q and out.  Its 8 wavefronts form 4 pairs; both wavefronts of a
 // pair hold the same 32 queries and take alternate 32-key tiles, so the block walks the keys in
 // stages of 64.  Each stage's K and V tiles are fetched once into LDS for all 128 queries with
-// direct global->LDS loads, double-buffered so the next stage streams in while this one is
-// computed; a tile lying wholly in the cache or wholly in the canvas is addressed from a scalar
-// base, and only a tile across the seam (or the end of the keys) forms per-row addresses.
-// Scores and the value product run on the bf16 matrix pipe with each f32 operand split in three
-// bf16 terms (six products per f32 product; kF32OnBf16 below; the f32-MFMA pieces of
-// flash_core.hpp remain for the switch).  At the end each pair merges
-// its two partial softmax states through LDS, and the workgroup writes its rows out whole.
+// direct global->LDS loads, so the next stage streams in while this one is computed; a tile
+// lying wholly in the cache or wholly in the canvas is addressed from a scalar base, and only a
+// tile across the seam (or the end of the keys) forms per-row addresses.  Scores and the value
+// product run on the bf16 matrix pipe: f32 K/V land in one staging buffer, the workgroup splits
+// each stage once into three bf16 planes (six bf16 products per f32 product; kF32OnBf16 below,
+// whose false setting keeps the double-buffered f32 MFMA path of flash_core.hpp), and 16-bit
+// K/V stages are double-buffered as stored.  At the end each pair merges its two partial
+// softmax states through LDS, and the workgroup writes its rows out whole.
 //
 // dg_attn_split_gqa_qnorm takes the raw q projection instead and applies the q dispatch of
 // DG_HEADNORM_ROPE (RMSNorm, weight, NeoX rope) to the workgroup's query vectors as it stages
@@ -282,8 +283,9 @@ __device__ inline f32x16 scores_bf16x3(const char* __restrict__ ks, int l32, int
 // ah*bm, am*bh, ah*bl, al*bh, am*bm); the three dropped ones (am*bl, al*bm, al*bl) and the
 // splits' own 2^-27 leave each product within about 2^-25 of its value, inside f32's rounding
 // of a product (2^-24), so the result stays on the f32 bar.  Six v_mfma_f32_32x32x16_bf16 per
-// step are 2.7 times less matrix-pipe time than v_mfma_f32_32x32x2f32; the splitting costs
-// vector instructions instead (7 per pair of values).
+// step are 2.7 times less matrix-pipe time than v_mfma_f32_32x32x2f32.  The K and V tiles are
+// split once per stage by the whole workgroup (split_stage), q once per wavefront, and the
+// probabilities per tile (7 vector instructions per pair of values).  false: f32 MFMA.
 constexpr bool kF32OnBf16 = true;
 
 // The leading products go to `c`, the five smaller ones to `d`: kept apart, the corrections
@@ -309,85 +311,6 @@ __device__ inline void split8(const float (&x)[8], const SplitWeights& w, u32x4&
         h[i] = th;
         m[i] = tm;
         l[i] = tl;
-    }
-}
-
-// The query operand in three terms from the f32 layout of dgk::load_q: step st, k-slot e is
-// qreg[8*st + e], head element 16*st + 8*(e/4) + 4*half + e%4.
-template <int HD>
-__device__ inline void split_q_bf16x3(const float (&qreg)[HD / 2], QSplit<HD>& q) {
-    const SplitWeights w;
-#pragma unroll
-    for (int st = 0; st < HD / 16; ++st) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = qreg[8 * st + e];
-        split8(x, w, q.h[st], q.m[st], q.l[st]);
-    }
-}
-
-// S^T += K Q^T from an f32 K tile (padded or swizzled layout): step st reads the lane's head
-// elements 16*st + 4*half + 0..3 and 16*st + 8 + 4*half + 0..3 of its key row.
-template <int HD, bool kPadded>
-__device__ inline f32x16 scores_f32_bf16x6(const char* __restrict__ ks, int l32, int half,
-                                           const QSplit<HD>& q, f32x16 s) {
-    const SplitWeights w;
-    const float* kr = kPadded ? reinterpret_cast<const float*>(ks + KLayout<HD, 0>::row(l32)) + 4 * half
-                              : reinterpret_cast<const float*>(ks) + l32 * HD;
-    const int sw = l32 % (HD / 4);
-    f32x16 d = {};
-#pragma unroll
-    for (int st = 0; st < HD / 16; ++st) {
-        float4 k0, k1;
-        if constexpr (kPadded) {
-            k0 = *reinterpret_cast<const float4*>(kr + 16 * st);
-            k1 = *reinterpret_cast<const float4*>(kr + 16 * st + 8);
-        } else {
-            k0 = *reinterpret_cast<const float4*>(kr + 4 * ((4 * st + half) ^ sw));
-            k1 = *reinterpret_cast<const float4*>(kr + 4 * ((4 * st + 2 + half) ^ sw));
-        }
-        const float x[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-        u32x4 kh, km, kl;
-        split8(x, w, kh, km, kl);
-        mfma_bf16x6(kh, km, kl, q.h[st], q.m[st], q.l[st], s, d);
-        __builtin_amdgcn_sched_barrier(0);   // keep the K reads of later steps from piling up
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += d[r];
-    return s;
-}
-
-// O^T += V^T P^T from an f32 V tile (plain rows, the dgk::accumulate_pv layout: output row m
-// of group t is head element m*G + t): step st takes keys dgk::key_of(8*st + e, half).
-template <int HD>
-__device__ inline void accumulate_pv_f32_bf16x6(const float* __restrict__ vs, int l32, int half,
-                                                const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
-    constexpr int G = dgk::Tile<HD>::kGroups;
-    const SplitWeights w;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[8 * st + e];
-        u32x4 bh, bm, bl;
-        split8(x, w, bh, bm, bl);
-        // two output groups at a time (8-byte reads), so that 16 V values are live, not 32
-#pragma unroll
-        for (int tp = 0; tp < G; tp += 2) {
-            float v0[8], v1[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float2 f = *reinterpret_cast<const float2*>(
-                    vs + dgk::key_of(8 * st + e, half) * HD + l32 * G + tp);
-                v0[e] = f.x;
-                v1[e] = f.y;
-            }
-            u32x4 ah, am, al;
-            split8(v0, w, ah, am, al);
-            mfma_bf16x6(ah, am, al, bh, bm, bl, o[tp], o[tp]);
-            split8(v1, w, ah, am, al);
-            mfma_bf16x6(ah, am, al, bh, bm, bl, o[tp + 1], o[tp + 1]);
-        }
     }
 }
 
@@ -445,6 +368,99 @@ __device__ inline void accumulate_pv_bf16x3(const char* __restrict__ vs, const i
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bh), o[t], 0, 0, 0);
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bm), o[t], 0, 0, 0);
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bl), o[t], 0, 0, 0);
+        }
+    }
+}
+
+// f32 K/V tiles split once per stage into bf16 planes.  The workgroup turns each staged f32
+// tile (plain rows, so each load of the stage is a scalar offset from the last) into three bf16
+// tiles hi, mid, lo laid out as the
+// bf16 K/V path lays out its tiles, so every wavefront then reads ready MFMA operands: the
+// split is done once per element instead of once per element and query group.
+template <int HD>
+struct Planes {
+    static constexpr int kBytes = dgk::kKeys * HD * 2;   // one bf16 plane of a tile
+    static constexpr int kOct = HD / 8;                   // 8-element groups per row
+    // plane p of the K (isv 0) or V (isv 1) tile `tile`
+    __device__ static char* at(char* base, int tile, int isv, int p) {
+        return base + ((tile * 2 + isv) * 3 + p) * kBytes;
+    }
+};
+
+template <int HD>
+__device__ inline void split_stage(const char* __restrict__ stage, int slot_bytes,
+                                   char* __restrict__ planes, int ntile, int tid) {
+    using P = Planes<HD>;
+    constexpr int kPerTile = 2 * dgk::kKeys * P::kOct;    // K and V items of one tile
+    const SplitWeights w;
+#pragma unroll
+    for (int i = 0; i < 2 * kPerTile / 512; ++i) {
+        const int it = tid + 512 * i;
+        const int tile = it / kPerTile;
+        if (tile >= ntile) continue;   // uniform per iteration: whole tiles are absent
+        const int o = it % P::kOct, r = (it / P::kOct) % dgk::kKeys;
+        const int isv = (it / (P::kOct * dgk::kKeys)) & 1;
+        const float* row = reinterpret_cast<const float*>(stage + (tile * 2 + isv) * slot_bytes) + r * HD;
+        const float4 x0 = *reinterpret_cast<const float4*>(row + 8 * o);
+        const float4 x1 = *reinterpret_cast<const float4*>(row + 8 * o + 4);
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        u32x4 h, m, l;
+        split8(x, w, h, m, l);
+        const int pos = o ^ (isv ? vswz<HD>(r) : r % P::kOct);
+        char* dst = P::at(planes, tile, isv, 0) + r * HD * 2 + 16 * pos;
+        *reinterpret_cast<u32x4*>(dst) = h;
+        *reinterpret_cast<u32x4*>(dst + P::kBytes) = m;
+        *reinterpret_cast<u32x4*>(dst + 2 * P::kBytes) = l;
+    }
+}
+
+// S^T += K Q^T from the three K planes of a tile; q in the load_q_bf16x3 layout.
+template <int HD>
+__device__ inline f32x16 scores_planes(const char* __restrict__ kp, int l32, int half,
+                                       const QSplit<HD>& q, f32x16 s) {
+    using P = Planes<HD>;
+    const char* kr = kp + l32 * HD * 2;
+    const int sw = l32 % P::kOct;
+    f32x16 d = {};
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        const int off = 16 * ((2 * st + half) ^ sw);
+        const u32x4 kh = *reinterpret_cast<const u32x4*>(kr + off);
+        const u32x4 km = *reinterpret_cast<const u32x4*>(kr + P::kBytes + off);
+        const u32x4 kl = *reinterpret_cast<const u32x4*>(kr + 2 * P::kBytes + off);
+        mfma_bf16x6(kh, km, kl, q.h[st], q.m[st], q.l[st], s, d);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += d[r];
+    return s;
+}
+
+// O^T += V^T P^T from the three V planes of a tile (layout and reads as accumulate_pv_bf16x3).
+template <int HD>
+__device__ inline void accumulate_pv_planes(const char* __restrict__ vp,
+                                            const int (&off)[dgk::Tile<HD>::kGroups],
+                                            const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
+    constexpr int G = dgk::Tile<HD>::kGroups, PB = Planes<HD>::kBytes;
+    const SplitWeights w;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[8 * st + e];
+        u32x4 bh, bm, bl;
+        split8(x, w, bh, bm, bl);
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            u32x4 a[3];
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) {
+                const char* r0 = vp + pl * PB + st * 16 * HD * 2 + off[t];
+                const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0));
+                const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0 + 8 * HD * 2));
+                const uint2 u0 = __builtin_bit_cast(uint2, x0), u1 = __builtin_bit_cast(uint2, x1);
+                a[pl] = u32x4{u0.x, u0.y, u1.x, u1.y};
+            }
+            mfma_bf16x6(a[0], a[1], a[2], bh, bm, bl, o[t], o[t]);
         }
     }
 }
@@ -589,7 +605,7 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
 // no table loads), kept apart so that few registers are live beside the attention state.
 // Chunks past hd keep their raw copies (they meet zero query elements, or fill output
 // elements that are never stored).
-template <int HD, bool kPad>
+template <int HD, bool kPad, bool kPadK = KLayout<HD, 0>::kPadded, bool kSwzK = true>
 __device__ inline void norm_canvas_tile(const SplitArgs& a, float* __restrict__ kt,
                                         float* __restrict__ vt, int j0, int kend, int wave,
                                         int lane, int hd) {
@@ -603,9 +619,9 @@ __device__ inline void norm_canvas_tile(const SplitArgs& a, float* __restrict__ 
         const int j = min(j0 + trow, kend - 1);
         if (j < a.ctx) continue;                 // a cache row; its L lanes leave together
         using KL = KLayout<HD, 0>;
-        float* rowp = isv ? vt + trow * HD : kt + KL::row(trow) / 4;
+        float* rowp = isv ? vt + trow * HD : kt + (kPadK ? KL::row(trow) / 4 : trow * HD);
         // K rows of unpadded tiles are stored chunk-swizzled
-        const int sw = isv || KL::kPadded ? 0 : trow % kChunks;
+        const int sw = isv || kPadK || !kSwzK ? 0 : trow % kChunks;
         float4 x[2];
         float ss = 0.0f;
 #pragma unroll
@@ -697,16 +713,26 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     // buffer 1 (free until the second stage is issued) and a little past it; the pair merge
     // reuses the space at the end.
     using KL = KLayout<HD, kKV>;
-    constexpr int kStageFloats = 2 * 2 * 2 * KL::kSlotBytes / 4;
-    constexpr int kQStageEnd = 2 * 2 * KL::kSlotBytes / 4 + kBlockQ * kQStride<HD>;
+    // kPlanes (f32 K/V on the bf16 pipe): one staging buffer [tile][K, V] of plain f32 tiles,
+    // then the bf16 planes [tile][K, V][hi, mid, lo] the split writes; the
+    // normalised queries are staged over the planes, which are free until the first split.
+    constexpr bool kPlanes = kKV == 0 && kF32OnBf16;
+    constexpr bool kPadK = KL::kPadded && !kPlanes;
+    constexpr int kSlot = kPlanes ? KT::kBytes : KL::kSlotBytes;
+    constexpr int kPlanesOff = 2 * 2 * kSlot;
+    constexpr int kStageFloats = kPlanes ? (kPlanesOff + 2 * 2 * 3 * Planes<HD>::kBytes) / 4
+                                         : 2 * 2 * 2 * KL::kSlotBytes / 4;
+    constexpr int kQOff = kPlanes ? kPlanesOff / 4 : 2 * 2 * KL::kSlotBytes / 4;
+    constexpr int kQStageEnd = kQOff + kBlockQ * kQStride<HD>;
     constexpr int kMergeFloats = kPairs * 64 * (TL::kGroups * 16 + 2) + 2 * kBlockQ;  // + row indices
     constexpr int kA = kNormQ && kQStageEnd > kStageFloats ? kQStageEnd : kStageFloats;
     constexpr int kSmemFloats = kA > kMergeFloats ? kA : kMergeFloats;
     __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
     const int hd = kPad ? a.hd : HD;
     auto tile_ptr = [&](int buf, int tile, int isv) {
-        return reinterpret_cast<char*>(smem) + ((buf * 2 + tile) * 2 + isv) * KL::kSlotBytes;
+        return reinterpret_cast<char*>(smem) + ((buf * 2 + tile) * 2 + isv) * kSlot;
     };
+    char* const planes = reinterpret_cast<char*>(smem) + kPlanesOff;
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks, a.nxcd);
     const int qb = lid % a.qblocks;
@@ -788,7 +814,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         char* dst = tile_ptr(buf, ld_tile, ld_isv);
         // A padded K tile takes rows i and i + 16 in load i (KLayout); V tiles and unpadded K
         // tiles take rows 2i, 2i + 1 (HD 128) or 4i..4i + 3 (HD 64).
-        const bool padk = KL::kPadded && !ld_isv;
+        const bool padk = kPadK && !ld_isv;
         const int load_bytes = padk ? KL::kLoadBytes : 1024;
         const bool in_cache = j0 + dgk::kKeys <= a.ctx, in_canvas = j0 >= a.ctx;
         if ((in_cache || in_canvas) && j0 + dgk::kKeys <= kend) {   // one side of the seam
@@ -799,7 +825,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             for (int i = 0; i < kLoadsPerWave; ++i) {
                 const int trow = padk ? i + KT::kLoadsPerTile * rsub : i * R + rsub;
                 int chunk = ld_isv ? (kBf16 ? pos ^ vswz<HD>(trow) : pos)
-                                   : (KL::kPadded ? pos : (pos ^ (trow % KT::kChunks)));
+                                   : (kPadK || kPlanes ? pos : (pos ^ (trow % KT::kChunks)));
                 if (kPad) chunk = min(chunk, last_chunk);
                 __builtin_amdgcn_global_load_lds(b + ((unsigned)trow * rs + 16u * chunk),
                                                  (dgk::lds_void*)(dst + i * load_bytes), 16, 0, 0);
@@ -810,7 +836,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
                 const int trow = padk ? i + KT::kLoadsPerTile * rsub : i * R + rsub;
                 const int j = min(j0 + trow, kend - 1);
                 int chunk = ld_isv ? (kBf16 ? pos ^ vswz<HD>(trow) : pos)
-                                   : (KL::kPadded ? pos : (pos ^ (trow % KT::kChunks)));
+                                   : (kPadK || kPlanes ? pos : (pos ^ (trow % KT::kChunks)));
                 if (kPad) chunk = min(chunk, last_chunk);
                 const char* p = (j < a.ctx ? cache_base + (size_t)j * rstride_c
                                            : canvas_base + (size_t)(j - a.ctx) * rstride_v) +
@@ -822,21 +848,24 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
 
     // The first stage's loads go out before the queries are fetched, so the two overlap.
     if (!hi && nst > 0) issue_stage(0, 0);
-    constexpr bool kEmu = kKV == 0 && kF32OnBf16;   // f32 K/V on the bf16 pipe
-    float qreg[kBf16 ? 1 : HD / 2];
-    QSplit<(kBf16 || kEmu) ? HD : 16> q3;
-    if constexpr (kBf16) {
-        static_assert(!kNormQ, "16-bit K/V take normalised q");
-        load_q_bf16x3<HD>(a.q + gq * hd, valid, half, a.qmul, q3, hd);
-    } else if constexpr (kNormQ) {
-        float* qs = smem + 2 * 2 * KL::kSlotBytes / 4;
+    constexpr bool kQ3 = kBf16 || kPlanes;   // q as three bf16 terms
+    float qreg[kQ3 ? 1 : HD / 2];
+    QSplit<kQ3 ? HD : 16> q3;
+    if constexpr (kNormQ) {
+        static_assert(!kBf16, "16-bit K/V take normalised q");
+        float* qs = smem + kQOff;
         stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
         __syncthreads();
-        dgk::load_q<HD>(qs + (pair * dgk::kQuery + l32) * kQStride<HD>, true, half, 1.0f, qreg);
+        const float* qrow = qs + (pair * dgk::kQuery + l32) * kQStride<HD>;
+        if constexpr (kQ3)
+            load_q_bf16x3<HD>(qrow, true, half, 1.0f, q3, HD);
+        else
+            dgk::load_q<HD>(qrow, true, half, 1.0f, qreg);
+    } else if constexpr (kQ3) {
+        load_q_bf16x3<HD>(a.q + gq * hd, valid, half, a.qmul, q3, hd);
     } else {
         dgk::load_q<HD>(a.q + gq * hd, valid, half, a.qmul, qreg, hd);
     }
-    if constexpr (kEmu) split_q_bf16x3<HD>(qreg, q3);
     f32x16 o[TL::kGroups];
 #pragma unroll
     for (int t = 0; t < TL::kGroups; ++t)
@@ -844,13 +873,13 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
     int voff[TL::kGroups];   // bf16 V: the lane's transposed-read offsets
-    if constexpr (kBf16) vtr_offsets<HD>(lane, voff);
+    if constexpr (kBf16 || kPlanes) vtr_offsets<HD>(lane, voff);
 
     for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
+        const int buf = kPlanes ? 0 : st & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
         __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
-        if (!hi && st + 1 < nst) issue_stage(st + 1, buf ^ 1);
+        if (!kPlanes && !hi && st + 1 < nst) issue_stage(st + 1, buf ^ 1);
         if constexpr (kNormKV) {
             // Canvas rows are normalised in place before anyone reads them (the next stage's
             // loads, issued just before, stream in meanwhile).
@@ -859,24 +888,30 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
             const bool cb = jb < kend && jb + dgk::kKeys > a.ctx;
             if (ca || cb) {
                 if (ca)
-                    norm_canvas_tile<HD, kPad>(a, reinterpret_cast<float*>(tile_ptr(buf, 0, 0)),
+                    norm_canvas_tile<HD, kPad, kPadK, !kPlanes>(a, reinterpret_cast<float*>(tile_ptr(buf, 0, 0)),
                                                reinterpret_cast<float*>(tile_ptr(buf, 0, 1)), ja,
                                                kend, wave, lane, hd);
                 if (cb)
-                    norm_canvas_tile<HD, kPad>(a, reinterpret_cast<float*>(tile_ptr(buf, 1, 0)),
+                    norm_canvas_tile<HD, kPad, kPadK, !kPlanes>(a, reinterpret_cast<float*>(tile_ptr(buf, 1, 0)),
                                                reinterpret_cast<float*>(tile_ptr(buf, 1, 1)), jb,
                                                kend, wave, lane, hd);
                 __syncthreads();
             }
         }
+        if constexpr (kPlanes) {
+            // the whole workgroup splits the staged tiles, then the staging buffer is free
+            split_stage<HD>(tile_ptr(0, 0, 0), kSlot, planes, key0(st, 1) < kend ? 2 : 1, tid);
+            __syncthreads();
+            if (!hi && st + 1 < nst) issue_stage(st + 1, 0);
+        }
         const int t0 = key0(st, hi);
         if (pair_active && t0 < kend) {
             f32x16 s;
-            if constexpr (kEmu) {
+            if constexpr (kPlanes) {
                 const float shift = -dgk::ref_of(m);
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(half ? 0.0f : 1.0f, half ? 0.0f : shift,
                                                          f32x16{}, 0, 0, 0);
-                s = scores_f32_bf16x6<HD, KL::kPadded>(tile_ptr(buf, hi, 0), l32, half, q3, s);
+                s = scores_planes<HD>(Planes<HD>::at(planes, hi, 0, 0), l32, half, q3, s);
             } else if constexpr (kKV == 0) {
                 if constexpr (KL::kPadded) {
                     const float shift = -dgk::ref_of(m);
@@ -906,8 +941,8 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
                 }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            if constexpr (kEmu)
-                accumulate_pv_f32_bf16x6<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 1)), l32, half, s, o);
+            if constexpr (kPlanes)
+                accumulate_pv_planes<HD>(Planes<HD>::at(planes, hi, 1, 0), voff, s, o);
             else if constexpr (kKV == 0)
                 dgk::accumulate_pv<HD>(reinterpret_cast<const float*>(tile_ptr(buf, hi, 1)), l32, half, s, o);
             else if constexpr (kBf16)
@@ -929,7 +964,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     long long* rowg = reinterpret_cast<long long*>(smem + kPairs * dgk::kQuery * kOStride);
     if (!hi) {
         const float oscale = a.nsplit == 1 && valid ? 1.0f / ltot : 1.0f;
-        if constexpr (kBf16)
+        if constexpr (kBf16 || kPlanes)
             stage_row_blocked<HD>(smem + pair * dgk::kQuery * kOStride, l32, oscale, o, half);
         else
             dgk::stage_row<HD>(smem + pair * dgk::kQuery * kOStride, l32, oscale, o, half);
