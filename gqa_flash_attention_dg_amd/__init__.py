@@ -20,7 +20,7 @@ DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_ELAUNCH = 0, -1, -2, -3
 DG_NORM_WEIGHTED, DG_NORM_ROPE, DG_NORM_SKIP, DG_NORM_V_FROM_K = 1, 2, 4, 8
 DG_KV_F16, DG_KV_BF16 = 1, 2
 DG_NOALLOC_SCRATCH_BYTES = 32 << 20
-DG_KERNEL_NONE, DG_KERNEL_SMALL, DG_KERNEL_TILE32, DG_KERNEL_TILE16 = 0, 1, 2, 3
+DG_KERNEL_NONE, DG_KERNEL_SMALL, DG_KERNEL_TILE32 = 0, 1, 2
 
 
 class AttnPlan(ctypes.Structure):

@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (DG_KERNEL_TILE16, DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP,
+from . import (DG_KV_BF16, DG_KV_F16, DG_NORM_ROPE, DG_NORM_SKIP,
                DG_NORM_V_FROM_K, DG_NORM_WEIGHTED, dg_attn_split_gqa, dg_attn_split_gqa_kv16,
                dg_attn_split_gqa_plan,
                dg_attn_split_gqa_qkvnorm, dg_attn_split_gqa_qnorm,
@@ -38,8 +38,8 @@ KV_FORMATS = {"f16": DG_KV_F16, "bf16": DG_KV_BF16}
 
 NORM_MODES = ("auto", "fused", "in_attention", "one_launch", "separate")
 # Canvas keys per attention workgroup up to which "auto" norms k and v inside the kernel:
-# measured faster at one 32-key tile (a split key range, or a canvas of at most 32 rows), and
-# with the 16-key-tile kernel at four 16-key tiles; slower at 8 tiles of 32.
+# measured faster at one or two 32-key tiles (a split key range, or a short canvas); slower at
+# 8 tiles of 32.
 AUTO_FUSED_KEYS = 64
 
 
@@ -52,7 +52,7 @@ def auto_norm_mode(B, T, ctx, nh, nkv, hd, causal=False, cus=0, split=True):
     if B * T * nh == 0:
         return "fused"
     p = dg_attn_split_gqa_plan(B, T, ctx, nh, nkv, hd, int(causal), 0, cus)
-    tile = 16 if p.kernel == DG_KERNEL_TILE16 else 32
+    tile = 32
     nsplit = p.nsplit if split else 1
     tiles = (T + tile - 1) // tile                   # canvas tiles
     per_wg = (tiles + nsplit - 1) // nsplit          # ... met by one workgroup

@@ -989,583 +989,6 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------------------------
-// attn_tile16_kernel: the same attention for head dims above 64 when 128-query workgroups are
-// too few to fill the GPU (the DiffusionGemma-like step has 32 of them).  Splitting the key
-// range of such shapes across workgroups costs a partial result per (split, query vector) and a
-// re-read of every query block per split; this kernel halves both by owning 64 query vectors per
-// workgroup, which it keeps busy with 16-key tiles on v_mfma_f32_16x16x4f32:
-//  * 8 wavefronts = 2 query groups x 4 key parts.  Each wavefront holds 32 query vectors of its
-//    group as two 16-column blocks, and takes tile `part` of every 64-key stage; the two
-//    wavefronts of a part (on one SIMD) read the same tile.  The stage's 4 K and 4 V tiles
-//    (65 KiB at hd 128) are fetched by the group-0 wavefronts with direct global->LDS loads into
-//    a double buffer while the group-1 wavefronts start on the matrix work, one wait and one
-//    barrier per stage, as in attn_split_gqa_kernel.
-//  * Scores S^T = K Q^T per 16x16 block: lane l supplies K row l%16 (A) and query column l%16
-//    (B) at contraction index k = l/16; step 4u+i contracts head element 16u + 4k + i, so one
-//    16-byte K read feeds 4 steps of both query blocks.  Lane l then holds keys 4k..4k+3 of its
-//    query column: the softmax needs no lane exchange except on the rare rescale, where the 4
-//    lanes of a column agree on one reference.
-//  * Values O^T += V^T P^T: at step s the contraction index k stands for key 4k+s, so the B
-//    operand is the lane's own probability register s; the A operand is two 16-byte V reads
-//    (head elements 4m..4m+3 and 64+4m..64+4m+3 of row 4k+s for m = l%16) feeding 8 output
-//    blocks.  Lane l ends with head elements 16k..16k+15 and 64+16k..64+16k+15 of its column.
-//  * K tiles in LDS: wave-wide load i holds rows 2i and 2i+1 (the second with its 16-byte
-//    chunks swapped pairwise, chunk c at c^1) and loads start 1056 bytes apart, so the 16 lanes
-//    reading one chunk of 16 rows hit 16 different 16-byte bank groups (and any 8 of them, 8
-//    different groups of 32 banks), and a lane's K reads are one base plus constants.  V tiles
-//    are plain rows: 16 lanes read 256 contiguous bytes of one row.
-//  * The 4 parts of a group merge their softmax states through LDS at the end; the merged rows
-//    are restaged row-major and written whole, to `out` or, with split-KV, to the workspace.
-// kNormQ / kNormKV / kPad as in attn_split_gqa_kernel (the tile is 128 wide; hd in (64, 128]).
-namespace t16 {
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int HD = 128;
-constexpr int kGroups = 2;                      // query groups per workgroup
-constexpr int kParts = 4;                       // key tiles per stage, one per wave of a group
-constexpr int kQB = 2;                          // 16-column query blocks per wavefront
-constexpr int kTile = 16;                       // keys per tile
-constexpr int kQW = 16 * kQB;                   // query vectors per wavefront
-constexpr int kBlockQ16 = kGroups * kQW;          // query vectors per workgroup
-constexpr int kStage16 = kParts * kTile;          // keys per stage
-constexpr int kKLoad = 1056;                    // bytes from one K wave-load to the next
-constexpr int kKBytes = 8 * kKLoad;             // one K tile
-constexpr int kVBytes = kTile * HD * 4;         // one V tile
-constexpr int kPartBytes = kKBytes + kVBytes;   // K and V of one tile
-constexpr int kBufBytes = kParts * kPartBytes;  // one stage buffer
-constexpr int kQStageBytes = kBlockQ16 * kQStride<HD> * 4;
-constexpr int kMergeVals = kQB * 8 * 4 + 2 * kQB;   // o, m and l of one lane
-constexpr int kMergeBytes = kGroups * 2 * kMergeVals * 64 * 4;   // two records per group
-constexpr int kRowBytes = kBlockQ16 * kQStride<HD> * 4;   // restaged output rows
-constexpr int kRowIdxBytes = kBlockQ16 * 8;
-constexpr int kSmemA = 2 * kBufBytes > kBufBytes + kQStageBytes ? 2 * kBufBytes : kBufBytes + kQStageBytes;
-constexpr int kSmemB = kMergeBytes + kRowBytes + kRowIdxBytes;
-constexpr int kSmemBytes = kSmemA > kSmemB ? kSmemA : kSmemB;
-static_assert(kSmemBytes <= 160 * 1024, "fits the LDS of one CU");
-// Byte offset of K row r's chunk 0 in a K tile, and the XOR applied to its chunk indices.
-__device__ inline int krow(int r) { return (r >> 1) * kKLoad + (r & 1) * 512; }
-}  // namespace t16
-
-template <bool kNormQ, bool kNormKV, bool kPad>
-__device__ inline void norm_canvas_tile16(const SplitArgs& a, char* __restrict__ kt,
-                                          char* __restrict__ vt, int j0, int kend, int wave,
-                                          int lane, int hd) {
-    // One pass per tile: wavefronts 0-3 take its 16 K rows, 4-7 its 16 V rows, 16 lanes a row,
-    // lane c holding chunks c and c + 16 (hd/2 apart at hd 128: the rope partner is in-lane).
-    using namespace t16;
-    constexpr int L = 16;
-    const int R = wave * 4 + lane / L;          // 0..31
-    const bool isv = R >= kTile;                // wave-uniform
-    const int trow = R & (kTile - 1);
-    const int j = min(j0 + trow, kend - 1);
-    if (j < a.ctx) return;                      // a cache row, stored normalised
-    const int c = lane % L;
-    float* rowp = reinterpret_cast<float*>(isv ? vt + trow * HD * 4 : kt + krow(trow));
-    const int sw = isv ? 0 : (trow & 1);
-    float4 x[2];
-    float ss = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int ch = c + L * k;
-        x[k] = !kPad || 4 * ch < hd ? *reinterpret_cast<const float4*>(rowp + 4 * (ch ^ sw))
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-        ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
-    }
-    ss = group_sum<L>(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
-    const bool weighted = !isv && (a.qflags & DG_NORM_WEIGHTED);
-    const bool rope = !isv && (a.qflags & DG_NORM_ROPE);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int ch = c + L * k;
-        const float4 w = weighted && (!kPad || 4 * ch < hd)
-                             ? *reinterpret_cast<const float4*>(a.wk + 4 * ch)
-                             : make_float4(1.f, 1.f, 1.f, 1.f);
-        x[k] = make_float4(x[k].x * inv * w.x, x[k].y * inv * w.y, x[k].z * inv * w.z,
-                           x[k].w * inv * w.w);
-    }
-    if (rope) {
-        const int half_hd = hd >> 1;
-        const float* cr = a.cs + (size_t)(j - a.ctx) * 2 * hd;
-        float4 part[2];
-        if constexpr (!kPad) {
-            part[0] = x[1];
-            part[1] = x[0];
-        } else {
-            // the partner of element e is e +- hd/2: read it back from the normed row, which
-            // this wavefront writes first (its LDS accesses complete in order)
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int ch = c + L * k;
-                if (4 * ch < hd) *reinterpret_cast<float4*>(rowp + 4 * (ch ^ sw)) = x[k];
-            }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                float pv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * (c + L * k) + i;
-                    const int pe = e < half_hd ? e + half_hd : e - half_hd;
-                    pv[i] = e < hd ? rowp[4 * ((pe >> 2) ^ sw) + (pe & 3)] : 0.0f;
-                }
-                part[k] = make_float4(pv[0], pv[1], pv[2], pv[3]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int e0 = 4 * (c + L * k);
-            if (kPad && e0 >= hd) continue;
-            const float4 co = *reinterpret_cast<const float4*>(cr + e0);
-            const float4 si = *reinterpret_cast<const float4*>(cr + hd + e0);
-            const float y[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-            const float p[4] = {part[k].x, part[k].y, part[k].z, part[k].w};
-            const float cc[4] = {co.x, co.y, co.z, co.w}, sn[4] = {si.x, si.y, si.z, si.w};
-            float r[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float rot = e0 + i < half_hd ? -p[i] : p[i];
-                r[i] = y[i] * cc[i] + rot * sn[i];
-            }
-            x[k] = make_float4(r[0], r[1], r[2], r[3]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int ch = c + L * k;
-        if (!kPad || 4 * ch < hd) *reinterpret_cast<float4*>(rowp + 4 * (ch ^ sw)) = x[k];
-    }
-}
-
-// All canvas tiles of one stage (up to kParts), for hd == 128: the rows' cos|sin entries for
-// every tile are requested before any tile is computed, so the stage waits for memory once
-// rather than once per tile, and the k weight arrives in registers (wkr) loaded before the key
-// loop.  Row and lane assignment as in norm_canvas_tile16.
-__device__ inline void norm_canvas_stage16(const SplitArgs& a, char* __restrict__ sbuf,
-                                           const int (&j0)[t16::kParts], int kend, int wave,
-                                           int lane, const float4 (&wkr)[2]) {
-    using namespace t16;
-    constexpr int L = 16;
-    const int R = wave * 4 + lane / L;
-    const bool isv = R >= kTile;                // wave-uniform
-    const int trow = R & (kTile - 1);
-    const int c = lane % L;
-    const bool rope = !isv && (a.qflags & DG_NORM_ROPE);
-    const bool weighted = !isv && (a.qflags & DG_NORM_WEIGHTED);
-    constexpr int kBatch = 2;   // tiles whose table entries are in flight together
-#pragma unroll
-    for (int p0 = 0; p0 < kParts; p0 += kBatch) {
-    bool act[kBatch];
-    int jr[kBatch];
-    float4 co[kBatch][2], si[kBatch][2];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-        const int p = p0 + q;
-        const int j = min(j0[p] + trow, kend - 1);
-        act[q] = j0[p] < kend && j >= a.ctx;    // canvas rows only; the same for a row's lanes
-        jr[q] = j - a.ctx;
-        if (rope && act[q]) {
-            const float* cr = a.cs + (size_t)jr[q] * 2 * HD;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                co[q][k] = *reinterpret_cast<const float4*>(cr + 4 * (c + L * k));
-                si[q][k] = *reinterpret_cast<const float4*>(cr + HD + 4 * (c + L * k));
-            }
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-        const int p = p0 + q;
-        if (!act[q]) continue;
-        char* kt = sbuf + p * kPartBytes;
-        float* rowp = reinterpret_cast<float*>(isv ? kt + kKBytes + trow * HD * 4 : kt + krow(trow));
-        const int sw = isv ? 0 : (trow & 1);
-        float4 x[2];
-        float ss = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            x[k] = *reinterpret_cast<const float4*>(rowp + 4 * ((c + L * k) ^ sw));
-            ss += x[k].x * x[k].x + x[k].y * x[k].y + x[k].z * x[k].z + x[k].w * x[k].w;
-        }
-        ss = group_sum<L>(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float4 w = weighted ? wkr[k] : make_float4(1.f, 1.f, 1.f, 1.f);
-            x[k] = make_float4(x[k].x * inv * w.x, x[k].y * inv * w.y, x[k].z * inv * w.z,
-                               x[k].w * inv * w.w);
-        }
-        if (rope) {   // chunk c + 16 is chunk c's partner, hd/2 away: both in this lane
-            const float4 y0 = x[0], y1 = x[1];
-            x[0] = make_float4(y0.x * co[q][0].x - y1.x * si[q][0].x, y0.y * co[q][0].y - y1.y * si[q][0].y,
-                               y0.z * co[q][0].z - y1.z * si[q][0].z, y0.w * co[q][0].w - y1.w * si[q][0].w);
-            x[1] = make_float4(y1.x * co[q][1].x + y0.x * si[q][1].x, y1.y * co[q][1].y + y0.y * si[q][1].y,
-                               y1.z * co[q][1].z + y0.z * si[q][1].z, y1.w * co[q][1].w + y0.w * si[q][1].w);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            *reinterpret_cast<float4*>(rowp + 4 * ((c + L * k) ^ sw)) = x[k];
-    }
-    }
-}
-
-template <bool kNormQ, bool kNormKV, bool kPad>
-__global__ void __launch_bounds__(512) attn_tile16_kernel(SplitArgs a) {
-    using namespace t16;
-    using dgk::kHeadroom;
-    __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-    const int hd = kPad ? a.hd : HD;
-
-    const int lid = xcd_remap(blockIdx.x, a.nblocks, a.nxcd);
-    const int qb = lid % a.qblocks;
-    const int rest = lid / a.qblocks;
-    const int split = rest % a.nsplit;
-    const int bk = rest / a.nsplit;            // b * nkv + kv
-    const int kv = bk % a.nkv;
-    const int b = bk / a.nkv;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
-    const int grp = wave >> 2, part = wave & 3;
-
-    const int nq = a.T * a.G;                  // query vectors of this (b, kv)
-    const int wfirst = qb * kBlockQ16 + grp * kQW;
-    const bool wave_active = wfirst < nq;
-    int qv[kQB], row[kQB];
-    bool valid[kQB];
-    size_t gq[kQB];
-#pragma unroll
-    for (int c = 0; c < kQB; ++c) {
-        qv[c] = wfirst + 16 * c + l16;
-        valid[c] = qv[c] < nq;
-        row[c] = valid[c] ? qv[c] / a.G : 0;
-        gq[c] = ((size_t)b * a.T + row[c]) * a.nh + kv * a.G + (valid[c] ? qv[c] % a.G : 0);
-    }
-    const int row_min = wave_active ? wfirst / a.G : 0;
-
-    const int S = a.ctx + a.T;
-    int kend = S;
-    if (a.causal) {
-        const int last = min(nq - 1, qb * kBlockQ16 + kBlockQ16 - 1) / a.G;
-        kend = min(S, a.ctx + last + 1);
-    }
-    // Splits divide the key range in whole 16-key tiles (so they differ by at most one tile); a
-    // stage takes 4 tiles, and a split's last stage may hold fewer.
-    const int ntile = (kend + kTile - 1) / kTile;
-    const int tile_begin = (int)((long long)split * ntile / a.nsplit);
-    const int tile_end = (int)((long long)(split + 1) * ntile / a.nsplit);
-    int ntl;
-    if constexpr (kNormKV) {                   // round robin: tiles split, split + nsplit, ...
-        ntl = split < ntile ? (ntile - split + a.nsplit - 1) / a.nsplit : 0;
-    } else {
-        kend = min(kend, tile_end * kTile);
-        ntl = tile_end - tile_begin;
-    }
-    const int nst = (ntl + kParts - 1) / kParts;
-    auto key0 = [&](int st, int p) {
-        if constexpr (kNormKV) return (split + a.nsplit * (kParts * st + p)) * kTile;
-        else return (tile_begin + kParts * st + p) * kTile;
-    };
-
-    const char* kcb = reinterpret_cast<const char*>(a.kc) + (size_t)bk * a.ctx * hd * 4;
-    const char* vcb = reinterpret_cast<const char*>(a.vc) + (size_t)bk * a.ctx * hd * 4;
-    const char* kb = reinterpret_cast<const char*>(a.k) + ((size_t)b * a.T * a.nkv + kv) * hd * 4;
-    const char* vb = reinterpret_cast<const char*>(a.v) + ((size_t)b * a.T * a.nkv + kv) * hd * 4;
-    const unsigned rstride_c = (unsigned)hd * 4, rstride_v = (unsigned)a.nkv * hd * 4;
-    auto kt_ptr = [&](int buf, int p) { return smem + buf * kBufBytes + p * kPartBytes; };
-
-    // Loads: the group-0 wavefront of part p fetches K and V of tile p (8 wave-wide loads each:
-    // load i, rows 2i and 2i + 1).  Padded head dims repeat the last valid chunk of a row.
-    const int hrow = lane >> 5, pos = lane & 31;
-    const int last_chunk = hd / 4 - 1;
-    const int kchunk = kPad ? min(pos ^ hrow, last_chunk) : (pos ^ hrow);
-    const int vchunk = kPad ? min(pos, last_chunk) : pos;
-    auto issue_tile = [&](int st, int buf) {
-        const int j0 = key0(st, part);
-        if (j0 >= kend) return;
-        char* kd = kt_ptr(buf, part);
-        char* vd = kd + kKBytes;
-        const bool in_cache = j0 + kTile <= a.ctx, in_canvas = j0 >= a.ctx;
-        if ((in_cache || in_canvas) && j0 + kTile <= kend) {
-            const char* kbase = in_cache ? kcb + (size_t)j0 * rstride_c : kb + (size_t)(j0 - a.ctx) * rstride_v;
-            const char* vbase = in_cache ? vcb + (size_t)j0 * rstride_c : vb + (size_t)(j0 - a.ctx) * rstride_v;
-            const unsigned rs = in_cache ? rstride_c : rstride_v;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_global_load_lds(kbase + ((unsigned)(2 * i + hrow) * rs + 16u * kchunk),
-                                                 (dgk::lds_void*)(kd + i * kKLoad), 16, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_global_load_lds(vbase + ((unsigned)(2 * i + hrow) * rs + 16u * vchunk),
-                                                 (dgk::lds_void*)(vd + i * 1024), 16, 0, 0);
-        } else {   // straddles the seam or the end: per-row addresses, rows past the end repeat
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = min(j0 + 2 * i + hrow, kend - 1);
-                const size_t off = j < a.ctx ? (size_t)j * rstride_c : (size_t)(j - a.ctx) * rstride_v;
-                const char* kp = (j < a.ctx ? kcb : kb) + off;
-                const char* vp = (j < a.ctx ? vcb : vb) + off;
-                __builtin_amdgcn_global_load_lds(kp + 16u * kchunk, (dgk::lds_void*)(kd + i * kKLoad), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vp + 16u * vchunk, (dgk::lds_void*)(vd + i * 1024), 16, 0, 0);
-            }
-        }
-    };
-
-    if (grp == 0 && nst > 0) issue_tile(0, 0);
-    // Queries in the B-operand order: qreg[c][4u + i] = q[column c*16 + l16][16u + 4kk + i].
-    float qreg[kQB][32];
-    if constexpr (kNormQ) {
-        float* qs = reinterpret_cast<float*>(smem + kBufBytes);   // buffer 1, free until stage 1
-        stage_q_normed<HD, kBlockQ16>(a, qs, b, kv, qb, wave, lane, hd);
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) {
-            const float* qr = qs + (grp * kQW + 16 * c + l16) * kQStride<HD> + 4 * kk;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float4 t = *reinterpret_cast<const float4*>(qr + 16 * u);
-                qreg[c][4 * u] = t.x; qreg[c][4 * u + 1] = t.y; qreg[c][4 * u + 2] = t.z; qreg[c][4 * u + 3] = t.w;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) {
-            const float* qr = a.q + gq[c] * hd + 4 * kk;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const bool in = valid[c] && 16 * u + 4 * kk < hd;
-                const float4 t = in ? *reinterpret_cast<const float4*>(qr + 16 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
-                qreg[c][4 * u] = t.x * a.qmul; qreg[c][4 * u + 1] = t.y * a.qmul;
-                qreg[c][4 * u + 2] = t.z * a.qmul; qreg[c][4 * u + 3] = t.w * a.qmul;
-            }
-        }
-    }
-    f32x4 o[kQB][8];
-#pragma unroll
-    for (int c = 0; c < kQB; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[kQB], lsum[kQB];
-#pragma unroll
-    for (int c = 0; c < kQB; ++c) { m[c] = -INFINITY; lsum[c] = 0.0f; }
-    // the k weight of this lane's two chunks (used by the k/v norm of canvas tiles, hd 128)
-    float4 wkr[2] = {make_float4(1.f, 1.f, 1.f, 1.f), make_float4(1.f, 1.f, 1.f, 1.f)};
-    if (kNormKV && !kPad && wave < 4 && (a.qflags & DG_NORM_WEIGHTED)) {
-        wkr[0] = *reinterpret_cast<const float4*>(a.wk + 4 * (lane % 16));
-        wkr[1] = *reinterpret_cast<const float4*>(a.wk + 4 * (lane % 16 + 16));
-    }
-    const int kboff = t16::krow(l16) + 16 * (kk ^ (l16 & 1));   // this lane's K row chunk
-    const int vboff = 16 * l16;
-
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
-        __syncthreads();                 // ...everyone's; and stage st-1 is fully consumed
-        if (grp == 0 && st + 1 < nst) issue_tile(st + 1, buf ^ 1);
-        if constexpr (kNormKV) {
-            bool any = false;
-            int j0s[kParts];
-#pragma unroll
-            for (int p = 0; p < kParts; ++p) {
-                j0s[p] = key0(st, p);
-                any = any || (j0s[p] < kend && j0s[p] + kTile > a.ctx);
-            }
-            if (any) {
-                if constexpr (kPad) {
-#pragma unroll
-                    for (int p = 0; p < kParts; ++p)
-                        if (j0s[p] < kend && j0s[p] + kTile > a.ctx)
-                            norm_canvas_tile16<kNormQ, kNormKV, kPad>(a, kt_ptr(buf, p), kt_ptr(buf, p) + kKBytes,
-                                                                      j0s[p], kend, wave, lane, hd);
-                } else {
-                    norm_canvas_stage16(a, kt_ptr(buf, 0), j0s, kend, wave, lane, wkr);
-                }
-                __syncthreads();
-            }
-        }
-        const int t0 = key0(st, part);
-        if (!(wave_active && t0 < kend)) continue;
-        const char* kt = kt_ptr(buf, part);
-        const char* vt = kt + kKBytes;
-        // All 8 K reads of the tile go out before the first MFMA: one LDS wait per tile.
-        f32x4 kf[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) kf[u] = *reinterpret_cast<const f32x4*>(kt + kboff + 64 * u);
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the matrix work
-        f32x4 s[kQB];
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) s[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < kQB; ++c)
-                    s[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[u][i], qreg[c][4 * u + i], s[c], 0, 0, 0);
-        }
-        // score - reference; masked keys (past the end, or causal) -inf, in a block of its own
-        // so that the common path has no per-key branches
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) {
-            const float ref = dgk::ref_of(m[c]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[c][r] -= ref;
-        }
-        if (t0 + kTile > kend || (a.causal && t0 + kTile - 1 - a.ctx > row_min)) {
-#pragma unroll
-            for (int c = 0; c < kQB; ++c)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = t0 + 4 * kk + r;
-                    if (j >= kend || (a.causal && j - a.ctx > row[c])) s[c][r] = -INFINITY;
-                }
-        }
-        // The tile's V operands (rows 4kk + step, head elements 4*l16.. and 64 + 4*l16..) are
-        // read now, so that their latency passes under the softmax.
-        f32x4 vf[8];
-#pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx) {
-            const char* vr = vt + (4 * kk + sidx) * HD * 4 + vboff;
-            vf[2 * sidx] = *reinterpret_cast<const f32x4*>(vr);
-            vf[2 * sidx + 1] = *reinterpret_cast<const f32x4*>(vr + 256);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Online softmax (flash_core.hpp's rule: the reference moves only when a score exceeds
-        // it by more than kHeadroom, or while it is still -inf).
-        float lmax = s[0][0];
-#pragma unroll
-        for (int c = 0; c < kQB; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, s[c][r]);
-        bool unset = false;
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) unset = unset || m[c] == -INFINITY;
-        if (__any(lmax > kHeadroom || unset)) {
-#pragma unroll
-            for (int c = 0; c < kQB; ++c) {
-                float tmax = fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3]));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));   // the 4 lanes of a query column
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                const float ref = dgk::ref_of(m[c]);
-                const float m_new = fmaxf(m[c], ref + tmax);
-                const float nref = dgk::ref_of(m_new);
-                const float corr = dgk::fast_exp2(m[c] - nref);
-                const float shift = ref - nref;
-                lsum[c] *= corr;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) o[c][j] *= corr;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s[c][r] += shift;
-                m[c] = m_new;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) {
-            float ps = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s[c][r] = dgk::fast_exp2(s[c][r]);
-                ps += s[c][r];
-            }
-            lsum[c] += ps;
-        }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx) {
-            const f32x4 va = vf[2 * sidx];
-            const f32x4 vb2 = vf[2 * sidx + 1];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int c = 0; c < kQB; ++c) {
-                    o[c][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[j], s[c][sidx], o[c][j], 0, 0, 0);
-                    o[c][4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb2[j], s[c][sidx], o[c][4 + j], 0, 0, 0);
-                }
-        }
-    }
-
-    // Merge the 4 parts of each group in two rounds through LDS (parts 1 and 3 into 0 and 2,
-    // then 2 into 0), 16-byte accesses laid out [value][lane] so a wavefront's accesses are
-    // contiguous.  Lane-wise: the 4 lanes of a query column share one reference m in each part.
-    float* rows = reinterpret_cast<float*>(smem + kMergeBytes);
-    long long* rowg = reinterpret_cast<long long*>(smem + kMergeBytes + kRowBytes);
-    auto merge_slot = [&](int g, int p) {   // scratch of the wave (group g, part p) handing over
-        return reinterpret_cast<f32x4*>(smem) + (size_t)((g * 2 + (p >> 1)) * (kMergeVals / 4)) * 64 + lane;
-    };
-    auto put = [&](f32x4* d) {
-#pragma unroll
-        for (int c = 0; c < kQB; ++c)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) d[(c * 8 + j) * 64] = o[c][j];
-        d[kQB * 8 * 64] = f32x4{m[0], m[kQB - 1], lsum[0], lsum[kQB - 1]};
-    };
-    auto take = [&](const f32x4* d) {
-        const f32x4 ml = d[kQB * 8 * 64];
-        const float m2[2] = {ml[0], ml[1]}, l2[2] = {ml[2], ml[3]};
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) {
-            const float mn = fmaxf(m[c], m2[c]);
-            const float mu = mn == -INFINITY ? 0.0f : mn;
-            const float ca = dgk::fast_exp2(m[c] - mu), cb = dgk::fast_exp2(m2[c] - mu);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[c][j] = o[c][j] * ca + d[(c * 8 + j) * 64] * cb;
-            lsum[c] = lsum[c] * ca + l2[c] * cb;
-            m[c] = mn;
-        }
-    };
-    static_assert(kQB == 2 && kMergeVals == kQB * 32 + 4, "merge record: o, then (m0, m1, l0, l1)");
-    __syncthreads();   // every wave is done with the stage buffers
-    if ((part & 1) && wave_active) put(merge_slot(grp, part));
-    __syncthreads();
-    if (!(part & 1) && wave_active) take(merge_slot(grp, part + 1));
-    __syncthreads();   // part 0's slot is free of part 1's record (read by part 0 above)
-    if (part == 2 && wave_active) put(merge_slot(grp, 0));
-    __syncthreads();
-    if (part == 0) {
-        if (wave_active) take(merge_slot(grp, 0));
-        // Denominators: the 4 lanes of a column summed disjoint keys.
-#pragma unroll
-        for (int c = 0; c < kQB; ++c) {
-            float lt = lsum[c] + __shfl_xor(lsum[c], 16);
-            lt += __shfl_xor(lt, 32);
-            const int rl = grp * kQW + 16 * c + l16;     // row of the block
-            const bool ok = wave_active && valid[c];
-            const float sc = a.nsplit == 1 && ok ? 1.0f / lt : 1.0f;
-            float* dst = rows + rl * kQStride<HD>;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = 16 * kk + 4 * r;
-                *reinterpret_cast<float4*>(dst + e) =
-                    make_float4(o[c][0][r] * sc, o[c][1][r] * sc, o[c][2][r] * sc, o[c][3][r] * sc);
-                *reinterpret_cast<float4*>(dst + 64 + e) =
-                    make_float4(o[c][4][r] * sc, o[c][5][r] * sc, o[c][6][r] * sc, o[c][7][r] * sc);
-            }
-            if (kk == 0) {
-                rowg[rl] = ok ? (long long)gq[c] : -1;
-                dst[HD] = m[c];      // the split's (m, l), stored with the row below: a store
-                dst[HD + 1] = lt;    // here would hold up the barrier until it completes
-            }
-        }
-    }
-    __syncthreads();
-    float* obase = a.nsplit == 1 ? a.out : a.ws + (size_t)split * a.nqtot * hd;
-    constexpr int kChunksO = HD / 4;
-    constexpr int kRowsPerPass = 512 / kChunksO;
-#pragma unroll
-    for (int r0 = 0; r0 < kBlockQ16; r0 += kRowsPerPass) {
-        const int rloc = r0 + tid / kChunksO, c = tid % kChunksO;
-        const long long g = rowg[rloc];
-        if (g < 0) continue;
-        if (!kPad || 4 * c < hd)
-            *reinterpret_cast<float4*>(obase + (size_t)g * hd + 4 * c) =
-                *reinterpret_cast<const float4*>(rows + rloc * kQStride<HD> + 4 * c);
-        if (a.nsplit > 1 && c == 0) {
-            float* wm = a.ws + (size_t)a.nsplit * a.nqtot * hd;
-            wm[(size_t)split * a.nqtot + g] = rows[rloc * kQStride<HD> + HD];
-            wm[(size_t)(a.nsplit + split) * a.nqtot + g] = rows[rloc * kQStride<HD> + HD + 1];
-        }
-    }
-}
-
 // Short key sets (ctx + T <= 8, e.g. the depformer's causal frames of 8 steps): there is too
 // little work per query for matrix tiles, and the call is HBM-bound.  One wavefront per
 // (batch entry, q head): lane (r, c) = (lane / 8, lane % 8) owns query row r and the c-th
@@ -1841,11 +1264,10 @@ __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restr
 // Launch plan shared by the workspace query and the launch: which kernel, how many query
 // vectors per workgroup, and how many key-range splits, for a device with `cus` compute units.
 //  * ctx + T <= 8: attn_small_kernel.
-//  * Otherwise attn_split_gqa_kernel (128 query vectors per workgroup), except for head dims
-//    above 64 with f32 K/V whose 128-query plan leaves CUs idle: attn_tile16_kernel (64 query
-//    vectors per workgroup) when that fills more of them.
+//  * Otherwise attn_split_gqa_kernel (128 query vectors per workgroup).
 // A shape with fewer workgroups than CUs splits its key range (not causal calls), at least two
-// 64-key stages per split.
+// 64-key stages per split.  (Fewer, longer splits were measured slower on the DiffusionGemma-like
+// step: 36.3 us per step at 4 to 5 splits against 29.6 us at 8.)
 struct Plan {
     int kernel = DG_KERNEL_TILE32;
     int blockq = kBlockQ;
@@ -1878,23 +1300,6 @@ Plan plan(int batch, int T, int ctx, int nh, int nkv, int hd, int causal, int kv
     long long blocks = (long long)batch * nkv * p.qblocks;
     p.nsplit = split_count(blocks, S, causal, cus);
     p.nblocks = blocks * p.nsplit;
-    // Where the 128-query plan leaves CUs idle (its splits are capped by the key count), the
-    // 64-query tile16 kernel fills more of them with the same keys per split.  Measured on the
-    // DiffusionGemma-like layer stack: its 512-entry sliding layers (192 of 256 CUs busy with
-    // 128-query workgroups) gain; the 1024-entry cache step, already full, is faster with the
-    // 32-key tiles.
-    if (hd > 64 && kv == 0 && p.nblocks < cus) {
-        const int q16 = (int)(((long long)T * G + t16::kBlockQ16 - 1) / t16::kBlockQ16);
-        const long long b16 = (long long)batch * nkv * q16;
-        const int n16 = split_count(b16, S, causal, cus);
-        if (b16 * n16 > p.nblocks && b16 * n16 <= cus) {
-            p.kernel = DG_KERNEL_TILE16;
-            p.blockq = t16::kBlockQ16;
-            p.qblocks = q16;
-            p.nsplit = n16;
-            p.nblocks = b16 * n16;
-        }
-    }
     if (p.nsplit > 1)
         p.ws_bytes = (size_t)p.nsplit * batch * T * nh * (size_t)(hd + 2) * sizeof(float);
     return p;
@@ -1998,13 +1403,6 @@ SplitKernel split_norm_variant(int hd, int norm) {
 }
 
 // kv: 0 (f32), DG_KV_F16 or DG_KV_BF16; the 16-bit variants take no in-kernel norm.
-// The 16-key-tile kernel (f32 K/V, 64 < hd <= 128).
-SplitKernel pick_tile16(int hd, int norm) {
-    const bool pad = hd != 128;
-    if (norm == 2) return pad ? attn_tile16_kernel<true, true, true> : attn_tile16_kernel<true, true, false>;
-    if (norm == 1) return pad ? attn_tile16_kernel<true, false, true> : attn_tile16_kernel<true, false, false>;
-    return pad ? attn_tile16_kernel<false, false, true> : attn_tile16_kernel<false, false, false>;
-}
 
 SplitKernel pick_split(int hd, int norm, int kv) {
     if (kv == DG_KV_F16) return hd > 64 ? split_variant<128, 0, DG_KV_F16>(hd) : split_variant<64, 0, DG_KV_F16>(hd);
@@ -2136,7 +1534,7 @@ int attn_call(const char* fn, const float* q, const void* kc, const void* vc, co
         hipLaunchKernelGGL(pick_small(hd, norm, kv), dim3((unsigned)blocks), dim3(256), 0, s, a, units);
         return dg::launch_status(fn);
     }
-    auto* kern = p.kernel == DG_KERNEL_TILE16 ? pick_tile16(hd, norm) : pick_split(hd, norm, kv);
+    auto* kern = pick_split(hd, norm, kv);
     hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(512), 0, s, a);
     if (p.nsplit > 1) {
         const size_t total = (size_t)batch * T * nh;

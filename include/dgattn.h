@@ -159,8 +159,6 @@ size_t dg_attn_split_gqa_workspace_size(int batch, int T, int ctx, int nh, int n
 #define DG_KERNEL_NONE 0     /* empty output: nothing is launched */
 #define DG_KERNEL_SMALL 1    /* ctx + T <= 8: one wavefront per (batch entry, q head) */
 #define DG_KERNEL_TILE32 2   /* 32-key tiles, 128 query vectors per workgroup */
-#define DG_KERNEL_TILE16 3   /* 16-key tiles, 64 query vectors per workgroup (64 < hd <= 128,
-                                f32 K/V, shapes too small to fill the device otherwise) */
 
 /* How a split-GQA attention call is launched (see dg_attn_split_gqa_plan). */
 typedef struct dg_attn_plan {
@@ -214,7 +212,7 @@ int dg_attn_split_gqa_plan(int batch, int T, int ctx, int nh, int nkv, int hd, i
  * within 2^-27 of it) and each product q.k and p.v as the six leading bf16 x bf16 products,
  * each exact in f32, summed in f32 on the bf16 matrix pipe: every product is within about
  * 2^-25 of its value (f32 rounds a product to 2^-24), and the large score terms are summed
- * apart from the small ones.  The short-key-set and 16-key tile kernels use f32 arithmetic.
+ * apart from the small ones.  The short-key-set kernel (ctx + T <= 8) uses f32 arithmetic.
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
  * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, a tensor pointer
  * that is not 16-byte aligned, or a workspace pointer that is misaligned or has

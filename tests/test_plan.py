@@ -38,14 +38,13 @@ EXPECTED = [
     # the long cache fills 256 CUs without a split
     ((4, 256, 8192, 32, 8, 128), 256, (dg.DG_KERNEL_TILE32, 128, 1, 256)),
     ((4, 256, 8192, 32, 8, 128), 32, (dg.DG_KERNEL_TILE32, 128, 1, 256)),
-    # a sliding layer (768 keys): 128-query workgroups cap at 6 splits (192 of 256 CUs), the
-    # 64-query 16-key-tile kernel fills all 256 with 4
-    ((1, 256, 512, 16, 8, 128), 256, (dg.DG_KERNEL_TILE16, 64, 4, 256)),
+    # a sliding layer (768 keys): 128-query workgroups cap at 6 splits (192 of 256 CUs)
+    ((1, 256, 512, 16, 8, 128), 256, (dg.DG_KERNEL_TILE32, 128, 6, 192)),
     ((1, 256, 512, 16, 8, 128), 32, (dg.DG_KERNEL_TILE32, 128, 1, 32)),
     # the global hd-96 layer (G = 4): 32 workgroups of 128, 8 splits fill the device
     ((1, 256, 1024, 16, 4, 96), 256, (dg.DG_KERNEL_TILE32, 128, 8, 256)),
-    # causal calls do not split: 32 workgroups of 128 leave CUs idle, 64 of 64 fewer
-    ((1, 256, 1024, 16, 8, 128, 1), 256, (dg.DG_KERNEL_TILE16, 64, 1, 64)),
+    # causal calls do not split
+    ((1, 256, 1024, 16, 8, 128, 1), 256, (dg.DG_KERNEL_TILE32, 128, 1, 32)),
     # 16-bit K/V stay on the 32-key tiles
     ((1, 256, 1024, 16, 8, 128, 0, dg.DG_KV_BF16), 256, (dg.DG_KERNEL_TILE32, 128, 8, 256)),
     # hd 64 stays on the 32-key tiles; short key sets take the small kernel
@@ -87,8 +86,6 @@ def test_plan_invariants_over_shapes(cus):
                                 assert p.nsplit == 1
                             if p.nsplit > 1:   # a split only where the device would idle
                                 assert p.workgroups // p.nsplit < cus
-                            if p.kernel == dg.DG_KERNEL_TILE16:
-                                assert hd > 64 and p.workgroups <= cus
 
 
 def test_workspace_size_covers_both_kv_formats():
