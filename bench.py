@@ -393,8 +393,16 @@ class RelposWork:
         self.ws_bytes = dg.relpos_flash_attn_windows_workspace_size(
             self.nwin, case.gh, case.gw, case.heads, case.hd)
         self.ws = torch.empty((max(self.ws_bytes, 4) // 4,), device="cuda")
-        self.flops = self.nwin * (case.heads * n * n * 4 * case.hd + (
-            case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0))
+        attn = self.nwin * case.heads * n * n * 4 * case.hd
+        bias = self.nwin * case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0
+        self.flops = attn + bias
+        # grids up to 16 x 16 run the windowed kernel (f32 MFMA); larger grids the 8-wavefront
+        # grid kernel, whose q.k and p.v take six bf16 products each; the bias rows are f32 MFMA
+        win = case.gh <= 16 and case.gw <= 16
+        self.mfma_peak, self.mfma_peak_name = combined_ceiling(
+            [(attn, (PEAK_F32_MFMA, "f32 MFMA") if win else
+              (PEAK_BF16_MFMA / 6, "bf16 MFMA / 6 (six bf16 products per f32 product)"))] +
+            ([(bias, (PEAK_F32_MFMA, "f32 MFMA"))] if bias else []))
         # every input read once, the output written once (the bias rows it keeps in its
         # workspace are the method's own intermediate, not counted)
         self.attn_bytes = 4 * (self.nwin * (n * 3 * W + n * W) +

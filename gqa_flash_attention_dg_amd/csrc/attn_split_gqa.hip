@@ -43,11 +43,13 @@
 // that share K/V are placed on the same XCD so its L2 serves the re-reads.
 #include <mutex>
 
+#include "bf16x3.hpp"
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
 namespace {
 
+using namespace bf3;
 using dgk::f32x16;
 constexpr int kWaves = 8;
 constexpr int kPairs = 4;
@@ -178,88 +180,15 @@ __device__ inline void accumulate_pv16(const char* __restrict__ vs, int l32, int
     }
 }
 
-// bf16 K/V on the bf16 matrix pipe.  A product of two bf16 values is exact in f32, and an f32
-// value x is the sum of three bf16 values to within 2^-27 |x|: hi = bf16(x), mid = bf16(x - hi),
-// lo = bf16(x - hi - mid), rounding to nearest (both differences are exact: each is a multiple
-// of x's last significand bit and at most 2^-9 of the value it is taken from).  So with x = q
-// (scores) or x = p (the value product) each MFMA step runs three v_mfma_f32_32x32x16_bf16, one
-// per term, with exact products and the sums in f32: the f32 path's arithmetic up to a 2^-27
-// relative change of one operand and the summation order, at about a fifth of the matrix-pipe
-// time of v_mfma_f32_32x32x2f32 on the same tile.  The k-slots a lane supplies are the same for
-// the A and the B operand, so which 8 of the 16 a lane half holds does not matter; the 32x32
-// accumulator layout is that of the f32 instruction.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// The weight pairs (-1, 0) and (0, -1) of split_bf16x3, as register values: the empty asm keeps
-// the compiler from encoding them as an inline constant, which the hardware would widen as an
-// f32 constant rather than place in the low half.
-struct SplitWeights {
-    bf16x2 n0, n1;
-    __device__ SplitWeights() {
-        unsigned w0 = 0x0000bf80u, w1 = 0xbf800000u;
-        asm volatile("" : "+s"(w0), "+s"(w1));
-        n0 = __builtin_bit_cast(bf16x2, w0);
-        n1 = __builtin_bit_cast(bf16x2, w1);
-    }
-};
-
-// The three terms of x0 and x1, each pair packed in one dword (x0 in the low half).  The
-// differences come from v_dot2c_f32_bf16 with weights (-1, 0) and (0, -1): x - term in one
-// instruction, exact since the result is representable.
-__device__ inline void split_bf16x3(float x0, float x1, const SplitWeights& w, unsigned& hi,
-                                    unsigned& mid, unsigned& lo) {
-    const bf16x2 n0 = w.n0, n1 = w.n1;
-    const bf16x2 h = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
-    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, n0, x0, false);
-    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, n1, x1, false);
-    const bf16x2 m = __builtin_convertvector((f32x2){r0, r1}, bf16x2);
-    const float t0 = __builtin_amdgcn_fdot2_f32_bf16(m, n0, r0, false);
-    const float t1 = __builtin_amdgcn_fdot2_f32_bf16(m, n1, r1, false);
-    const bf16x2 l = __builtin_convertvector((f32x2){t0, t1}, bf16x2);
-    hi = __builtin_bit_cast(unsigned, h);
-    mid = __builtin_bit_cast(unsigned, m);
-    lo = __builtin_bit_cast(unsigned, l);
-}
-
-// The lane's query operand in three bf16 terms: step st, k-slot e of lane half `half` is head
-// element 16*st + 8*half + e, times mul; elements at or past lim (a multiple of 4) are zero.
-template <int HD>
-struct QSplit {
-    u32x4 h[HD / 16], m[HD / 16], l[HD / 16];
-};
-
-template <int HD>
-__device__ inline void load_q_bf16x3(const float* __restrict__ qrow, bool valid, int half,
-                                     float mul, QSplit<HD>& q, int lim) {
-    const SplitWeights w;
-#pragma unroll
-    for (int st = 0; st < HD / 16; ++st) {
-        float x[8];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int d0 = 16 * st + 8 * half + 4 * c;
-            const float4 v = valid && d0 < lim ? *reinterpret_cast<const float4*>(qrow + d0)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            x[4 * c + 0] = v.x * mul;
-            x[4 * c + 1] = v.y * mul;
-            x[4 * c + 2] = v.z * mul;
-            x[4 * c + 3] = v.w * mul;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            unsigned th, tm, tl;
-            split_bf16x3(x[2 * i], x[2 * i + 1], w, th, tm, tl);
-            q.h[st][i] = th;
-            q.m[st][i] = tm;
-            q.l[st][i] = tl;
-        }
-    }
-}
+// f32 K/V on the bf16 pipe.  With both operands split in three terms, a = ah + am + al and
+// b = bh + bm + bl, the product a*b is taken as the six terms down to order 2^-18 (ah*bh,
+// ah*bm, am*bh, ah*bl, al*bh, am*bm); the three dropped ones (am*bl, al*bm, al*bl) and the
+// splits' own 2^-27 leave each product within about 2^-25 of its value, inside f32's rounding
+// of a product (2^-24), so the result stays on the f32 bar.  Six v_mfma_f32_32x32x16_bf16 per
+// step are 2.7 times less matrix-pipe time than v_mfma_f32_32x32x2f32.  The K and V tiles are
+// split once per stage by the whole workgroup (split_stage), q once per wavefront, and the
+// probabilities per tile (7 vector instructions per pair of values).  false: f32 MFMA.
+constexpr bool kF32OnBf16 = true;
 
 // S^T += K Q^T from a bf16 K tile (rows of HD elements, 16-byte chunks swizzled as in
 // scores_from16): step st reads chunk 2*st + half of the lane's key row, 8 elements at once.
@@ -276,42 +205,6 @@ __device__ inline f32x16 scores_bf16x3(const char* __restrict__ ks, int l32, int
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(q.l[st]), s, 0, 0, 0);
     }
     return s;
-}
-
-// f32 K/V on the bf16 pipe.  With both operands split in three terms, a = ah + am + al and
-// b = bh + bm + bl, the product a*b is taken as the six terms down to order 2^-18 (ah*bh,
-// ah*bm, am*bh, ah*bl, al*bh, am*bm); the three dropped ones (am*bl, al*bm, al*bl) and the
-// splits' own 2^-27 leave each product within about 2^-25 of its value, inside f32's rounding
-// of a product (2^-24), so the result stays on the f32 bar.  Six v_mfma_f32_32x32x16_bf16 per
-// step are 2.7 times less matrix-pipe time than v_mfma_f32_32x32x2f32.  The K and V tiles are
-// split once per stage by the whole workgroup (split_stage), q once per wavefront, and the
-// probabilities per tile (7 vector instructions per pair of values).  false: f32 MFMA.
-constexpr bool kF32OnBf16 = true;
-
-// The leading products go to `c`, the five smaller ones to `d`: kept apart, the corrections
-// are summed at their own magnitude (about 2^-8 of c's), so only the leading chain rounds at
-// the full magnitude of the result.
-__device__ inline void mfma_bf16x6(u32x4 ah, u32x4 am, u32x4 al, u32x4 bh, u32x4 bm, u32x4 bl,
-                                   f32x16& c, f32x16& d) {
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(am), as_bf16x8(bm), d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bh), d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bl), d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(am), as_bf16x8(bh), d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bm), d, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bh), c, 0, 0, 0);
-}
-
-// Splits 8 f32 values into the three bf16x8 operands of one MFMA step.
-__device__ inline void split8(const float (&x)[8], const SplitWeights& w, u32x4& h, u32x4& m,
-                              u32x4& l) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        unsigned th, tm, tl;
-        split_bf16x3(x[2 * i], x[2 * i + 1], w, th, tm, tl);
-        h[i] = th;
-        m[i] = tm;
-        l[i] = tl;
-    }
 }
 
 // bf16 V tiles sit in LDS row-major with each row's 16-byte chunks permuted, chunk c of key row

@@ -19,6 +19,7 @@
 // through the MFMA accumulator's starting value (see relpos_flash_kernel).  64-query
 // workgroups give 768 workgroups at the 64x64-grid, 12-head shape: three full rounds on an
 // MI355X's 256 CUs.
+#include "bf16x3.hpp"
 #include "dg_common.hpp"
 #include "flash_core.hpp"
 
@@ -556,6 +557,14 @@ __host__ __device__ inline Tiling make_tiling(int gh, int gw) {
     return t;
 }
 
+// Scores and the value product of the 8-wavefront grid kernels run on the bf16 matrix pipe: q
+// once, and each K and V value as it is read from LDS, taken as three bf16 terms, every product
+// as six exact bf16 products summed in f32 (bf16x3.hpp); within about 2^-25 of each f32
+// product.  Two query groups share each tile, so each value is split twice.  The bias terms
+// stay on f32 MFMA, and so does the 4-wavefront shape (three workgroups per CU leave it no
+// registers for the split).  false: f32 MFMA throughout.
+constexpr bool kRelF32OnBf16 = true;
+
 // kFull: every tile holds 32 keys (no padding slots, no short last tile); kOneShift: the height
 // bias takes one MFMA step (at most two grid rows per tile).
 // kPatch: the workgroup's 64 queries are an 8 x 8 patch of the grid (both sides multiples of
@@ -779,6 +788,9 @@ __global__ void __launch_bounds__(64 * kWavesT)
 
     float qreg[HD / 2];
     dgk::load_q<HD>(qrow, valid, half, a.qmul, qreg);
+    constexpr bool kBf16Pipe = kRelF32OnBf16 && kWavesT == 8;
+    bf3::QSplit<kBf16Pipe ? HD : 16> q3;
+    if constexpr (kBf16Pipe) bf3::split_q_bf16x3<HD>(qreg, q3);
     f32x16 o[TL::kGroups];
 #pragma unroll
     for (int t = 0; t < TL::kGroups; ++t)
@@ -835,7 +847,10 @@ __global__ void __launch_bounds__(64 * kWavesT)
                         s = __builtin_amdgcn_mfma_f32_32x32x2f32(arow == 2 * ms + half ? 1.0f : 0.0f,
                                                                  dhv[ms] - ref, s, 0, 0, 0);
             }
-            s = dgk::scores_from<HD>(tile_ptr(buf, part, 0), l32, half, qreg, s);
+            if constexpr (kBf16Pipe)
+                s = bf3::scores_f32_bf16x6<HD>(tile_ptr(buf, part, 0), l32, half, q3, s);
+            else
+                s = dgk::scores_from<HD>(tile_ptr(buf, part, 0), l32, half, qreg, s);
             if (!kFull) {
                 const int len = tile_len(t);
                 if (len < tlen_w) {  // the last row tile is short
@@ -845,7 +860,10 @@ __global__ void __launch_bounds__(64 * kWavesT)
                 }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            dgk::accumulate_pv<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
+            if constexpr (kBf16Pipe)
+                bf3::accumulate_pv_f32_bf16x6<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
+            else
+                dgk::accumulate_pv<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
         }
     };
     for (int st = 0; st < nstage; st += 2) {

@@ -334,6 +334,10 @@ int dg_attn_split_gqa_noalloc(const float* q, const float* kc, const float* vc, 
  *   Every tensor pointer must be 16-byte aligned.  The library allocates nothing, so without a
  *   workspace the bias dot products are formed inside each attention workgroup for its own
  *   queries; relpos_flash_attn_ws takes a workspace for them instead.
+ * Arithmetic: grids above 16 x 16 form <q_i, k_j> and the value product from f32 operands taken
+ * as three bf16 terms each, six exact bf16 matrix products per f32 product summed in f32
+ * (within about 2^-25 of the f32 product); the bias dot products, and grids up to 16 x 16,
+ * use f32 MFMA.
  * Errors: DG_EINVAL for gh, gw or heads < 0, exactly one of rh/rw NULL, a NULL qkv/out with
  * n > 0, a non-finite scale, overlapping buffers, a tensor pointer that is not 16-byte
  * aligned;
