@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s and HBM GB/s (% of MI355X roofline) per canvas step"
 PEAK_F32_MFMA = 157.3      # TFLOP/s, dense f32 matrix
 PEAK_BF16_MFMA = 2500.0    # TFLOP/s, dense bf16 matrix
+CLOCK_SETTLE_S = 0.3       # untimed load before the warmup steps (see run())
 
 
 def mfma_ceiling(plan_kernel, kv16=None):
@@ -582,6 +583,19 @@ def run(work, steps=None, warmup=None, cold=0):
         if steps is None:
             steps = max(20, min(2000, int(0.25 / est))) if est else 20
             steps = -(-steps // per) * per
+    # The GPU raises its clock over tens of milliseconds of load, so a few warmup steps leave
+    # the timed ones on a ramping clock (long cache: 0.80 ms per step after 5 warmup steps,
+    # 0.71 ms once settled).  Before the W warmup steps the step therefore runs untimed for at
+    # least CLOCK_SETTLE_S of wall time; the count is reported as clock_settle_steps.
+    settle = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CLOCK_SETTLE_S:
+        for _ in range(per):
+            work.step()
+        settle += per
+        if settle % (16 * per) == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     for _ in range(warmup - nprobe):
         work.step()
     torch.cuda.synchronize()
@@ -621,7 +635,7 @@ def run(work, steps=None, warmup=None, cold=0):
     torch.cuda.synchronize()
     step_ms = [marks[j].elapsed_time(marks[j + 1]) / per for j in range(len(marks) - 1)]
     r = {"steps": steps, "warmup": warmup, "ms_step": ms_step, "kern_ms": kern_ms,
-         "step_ms": step_ms}
+         "step_ms": step_ms, "clock_settle_steps": settle}
     if cold > 0:
         flush = torch.ones((512 << 20) // 4, device="cuda")
         cold_ms = []
@@ -760,7 +774,8 @@ def main():
     step_bytes = work.attn_bytes + work.norm_bytes
     rec = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": r["steps"],
-        "warmup": r["warmup"], "ms_per_step": r["ms_step"], "higher_is_better": True,
+        "warmup": r["warmup"], "clock_settle_steps": r["clock_settle_steps"],
+        "ms_per_step": r["ms_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "arith": "; ".join(ARITH.get(n, n) for n in
                            getattr(work, "mfma_peak_name", "f32 MFMA").split(" + ")),
