@@ -66,7 +66,7 @@ ARITH = {
     "f32 MFMA": "f32 (f32 MFMA)",
     "bf16 MFMA / 6 (six bf16 products per f32 product)":
         "f32 operands as three bf16 terms each; every product as six exact bf16 MFMA products "
-        "summed in f32 (within 2^-25 of the f32 product)",
+        "summed in f32 (within 2^-23 |a||b| of the f32 product, typically 2^-29)",
     "bf16 MFMA / 3 (three bf16 products per f32 product)":
         "bf16 K/V; q and p as three bf16 terms; exact bf16 MFMA products summed in f32",
 }

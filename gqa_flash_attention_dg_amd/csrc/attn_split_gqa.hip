@@ -180,11 +180,11 @@ __device__ inline void accumulate_pv16(const char* __restrict__ vs, int l32, int
     }
 }
 
-// f32 K/V on the bf16 pipe.  With both operands split in three terms, a = ah + am + al and
-// b = bh + bm + bl, the product a*b is taken as the six terms down to order 2^-18 (ah*bh,
-// ah*bm, am*bh, ah*bl, al*bh, am*bm); the three dropped ones (am*bl, al*bm, al*bl) and the
-// splits' own 2^-27 leave each product within about 2^-25 of its value, inside f32's rounding
-// of a product (2^-24), so the result stays on the f32 bar.  Six v_mfma_f32_32x32x16_bf16 per
+// f32 K/V on the bf16 pipe.  With both operands split exactly in three terms, a = ah + am + al
+// and b = bh + bm + bl, the product a*b is taken as the six terms down to order 2^-16 (ah*bh,
+// ah*bm, am*bh, ah*bl, al*bh, am*bm); the dropped ones (am*bl, al*bm, al*bl) leave each product
+// within 2^-23 |a||b| and typically within 2^-29, where f32 rounds a product by up to 2^-24
+// (median 2^-25.5), so the result stays on the f32 bar.  Six v_mfma_f32_32x32x16_bf16 per
 // step are 2.7 times less matrix-pipe time than v_mfma_f32_32x32x2f32.  The K and V tiles are
 // split once per stage by the whole workgroup (split_stage), q once per wavefront, and the
 // probabilities per tile (7 vector instructions per pair of values).  false: f32 MFMA.

@@ -11,14 +11,15 @@ namespace bf3 {
 
 using dgk::f32x16;
 
-// A product of two bf16 values is exact in f32, and an f32 value x is the sum of three bf16
-// values to within 2^-27 |x|: hi = bf16(x), mid = bf16(x - hi),
-// lo = bf16(x - hi - mid), rounding to nearest (both differences are exact: each is a multiple
-// of x's last significand bit and at most 2^-9 of the value it is taken from).  So with x = q
+// A product of two bf16 values is exact in f32, and an f32 value x is exactly the sum of three
+// bf16 values: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid), rounding to nearest.
+// Both differences are exact (multiples of x's last significand bit, each at most half a bf16
+// step, 2^-8, of the value it is taken from), x - hi keeps at most 16 significant bits and
+// x - hi - mid at most 8, so lo takes it exactly (outside the subnormal range).  So with x = q
 // (scores) or x = p (the value product) each MFMA step runs three v_mfma_f32_32x32x16_bf16, one
-// per term, with exact products and the sums in f32: the f32 path's arithmetic up to a 2^-27
-// relative change of one operand and the summation order, at about a fifth of the matrix-pipe
-// time of v_mfma_f32_32x32x2f32 on the same tile (bf16 K/V, which are exact in bf16).  The k-slots a lane supplies are the same for
+// per term, with exact products and the sums in f32: the f32 path's arithmetic up to the
+// summation order, at about a fifth of the matrix-pipe time of v_mfma_f32_32x32x2f32 on the
+// same tile (bf16 K/V, which are exact in bf16).  The k-slots a lane supplies are the same for
 // the A and the B operand, so which 8 of the 16 a lane half holds does not matter; the 32x32
 // accumulator layout is that of the f32 instruction.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -559,8 +559,8 @@ __host__ __device__ inline Tiling make_tiling(int gh, int gw) {
 
 // Scores and the value product of the 8-wavefront grid kernels run on the bf16 matrix pipe: q
 // once, and each K and V value as it is read from LDS, taken as three bf16 terms, every product
-// as six exact bf16 products summed in f32 (bf16x3.hpp); within about 2^-25 of each f32
-// product.  Two query groups share each tile, so each value is split twice.  The bias terms
+// as six exact bf16 products summed in f32 (bf16x3.hpp); within 2^-23 |q||k| of each f32
+// product, typically 2^-29.  Two query groups share each tile, so each value is split twice.  The bias terms
 // stay on f32 MFMA, and so does the 4-wavefront shape (three workgroups per CU leave it no
 // registers for the split).  false: f32 MFMA throughout.
 constexpr bool kRelF32OnBf16 = true;

@@ -208,11 +208,11 @@ int dg_attn_split_gqa_plan(int batch, int T, int ctx, int nh, int nkv, int hd, i
  *   torch allocations are).
  *   hd         any multiple of 4 up to 128 (the page allows hd <= 128); heads narrower than
  *              64 or 128 run in the 64- or 128-wide kernel with zero padding.
- * Arithmetic: in the 32-key tile kernel each f32 operand is taken as three bf16 terms (sum
- * within 2^-27 of it) and each product q.k and p.v as the six leading bf16 x bf16 products,
- * each exact in f32, summed in f32 on the bf16 matrix pipe: every product is within about
- * 2^-25 of its value (f32 rounds a product to 2^-24), and the large score terms are summed
- * apart from the small ones.  The short-key-set kernel (ctx + T <= 8) uses f32 arithmetic.
+ * Arithmetic: in the 32-key tile kernel each f32 operand is taken as three bf16 terms (whose
+ * sum is exactly the operand) and each product q.k and p.v as the six leading bf16 x bf16
+ * products, each exact in f32, summed in f32 on the bf16 matrix pipe: every product is within
+ * 2^-23 |a||b| of its value, typically 2^-29 (f32 rounds a product by up to 2^-24), and the
+ * large score terms are summed apart from the small ones.  The short-key-set kernel (ctx + T <= 8) uses f32 arithmetic.
  * Errors: DG_EINVAL for negative sizes, nkv < 1, nh % nkv != 0, a NULL pointer with a
  * nonzero extent, a non-finite scale, causal not 0/1, overlapping buffers, a tensor pointer
  * that is not 16-byte aligned, or a workspace pointer that is misaligned or has
@@ -279,8 +279,8 @@ int dg_attn_split_gqa_qkvnorm(const float* q, const float* wq, const float* k, c
  *   f16   each value is widened exactly to f32 and runs the f32 MFMA arithmetic;
  *   bf16  both products run on the bf16 matrix pipe: the f32 operand (q for the scores, the
  *         probabilities for the value product) is taken as three bf16 terms whose sum is
- *         within 2^-27 of it, each product of two bf16 values is exact in f32, and all sums
- *         are f32 -- at about a fifth of the f32 MFMA time.
+ *         exactly it, each product of two bf16 values is exact in f32, and all sums are f32
+ *         -- at about a fifth of the f32 MFMA time.
  * Stage tiles in LDS are half the bytes of f32 ones.
  *   hd must be a multiple of 8 (16-byte rows of 16-bit values); q and out are f32.
  *   Other arguments, the workspace and its size function as dg_attn_split_gqa.
@@ -336,8 +336,8 @@ int dg_attn_split_gqa_noalloc(const float* q, const float* kc, const float* vc, 
  *   queries; relpos_flash_attn_ws takes a workspace for them instead.
  * Arithmetic: grids above 16 x 16 form <q_i, k_j> and the value product from f32 operands taken
  * as three bf16 terms each, six exact bf16 matrix products per f32 product summed in f32
- * (within about 2^-25 of the f32 product); the bias dot products, and grids up to 16 x 16,
- * use f32 MFMA.
+ * (within 2^-23 |q||k| of the f32 product, typically 2^-29); the bias dot products, and grids
+ * up to 16 x 16, use f32 MFMA.
  * Errors: DG_EINVAL for gh, gw or heads < 0, exactly one of rh/rw NULL, a NULL qkv/out with
  * n > 0, a non-finite scale, overlapping buffers, a tensor pointer that is not 16-byte
  * aligned;
