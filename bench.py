@@ -378,7 +378,9 @@ class LayerStackWork:
 
 class RelposWork:
     """Rel-pos flash attention over one grid (sam_relpos) or a batch of windows
-    (sam_windowed): the bias-row pass into the workspace, then the flash kernel."""
+    (sam_windowed), one relpos_flash_attn_windows call with a workspace: the 64 x 64 grid's
+    workgroups and the windows' form their bias rows themselves, other grids go through a
+    bias pass into the workspace."""
     dominant = "relpos_flash"
 
     def __init__(self, name, case):
@@ -397,12 +399,9 @@ class RelposWork:
         attn = self.nwin * case.heads * n * n * 4 * case.hd
         bias = self.nwin * case.heads * n * 2 * case.hd * (case.gh + case.gw) if case.rh is not None else 0
         self.flops = attn + bias
-        # grids up to 16 x 16 run the windowed kernel (f32 MFMA); larger grids the 8-wavefront
-        # grid kernel, whose q.k and p.v take six bf16 products each; the bias rows are f32 MFMA
-        win = case.gh <= 16 and case.gw <= 16
+        # q.k and p.v take six bf16 products each; the bias rows are f32 MFMA
         self.mfma_peak, self.mfma_peak_name = combined_ceiling(
-            [(attn, (PEAK_F32_MFMA, "f32 MFMA") if win else
-              (PEAK_BF16_MFMA / 6, "bf16 MFMA / 6 (six bf16 products per f32 product)"))] +
+            [(attn, (PEAK_BF16_MFMA / 6, "bf16 MFMA / 6 (six bf16 products per f32 product)"))] +
             ([(bias, (PEAK_F32_MFMA, "f32 MFMA"))] if bias else []))
         # every input read once, the output written once (the bias rows it keeps in its
         # workspace are the method's own intermediate, not counted)

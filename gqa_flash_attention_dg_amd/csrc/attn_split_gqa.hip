@@ -207,34 +207,8 @@ __device__ inline f32x16 scores_bf16x3(const char* __restrict__ ks, int l32, int
     return s;
 }
 
-// bf16 V tiles sit in LDS row-major with each row's 16-byte chunks permuted, chunk c of key row
-// k at position c ^ vswz(k): the 8 rows a wavefront's transposed reads touch at once (4 per
-// lane half) then cover all 64 banks twice instead of 16 banks eight times.
-template <int HD>
-__device__ inline int vswz(int row) {
-    return HD == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
-// O^T += V^T P^T from a bf16 V tile.  Step st takes the 16 keys whose probabilities are the
-// lane's registers p[8*st .. 8*st + 7] (keys dgk::key_of(r, half)), so the B operand is those
-// registers split in three.  The A operand of output group t holds, for the lane's head element
-// 32*t + l32, the same 16 keys; two ds_read_b64_tr_b16 fetch it straight from the row-major tile.
-// That instruction hands out, within each 16 lanes, element j%4 of the 8 bytes addressed by lane
-// 4*e + j/4 as element e of lane j: so lane 4*e + c of a 16-lane group addresses key row
-// (4*half + e) (plus 8 for the second read) at head elements 32*t + 16*((lane/16)%2) + 4*c.
-// Output rows are therefore head elements 32*t + key_of(r, half): stage_row_blocked.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-template <int HD>
-__device__ inline void vtr_offsets(int lane, int (&off)[dgk::Tile<HD>::kGroups]) {
-    const int j = lane & 15, e = j >> 2, c = j & 3, sg = (lane >> 4) & 1, half = lane >> 5;
-    const int row = 4 * half + e;
-#pragma unroll
-    for (int t = 0; t < dgk::Tile<HD>::kGroups; ++t)
-        off[t] = row * HD * 2 + 16 * ((4 * t + 2 * sg + (c >> 1)) ^ vswz<HD>(row)) + 8 * (c & 1);
-}
-
+// O^T += V^T P^T from a bf16 V tile as stored (rows permuted by vswz), read transposed at the
+// vtr_offsets addresses.
 template <int HD>
 __device__ inline void accumulate_pv_bf16x3(const char* __restrict__ vs, const int (&off)[dgk::Tile<HD>::kGroups],
                                             const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
@@ -263,113 +237,6 @@ __device__ inline void accumulate_pv_bf16x3(const char* __restrict__ vs, const i
             o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bl), o[t], 0, 0, 0);
         }
     }
-}
-
-// f32 K/V tiles split once per stage into bf16 planes.  The workgroup turns each staged f32
-// tile (plain rows, so each load of the stage is a scalar offset from the last) into three bf16
-// tiles hi, mid, lo laid out as the
-// bf16 K/V path lays out its tiles, so every wavefront then reads ready MFMA operands: the
-// split is done once per element instead of once per element and query group.
-template <int HD>
-struct Planes {
-    static constexpr int kBytes = dgk::kKeys * HD * 2;   // one bf16 plane of a tile
-    static constexpr int kOct = HD / 8;                   // 8-element groups per row
-    // plane p of the K (isv 0) or V (isv 1) tile `tile`
-    __device__ static char* at(char* base, int tile, int isv, int p) {
-        return base + ((tile * 2 + isv) * 3 + p) * kBytes;
-    }
-};
-
-template <int HD>
-__device__ inline void split_stage(const char* __restrict__ stage, int slot_bytes,
-                                   char* __restrict__ planes, int ntile, int tid) {
-    using P = Planes<HD>;
-    constexpr int kPerTile = 2 * dgk::kKeys * P::kOct;    // K and V items of one tile
-    const SplitWeights w;
-#pragma unroll
-    for (int i = 0; i < 2 * kPerTile / 512; ++i) {
-        const int it = tid + 512 * i;
-        const int tile = it / kPerTile;
-        if (tile >= ntile) continue;   // uniform per iteration: whole tiles are absent
-        const int o = it % P::kOct, r = (it / P::kOct) % dgk::kKeys;
-        const int isv = (it / (P::kOct * dgk::kKeys)) & 1;
-        const float* row = reinterpret_cast<const float*>(stage + (tile * 2 + isv) * slot_bytes) + r * HD;
-        const float4 x0 = *reinterpret_cast<const float4*>(row + 8 * o);
-        const float4 x1 = *reinterpret_cast<const float4*>(row + 8 * o + 4);
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        u32x4 h, m, l;
-        split8(x, w, h, m, l);
-        const int pos = o ^ (isv ? vswz<HD>(r) : r % P::kOct);
-        char* dst = P::at(planes, tile, isv, 0) + r * HD * 2 + 16 * pos;
-        *reinterpret_cast<u32x4*>(dst) = h;
-        *reinterpret_cast<u32x4*>(dst + P::kBytes) = m;
-        *reinterpret_cast<u32x4*>(dst + 2 * P::kBytes) = l;
-    }
-}
-
-// S^T += K Q^T from the three K planes of a tile; q in the load_q_bf16x3 layout.
-template <int HD>
-__device__ inline f32x16 scores_planes(const char* __restrict__ kp, int l32, int half,
-                                       const QSplit<HD>& q, f32x16 s) {
-    using P = Planes<HD>;
-    const char* kr = kp + l32 * HD * 2;
-    const int sw = l32 % P::kOct;
-    f32x16 d = {};
-#pragma unroll
-    for (int st = 0; st < HD / 16; ++st) {
-        const int off = 16 * ((2 * st + half) ^ sw);
-        const u32x4 kh = *reinterpret_cast<const u32x4*>(kr + off);
-        const u32x4 km = *reinterpret_cast<const u32x4*>(kr + P::kBytes + off);
-        const u32x4 kl = *reinterpret_cast<const u32x4*>(kr + 2 * P::kBytes + off);
-        mfma_bf16x6(kh, km, kl, q.h[st], q.m[st], q.l[st], s, d);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += d[r];
-    return s;
-}
-
-// O^T += V^T P^T from the three V planes of a tile (layout and reads as accumulate_pv_bf16x3).
-template <int HD>
-__device__ inline void accumulate_pv_planes(const char* __restrict__ vp,
-                                            const int (&off)[dgk::Tile<HD>::kGroups],
-                                            const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
-    constexpr int G = dgk::Tile<HD>::kGroups, PB = Planes<HD>::kBytes;
-    const SplitWeights w;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[8 * st + e];
-        u32x4 bh, bm, bl;
-        split8(x, w, bh, bm, bl);
-#pragma unroll
-        for (int t = 0; t < G; ++t) {
-            u32x4 a[3];
-#pragma unroll
-            for (int pl = 0; pl < 3; ++pl) {
-                const char* r0 = vp + pl * PB + st * 16 * HD * 2 + off[t];
-                const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0));
-                const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0 + 8 * HD * 2));
-                const uint2 u0 = __builtin_bit_cast(uint2, x0), u1 = __builtin_bit_cast(uint2, x1);
-                a[pl] = u32x4{u0.x, u0.y, u1.x, u1.y};
-            }
-            mfma_bf16x6(a[0], a[1], a[2], bh, bm, bl, o[t], o[t]);
-        }
-    }
-}
-
-// dgk::stage_row for the bf16 path's output layout (row m of group t is head element 32*t + m).
-template <int HD>
-__device__ inline void stage_row_blocked(float* __restrict__ rows, int l32, float scale,
-                                         const f32x16 (&o)[dgk::Tile<HD>::kGroups], int half) {
-    float* dst = rows + l32 * (HD + 4) + 4 * half;
-#pragma unroll
-    for (int t = 0; t < dgk::Tile<HD>::kGroups; ++t)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            *reinterpret_cast<float4*>(dst + 32 * t + 8 * rb) =
-                make_float4(o[t][4 * rb] * scale, o[t][4 * rb + 1] * scale,
-                            o[t][4 * rb + 2] * scale, o[t][4 * rb + 3] * scale);
 }
 
 using dg::group_sum;
@@ -793,7 +660,7 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         }
         if constexpr (kPlanes) {
             // the whole workgroup splits the staged tiles, then the staging buffer is free
-            split_stage<HD>(tile_ptr(0, 0, 0), kSlot, planes, key0(st, 1) < kend ? 2 : 1, tid);
+            split_stage<HD, 64 * kWaves, 2>(tile_ptr(0, 0, 0), kSlot, planes, key0(st, 1) < kend ? 2 : 1, tid);
             __syncthreads();
             if (!hi && st + 1 < nst) issue_stage(st + 1, 0);
         }

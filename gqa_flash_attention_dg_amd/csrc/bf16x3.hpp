@@ -195,4 +195,145 @@ __device__ inline void accumulate_pv_f32_bf16x6(const float* __restrict__ vs, in
     }
 }
 
+// bf16 V tiles sit in LDS row-major with each row's 16-byte chunks permuted, chunk c of key row
+// k at position c ^ vswz(k): the 8 rows a wavefront's transposed reads touch at once (4 per
+// lane half) then cover all 64 banks twice instead of 16 banks eight times.
+template <int HD>
+__device__ inline int vswz(int row) {
+    return HD == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// O^T += V^T P^T from a bf16 V tile (as stored, or a plane of a split f32 tile).  Step st takes
+// the 16 keys whose probabilities are the lane's registers p[8*st .. 8*st + 7] (keys
+// dgk::key_of(r, half)), so the B operand is those registers split in three.  The A operand of
+// output group t holds, for the lane's head element 32*t + l32, the same 16 keys; two
+// ds_read_b64_tr_b16 fetch it straight from the row-major tile (vtr_offsets gives the lane's
+// addresses).
+// That instruction hands out, within each 16 lanes, element j%4 of the 8 bytes addressed by lane
+// 4*e + j/4 as element e of lane j: so lane 4*e + c of a 16-lane group addresses key row
+// (4*half + e) (plus 8 for the second read) at head elements 32*t + 16*((lane/16)%2) + 4*c.
+// Output rows are therefore head elements 32*t + key_of(r, half): stage_row_blocked.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int HD>
+__device__ inline void vtr_offsets(int lane, int (&off)[dgk::Tile<HD>::kGroups]) {
+    const int j = lane & 15, e = j >> 2, c = j & 3, sg = (lane >> 4) & 1, half = lane >> 5;
+    const int row = 4 * half + e;
+#pragma unroll
+    for (int t = 0; t < dgk::Tile<HD>::kGroups; ++t)
+        off[t] = row * HD * 2 + 16 * ((4 * t + 2 * sg + (c >> 1)) ^ vswz<HD>(row)) + 8 * (c & 1);
+}
+
+// f32 K/V tiles split once per stage into bf16 planes.  The workgroup turns each staged f32
+// tile (plain rows, so each load of the stage is a scalar offset from the last) into three bf16
+// tiles hi, mid, lo: K rows with chunk c of row k at position c ^ (k mod HD/8), V rows permuted
+// by vswz.  Every wavefront then reads ready MFMA operands, and the split is done once per
+// element instead of once per element and query group.
+template <int HD>
+struct Planes {
+    static constexpr int kBytes = dgk::kKeys * HD * 2;   // one bf16 plane of a tile
+    static constexpr int kOct = HD / 8;                   // 8-element groups per row
+    // plane p of the K (isv 0) or V (isv 1) tile `tile`
+    __device__ static char* at(char* base, int tile, int isv, int p) {
+        return base + ((tile * 2 + isv) * 3 + p) * kBytes;
+    }
+};
+
+// The staged tile `tile` has its K at stage + 2*tile*slot_bytes and its V one slot further.
+// kThreads threads (tid < kThreads) split up to kMaxTiles tiles, of which the first ntile are
+// present.
+template <int HD, int kThreads, int kMaxTiles>
+__device__ inline void split_stage(const char* __restrict__ stage, int slot_bytes,
+                                   char* __restrict__ planes, int ntile, int tid) {
+    using P = Planes<HD>;
+    constexpr int kPerTile = 2 * dgk::kKeys * P::kOct;    // K and V items of one tile
+    static_assert(kMaxTiles * kPerTile % kThreads == 0, "whole passes");
+    const SplitWeights w;
+#pragma unroll
+    for (int i = 0; i < kMaxTiles * kPerTile / kThreads; ++i) {
+        const int it = tid + kThreads * i;
+        const int tile = it / kPerTile;
+        if (tile >= ntile) continue;   // uniform per iteration: whole tiles are absent
+        const int o = it % P::kOct, r = (it / P::kOct) % dgk::kKeys;
+        const int isv = (it / (P::kOct * dgk::kKeys)) & 1;
+        const float* row = reinterpret_cast<const float*>(stage + (tile * 2 + isv) * slot_bytes) + r * HD;
+        const float4 x0 = *reinterpret_cast<const float4*>(row + 8 * o);
+        const float4 x1 = *reinterpret_cast<const float4*>(row + 8 * o + 4);
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        u32x4 h, m, l;
+        split8(x, w, h, m, l);
+        const int pos = o ^ (isv ? vswz<HD>(r) : r % P::kOct);
+        char* dst = P::at(planes, tile, isv, 0) + r * HD * 2 + 16 * pos;
+        *reinterpret_cast<u32x4*>(dst) = h;
+        *reinterpret_cast<u32x4*>(dst + P::kBytes) = m;
+        *reinterpret_cast<u32x4*>(dst + 2 * P::kBytes) = l;
+    }
+}
+
+// S^T += K Q^T from the three K planes of a tile; q in the load_q_bf16x3 layout.
+template <int HD>
+__device__ inline f32x16 scores_planes(const char* __restrict__ kp, int l32, int half,
+                                       const QSplit<HD>& q, f32x16 s) {
+    using P = Planes<HD>;
+    const char* kr = kp + l32 * HD * 2;
+    const int sw = l32 % P::kOct;
+    f32x16 d = {};
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        const int off = 16 * ((2 * st + half) ^ sw);
+        const u32x4 kh = *reinterpret_cast<const u32x4*>(kr + off);
+        const u32x4 km = *reinterpret_cast<const u32x4*>(kr + P::kBytes + off);
+        const u32x4 kl = *reinterpret_cast<const u32x4*>(kr + 2 * P::kBytes + off);
+        mfma_bf16x6(kh, km, kl, q.h[st], q.m[st], q.l[st], s, d);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += d[r];
+    return s;
+}
+
+// O^T += V^T P^T from the three V planes of a tile (layout and reads as accumulate_pv_bf16x3).
+template <int HD>
+__device__ inline void accumulate_pv_planes(const char* __restrict__ vp,
+                                            const int (&off)[dgk::Tile<HD>::kGroups],
+                                            const f32x16& p, f32x16 (&o)[dgk::Tile<HD>::kGroups]) {
+    constexpr int G = dgk::Tile<HD>::kGroups, PB = Planes<HD>::kBytes;
+    const SplitWeights w;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[8 * st + e];
+        u32x4 bh, bm, bl;
+        split8(x, w, bh, bm, bl);
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            u32x4 a[3];
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) {
+                const char* r0 = vp + pl * PB + st * 16 * HD * 2 + off[t];
+                const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0));
+                const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0 + 8 * HD * 2));
+                const uint2 u0 = __builtin_bit_cast(uint2, x0), u1 = __builtin_bit_cast(uint2, x1);
+                a[pl] = u32x4{u0.x, u0.y, u1.x, u1.y};
+            }
+            mfma_bf16x6(a[0], a[1], a[2], bh, bm, bl, o[t], o[t]);
+        }
+    }
+}
+
+// dgk::stage_row for the bf16 path's output layout (row m of group t is head element 32*t + m).
+template <int HD>
+__device__ inline void stage_row_blocked(float* __restrict__ rows, int l32, float scale,
+                                         const f32x16 (&o)[dgk::Tile<HD>::kGroups], int half) {
+    float* dst = rows + l32 * (HD + 4) + 4 * half;
+#pragma unroll
+    for (int t = 0; t < dgk::Tile<HD>::kGroups; ++t)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            *reinterpret_cast<float4*>(dst + 32 * t + 8 * rb) =
+                make_float4(o[t][4 * rb] * scale, o[t][4 * rb + 1] * scale,
+                            o[t][4 * rb + 2] * scale, o[t][4 * rb + 3] * scale);
+}
+
 }  // namespace bf3

@@ -9,10 +9,13 @@
 // SAM blocks that the page's encoder cost model counts (25 windows of 14 x 14 tokens) are the
 // same attention run independently per window with shared tables: a batch of grids.
 //
-// With a workspace, a bias pass first writes the hoisted bias rows (dh: gh floats, dw: gw
-// floats per (window, head, query), in log2 units), as the page's DHDW step does; without one,
-// each attention workgroup forms the dot products of its own queries in a prologue.  The
-// attention is the f32-MFMA flash loop of flash_core.hpp.  For large grids a workgroup is 2
+// The hoisted bias rows (dh: gh floats, dw: gw floats per (window, head, query), in log2
+// units), the page's DHDW step, are formed as small matrix products by the attention
+// workgroups themselves where their queries allow it (8 x 8 patches of large grids, the
+// windowed grids), else by a bias pass into the workspace; without a workspace, each
+// attention workgroup forms the dot products of its own queries in a prologue.  The attention
+// is the flash loop of flash_core.hpp with its tile products on the bf16 matrix pipe
+// (kRelF32OnBf16).  For large grids a workgroup is 2
 // groups of 32 queries x 4 wavefronts; the 4 wavefronts of a group take every 4th 32-key tile
 // (stages of 128 keys, double-buffered direct global->LDS tiles) and merge their softmax
 // states at the end.  Small grids use the shapes of RelShape.  The bias enters each score
@@ -35,10 +38,11 @@ constexpr int kWaves = 8;
 //    workgroups amortise their prologue and merge;
 //  * 4 x 1 for small grids of at most 16 rows of at most 32, such as 14x14 windows (4
 //    wavefronts, 128 queries, no key split; row tiles only, as every wavefront takes every
-//    tile): with its height-bias table cut to 16 rows a workgroup needs 40 KiB
-//    of LDS, so three fit on a CU beside each other and the windows' workgroups run in one
-//    round, each CU's matrix pipes kept busy by whichever workgroup is not waiting.  Used
-//    when the launch has more workgroups than the GPU has CUs.
+//    tile): with its height-bias table cut to 16 rows and single-buffered stages (one f32
+//    tile and its bf16 planes) a workgroup needs 48 KiB of LDS, so three fit on a CU beside
+//    each other and the windows' workgroups run in one round, each CU's matrix pipes kept
+//    busy by whichever workgroup is not waiting.  Used when the launch has more workgroups
+//    than the GPU has CUs.
 template <int kParts, int kWavesT = 8>
 struct RelShape {
     static constexpr int kQGroups = kWavesT / kParts;
@@ -53,7 +57,11 @@ struct RelArgs {
     const float* qkv;  // [nwin][n][3W]
     const float* rh;
     const float* rw;
-    const float* dhw;  // precomputed bias rows (dh [nwin][heads][n][gh], then dw [..][gw]), or null
+    const float* dhw;  // precomputed bias rows, or null
+    // the dh row of (window, head, query) row index r = (win * heads + head) * n + query sits at
+    // dhw + r * dh_stride, its dw row at dhw + dw_off + r * dw_stride (floats)
+    size_t dw_off;
+    int dh_stride, dw_stride;
     float* out;        // [nwin][n][W]
     int n, gh, gw, heads, W, nwin;
     int qblocks, nblocks;
@@ -62,9 +70,12 @@ struct RelArgs {
     // key tiling (see make_tiling): tile t starts at key (t >> tsh) * ta + (t & tmsk) * tb and
     // holds min(tl0 + (t & tmsk) * td, n - start) keys
     int tsh, ta, tmsk, tb, tl0, td, ntiles;
-    // small grids (gh, gw <= 16): bias row layout [dh (gh4 floats) | dw] with stride brs floats,
-    // and 16-query tiles per (window, head)
-    int gh4, brs, qtiles;
+    // windowed grids (gh, gw <= 16): relpos_bias16_kernel's bias row layout, [dh (gh4 floats) |
+    // dw] with stride brs floats
+    int gh4, brs;
+    // 4 x 1 shape on a windowed grid (gh, gw <= 16) with tables: each workgroup forms the bias
+    // rows of its queries itself (no bias pass, no workspace)
+    int lines;
 };
 
 using dg::xcd_remap;
@@ -88,15 +99,16 @@ constexpr int kBiasWaves = 4;
 // the XCD whose attention workgroups read them: writing lines that another XCD's L2 has just
 // read was measured to be the slow case for the split-KV workspace.
 //
-// Lines of at most 16 queries against at most 16 table rows (windowed grids): one 16x16 tile
-// per line with v_mfma_f32_16x16x4f32, a quarter of the 32x32 tile's matrix work.  Lane l
+// Lines of at most 16 queries against at most 16 table rows (windowed grids in the 8-wavefront
+// shapes; the 4-wavefront shape forms its lines itself, see form_lines): one 16x16 tile per
+// line with v_mfma_f32_16x16x4f32, a quarter of the 32x32 tile's matrix work.  Lane l
 // supplies query row l%16 (A) and table row l%16 (B) at contraction index k = l/16; step
 // 4c+e contracts element 16c+4k+e, so in each of the 4 float4 loads per operand the 4 lanes
 // of a row read 64 contiguous bytes.  The 4 accumulators hold queries 4*(l/16)+r of table
 // row l%16.  One wavefront per line (measured fastest: two or four lines per wavefront, with
 // their loads in flight together, took 12.0 and 14.7 us against 10.3 for the SAM windows).
 // The output is one row per (window, head, query), dh then dw, each part padded to a multiple
-// of 4 floats (the layout relpos_win_kernel reads); the head is the fastest-varying task
+// of 4 floats (read through RelArgs' dh_stride, dw_off, dw_stride); the head is the fastest-varying task
 // index, so the wavefronts running together read the q slices of all heads of the same tokens,
 // which lie next to each other in each qkv row.
 __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias16_kernel(RelArgs a, float* __restrict__ dhw,
@@ -185,340 +197,8 @@ __global__ void __launch_bounds__(64 * kBiasWaves) relpos_bias_kernel(RelArgs a,
     }
 }
 
-// Small grids (gh, gw <= 16: the SAM windows) on v_mfma_f32_16x16x4f32.  One wavefront owns
-// one (window, head, 16-query tile) and runs on its own: no LDS staging of K or V and no
-// barriers, so wavefronts of any tile and window fill a SIMD and the launch balances at tile
-// granularity (a 14x14 window is 13 tiles; 300 window-heads would not balance over 256 CUs).
-//
-// Scores are S^T = K Q^T per 16-key tile: lane (n = l%16, g = l/16) holds query n and, in
-// accumulator r, key 16t + 4r + g.  The K rows are fed to the matrix rows in that order (matrix
-// row 4g + r takes key 16t + 4r + g), so the output step O^T += V^T P^T contracts in its step r
-// exactly the four keys 16t + 4r .. 16t + 4r + 3, with the lane's own register r as the B
-// operand: a key set of n keys needs ceil(n / 4) steps, not a multiple of 16.  Output row m of
-// head-dim tile h is head element 4m + h, so each lane reads 16 contiguous bytes of a V row per
-// step and writes 16 contiguous bytes of an output row per register.  Contraction order of the
-// scores: step 4c + e, lane group g, element 16c + 4g + e (one 16-byte K read per 4 steps).
-//
-// The bias of every (query, key) pair the lane holds is formed once, before the key loop: the
-// wavefront expands its 16 queries' dh/dw rows into a [key][query] table in LDS (dh[ky] +
-// dw[kx], -inf past the last key) and each lane reads its 4 * NT values into registers, where
-// they start the score accumulators.  The padding keys of the last tile so carry -inf and need
-// no mask.  K and V are read with buffer loads (the tile offset in a scalar register), two tiles
-// ahead of their use.  Softmax reference: scores stay in log2 units, the reference
-// stays 0 while the running maximum lies within +-kHeadroom (no subtraction at all) and moves
-// only when a score would overflow exp2 or the first tile's maximum is far below 0.
-constexpr int kWinGrid = 16;       // grids with gh, gw <= 16 take the 16x16 path
-namespace win {
-constexpr int kWaves = 4;          // wavefronts per workgroup (independent tasks)
-constexpr int kQT = 16;            // queries per wavefront
+constexpr int kWinGrid = 16;   // windowed grids: gh, gw <= 16 (bias lines fit one 16 x 16 tile)
 constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw 32-bit buffer descriptor (gfx9 family)
-// The bias-row layout of a query with no bias (dh and dw all zero, never written): read in
-// place of the rows when the call has no tables, so the loads are the same either way.  Not
-// const, so it shares the global address space with the workspace and the loads stay global
-// loads (a flat load would make every wait a wait for all loads).
-__device__ __attribute__((aligned(16))) float kZeroRow[2 * 16];
-}  // namespace win
-
-// NT is the exact number of 16-key tiles (ceil(n / 16)), so only the last tile has runtime
-// conditions.  Two wavefronts per SIMD cap the kernel at 256 VGPRs, which keeps every MFMA
-// operand and accumulator in VGPRs (no copies to and from accumulation registers).
-//
-// The grid holds as many wavefronts as run at once and each takes tasks gw, gw + G, ... (G
-// wavefronts in the grid).  A wavefront loads the next task's bias rows and Q three tiles
-// before the end of the current one, and its first two K/V tiles in place of the current
-// task's tiles NT + 0 and NT + 1: only the first task of each wavefront waits for memory
-// before its first tile (measured with one task per wavefront, that wait was about 10 us of a
-// wavefront's 17 us, all wavefronts waiting at once).
-template <int NT>
-__global__ void __launch_bounds__(64 * win::kWaves) __attribute__((amdgpu_waves_per_eu(2)))
-    relpos_win_kernel(RelArgs a, int ntasks) {
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    // one spare 16-key tile per table takes the writes of columns past the grid's width
-    __shared__ __attribute__((aligned(16))) float ebuf[win::kWaves][(NT + 1) * 16 * win::kQT];
-    // the wavefront index is uniform: every task quantity below lives in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
-    // Tasks are split into one contiguous range per XCD (workgroup b runs on XCD b % nxcd), so
-    // the wavefronts streaming one window's K/V share an L2; within its XCD's range a wavefront
-    // takes every (wavefronts per XCD)-th task.  (Taking the next free task from a per-XCD
-    // atomic counter instead was measured 1.5x slower.)
-    const int per = (int)gridDim.x / a.nxcd;   // workgroups per XCD (the grid is a multiple)
-    const int lid = xcd_remap(blockIdx.x, gridDim.x, a.nxcd);
-    const int xcd = lid / per, wpx = per * win::kWaves;
-    const int range = (ntasks + a.nxcd - 1) / a.nxcd;
-    const int lo = xcd * range, hi = min(lo + range, ntasks);
-    int task = lo + (lid % per) * win::kWaves + wave;
-    if (task >= hi) return;   // wave-uniform; no barrier below
-    const int n = a.n;
-    const unsigned rsb = 12u * (unsigned)a.W;           // qkv row stride in bytes
-    const int krow = 4 * (l16 & 3) + (l16 >> 2);        // matrix row l16 takes key 16t + krow
-    const unsigned koff = (unsigned)krow * rsb + 16u * kq;
-    const unsigned voff = (unsigned)kq * rsb + 16u * l16;
-    constexpr bool kCross = NT >= 2;                     // next task's tiles 0, 1 prefetched
-
-    // A task is (window, 16-query tile, head), numbered (w * qtiles + qt) * heads + head: the
-    // heads of one query tile run together.
-    struct Task {
-        int w, head, qt;
-        __amdgpu_buffer_rsrc_t rsrc;   // this window's qkv rows
-        int kb, vb;                    // byte offsets of this head's k and v in a row
-    };
-    auto decode = [&](int tk) {
-        Task T;
-        T.head = tk % a.heads;
-        const int wq = tk / a.heads;
-        T.qt = wq % a.qtiles;
-        T.w = wq / a.qtiles;
-        T.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.qkv + (size_t)T.w * n * 3 * a.W), 0,
-                                                   (int)((unsigned)n * rsb), (int)win::kRsrcWord3);
-        T.kb = (a.W + T.head * HD) * 4;
-        T.vb = (2 * a.W + T.head * HD) * 4;
-        return T;
-    };
-    // This lane's bias-row values -- dh[0..gh) of its query and dw at kx = kq + 4i, the columns
-    // it expands -- and its Q values (B operand of the scores, in log2 units).  Rows past the
-    // window read row 0 and are zeroed.
-    // Every load here and in load_k / load_v is unconditional (addresses clamped into range), so
-    // the compiler can count exactly which loads a wait needs and never waits for later ones.
-    auto load_head = [&](const Task& T, float (&dhr)[kWinGrid], float (&dwv)[4], float (&qreg)[16]) {
-        const int qn = T.qt * win::kQT + l16;
-        const bool qvalid = qn < n;
-        // without bias rows, a row of zeros in the same layout
-        const bool bias = a.dhw != nullptr;
-        const float* br = bias ? a.dhw + ((size_t)(T.w * a.heads + T.head) * n + (qvalid ? qn : 0)) * a.brs
-                               : win::kZeroRow;
-        const int clast = (bias ? a.brs : 2 * kWinGrid) - 4;
-#pragma unroll
-        for (int c = 0; c < kWinGrid / 4; ++c) {
-            // dh[4c .. 4c+3]; past gh4 this reads other values of the row, never used
-            const float4 v = *reinterpret_cast<const float4*>(br + min(4 * c, clast));
-            dhr[4 * c] = v.x; dhr[4 * c + 1] = v.y; dhr[4 * c + 2] = v.z; dhr[4 * c + 3] = v.w;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dwv[i] = br[a.gh4 + min(kq + 4 * i, a.gw - 1)];
-        const float* qr = a.qkv + ((size_t)T.w * n + (qvalid ? qn : 0)) * 3 * a.W + T.head * HD + 4 * kq;
-        const float z = qvalid ? a.qmul : 0.0f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float4 v = *reinterpret_cast<const float4*>(qr + 16 * c);
-            qreg[4 * c + 0] = v.x * z;
-            qreg[4 * c + 1] = v.y * z;
-            qreg[4 * c + 2] = v.z * z;
-            qreg[4 * c + 3] = v.w * z;
-        }
-    };
-    auto load_k = [&](const Task& T, int t, f32x4 (&kf)[4]) {
-        if (t < NT - 1) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                kf[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      T.rsrc, (int)koff, T.kb + 16 * t * (int)rsb + 64 * c, 0));
-        } else {   // the last tile: rows past the last key repeat it (their bias is -inf)
-            const unsigned o = (unsigned)min(16 * t + krow, n - 1) * rsb + 16u * kq;
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                kf[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      T.rsrc, (int)o, T.kb + 64 * c, 0));
-        }
-    };
-    auto load_v = [&](const Task& T, int t, f32x4 (&vf)[4]) {
-        if (t < NT - 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vf[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      T.rsrc, (int)voff, T.vb + (16 * t + 4 * r) * (int)rsb, 0));
-        } else {   // keys past the last one read the last (their probability is 0)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const unsigned o = (unsigned)min(16 * t + 4 * r + kq, n - 1) * rsb + 16u * l16;
-                vf[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(T.rsrc, (int)o, T.vb, 0));
-            }
-        }
-    };
-
-    // Loads complete in issue order: bias rows and Q first, then K and V of the first two tiles
-    // (two tiles ahead of their use: the wavefronts of one (window, head) stream the same tiles
-    // at about the same time, so a tile's first read goes to HBM for all of them).
-    Task T = decode(task);
-    float dhr[kWinGrid], dwv[4], qreg[16];
-    load_head(T, dhr, dwv, qreg);
-    f32x4 kcur[4], vcur[4], k1[4], v1[4];
-    load_k(T, 0, kcur);
-    load_v(T, 0, vcur);
-    if (NT > 1) {
-        load_k(T, 1, k1);
-        load_v(T, 1, v1);
-    }
-    // The bias of every (query, key) pair of the task, E[key][query] in this wavefront's LDS:
-    // the lane writes its query's keys ky * gw + kx for kx = kq + 4i, and -inf past the last key
-    // (so the padding keys of the last tile need no mask).  The lane's own 4 keys of tile t,
-    // 16t + 4r + kq, are read back one tile ahead and start the score accumulators.
-    float* const E = ebuf[wave];
-    float* const col = E + kq * win::kQT + l16;   // E[kq][l16]; key j is j * kQT floats further
-    // Straight-line writes: a column kq + 4i at or past gw lands on a later key of the table
-    // (row ky + 1 or beyond), which is written afterwards in program order -- by a later row or,
-    // past the last row, by the -inf padding or in the spare tile -- so no write needs a guard.
-    auto build_e = [&](const float (&dh)[kWinGrid], const float (&dw)[4]) {
-        // LDS operations of one wavefront complete in issue order; the fences keep the
-        // compiler's order (earlier reads of E before these writes, these before later reads)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int ky = 0; ky < kWinGrid; ++ky) {
-            if (ky < a.gh) {   // wave-uniform
-                float* row = col + ky * a.gw * win::kQT;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) row[4 * i * win::kQT] = dh[ky] + dw[i];
-            }
-        }
-        for (int j = n + kq; j < 16 * NT; j += 4) E[j * win::kQT + l16] = -INFINITY;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    auto read_bias = [&](int t) {
-        f32x4 bv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bv[r] = col[(16 * t + 4 * r) * win::kQT];
-        return bv;
-    };
-    build_e(dhr, dwv);
-    f32x4 bnext = read_bias(0);
-    constexpr float kH = dgk::kHeadroom;
-    const float kBig = __builtin_exp2f(kH);
-
-    int nxt = task + wpx;
-    while (true) {
-        const bool has_next = nxt < hi;
-        const Task N = decode(has_next ? nxt : task);
-
-        f32x4 o[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) o[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Scores come out of the MFMAs relative to the reference `ref` (E holds bias - ref), so
-        // exp2 takes them as they are.  The first tile sets the reference from its maximum (0
-        // while that lies within +-kH: nothing to subtract, and the row's largest term is at
-        // least 2^-kH); later tiles keep it unless a probability exceeds 2^kH, seen from the
-        // tile's sum, which the denominator needs anyway.  Such a tile is redone from its maximum.
-        float m = -INFINITY, ref = 0.0f, lsum = 0.0f;
-        // New reference from the tile's scores (relative to `ref`); rescales o and lsum, and moves
-        // the current scores, the next tile's bias (in registers) and the later tiles' bias (the
-        // lane's own entries of E) to the new reference.
-        auto rebase = [&](int t, f32x4& sc) {
-            float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float m_new = fmaxf(m, ref + tmax);
-            const float nref = (m_new == -INFINITY || fabsf(m_new) <= kH) ? 0.0f : m_new;
-            const float d = nref - ref;
-            const float corr = m == -INFINITY ? 0.0f : dgk::fast_exp2(-d);
-            lsum *= corr;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) o[h] *= corr;
-            sc -= d;
-            if (t + 1 < NT) bnext -= d;
-            if (t + 2 < NT && __any(d != 0.0f)) {
-                for (int u = t + 2; u < NT; ++u)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) col[(16 * u + 4 * r) * win::kQT] -= d;
-            }
-            m = m_new;
-            ref = nref;
-        };
-
-        float dhr_n[kWinGrid], dwv_n[4], qreg_n[16];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            f32x4 k2[4], v2[4];
-            constexpr int kLast = NT - 1;
-            const bool more = t < kLast, more2 = t + 1 < kLast;
-            // k2/v2 take the next task's tile 0 or 1 (the last task reloads its own; unused)
-            const bool cross = kCross && !more2;
-            if (t == 0) {
-                load_head(N, dhr_n, dwv_n, qreg_n);   // the next task's bias rows and Q
-            }
-            if (more2) load_k(T, t + 2, k2);
-            else if (cross) load_k(N, t + 2 - NT, k2);
-            f32x4 sc = bnext;
-            if (more) bnext = read_bias(t + 1);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].x, qreg[4 * c + 0], sc, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].y, qreg[4 * c + 1], sc, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].z, qreg[4 * c + 2], sc, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kcur[c].w, qreg[4 * c + 3], sc, 0, 0, 0);
-            }
-            if (more2) load_v(T, t + 2, v2);
-            else if (cross) load_v(N, t + 2 - NT, v2);
-            if (t == 0) rebase(t, sc);
-            f32x4 p;
-            auto exps = [&]() {
-                p[0] = dgk::fast_exp2(sc[0]);
-                p[1] = dgk::fast_exp2(sc[1]);
-                p[2] = dgk::fast_exp2(sc[2]);
-                p[3] = dgk::fast_exp2(sc[3]);
-            };
-            exps();
-            float psum = (p[0] + p[1]) + (p[2] + p[3]);
-            if (t > 0 && __any(!(psum <= kBig))) {   // a score above the headroom (or inf)
-                rebase(t, sc);
-                exps();
-                psum = (p[0] + p[1]) + (p[2] + p[3]);
-            }
-            lsum += psum;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (t < kLast || r == 0 || 16 * t + 4 * r < n) {   // a step with no key is skipped
-                    o[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].x, p[r], o[0], 0, 0, 0);
-                    o[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].y, p[r], o[1], 0, 0, 0);
-                    o[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].z, p[r], o[2], 0, 0, 0);
-                    o[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(vcur[r].w, p[r], o[3], 0, 0, 0);
-                }
-            }
-            if (t == kLast) {   // this task is done with E: the next task's table (the last
-                                // task rebuilds its own, unused)
-                build_e(dhr_n, dwv_n);
-                bnext = read_bias(0);
-            }
-            if (more || cross) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    kcur[c] = k1[c];
-                    vcur[c] = v1[c];
-                }
-            }
-            if (more2 || cross) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    k1[c] = k2[c];
-                    v1[c] = v2[c];
-                }
-            }
-        }
-
-        float ltot = lsum + __shfl_xor(lsum, 16);
-        ltot += __shfl_xor(ltot, 32);
-        const int qn = T.qt * win::kQT + l16;
-        if (qn < n) {
-            const float inv = 1.0f / ltot;
-            float* orow = a.out + ((size_t)T.w * n + qn) * a.W + T.head * HD + 16 * kq;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<float4*>(orow + 4 * r) =
-                    make_float4(o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv);
-        }
-        if (!has_next) break;
-        task = nxt;
-        nxt += wpx;
-        T = N;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) qreg[i] = qreg_n[i];
-        if (!kCross) {
-            load_k(T, 0, kcur);
-            load_v(T, 0, vcur);
-        }
-    }
-}
 
 // Key tiles are cut along grid rows, so that every lane sees the same kx at the same register
 // slot in every tile:
@@ -557,12 +237,13 @@ __host__ __device__ inline Tiling make_tiling(int gh, int gw) {
     return t;
 }
 
-// Scores and the value product of the 8-wavefront grid kernels run on the bf16 matrix pipe: q
-// once, and each K and V value as it is read from LDS, taken as three bf16 terms, every product
-// as six exact bf16 products summed in f32 (bf16x3.hpp); within 2^-23 |q||k| of each f32
-// product, typically 2^-29.  Two query groups share each tile, so each value is split twice.  The bias terms
-// stay on f32 MFMA, and so does the 4-wavefront shape (three workgroups per CU leave it no
-// registers for the split).  false: f32 MFMA throughout.
+// Scores and the value product run on the bf16 matrix pipe: q, K, V and the probabilities taken
+// as three bf16 terms, every product as six exact bf16 products summed in f32 (bf16x3.hpp);
+// within 2^-23 |q||k| of each f32 product, typically 2^-29.  The 8-wavefront grid shapes split
+// each K and V value in registers as it is read from LDS (two query groups share each tile, so
+// each value is split twice); the 4-wavefront shape, whose four query groups all take every
+// tile, splits each staged tile once into bf16 planes in LDS (bf16x3.hpp, split_stage).  The
+// bias terms stay on f32 MFMA.  false: f32 MFMA throughout.
 constexpr bool kRelF32OnBf16 = true;
 
 // kFull: every tile holds 32 keys (no padding slots, no short last tile); kOneShift: the height
@@ -578,13 +259,20 @@ __global__ void __launch_bounds__(64 * kWavesT)
     constexpr int kTabRows = RelShape<kParts, kWavesT>::kTabRows;
     // staging: [buffer][tile][K, V] and bias tables [group][ky][query] (dh)
     constexpr int kOStride = HD + 4;   // row stride of the output rows restaged at the end
-    constexpr int kStageFloats = 2 * kParts * 2 * TL::kFloats;
+    // 4-wavefront shape on the bf16 pipe: one f32 staging buffer [K, V] of one tile, then the
+    // tile's six bf16 planes (single-buffered: the next tile's loads go out once the split is
+    // done): 40 KiB, 48 KiB with the height-bias table, so three workgroups fit on a CU.
+    constexpr bool kPl = kRelF32OnBf16 && kWavesT == 4;
+    static_assert(!kPl || kParts == 1, "the planes shape takes every tile");
+    constexpr int kStageFloats =
+        kPl ? 2 * TL::kFloats + 2 * 3 * bf3::Planes<HD>::kBytes / 4 : 2 * kParts * 2 * TL::kFloats;
     constexpr int kSmemFloats = kStageFloats > kBlockQ * kOStride ? kStageFloats : kBlockQ * kOStride;
     __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
     __shared__ float tab[kQGroups * kTabRows * dgk::kQuery];
     auto tile_ptr = [&](int buf, int tile, int isv) {
         return smem + ((buf * kParts + tile) * 2 + isv) * TL::kFloats;
     };
+    char* const planes = reinterpret_cast<char*>(smem + 2 * TL::kFloats);   // kPl only
 
     const int lid = xcd_remap(blockIdx.x, a.nblocks, a.nxcd);
     const int qb = lid % a.qblocks;
@@ -625,6 +313,90 @@ __global__ void __launch_bounds__(64 * kWavesT)
     // Prologue: the dh rows of this group's queries (all ky) into LDS, and the lane's dw terms.
     f32x16 dwreg;
     const int qx = valid ? qi % a.gw : 0, qy = valid ? qi / a.gw : 0;
+    // Windowed grids in the 4 x 1 shape on the bf16 pipe (a.lines): the bias rows of the
+    // workgroup's queries as small matrix products on v_mfma_f32_16x16x4f32, as
+    // relpos_bias16_kernel forms them: a row line is grid row qy's queries against rh[qy] (gh
+    // table rows), a column line grid column qx's queries against rw[qx] (gw rows), each one
+    // 16 x 16 tile with a 64-long contraction.  The workgroup's queries lie on grid rows
+    // qy0..qy1 (at most 16), so it takes those row lines and every column line restricted to
+    // those rows; wavefront w takes lines w, w + 4, ..., with the next line's loads in flight
+    // while a line is formed.  Row products go to the dh tables, column products to a
+    // [query][kx] table over the plane area (free until the first split), from which each lane
+    // then takes its dw terms.  Products of queries outside the workgroup are formed and
+    // dropped.  (Forming them after the first stage's loads had gone out measured slower:
+    // SAM windows 46.4 -> 48.0 us per call.)
+    auto form_lines = [&]() {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const int l16 = lane & 15, kq = lane >> 4;
+        const int q0 = qb * kBlockQ;
+        const int qy0 = q0 / a.gw, qy1 = (min(q0 + kBlockQ, a.n) - 1) / a.gw;
+        const int nrl = qy1 - qy0 + 1, nl = nrl + a.gw;
+        constexpr int kDwStride = 16 + 1;
+        float* dwt = reinterpret_cast<float*>(planes);   // [kBlockQ][kDwStride]
+        if (!valid)
+            for (int ky = half; ky < a.gh; ky += 2) dh_tab[ky * dgk::kQuery + l32] = 0.0f;
+        auto load_line = [&](int li, float4 (&x)[4], float4 (&y)[4]) {
+            const bool col = li >= nrl;
+            const int p = col ? li - nrl : qy0 + li;   // the line's grid column or row
+            const int nq = col ? nrl : a.gw, nr = col ? a.gw : a.gh;
+            const int v = min(l16, nq - 1);
+            const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
+            const float* qr = qkvw + (size_t)tok * rs + head * HD + 4 * kq;
+            const float* tr = (col ? a.rw + ((size_t)p * a.gw + min(l16, nr - 1)) * HD
+                                   : a.rh + ((size_t)p * a.gh + min(l16, nr - 1)) * HD) + 4 * kq;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[c] = *reinterpret_cast<const float4*>(qr + 16 * c);
+                y[c] = *reinterpret_cast<const float4*>(tr + 16 * c);
+            }
+        };
+        float4 x[4], y[4], xn[4], yn[4];
+        if (wave < nl) load_line(wave, x, y);
+        for (int li = wave; li < nl; li += kWavesT) {   // wave-uniform
+            if (li + kWavesT < nl) load_line(li + kWavesT, xn, yn);
+            const bool col = li >= nrl;
+            const int p = col ? li - nrl : qy0 + li;
+            const int nq = col ? nrl : a.gw, nr = col ? a.gw : a.gh;
+            // lane l supplies query slot l%16 (A) and table row l%16 (B) at contraction index
+            // l/16; step 4c+e contracts element 16c + 4(l/16) + e; accumulator r holds query
+            // slot 4(l/16) + r against table row l%16
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].x, y[c].x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].y, y[c].y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].z, y[c].z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].w, y[c].w, acc, 0, 0, 0);
+            }
+            if (l16 < nr) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int v = 4 * kq + r;
+                    const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
+                    const int loc = tok - q0;   // index in the workgroup
+                    if (v < nq && loc >= 0 && loc < kBlockQ && tok < a.n) {
+                        const float val = acc[r] * dgk::kLog2e;
+                        if (col)
+                            dwt[loc * kDwStride + l16] = val;
+                        else
+                            tab[((loc >> 5) * kTabRows + l16) * dgk::kQuery + (loc & 31)] = val;
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[c] = xn[c];
+                y[c] = yn[c];
+            }
+        }
+        __syncthreads();
+        const float* dwq = dwt + (grp * dgk::kQuery + l32) * kDwStride;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = dgk::key_of(r, half);
+            dwreg[r] = i < tlen_w ? (valid ? dwq[min(i % a.gw, a.gw - 1)] : 0.0f) : -INFINITY;
+        }
+    };
     if (kPatch && bias) {
         // The bias rows of the patch as small matrix products on v_mfma_f32_16x16x4f32:
         // wavefront w takes patch row w (8 queries of grid row py0 + w against rh[py0 + w]) and
@@ -691,10 +463,12 @@ __global__ void __launch_bounds__(64 * kWavesT)
             const int i = dgk::key_of(r, half);
             dwreg[r] = i < tlen_w ? dwt[p * kDwStride + min(kx0 + i, a.gw - 1)] : -INFINITY;
         }
+    } else if (kPl && bias && a.lines) {
+        form_lines();
     } else if (bias && active && a.dhw) {
-        const float* dhq = a.dhw + ((size_t)unit * a.n + (valid ? qi : 0)) * a.gh;
-        const float* dwq = a.dhw + (size_t)a.nwin * a.heads * a.n * a.gh +
-                           ((size_t)unit * a.n + (valid ? qi : 0)) * a.gw;
+        const size_t row = (size_t)unit * a.n + (valid ? qi : 0);
+        const float* dhq = a.dhw + row * a.dh_stride;
+        const float* dwq = a.dhw + a.dw_off + row * a.dw_stride;
         for (int ky = part * 2 + half; ky < a.gh; ky += 2 * kParts)
             dh_tab[ky * dgk::kQuery + l32] = valid ? dhq[ky] : 0.0f;
 #pragma unroll
@@ -752,7 +526,7 @@ __global__ void __launch_bounds__(64 * kWavesT)
     const int pos = lane % TL::kChunks, rsub = lane / TL::kChunks;
     const unsigned rsb = (unsigned)(rs * 4);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(qkvw), 0, (int)((unsigned)a.n * rsb), (int)win::kRsrcWord3);
+        const_cast<float*>(qkvw), 0, (int)((unsigned)a.n * rsb), (int)kRsrcWord3);
     const int colk = (a.W + head * HD) * 4, colv = (2 * a.W + head * HD) * 4;
     // lane offsets of full-tile loads: row rsub of load ld's 4 rows; K's chunk pos ^ (row % 16)
     // depends on ld % 4 only (row = 4 * ld + rsub < 32)
@@ -773,11 +547,11 @@ __global__ void __launch_bounds__(64 * kWavesT)
             unsigned off;
             int soff;
             if (kFull) {
-                off = isv ? voffs : koffs[i % 4];   // ld % 4 == i % 4 in every shape
+                off = isv || kPl ? voffs : koffs[i % 4];   // ld % 4 == i % 4 in every shape
                 soff = (isv ? colv : colk) + (j0 + R * ld) * (int)rsb;
             } else {
                 const int trow = ld * R + rsub;
-                const unsigned coff = 16u * (isv ? pos : (pos ^ (trow % TL::kChunks)));
+                const unsigned coff = 16u * (isv || kPl ? pos : (pos ^ (trow % TL::kChunks)));
                 off = (unsigned)min(trow, tile_len(t) - 1) * rsb + coff;
                 soff = (isv ? colv : colk) + j0 * (int)rsb;
             }
@@ -786,11 +560,15 @@ __global__ void __launch_bounds__(64 * kWavesT)
         }
     };
 
-    float qreg[HD / 2];
-    dgk::load_q<HD>(qrow, valid, half, a.qmul, qreg);
     constexpr bool kBf16Pipe = kRelF32OnBf16 && kWavesT == 8;
-    bf3::QSplit<kBf16Pipe ? HD : 16> q3;
-    if constexpr (kBf16Pipe) bf3::split_q_bf16x3<HD>(qreg, q3);
+    float qreg[kPl ? 1 : HD / 2];
+    bf3::QSplit<kBf16Pipe || kPl ? HD : 16> q3;
+    if constexpr (kPl) {
+        bf3::load_q_bf16x3<HD>(qrow, valid, half, a.qmul, q3, HD);
+    } else {
+        dgk::load_q<HD>(qrow, valid, half, a.qmul, qreg);
+        if constexpr (kBf16Pipe) bf3::split_q_bf16x3<HD>(qreg, q3);
+    }
     f32x16 o[TL::kGroups];
 #pragma unroll
     for (int t = 0; t < TL::kGroups; ++t)
@@ -802,11 +580,21 @@ __global__ void __launch_bounds__(64 * kWavesT)
     if (wave < 4) issue_stage(0, BufC<0>{});
     // One stage; the stage loop is unrolled by two so that the buffer index is a constant and
     // the LDS reads of a tile take immediate offsets.
+    int voff[TL::kGroups];   // planes: the lane's transposed-read offsets into a V plane
+    if constexpr (kPl) bf3::vtr_offsets<HD>(lane, voff);
     auto stage = [&](int st, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
+        constexpr int buf = kPl ? 0 : decltype(bufc)::value;
+        constexpr int nbuf = kPl ? 0 : buf ^ 1;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // stage st has landed everywhere, stage st-1 is consumed (and the
                           // bias tables are complete before the first use)
+        if constexpr (kPl) {
+            // the workgroup splits the staged tile into its planes; the staging buffer is then
+            // free for the next tile's loads
+            bf3::split_stage<HD, 64 * kWavesT, 1>(reinterpret_cast<const char*>(smem), TL::kFloats * 4,
+                                                  planes, 1, tid);
+            __syncthreads();
+        }
         const int t = st * kParts + part;
         // The height-bias table values of this tile (one per step; a row tile has at most 8 rows,
         // so at most 4 steps).  An LDS read issued after the next stage's loads makes the
@@ -831,7 +619,7 @@ __global__ void __launch_bounds__(64 * kWavesT)
             }
         };
         if constexpr (kParts == 1) read_dh();
-        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, BufC<buf ^ 1>{});
+        if (wave < 4 && st + 1 < nstage) issue_stage(st + 1, BufC<nbuf>{});
         if constexpr (kParts != 1) read_dh();
         if (active && t < a.ntiles) {
             const float ref = dgk::ref_of(m);
@@ -847,7 +635,9 @@ __global__ void __launch_bounds__(64 * kWavesT)
                         s = __builtin_amdgcn_mfma_f32_32x32x2f32(arow == 2 * ms + half ? 1.0f : 0.0f,
                                                                  dhv[ms] - ref, s, 0, 0, 0);
             }
-            if constexpr (kBf16Pipe)
+            if constexpr (kPl)
+                s = bf3::scores_planes<HD>(bf3::Planes<HD>::at(planes, 0, 0, 0), l32, half, q3, s);
+            else if constexpr (kBf16Pipe)
                 s = bf3::scores_f32_bf16x6<HD>(tile_ptr(buf, part, 0), l32, half, q3, s);
             else
                 s = dgk::scores_from<HD>(tile_ptr(buf, part, 0), l32, half, qreg, s);
@@ -860,7 +650,9 @@ __global__ void __launch_bounds__(64 * kWavesT)
                 }
             }
             dgk::softmax_update<HD>(s, m, lsum, o);
-            if constexpr (kBf16Pipe)
+            if constexpr (kPl)
+                bf3::accumulate_pv_planes<HD>(bf3::Planes<HD>::at(planes, 0, 1, 0), voff, s, o);
+            else if constexpr (kBf16Pipe)
                 bf3::accumulate_pv_f32_bf16x6<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
             else
                 dgk::accumulate_pv<HD>(tile_ptr(buf, part, 1), l32, half, s, o);
@@ -878,7 +670,14 @@ __global__ void __launch_bounds__(64 * kWavesT)
     // merge scratch) and written with 16 contiguous bytes per lane: whole 256-byte rows rather
     // than 8-byte pieces spread over 32 rows per instruction.
     __syncthreads();
-    if (part == 0) dgk::stage_row<HD>(smem + grp * dgk::kQuery * kOStride, l32, valid ? 1.0f / ltot : 0.0f, o, half);
+    if (part == 0) {
+        float* rows = smem + grp * dgk::kQuery * kOStride;
+        const float inv = valid ? 1.0f / ltot : 0.0f;
+        if constexpr (kPl)
+            bf3::stage_row_blocked<HD>(rows, l32, inv, o, half);   // output rows of the V planes
+        else
+            dgk::stage_row<HD>(rows, l32, inv, o, half);
+    }
     __syncthreads();
     constexpr int kChunksO = HD / 4;
     constexpr int kRowsPerPass = 64 * kWavesT / kChunksO;
@@ -895,7 +694,8 @@ __global__ void __launch_bounds__(64 * kWavesT)
 }  // namespace
 
 namespace {
-// Grids whose lines fit one 16x16 tile take the 16-query wavefront kernel.
+// Grids whose lines fit one 16x16 tile (the windows): the 4 x 1 shape forms their bias rows
+// itself; otherwise relpos_bias16_kernel writes them to the workspace.
 bool win_grid(int gh, int gw) { return gh <= kWinGrid && gw <= kWinGrid; }
 int round4(int x) { return (x + 3) & ~3; }
 // Floats per (window, head, query) of bias rows: dh then dw, each padded to 4 floats for the
@@ -969,8 +769,8 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     if ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(out) |
          reinterpret_cast<uintptr_t>(rh) | reinterpret_cast<uintptr_t>(rw)) & 15)
         return dg::fail(DG_EINVAL, "%s: tensor pointers must be 16-byte aligned", fn);
-    const bool use_win = win_grid(gh, gw) && (use_ws || !rh);
-    if (use_win && (size_t)n * 12 * W > 0x7fffffffu)
+    // every kernel addresses a window's qkv rows through one buffer descriptor
+    if ((size_t)n * 12 * W > 0x7fffffffu)
         return dg::fail(DG_EUNSUPPORTED, "%s: a window of %lld tokens x %zu floats exceeds 2 GiB", fn, n,
                         3 * W);
     const bool small = n <= kSmallGrid;              // 4 x 2 workgroups for small grids
@@ -984,11 +784,14 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     // each workgroup's time.
     const dg::Topology topo = dg::device_topology();
     const bool rows16 = small && gh <= kSmallRows && gw <= 32 && nblocks > topo.cus;
+    // that shape on the bf16 pipe forms the bias rows of windowed grids itself
+    const bool lines = kRelF32OnBf16 && rows16 && rh && win_grid(gh, gw);
     if (nblocks > 0x7fffffffLL || (long long)nwin * heads * (gh + gw) > 0x1fffffffLL)
         return dg::fail(DG_EUNSUPPORTED, "%s: too many workgroups", fn);
     RelArgs a;
     a.qkv = qkv; a.rh = rh; a.rw = rw; a.out = out;
-    a.dhw = use_ws ? static_cast<const float*>(workspace) : nullptr;
+    a.dhw = use_ws && !lines ? static_cast<const float*>(workspace) : nullptr;
+    a.lines = lines ? 1 : 0;
     a.n = (int)n; a.gh = gh; a.gw = gw; a.heads = heads; a.W = (int)W; a.nwin = nwin;
     a.qblocks = (int)qblocks;
     a.nblocks = (int)nblocks;
@@ -1003,42 +806,29 @@ int relpos_call(const char* fn, const float* qkv, const float* rh, const float* 
     }
     a.gh4 = round4(gh);
     a.brs = bias_row_floats(gh, gw);
-    a.qtiles = (int)((n + win::kQT - 1) / win::kQT);
+    // where the bias pass puts the rows: relpos_bias16_kernel one row [dh | dw] per query
+    // (windowed grids), relpos_bias_kernel a dh block and then a dw block
+    if (win_grid(gh, gw)) {
+        a.dh_stride = a.brs; a.dw_stride = a.brs; a.dw_off = (size_t)a.gh4;
+    } else {
+        a.dh_stride = gh; a.dw_stride = gw; a.dw_off = (size_t)nwin * heads * n * gh;
+    }
     hipStream_t s = (hipStream_t)stream;
-    if (use_win) {
-        const long long ntasks = (long long)nwin * heads * a.qtiles;
-        if (ntasks > 0x7fffffffLL)
-            return dg::fail(DG_EUNSUPPORTED, "%s: too many tasks", fn);
-        // as many workgroups as run at once (two per CU: 2 wavefronts per SIMD), each
-        // wavefront looping over tasks; a multiple of the XCD count for xcd_remap
-        const long long nx = topo.xcds;
-        const long long want = (ntasks + win::kWaves - 1) / win::kWaves;
-        const long long cap = 2LL * topo.cus;
-        const long long nwg = ((want < cap ? want : cap) + nx - 1) / nx * nx;
-        if (use_ws) {
+    const long long nx = topo.xcds;
+    if (use_ws && !lines) {   // the bias rows, before the attention
+        if (win_grid(gh, gw)) {
             const long long nbt = (long long)nwin * heads * (gh + gw);
             const long long nbias = (nbt + kBiasWaves - 1) / kBiasWaves;
             const dim3 bgrid((unsigned)((nbias + nx - 1) / nx * nx));
             hipLaunchKernelGGL(relpos_bias16_kernel, bgrid, dim3(64 * kBiasWaves), 0, s, a,
                                static_cast<float*>(workspace), (int)nbt);
+        } else {
+            const long long ntasks = (long long)nwin * heads * (gh + gw) * 4;
+            const long long nbias = (ntasks + kBiasWaves - 1) / kBiasWaves;
+            const dim3 grid((unsigned)((nbias + nx - 1) / nx * nx));   // whole XCD rounds for xcd_remap
+            hipLaunchKernelGGL(relpos_bias_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
+                               static_cast<float*>(workspace), ntasks);
         }
-        const dim3 grid((unsigned)nwg);
-        static void (*const kWin[16])(RelArgs, int) = {
-            relpos_win_kernel<1>,  relpos_win_kernel<2>,  relpos_win_kernel<3>,  relpos_win_kernel<4>,
-            relpos_win_kernel<5>,  relpos_win_kernel<6>,  relpos_win_kernel<7>,  relpos_win_kernel<8>,
-            relpos_win_kernel<9>,  relpos_win_kernel<10>, relpos_win_kernel<11>, relpos_win_kernel<12>,
-            relpos_win_kernel<13>, relpos_win_kernel<14>, relpos_win_kernel<15>, relpos_win_kernel<16>};
-        auto* wk = kWin[(n + 15) / 16 - 1];
-        hipLaunchKernelGGL(wk, grid, dim3(64 * win::kWaves), 0, s, a, (int)ntasks);
-        return dg::launch_status(fn);
-    }
-    if (use_ws) {
-        const long long ntasks = (long long)nwin * heads * (gh + gw) * 4;
-        const long long nbias = (ntasks + kBiasWaves - 1) / kBiasWaves;
-        const long long nx = topo.xcds;
-        const dim3 grid((unsigned)((nbias + nx - 1) / nx * nx));   // whole XCD rounds for xcd_remap
-        hipLaunchKernelGGL(relpos_bias_kernel, grid, dim3(64 * kBiasWaves), 0, s, a,
-                           static_cast<float*>(workspace), ntasks);
     }
     const bool full = tl.half_rows ? gw == 64 : (tl.kpt == dgk::kKeys && gh % tl.rpt == 0);
     const bool one = tl.nshift == 1;

@@ -515,6 +515,13 @@ def oracle_windows(c):
                                                    # more workgroups than CUs: the 4-wavefront
                                                    # shape, on ragged grids
                                                    (130, 5, 7, 2, True), (90, 11, 13, 3, False),
+                                                   # ... forming the bias rows of windowed grids
+                                                   # itself: full 16 x 16, one column, one row,
+                                                   # three columns (8-row tiles), workgroups
+                                                   # ending inside a grid row
+                                                   (260, 16, 16, 1, True), (300, 16, 1, 1, True),
+                                                   (300, 1, 16, 1, True), (300, 16, 3, 1, True),
+                                                   (270, 10, 9, 1, True),
                                                    # 8 x 8 query patches
                                                    (2, 16, 48, 1, True)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
