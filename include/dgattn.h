@@ -361,7 +361,9 @@ size_t relpos_flash_attn_workspace_size(int gh, int gw, int heads, int hd);
  * reads them.  Same results as relpos_flash_attn up to rounding; faster.  Grids of more than
  * 512 tokens whose sides are multiples of 8 and whose width is above 32 (the SAM global 64 x
  * 64 map) form the bias rows inside the attention from 8 x 8 patches of queries either way, and
- * leave the workspace unused.
+ * leave the workspace unused; so do grids of at most 16 x 16 (the windows) when the launch has
+ * more workgroups than the GPU has CUs (128 queries of one window and head per workgroup),
+ * from whole grid rows and columns of their queries.
  *   workspace  device scratch of at least relpos_flash_attn_workspace_size() bytes, 16-byte
  *              aligned, not overlapping any input or `out` (NULL/0: as relpos_flash_attn).
  * Errors: as relpos_flash_attn, plus DG_EINVAL for a misaligned or too small workspace.
