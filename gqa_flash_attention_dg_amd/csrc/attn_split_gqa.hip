@@ -253,7 +253,17 @@ constexpr int kQStride = HD + 4;
 // c+24; a wave covers 8 vectors per pass, and the sum of squares takes 3 lane exchanges.  The
 // rope partner of element e (e +- hd/2, any even hd) is read back from the staged row, which
 // the same wavefront wrote (LDS accesses of one wavefront complete in order).
-template <int HD, int QN = kBlockQ>
+//
+// kQPlanes (hd == HD, the bf16 pipe): the vectors are written instead as three bf16 planes,
+// split once here rather than by both wavefronts of a pair, for load_q_planes to read back.
+// Plane p holds row v at qs + (p * QN + v) * HD bf16, its 16-byte chunk j (elements 8j..8j+7)
+// at position j ^ (v mod HD/8), so the 32 rows a wavefront reads at once spread over all banks.
+// The rope partner of chunk k is the lane's own chunk k ^ (HD/64): hd/2 is 8 chunks of 4
+// elements away.
+template <int HD>
+constexpr int kQPlaneBytes = kBlockQ * HD * 2;   // one bf16 plane of the workgroup's queries
+
+template <int HD, int QN = kBlockQ, bool kQPlanes = false>
 __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs, int b, int kv,
                                       int qb, int wave, int lane, int hd) {
     constexpr int kPerLane = HD / 32;  // float4 chunks per lane
@@ -306,9 +316,11 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
             x[k].w = x[k].w * inv * w[k].w;
         }
         if (rope) {
+            if constexpr (!kQPlanes) {
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k)
-                *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) = x[k];
+                for (int k = 0; k < kPerLane; ++k)
+                    *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) = x[k];
+            }
             if (row != cs_row) {   // the same for the 8 lanes of a vector
                 const float* cr = a.cs + (size_t)row * 2 * hd;
 #pragma unroll
@@ -322,14 +334,22 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
                 cs_row = row;
             }
             float part[kPerLane][4];
+            if constexpr (kQPlanes) {
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * (c + 8 * k) + i;
-                    const int pe = e < half_hd ? e + half_hd : e - half_hd;
-                    part[k][i] = e < hd ? srow[pe] : 0.0f;
+                for (int k = 0; k < kPerLane; ++k) {
+                    const float4 pk = x[k ^ (kPerLane / 2)];
+                    part[k][0] = pk.x; part[k][1] = pk.y; part[k][2] = pk.z; part[k][3] = pk.w;
                 }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kPerLane; ++k)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * (c + 8 * k) + i;
+                        const int pe = e < half_hd ? e + half_hd : e - half_hd;
+                        part[k][i] = e < hd ? srow[pe] : 0.0f;
+                    }
+            }
 #pragma unroll
             for (int k = 0; k < kPerLane; ++k) {
                 const int e0 = 4 * (c + 8 * k);
@@ -347,10 +367,41 @@ __device__ inline void stage_q_normed(const SplitArgs& a, float* __restrict__ qs
                 }
             }
         }
+        if constexpr (kQPlanes) {
+            const SplitWeights sw;
+            char* prow = reinterpret_cast<char*>(qs) + vloc * HD * 2;
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k)
-            *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) =
-                make_float4(x[k].x * a.qmul, x[k].y * a.qmul, x[k].z * a.qmul, x[k].w * a.qmul);
+            for (int k = 0; k < kPerLane; ++k) {
+                const int ch = c + 8 * k;   // 4-element chunk: half ch & 1 of 16-byte chunk ch >> 1
+                unsigned h0, m0, l0, h1, m1, l1;
+                split_bf16x3(x[k].x * a.qmul, x[k].y * a.qmul, sw, h0, m0, l0);
+                split_bf16x3(x[k].z * a.qmul, x[k].w * a.qmul, sw, h1, m1, l1);
+                char* dst = prow + 16 * ((ch >> 1) ^ (vloc % (HD / 8))) + 8 * (ch & 1);
+                *reinterpret_cast<uint2*>(dst) = make_uint2(h0, h1);
+                *reinterpret_cast<uint2*>(dst + kQPlaneBytes<HD>) = make_uint2(m0, m1);
+                *reinterpret_cast<uint2*>(dst + 2 * kQPlaneBytes<HD>) = make_uint2(l0, l1);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k)
+                *reinterpret_cast<float4*>(srow + 4 * (c + 8 * k)) =
+                    make_float4(x[k].x * a.qmul, x[k].y * a.qmul, x[k].z * a.qmul, x[k].w * a.qmul);
+        }
+    }
+}
+
+// The lane's query operand (the load_q_bf16x3 layout) from the planes stage_q_normed<kQPlanes>
+// wrote: row v, step st reads 16-byte chunk 2*st + half of each plane.
+template <int HD>
+__device__ inline void load_q_planes(const char* __restrict__ qp, int v, int half, QSplit<HD>& q) {
+    const char* row = qp + v * HD * 2;
+    const int sw = v % (HD / 8);
+#pragma unroll
+    for (int st = 0; st < HD / 16; ++st) {
+        const char* src = row + 16 * ((2 * st + half) ^ sw);
+        q.h[st] = *reinterpret_cast<const u32x4*>(src);
+        q.m[st] = *reinterpret_cast<const u32x4*>(src + kQPlaneBytes<HD>);
+        q.l[st] = *reinterpret_cast<const u32x4*>(src + 2 * kQPlaneBytes<HD>);
     }
 }
 
@@ -614,13 +665,20 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
     if constexpr (kNormQ) {
         static_assert(!kBf16, "16-bit K/V take normalised q");
         float* qs = smem + kQOff;
-        stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
-        __syncthreads();
-        const float* qrow = qs + (pair * dgk::kQuery + l32) * kQStride<HD>;
-        if constexpr (kQ3)
-            load_q_bf16x3<HD>(qrow, true, half, 1.0f, q3, HD);
-        else
-            dgk::load_q<HD>(qrow, true, half, 1.0f, qreg);
+        if constexpr (kPlanes && !kPad) {   // q split once, into bf16 planes over the K/V planes
+            static_assert(3 * kQPlaneBytes<HD> <= 2 * 2 * 3 * Planes<HD>::kBytes, "q planes fit");
+            stage_q_normed<HD, kBlockQ, true>(a, qs, b, kv, qb, wave, lane, hd);
+            __syncthreads();
+            load_q_planes<HD>(reinterpret_cast<const char*>(qs), pair * dgk::kQuery + l32, half, q3);
+        } else {
+            stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
+            __syncthreads();
+            const float* qrow = qs + (pair * dgk::kQuery + l32) * kQStride<HD>;
+            if constexpr (kQ3)
+                load_q_bf16x3<HD>(qrow, true, half, 1.0f, q3, HD);
+            else
+                dgk::load_q<HD>(qrow, true, half, 1.0f, qreg);
+        }
     } else if constexpr (kQ3) {
         load_q_bf16x3<HD>(a.q + gq * hd, valid, half, a.qmul, q3, hd);
     } else {
