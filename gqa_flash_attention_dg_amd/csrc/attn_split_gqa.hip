@@ -657,8 +657,10 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         }
     };
 
-    // The first stage's loads go out before the queries are fetched, so the two overlap.
-    if (!hi && nst > 0) issue_stage(0, 0);
+    // The first stage's loads go out before the queries are fetched, so the two overlap; with
+    // the q norm inside, after the queries have been staged, so that the opening burst of every
+    // workgroup serves the queries first (measured: DiffusionGemma-like step 29.40 -> 29.22 us).
+    if (!kNormQ && !hi && nst > 0) issue_stage(0, 0);
     constexpr bool kQ3 = kBf16 || kPlanes;   // q as three bf16 terms
     float qreg[kQ3 ? 1 : HD / 2];
     QSplit<kQ3 ? HD : 16> q3;
@@ -668,10 +670,12 @@ __global__ void __launch_bounds__(512) attn_split_gqa_kernel(SplitArgs a) {
         if constexpr (kPlanes && !kPad) {   // q split once, into bf16 planes over the K/V planes
             static_assert(3 * kQPlaneBytes<HD> <= 2 * 2 * 3 * Planes<HD>::kBytes, "q planes fit");
             stage_q_normed<HD, kBlockQ, true>(a, qs, b, kv, qb, wave, lane, hd);
+            if (!hi && nst > 0) issue_stage(0, 0);
             __syncthreads();
             load_q_planes<HD>(reinterpret_cast<const char*>(qs), pair * dgk::kQuery + l32, half, q3);
         } else {
             stage_q_normed<HD>(a, qs, b, kv, qb, wave, lane, hd);
+            if (!hi && nst > 0) issue_stage(0, 0);
             __syncthreads();
             const float* qrow = qs + (pair * dgk::kQuery + l32) * kQStride<HD>;
             if constexpr (kQ3)
