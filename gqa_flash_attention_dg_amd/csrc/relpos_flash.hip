@@ -319,82 +319,107 @@ __global__ void __launch_bounds__(64 * kWavesT)
     // table rows), a column line grid column qx's queries against rw[qx] (gw rows), each one
     // 16 x 16 tile with a 64-long contraction.  The workgroup's queries lie on grid rows
     // qy0..qy1 (at most 16), so it takes those row lines and every column line restricted to
-    // those rows; wavefront w takes lines w, w + 4, ..., with the next line's loads in flight
-    // while a line is formed.  Row products go to the dh tables, column products to a
-    // [query][kx] table over the plane area (free until the first split), from which each lane
-    // then takes its dw terms.  Products of queries outside the workgroup are formed and
-    // dropped.  (Forming them after the first stage's loads had gone out measured slower:
-    // SAM windows 46.4 -> 48.0 us per call.)
+    // those rows; wavefront w takes lines w, w + 4, ..., three at a time with all their table
+    // loads in flight together.  The query operands come from the workgroup's query rows,
+    // staged in LDS once (each row serves a row line and a column line).  Row products go to
+    // the dh tables, column products to a [query][kx] table beside the staged rows, from which
+    // each lane then takes its dw terms.  Products of queries outside the workgroup are formed
+    // and dropped.  Measured on the SAM windows (per call): lines one at a time 46.4 us, three
+    // at a time 46.3 us, query rows from LDS 43.8 us; forming the lines after the first
+    // stage's loads had gone out, 48.0 us.
     auto form_lines = [&]() {
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         const int l16 = lane & 15, kq = lane >> 4;
         const int q0 = qb * kBlockQ;
         const int qy0 = q0 / a.gw, qy1 = (min(q0 + kBlockQ, a.n) - 1) / a.gw;
         const int nrl = qy1 - qy0 + 1, nl = nrl + a.gw;
-        constexpr int kDwStride = 16 + 1;
-        float* dwt = reinterpret_cast<float*>(planes);   // [kBlockQ][kDwStride]
+        // The workgroup's query rows (this head's 64 elements) are staged in LDS first, each
+        // read by one row line and one column line: row r at smem + 64 r, its 16-byte chunk j
+        // at position j ^ (r mod 16), so the 16 rows of a line's operand read spread over the
+        // banks.  The [query][kx] table follows them.  Both lie in the stage and plane areas,
+        // free until the first stage's loads.
+        constexpr int kDwStride = 16;
+        static_assert(kBlockQ * (HD + kDwStride) <= kSmemFloats, "query rows and dw table fit");
+        float* const qst = smem;
+        float* const dwt = smem + kBlockQ * HD;   // [kBlockQ][kDwStride]
+#pragma unroll
+        for (int i = 0; i < kBlockQ * (HD / 4) / (64 * kWavesT); ++i) {
+            const int id = tid + 64 * kWavesT * i, r = id / (HD / 4), j = id % (HD / 4);
+            const float4 v = *reinterpret_cast<const float4*>(
+                qkvw + (size_t)min(q0 + r, a.n - 1) * rs + head * HD + 4 * j);
+            *reinterpret_cast<float4*>(qst + r * HD + 4 * (j ^ (r % 16))) = v;
+        }
         if (!valid)
             for (int ky = half; ky < a.gh; ky += 2) dh_tab[ky * dgk::kQuery + l32] = 0.0f;
+        __syncthreads();
         auto load_line = [&](int li, float4 (&x)[4], float4 (&y)[4]) {
             const bool col = li >= nrl;
             const int p = col ? li - nrl : qy0 + li;   // the line's grid column or row
             const int nq = col ? nrl : a.gw, nr = col ? a.gw : a.gh;
             const int v = min(l16, nq - 1);
             const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
-            const float* qr = qkvw + (size_t)tok * rs + head * HD + 4 * kq;
+            // a slot outside the workgroup reads some staged row; its products are dropped
+            const int r = min(max(tok - q0, 0), kBlockQ - 1);
             const float* tr = (col ? a.rw + ((size_t)p * a.gw + min(l16, nr - 1)) * HD
                                    : a.rh + ((size_t)p * a.gh + min(l16, nr - 1)) * HD) + 4 * kq;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                x[c] = *reinterpret_cast<const float4*>(qr + 16 * c);
                 y[c] = *reinterpret_cast<const float4*>(tr + 16 * c);
+                x[c] = *reinterpret_cast<const float4*>(qst + r * HD + 4 * ((4 * c + kq) ^ (r % 16)));
             }
         };
-        float4 x[4], y[4], xn[4], yn[4];
-        if (wave < nl) load_line(wave, x, y);
-        for (int li = wave; li < nl; li += kWavesT) {   // wave-uniform
-            if (li + kWavesT < nl) load_line(li + kWavesT, xn, yn);
-            const bool col = li >= nrl;
-            const int p = col ? li - nrl : qy0 + li;
-            const int nq = col ? nrl : a.gw, nr = col ? a.gw : a.gh;
-            // lane l supplies query slot l%16 (A) and table row l%16 (B) at contraction index
-            // l/16; step 4c+e contracts element 16c + 4(l/16) + e; accumulator r holds query
-            // slot 4(l/16) + r against table row l%16
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // kLB lines per round trip: all their loads go out, then their products are formed
+        constexpr int kLB = 3;
+        for (int l0 = wave; l0 < nl; l0 += kLB * kWavesT) {   // wave-uniform
+            float4 x[kLB][4], y[kLB][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].x, y[c].x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].y, y[c].y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].z, y[c].z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c].w, y[c].w, acc, 0, 0, 0);
-            }
-            if (l16 < nr) {
+            for (int bl = 0; bl < kLB; ++bl)
+                if (l0 + bl * kWavesT < nl) load_line(l0 + bl * kWavesT, x[bl], y[bl]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int v = 4 * kq + r;
-                    const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
-                    const int loc = tok - q0;   // index in the workgroup
-                    if (v < nq && loc >= 0 && loc < kBlockQ && tok < a.n) {
-                        const float val = acc[r] * dgk::kLog2e;
-                        if (col)
-                            dwt[loc * kDwStride + l16] = val;
-                        else
-                            tab[((loc >> 5) * kTabRows + l16) * dgk::kQuery + (loc & 31)] = val;
+            for (int bl = 0; bl < kLB; ++bl) {
+                const int li = l0 + bl * kWavesT;
+                if (li >= nl) break;
+                const bool col = li >= nrl;
+                const int p = col ? li - nrl : qy0 + li;
+                const int nq = col ? nrl : a.gw, nr = col ? a.gw : a.gh;
+                // lane l supplies query slot l%16 (A) and table row l%16 (B) at contraction
+                // index l/16; step 4c+e contracts element 16c + 4(l/16) + e; accumulator r holds
+                // query slot 4(l/16) + r against table row l%16
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[bl][c].x, y[bl][c].x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[bl][c].y, y[bl][c].y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[bl][c].z, y[bl][c].z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[bl][c].w, y[bl][c].w, acc, 0, 0, 0);
+                }
+                if (l16 < nr) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int v = 4 * kq + r;
+                        const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
+                        const int loc = tok - q0;   // index in the workgroup
+                        if (v < nq && loc >= 0 && loc < kBlockQ && tok < a.n) {
+                            const float val = acc[r] * dgk::kLog2e;
+                            if (col)
+                                dwt[loc * kDwStride + l16] = val;
+                            else
+                                tab[((loc >> 5) * kTabRows + l16) * dgk::kQuery + (loc & 31)] = val;
+                        }
                     }
                 }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                x[c] = xn[c];
-                y[c] = yn[c];
             }
         }
         __syncthreads();
         const float* dwq = dwt + (grp * dgk::kQuery + l32) * kDwStride;
+        // kx = i mod gw without an integer division per slot: (i + 1/2) / gw lies at least
+        // 1/(2 gw) from an integer, far beyond the rounding of the product, so its floor is exact
+        const float inv_gw = 1.0f / (float)a.gw;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = dgk::key_of(r, half);
-            dwreg[r] = i < tlen_w ? (valid ? dwq[min(i % a.gw, a.gw - 1)] : 0.0f) : -INFINITY;
+            const int kx = i - a.gw * (int)(((float)i + 0.5f) * inv_gw);
+            dwreg[r] = i < tlen_w ? (valid ? dwq[kx] : 0.0f) : -INFINITY;
         }
     };
     if (kPatch && bias) {
