@@ -310,6 +310,10 @@ __global__ void __launch_bounds__(64 * kWavesT)
     const int arow = l32 < tlen_w ? (tl.half_rows ? 0 : l32 / a.gw) : -1;
     const float aone = arow == half ? 1.0f : 0.0f;   // the single step's A (kOneShift)
 
+    constexpr bool kBf16Pipe = kRelF32OnBf16 && kWavesT == 8;
+    float qreg[kPl ? 1 : HD / 2];
+    bf3::QSplit<kBf16Pipe || kPl ? HD : 16> q3;
+
     // Prologue: the dh rows of this group's queries (all ky) into LDS, and the lane's dw terms.
     f32x16 dwreg;
     const int qx = valid ? qi % a.gw : 0, qy = valid ? qi / a.gw : 0;
@@ -408,6 +412,27 @@ __global__ void __launch_bounds__(64 * kWavesT)
                         }
                     }
                 }
+            }
+        }
+        // the attention's own query operand (the load_q_bf16x3 layout), from the staged rows,
+        // before the barrier after which the first stage's loads may overwrite them
+        {
+            const int r = grp * dgk::kQuery + l32;   // the lane's query, index in the workgroup
+            const bf3::SplitWeights w;
+#pragma unroll
+            for (int st = 0; st < HD / 16; ++st) {
+                float x[8];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int ch = 4 * st + 2 * half + c;   // elements 16 st + 8 half + 4 c ..
+                    const float4 v = valid ? *reinterpret_cast<const float4*>(qst + r * HD + 4 * (ch ^ (r % 16)))
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                    x[4 * c + 0] = v.x * a.qmul;
+                    x[4 * c + 1] = v.y * a.qmul;
+                    x[4 * c + 2] = v.z * a.qmul;
+                    x[4 * c + 3] = v.w * a.qmul;
+                }
+                if constexpr (kPl) bf3::split8(x, w, q3.h[st], q3.m[st], q3.l[st]);
             }
         }
         __syncthreads();
@@ -585,11 +610,9 @@ __global__ void __launch_bounds__(64 * kWavesT)
         }
     };
 
-    constexpr bool kBf16Pipe = kRelF32OnBf16 && kWavesT == 8;
-    float qreg[kPl ? 1 : HD / 2];
-    bf3::QSplit<kBf16Pipe || kPl ? HD : 16> q3;
     if constexpr (kPl) {
-        bf3::load_q_bf16x3<HD>(qrow, valid, half, a.qmul, q3, HD);
+        if (!(bias && a.lines))   // with the lines, q3 was read from the staged query rows
+            bf3::load_q_bf16x3<HD>(qrow, valid, half, a.qmul, q3, HD);
     } else {
         dgk::load_q<HD>(qrow, valid, half, a.qmul, qreg);
         if constexpr (kBf16Pipe) bf3::split_q_bf16x3<HD>(qreg, q3);
