@@ -346,6 +346,35 @@ __global__ void __launch_bounds__(64 * kWavesT)
         static_assert(kBlockQ * (HD + kDwStride) <= kSmemFloats, "query rows and dw table fit");
         float* const qst = smem;
         float* const dwt = smem + kBlockQ * HD;   // [kBlockQ][kDwStride]
+        // Line li: grid row qy0 + li (li < nrl) or grid column li - nrl.
+        auto load_table = [&](int li, float4 (&y)[4]) {
+            const bool col = li >= nrl;
+            const int p = col ? li - nrl : qy0 + li;   // the line's grid column or row
+            const int nr = col ? a.gw : a.gh;
+            const float* tr = (col ? a.rw + ((size_t)p * a.gw + min(l16, nr - 1)) * HD
+                                   : a.rh + ((size_t)p * a.gh + min(l16, nr - 1)) * HD) + 4 * kq;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) y[c] = *reinterpret_cast<const float4*>(tr + 16 * c);
+        };
+        auto load_query = [&](int li, float4 (&x)[4]) {
+            const bool col = li >= nrl;
+            const int p = col ? li - nrl : qy0 + li;
+            const int nq = col ? nrl : a.gw;
+            const int v = min(l16, nq - 1);
+            const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
+            // a slot outside the workgroup reads some staged row; its products are dropped
+            const int r = min(max(tok - q0, 0), kBlockQ - 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                x[c] = *reinterpret_cast<const float4*>(qst + r * HD + 4 * ((4 * c + kq) ^ (r % 16)));
+        };
+        // kLB lines per round trip: all their table loads go out, then their products are
+        // formed; the first batch's go out before the query rows are staged
+        constexpr int kLB = 3;
+        float4 y[kLB][4];
+#pragma unroll
+        for (int bl = 0; bl < kLB; ++bl)
+            if (wave + bl * kWavesT < nl) load_table(wave + bl * kWavesT, y[bl]);
 #pragma unroll
         for (int i = 0; i < kBlockQ * (HD / 4) / (64 * kWavesT); ++i) {
             const int id = tid + 64 * kWavesT * i, r = id / (HD / 4), j = id % (HD / 4);
@@ -356,29 +385,16 @@ __global__ void __launch_bounds__(64 * kWavesT)
         if (!valid)
             for (int ky = half; ky < a.gh; ky += 2) dh_tab[ky * dgk::kQuery + l32] = 0.0f;
         __syncthreads();
-        auto load_line = [&](int li, float4 (&x)[4], float4 (&y)[4]) {
-            const bool col = li >= nrl;
-            const int p = col ? li - nrl : qy0 + li;   // the line's grid column or row
-            const int nq = col ? nrl : a.gw, nr = col ? a.gw : a.gh;
-            const int v = min(l16, nq - 1);
-            const int tok = col ? (qy0 + v) * a.gw + p : p * a.gw + v;
-            // a slot outside the workgroup reads some staged row; its products are dropped
-            const int r = min(max(tok - q0, 0), kBlockQ - 1);
-            const float* tr = (col ? a.rw + ((size_t)p * a.gw + min(l16, nr - 1)) * HD
-                                   : a.rh + ((size_t)p * a.gh + min(l16, nr - 1)) * HD) + 4 * kq;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                y[c] = *reinterpret_cast<const float4*>(tr + 16 * c);
-                x[c] = *reinterpret_cast<const float4*>(qst + r * HD + 4 * ((4 * c + kq) ^ (r % 16)));
-            }
-        };
-        // kLB lines per round trip: all their loads go out, then their products are formed
-        constexpr int kLB = 3;
         for (int l0 = wave; l0 < nl; l0 += kLB * kWavesT) {   // wave-uniform
-            float4 x[kLB][4], y[kLB][4];
+            if (l0 != wave) {
+#pragma unroll
+                for (int bl = 0; bl < kLB; ++bl)
+                    if (l0 + bl * kWavesT < nl) load_table(l0 + bl * kWavesT, y[bl]);
+            }
+            float4 x[kLB][4];
 #pragma unroll
             for (int bl = 0; bl < kLB; ++bl)
-                if (l0 + bl * kWavesT < nl) load_line(l0 + bl * kWavesT, x[bl], y[bl]);
+                if (l0 + bl * kWavesT < nl) load_query(l0 + bl * kWavesT, x[bl]);
 #pragma unroll
             for (int bl = 0; bl < kLB; ++bl) {
                 const int li = l0 + bl * kWavesT;
