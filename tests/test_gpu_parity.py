@@ -522,6 +522,11 @@ def oracle_windows(c):
                                                    (260, 16, 16, 1, True), (300, 16, 1, 1, True),
                                                    (300, 1, 16, 1, True), (300, 16, 3, 1, True),
                                                    (270, 10, 9, 1, True),
+                                                   # two query blocks per window and head
+                                                   # dispatched full blocks first: an even and an
+                                                   # odd number of workgroups per XCD, and rows
+                                                   # of 15 (two padding slots per key tile)
+                                                   (32, 12, 12, 8, True), (300, 16, 15, 1, True),
                                                    # 8 x 8 query patches
                                                    (2, 16, 48, 1, True)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
