@@ -527,6 +527,10 @@ def oracle_windows(c):
                                                    # odd number of workgroups per XCD, and rows
                                                    # of 15 (two padding slots per key tile)
                                                    (32, 12, 12, 8, True), (300, 16, 15, 1, True),
+                                                   # the 4-wavefront shape on rows wider than 16
+                                                   # (bias rows from the workspace, or the
+                                                   # prologue's dot products without one)
+                                                   (300, 4, 20, 1, True), (260, 8, 24, 1, True),
                                                    # 8 x 8 query patches
                                                    (2, 16, 48, 1, True)])
 @pytest.mark.parametrize("use_ws", [False, True], ids=["inline-bias", "ws"])
