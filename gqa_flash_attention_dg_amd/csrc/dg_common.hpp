@@ -63,6 +63,19 @@ __host__ __device__ inline int xcd_remap(int bid, int n, int nxcd) {
     return (bid % nxcd) * (n / nxcd) + bid / nxcd;
 }
 
+// For launches whose logical workgroups alternate a full and a lighter one (l even: full, l
+// odd: light; two query blocks per unit), the order within each XCD's contiguous range of
+// xcd_remap ids that dispatches that range's full workgroups first: the k-th workgroup to run
+// on an XCD takes the k-th even id of the range while there are any, then the odd ones.  A
+// bijection of [0, n) that keeps every id on its XCD; grids that xcd_remap leaves unchanged
+// (n not a multiple of nxcd) are left unchanged.
+__host__ __device__ inline int full_first(int lid, int n, int nxcd) {
+    if (nxcd < 1 || n % nxcd != 0) return lid;
+    const int m = n / nxcd, j0 = lid % m, base = lid - j0;
+    const int f = base & 1, n0 = (m - f + 1) / 2;   // ids base + f, base + f + 2, ... are even
+    return base + (j0 < n0 ? f + 2 * j0 : (1 - f) + 2 * (j0 - n0));
+}
+
 // Sum of v over each aligned group of N lanes (N = 8 or 16), left in every lane of the group,
 // with DPP lane moves within the lanes' own registers: two quad permutes (lane ^ 1, lane ^ 2),
 // then the mirror within 8 lanes and, for 16, within 16.  Each step adds a value and its

@@ -275,14 +275,10 @@ __global__ void __launch_bounds__(64 * kWavesT)
     char* const planes = reinterpret_cast<char*>(smem + 2 * TL::kFloats);   // kPl only
 
     int lid = xcd_remap(blockIdx.x, a.nblocks, a.nxcd);
-    if (kPl && a.qblocks == 2 && a.nblocks % a.nxcd == 0) {
-        // Two query blocks per (window, head), the second the lighter (196 queries: 128 and
-        // 68).  Within each XCD's range of workgroups, in dispatch order, the first blocks go
-        // out first, so the third workgroups that some CUs receive are light ones.
-        const int m = a.nblocks / a.nxcd, j0 = lid % m, base = lid - j0;
-        const int f = base & 1, n0 = (m - f + 1) / 2;
-        lid = base + (j0 < n0 ? f + 2 * j0 : (1 - f) + 2 * (j0 - n0));
-    }
+    // Two query blocks per (window, head), the second the lighter (196 queries: 128 and 68):
+    // within each XCD the first blocks go out first, so the third workgroups that some CUs
+    // receive are light ones.
+    if (kPl && a.qblocks == 2) lid = dg::full_first(lid, a.nblocks, a.nxcd);
     const int qb = lid % a.qblocks;
     const int unit = lid / a.qblocks;          // win * heads + head
     const int head = unit % a.heads, win = unit / a.heads;
